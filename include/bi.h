@@ -1,0 +1,231 @@
+/*
+ * bi.h -- C ABI of libbi.so: batch-invariant forward-pass kernels for
+ * MI355X (gfx950).
+ *
+ * The property every invariant entry point keeps ("Lockstep", sections "The
+ * fix" and "Proving it"): the bits of output row r depend only on row r's
+ * own inputs (and on the shared weights, or on request r's own KV pages) and
+ * on the call's shape constants other than the batch -- never on how many
+ * other rows share the call, their order, padding, or which physical pages
+ * hold r's KV.  Every reduction runs in one fixed order with split points
+ * fixed by the hidden size or by the request's own KV length.
+ *
+ * Each invariant entry point has a batch-adaptive "free" twin (suffix
+ * _free) that computes the same mathematics but picks its split points and
+ * tiles from the batch and the device's 256 compute units, as ordinary
+ * serving kernels do ("Batch invariance and reproducible inference",
+ * section "From batch size to reduction tree").  The twins exist to price
+ * invariance and to prove the harness notices a batch-dependent kernel.
+ *
+ * Conventions for every function:
+ *  - Pointers named as device data are device pointers (hipMalloc / torch
+ *    CUDA tensors) aligned to 16 bytes; tensors are dense row-major with the
+ *    shapes given.  bf16 data is raw IEEE bfloat16 bits (uint16).  The
+ *    caller owns every buffer; the invariant path allocates nothing.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls
+ *    only enqueue work: a BI_OK return means "launched"; device faults
+ *    surface at the caller's next synchronisation.
+ *  - Arguments are validated on the host before anything is launched.  A
+ *    rejected call launches nothing and returns BI_ERR_INVALID (null
+ *    pointer, bad size), BI_ERR_UNSUPPORTED (a dtype, head size, group
+ *    ratio or chunk the kernels do not implement -- they fail closed rather
+ *    than fall back, as the pages ask of kernels that cannot keep the
+ *    property: "Batch invariance and reproducible inference", the
+ *    fused-MoE opt-out and the Mamba refusal) or BI_ERR_WORKSPACE (a
+ *    workspace that is too small).  BI_ERR_HIP reports a launch error.
+ *    bi_last_error() returns a message for the calling thread's last
+ *    failure.
+ *  - Preconditions that live in device memory (kv_len >= 1, block-table
+ *    entries naming valid pages, positions inside the RoPE tables) are the
+ *    caller's to keep; they are not checked on the device.
+ */
+#ifndef BI_H
+#define BI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int bi_status;
+#define BI_OK 0
+#define BI_ERR_INVALID 1
+#define BI_ERR_UNSUPPORTED 2
+#define BI_ERR_WORKSPACE 3
+#define BI_ERR_HIP 4
+
+/* element types */
+#define BI_F32 0
+#define BI_BF16 1
+
+typedef void *bi_stream; /* hipStream_t */
+
+/* Version of this ABI (changes when a signature changes). */
+int bi_abi_version(void);
+/* Static text for a status code. */
+const char *bi_status_string(bi_status s);
+/* Message of the calling thread's last failed call ("" if none). */
+const char *bi_last_error(void);
+
+/* ---------------------------------------------------------------------- */
+/* RMSNorm                                                                */
+/* ---------------------------------------------------------------------- */
+/*
+ * y[i][:] = x[i][:] * (1 / sqrt(mean_j x[i][j]^2 + eps)) * gamma[:], one
+ * workgroup per row, no cross-workgroup reduction ("Batch invariance and
+ * reproducible inference": rms_norm is one of the dull one-block-per-row
+ * kernels).  Fixed order of the fp32 sum of squares: vectors of 8
+ * consecutive elements; 256 lanes, lane t visits vectors t, t+256, ... with
+ * fma(x, x, acc); each 64-lane wave reduces by xor butterfly 32,16,8,4,2,1;
+ * the four wave sums are added in order.  Then r = 1/sqrt(ss/d + eps) and
+ * y = round((x * r) * gamma), each step correctly rounded.
+ *   x, y   : device [M][d] of `dtype` (y may alias x);  gamma: device [d].
+ *   M >= 0 (0 is a no-op), d >= 1.  dtype BI_F32 or BI_BF16.
+ */
+bi_status bi_rmsnorm(const void *x, const void *gamma, void *y, int M, int d, float eps,
+                     int dtype, bi_stream stream);
+
+/* ---------------------------------------------------------------------- */
+/* GEMM  C = A W^T                                                        */
+/* ---------------------------------------------------------------------- */
+/*
+ * C[i][j] = sum_k A[i][k] W[j][k].  A: device [M][K], W: device [N][K] (the
+ * weight's natural [out][in] layout), C: device [M][N].
+ * in_dtype BI_BF16: out_dtype BI_BF16 or BI_F32; every output element is one
+ * chain of v_mfma_f32_16x16x32_bf16 over K-tiles of 32 in ascending order,
+ * fp32 accumulation, no split of K across workgroups, and the same chain
+ * whatever M is (small M and large M use different tilings of the same
+ * per-element arithmetic) -- "Batch invariance and reproducible inference",
+ * "2 . Cross-block accumulation" (no split-K; one fixed K order per output
+ * tile) and "3 . Kernel selection changing with shape" (nothing that
+ * changes the arithmetic reads M).  K % 8 == 0.
+ * in_dtype BI_F32 (out BI_F32): one serial fp32 fma chain per element over
+ * k ascending.
+ * M >= 0 (0 is a no-op), N >= 1, K >= 1.
+ */
+bi_status bi_gemm(const void *A, const void *W, void *C, int M, int N, int K, int in_dtype,
+                  int out_dtype, bi_stream stream);
+
+/* ---------------------------------------------------------------------- */
+/* split-KV attention over a paged KV cache                               */
+/* ---------------------------------------------------------------------- */
+/*
+ * KV cache layout (both pools): [num_pages][h_kv][page_size][d_h] of
+ * `dtype`; token j of a request lives in page block_table[r][j / page_size]
+ * at slot j % page_size.  block_table: device int32 [B][max_pages].
+ * Query head i reads kv head i / (h / h_kv).
+ *
+ * Chunking ("Lockstep", "The fix": attention split points come from the
+ * request, not the batch; "Batch invariance and reproducible inference",
+ * "1 . Split-K and segmented attention reductions": split count =
+ * ceil(seq_len / split tile) alone or in any batch): request r with
+ * kv_len[r] tokens has ceil(kv_len[r] / kv_chunk) chunks, chunk c covering
+ * absolute positions [c*kv_chunk, min((c+1)*kv_chunk, kv_len[r])).
+ * chunk_off[r] (int32 [B+1], prefix sum of those counts) numbers the
+ * partial rows; bi_chunk_offsets computes it on the host.
+ *
+ * Per (request, query head, chunk) partial, all fp32:
+ *   S_u = fl(q . k_u) * scale (dot: one fma chain over d ascending);
+ *   m = max_u S_u (+0 for -0);  p_u = exp(S_u - m);
+ *   keys in blocks of 64: L_b = serial sum of p_u, A_b[d] = serial
+ *   fma(p_u, v_u[d], .); l = ((L_0 + L_1) + L_2) + ..., acc likewise.
+ * exp is one fixed binary32 routine (Cody-Waite reduction, degree-7 Taylor
+ * polynomial), not the hardware approximation.
+ */
+
+/* Host helper: chunk_off[0] = 0, chunk_off[r+1] = chunk_off[r] +
+ * ceil(kv_len[r] / kv_chunk).  Host arrays.  Returns the total. */
+int bi_chunk_offsets(const int32_t *kv_len_host, int B, int kv_chunk, int32_t *chunk_off_host);
+
+/* Bytes of the partial buffers for `total_chunks` chunk rows:
+ * part_ml = total_chunks * h * 2 floats (m, l), part_acc = total_chunks * h
+ * * d_h floats. */
+size_t bi_attn_partials_bytes(int total_chunks, int h, int d_h);
+
+/*
+ * Decode: one query row per request.  q: device [B][h][d_h] of `dtype`;
+ * kv_len: device int32 [B] (the current token included, >= 1); chunk_off:
+ * device int32 [B+1]; total_chunks == chunk_off[B] (host copy of the last
+ * entry).  Writes part_ml [total_chunks][h][2] and part_acc
+ * [total_chunks][h][d_h] (device fp32).
+ * Supported (anything else returns BI_ERR_UNSUPPORTED): d_h in {64, 128};
+ * h % h_kv == 0 with h/h_kv in {2, 4}; kv_chunk in {64, 256}; page_size in
+ * {16, 32, 64}; dtype BI_F32 or BI_BF16.  Every row of q, k and v is
+ * 16-byte aligned.
+ */
+bi_status bi_decode_attn(const void *q, const void *k_pool, const void *v_pool,
+                         const int32_t *block_table, const int32_t *kv_len,
+                         const int32_t *chunk_off, int B, int total_chunks, int h, int h_kv,
+                         int d_h, int page_size, int max_pages, int kv_chunk, float scale,
+                         int dtype, float *part_ml, float *part_acc, bi_stream stream);
+
+/*
+ * Serial merge of each (request, head) over its chunks in order c = 0..n-1
+ * ("Batch invariance and reproducible inference", "From batch size to
+ * reduction tree": a merge kernel adds the fp32 partials):
+ *   (M, L, Acc) = chunk 0; for c >= 1: M' = max(M, m_c), a = exp(M - M'),
+ *   b = exp(m_c - M'), L = fma(l_c, b, L * a), Acc = fma(acc_c, b, Acc * a);
+ *   out = round(Acc / L).
+ * out: device [B][h][d_h] of out_dtype.
+ */
+bi_status bi_merge_partials(const float *part_ml, const float *part_acc,
+                            const int32_t *chunk_off, int B, int h, int d_h, void *out,
+                            int out_dtype, bi_stream stream);
+
+/*
+ * Causal prefill over packed query rows.  q: device [T][h][d_h]; request r
+ * owns rows q_start[r] .. q_start[r+1]-1 (device int32 [R+1], T ==
+ * q_start[R]); row t sits at absolute position q_pos0[r] + t - q_start[r]
+ * (device int32 [R]) and attends positions 0 .. pos, which must already be
+ * in the cache.  Every row is computed exactly as the decode path computes
+ * a request of kv_len = pos + 1 (same chunks at absolute multiples of
+ * kv_chunk, same partial arithmetic, same serial merge), so a prompt gives
+ * the same bits however it is cut into prefill chunks and whether a
+ * position is produced by prefill or by decode ("Batch invariance and
+ * reproducible inference": chunked prefill must not move split
+ * boundaries).  out: device [T][h][d_h] of `dtype`.  Same support limits as
+ * bi_decode_attn.
+ */
+bi_status bi_prefill_attn(const void *q, const int32_t *q_start, const int32_t *q_pos0, int R,
+                          int T, const void *k_pool, const void *v_pool,
+                          const int32_t *block_table, int h, int h_kv, int d_h, int page_size,
+                          int max_pages, int kv_chunk, float scale, int dtype, void *out,
+                          bi_stream stream);
+
+/* ---------------------------------------------------------------------- */
+/* elementwise glue of a Llama-shaped layer (no reductions)               */
+/* ---------------------------------------------------------------------- */
+
+/* out[i][:] = table[ids[i]][:]; table device [V][d], ids device int32 [M]. */
+bi_status bi_embed(const void *table, const int32_t *ids, void *out, int M, int d, int dtype,
+                   bi_stream stream);
+
+/*
+ * Split a fused QKV row [q (h*d_h) | k (h_kv*d_h) | v (h_kv*d_h)], apply
+ * rotate-half RoPE to q and k at position pos[i] (x'[i] = fma(a, c, -(b*s)),
+ * x'[i+d_h/2] = fma(b, c, a*s) with a = x[i], b = x[i+d_h/2]), write q to
+ * q_out [M][h][d_h] and k, v into the pools at flat slot slot_mapping[i]
+ * (= page * page_size + offset).  cos_t / sin_t: device fp32
+ * [max_pos][d_h/2]; both NULL = no rotation.  Results rounded to `dtype`.
+ */
+bi_status bi_rope_kv_append(const void *qkv, int M, int h, int h_kv, int d_h,
+                            const int32_t *pos, const float *cos_t, const float *sin_t,
+                            const int32_t *slot_mapping, int page_size, void *q_out,
+                            void *k_pool, void *v_pool, int dtype, bi_stream stream);
+
+/* y = round(a + b) elementwise over n elements (y may alias a or b). */
+bi_status bi_add(const void *a, const void *b, void *y, long n, int dtype, bi_stream stream);
+
+/* SwiGLU: gu [M][2F] = [gate | up]; y[i][j] = round(g / (1 + exp(-g)) * u). */
+bi_status bi_silu_mul(const void *gu, void *y, int M, int F, int dtype, bi_stream stream);
+
+/* idx[i] = argmax_j x[i][j] over fp32 x [M][V]; lowest index wins ties. */
+bi_status bi_argmax(const float *x, int32_t *idx, int M, int V, bi_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BI_H */

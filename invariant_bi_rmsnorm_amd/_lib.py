@@ -1,0 +1,208 @@
+"""Thin ctypes binding of libbi.so (include/bi.h).
+
+Argument marshalling only: each function takes torch tensors, checks dtype,
+device and contiguity, and passes raw device pointers, sizes and the current
+HIP stream to the C function of the same name.  Every computation happens in
+the library's HIP kernels.  There is no fallback: if libbi.so is missing or a
+call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbi.so")
+
+BI_OK, BI_ERR_INVALID, BI_ERR_UNSUPPORTED, BI_ERR_WORKSPACE, BI_ERR_HIP = 0, 1, 2, 3, 4
+BI_F32, BI_BF16 = 0, 1
+
+_c_int, _c_long, _c_float, _c_size, _vp = (ctypes.c_int, ctypes.c_long, ctypes.c_float,
+                                          ctypes.c_size_t, ctypes.c_void_p)
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+# name -> (restype, argtypes); mirrors include/bi.h
+SIGNATURES = {
+    "bi_abi_version": (_c_int, []),
+    "bi_status_string": (ctypes.c_char_p, [_c_int]),
+    "bi_last_error": (ctypes.c_char_p, []),
+    "bi_chunk_offsets": (_c_int, [_i32p, _c_int, _c_int, _i32p]),
+    "bi_attn_partials_bytes": (_c_size, [_c_int, _c_int, _c_int]),
+    "bi_rmsnorm": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_float, _c_int, _vp]),
+    "bi_gemm": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
+    "bi_decode_attn": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp] + [_c_int] * 8
+                       + [_c_float, _c_int, _vp, _vp, _vp]),
+    "bi_merge_partials": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _c_int, _vp]),
+    "bi_prefill_attn": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp] + [_c_int] * 6
+                        + [_c_float, _c_int, _vp, _vp]),
+    "bi_embed": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp]),
+    "bi_rope_kv_append": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp,
+                                   _c_int, _vp, _vp, _vp, _c_int, _vp]),
+    "bi_add": (_c_int, [_vp, _vp, _vp, _c_long, _c_int, _vp]),
+    "bi_silu_mul": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _vp]),
+    "bi_argmax": (_c_int, [_vp, _vp, _c_int, _c_int, _vp]),
+}
+
+_lib = None
+
+
+class BiError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {status} ({msg})")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libbi.so (built in-tree by invariant_bi_rmsnorm_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run invariant_bi_rmsnorm_amd/build.py "
+                               "(or __graft_entry__.build()) first; there is no fallback")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != BI_OK:
+        msg = load().bi_last_error().decode()
+        raise BiError(fn, status, msg)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BI_BF16
+    if t.dtype == torch.float32:
+        return BI_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _i32(t: torch.Tensor):
+    if t.dtype != torch.int32:
+        raise TypeError(f"expected int32, got {t.dtype}")
+    return _ptr(t)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+# ---------------------------------------------------------------------------
+
+def bi_abi_version() -> int:
+    return load().bi_abi_version()
+
+
+def bi_chunk_offsets(kv_len_host, kv_chunk: int) -> torch.Tensor:
+    """Host helper: int32 [B+1] prefix sum of ceil(kv_len / kv_chunk)."""
+    kv = torch.as_tensor(kv_len_host, dtype=torch.int32).contiguous().cpu()
+    out = torch.zeros(kv.numel() + 1, dtype=torch.int32)
+    n = load().bi_chunk_offsets(ctypes.cast(kv.data_ptr(), _i32p), kv.numel(), kv_chunk,
+                                ctypes.cast(out.data_ptr(), _i32p))
+    if n < 0:
+        raise BiError("bi_chunk_offsets", BI_ERR_INVALID, "bad arguments")
+    return out
+
+
+def bi_attn_partials_bytes(total_chunks: int, h: int, d_h: int) -> int:
+    return load().bi_attn_partials_bytes(total_chunks, h, d_h)
+
+
+def bi_rmsnorm(x, gamma, y, eps: float, stream=None):
+    M, d = (x.shape[0], x.shape[-1]) if x.dim() == 2 else (x.numel() // x.shape[-1], x.shape[-1])
+    _check("bi_rmsnorm", load().bi_rmsnorm(_ptr(x), _ptr(gamma), _ptr(y), M, d, eps, _dt(x),
+                                           _stream(stream)))
+    return y
+
+
+def bi_gemm(A, W, C, stream=None):
+    M, K = A.shape
+    N = W.shape[0]
+    if W.shape[1] != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch A{tuple(A.shape)} W{tuple(W.shape)} C{tuple(C.shape)}")
+    _check("bi_gemm", load().bi_gemm(_ptr(A), _ptr(W), _ptr(C), M, N, K, _dt(A), _dt(C),
+                                     _stream(stream)))
+    return C
+
+
+def bi_decode_attn(q, k_pool, v_pool, block_table, kv_len, chunk_off, total_chunks: int,
+                   kv_chunk: int, scale: float, part_ml, part_acc, stream=None):
+    B, h, d_h = q.shape
+    _, h_kv, page_size, _ = k_pool.shape
+    _check("bi_decode_attn", load().bi_decode_attn(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _i32(block_table), _i32(kv_len), _i32(chunk_off),
+        B, total_chunks, h, h_kv, d_h, page_size, block_table.shape[1], kv_chunk, scale, _dt(q),
+        _ptr(part_ml), _ptr(part_acc), _stream(stream)))
+
+
+def bi_merge_partials(part_ml, part_acc, chunk_off, out, stream=None):
+    B, h, d_h = out.shape
+    _check("bi_merge_partials", load().bi_merge_partials(
+        _ptr(part_ml), _ptr(part_acc), _i32(chunk_off), B, h, d_h, _ptr(out), _dt(out),
+        _stream(stream)))
+    return out
+
+
+def bi_prefill_attn(q, q_start, q_pos0, k_pool, v_pool, block_table, kv_chunk: int,
+                    scale: float, out, stream=None):
+    T, h, d_h = q.shape
+    _, h_kv, page_size, _ = k_pool.shape
+    R = q_pos0.numel()
+    _check("bi_prefill_attn", load().bi_prefill_attn(
+        _ptr(q), _i32(q_start), _i32(q_pos0), R, T, _ptr(k_pool), _ptr(v_pool),
+        _i32(block_table), h, h_kv, d_h, page_size, block_table.shape[1], kv_chunk, scale,
+        _dt(q), _ptr(out), _stream(stream)))
+    return out
+
+
+def bi_embed(table, ids, out, stream=None):
+    M, d = out.shape
+    _check("bi_embed", load().bi_embed(_ptr(table), _i32(ids), _ptr(out), M, d, _dt(table),
+                                       _stream(stream)))
+    return out
+
+
+def bi_rope_kv_append(qkv, h: int, h_kv: int, d_h: int, pos, cos_t, sin_t, slot_mapping,
+                      q_out, k_pool, v_pool, stream=None):
+    M = qkv.shape[0]
+    page_size = k_pool.shape[2]
+    _check("bi_rope_kv_append", load().bi_rope_kv_append(
+        _ptr(qkv), M, h, h_kv, d_h, _i32(pos) if pos is not None else None, _ptr(cos_t),
+        _ptr(sin_t), _i32(slot_mapping), page_size, _ptr(q_out), _ptr(k_pool), _ptr(v_pool),
+        _dt(qkv), _stream(stream)))
+
+
+def bi_add(a, b, y, stream=None):
+    _check("bi_add", load().bi_add(_ptr(a), _ptr(b), _ptr(y), a.numel(), _dt(a), _stream(stream)))
+    return y
+
+
+def bi_silu_mul(gu, y, stream=None):
+    M, F = y.shape
+    _check("bi_silu_mul", load().bi_silu_mul(_ptr(gu), _ptr(y), M, F, _dt(gu), _stream(stream)))
+    return y
+
+
+def bi_argmax(x, idx, stream=None):
+    M, V = x.shape
+    _check("bi_argmax", load().bi_argmax(_ptr(x), _i32(idx), M, V, _stream(stream)))
+    return idx

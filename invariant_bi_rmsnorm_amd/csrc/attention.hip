@@ -1,0 +1,658 @@
+// Split-KV attention over a paged KV cache with request-derived split points.
+//
+// "Lockstep", "The fix": attention split points come from the request, not
+// the batch.  "Batch invariance and reproducible inference", "1 . Split-K
+// and segmented attention reductions": the split count is ceil(seq_len /
+// split tile) whatever else is in the batch, and "From batch size to
+// reduction tree": the fp32 partials of the splits are added by a merge.
+//
+// Chunk c of a request covers absolute positions [c*C, min((c+1)*C, s)).
+// One workgroup of C/64 waves computes one (chunk, kv head) partial for the
+// R query heads of that kv head:
+//   QK  lane-per-key: lane u of wave w owns key 64w+u; its K row sits in LDS
+//       (copied there by direct global->LDS copies, 16-byte columns XOR-
+//       swizzled by the key index so lanes reading the same column hit
+//       different banks); S = fl(dot) * scale with the dot one fma chain
+//       over d ascending, q broadcast from LDS as fp32.
+//   max over the chunk (exact, any order), +0 for -0; p = exp_fixed(S - m).
+//   PV  lane-per-dim: lane l owns dims [DPL*l, DPL*l+DPL) and keeps the V of
+//       its wave's 64 keys in registers; within the wave (= a block of 64
+//       keys) l and acc are serial sums over keys ascending (acc by fma).
+//   blocks are added in wave order: ((B0 + B1) + B2) + B3.
+// Prefill runs the same device code per query row and merges the chunks on
+// the fly with the merge kernel's formula, so prefill row t equals a decode
+// of kv_len = t + 1 bit for bit.
+#include "api.h"
+#include "common.h"
+
+namespace bi {
+
+template <int DT, int DH>
+struct AttnShape {
+  static constexpr int ES = Elem<DT>::bytes;
+  static constexpr int RB = DH * ES;          // bytes per K/V row
+  static constexpr int SLOTS = RB / 16;       // 16-byte columns per row
+  static constexpr int EPS = 16 / ES;         // elements per column
+  static constexpr int SW = SLOTS < 16 ? SLOTS : 16;  // swizzle width
+  static constexpr int KPI = 1024 / RB;       // keys per 1 KiB wave copy
+  static constexpr int DPL = DH / 64;         // V elements per lane
+  static constexpr int VW = (DPL * ES + 3) / 4;  // 32-bit registers per key for V
+  static_assert(RB % 16 == 0 && 1024 % RB == 0, "row size");
+};
+
+// byte offset of (key u, column c) in the swizzled K block
+template <int DT, int DH>
+__device__ __forceinline__ int kswz(int u, int c) {
+  typedef AttnShape<DT, DH> S;
+  return u * S::RB + 16 * (c ^ (u & (S::SW - 1)));
+}
+
+// LDS layout of one attention workgroup
+template <int DT, int DH, int R, int NW>
+struct AttnLds {
+  static constexpr int KEYS = 64 * NW;
+  static constexpr int K_BYTES = KEYS * AttnShape<DT, DH>::RB;
+  static constexpr int Q_OFF = K_BYTES;                        // fp32 q [R][DH]
+  static constexpr int P_OFF = Q_OFF + R * DH * 4;             // fp32 p [KEYS][R]
+  static constexpr int MX_OFF = P_OFF + KEYS * R * 4;          // fp32 [NW][R]
+  static constexpr int CB_OFF = MX_OFF + NW * R * 4;           // fp32 [NW][R][DH+1]
+  static constexpr int BYTES = CB_OFF + NW * R * (DH + 1) * 4;
+};
+
+// Per-thread result of a chunk: thread tid (< R*DH/DPL... see owner map)
+// holds, for the (head, dim) pairs it owns after the block combine, the
+// chunk's m, l and acc.  Owner map: pair index q = tid + 64*NW*k covers
+// head q / (DH/DPL... ) -- implemented as: head = q / DH_LANES, lane-dims.
+template <int R, int NW, int DPL>
+struct ChunkOut {
+  static constexpr int NT = 64 * NW;
+  static constexpr int SLOTS_PER_HEAD = 64;            // DPL dims per slot
+  static constexpr int ITEMS = (R * 64 + NT - 1) / NT; // (head, lane) items per thread
+  float m[ITEMS], l[ITEMS], acc[ITEMS][DPL];
+};
+
+// Computes the partial of keys [j0, j0 + n) (1 <= n <= 64*NW) of kv head g
+// for the R query heads whose q vectors are already in LDS (fp32).  The K
+// block must be fully copied (this wave's part) before the call; vregs holds
+// this lane's V dims for the wave's 64 keys.  All threads of the workgroup
+// call it.  Result: item k of thread tid is (head, lane) = divmod(tid + NT*k,
+// 64), lane owning dims [DPL*lane, DPL*lane + DPL).
+// V element e of this lane's packed V registers for one key
+template <int DT, int DH>
+__device__ __forceinline__ float v_elem(const uint32_t* v, int e) {
+  if (DT == 1) return (AttnShape<DT, DH>::DPL == 2 && e == 1) ? bf16_hi(v[0]) : bf16_lo(v[0]);
+  return __uint_as_float(v[e]);
+}
+
+template <int DT, int DH, int R, int NW>
+__device__ __forceinline__ void chunk_partial(char* lds, int n, float scale,
+                                              const uint32_t (&vreg)[64][AttnShape<DT, DH>::VW],
+                                              ChunkOut<R, NW, AttnShape<DT, DH>::DPL>& out) {
+  typedef AttnShape<DT, DH> S;
+  typedef AttnLds<DT, DH, R, NW> L;
+  constexpr int DPL = S::DPL;
+  constexpr int NT = 64 * NW;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int u = tid;  // this lane's key within the chunk
+  const float* qs = reinterpret_cast<const float*>(lds + L::Q_OFF);
+  float* ps = reinterpret_cast<float*>(lds + L::P_OFF);
+  float* mx = reinterpret_cast<float*>(lds + L::MX_OFF);
+  float* cb = reinterpret_cast<float*>(lds + L::CB_OFF);
+
+  // ---- QK, lane per key
+  float sc[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) sc[i] = 0.0f;
+  const bool valid = u < n;
+  if (valid) {
+    const char* krow = lds;
+#pragma unroll
+    for (int c = 0; c < S::SLOTS; ++c) {
+      const uint4 w = *reinterpret_cast<const uint4*>(krow + kswz<DT, DH>(u, c));
+      float kv[S::EPS];
+      if (DT == 1) {
+        kv[0] = bf16_lo(w.x); kv[1] = bf16_hi(w.x); kv[2] = bf16_lo(w.y); kv[3] = bf16_hi(w.y);
+        kv[4] = bf16_lo(w.z); kv[5] = bf16_hi(w.z); kv[6] = bf16_lo(w.w); kv[7] = bf16_hi(w.w);
+      } else {
+        kv[0] = __uint_as_float(w.x); kv[1] = __uint_as_float(w.y);
+        kv[2] = __uint_as_float(w.z); kv[3] = __uint_as_float(w.w);
+      }
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const float4* qv = reinterpret_cast<const float4*>(qs + i * DH + c * S::EPS);
+#pragma unroll
+        for (int e4 = 0; e4 < S::EPS / 4; ++e4) {
+          const float4 q4 = qv[e4];
+          sc[i] = __builtin_fmaf(q4.x, kv[4 * e4 + 0], sc[i]);
+          sc[i] = __builtin_fmaf(q4.y, kv[4 * e4 + 1], sc[i]);
+          sc[i] = __builtin_fmaf(q4.z, kv[4 * e4 + 2], sc[i]);
+          sc[i] = __builtin_fmaf(q4.w, kv[4 * e4 + 3], sc[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) sc[i] = sc[i] * scale;
+  }
+  // ---- chunk max (exact in any order)
+  float m[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    float v = valid ? sc[i] : -__builtin_inff();
+    v = fmaxf(v, __shfl_xor(v, 32));
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 8));
+    v = fmaxf(v, __shfl_xor(v, 4));
+    v = fmaxf(v, __shfl_xor(v, 2));
+    v = fmaxf(v, __shfl_xor(v, 1));
+    m[i] = v;
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) mx[wave * R + i] = m[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    float v = mx[i];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v = fmaxf(v, mx[w * R + i]);
+    m[i] = v + 0.0f;
+  }
+  // ---- p = exp(S - m), published for the wave's PV loop
+  if (valid) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) ps[u * R + i] = exp_fixed(sc[i] - m[i]);
+  }
+  // the PV loop of a wave reads only its own keys' p: wave-local order suffices
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // ---- PV, lane per dim, serial over this wave's keys
+  const int nk = min(64, n - 64 * wave);  // keys of this block (may be <= 0)
+  float lsum[R], acc[R][DPL];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    lsum[i] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[i][e] = 0.0f;
+  }
+#pragma unroll
+  for (int k = 0; k < 64; ++k) {
+    if (k < nk) {
+      const float* pk = ps + (64 * wave + k) * R;
+      float pv[R];
+      if (R % 4 == 0) {
+#pragma unroll
+        for (int i4 = 0; i4 < R / 4; ++i4) {
+          const float4 t = reinterpret_cast<const float4*>(pk)[i4];
+          pv[4 * i4] = t.x; pv[4 * i4 + 1] = t.y; pv[4 * i4 + 2] = t.z; pv[4 * i4 + 3] = t.w;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < R; ++i) pv[i] = pk[i];
+      }
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        lsum[i] = lsum[i] + pv[i];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e)
+          acc[i][e] = __builtin_fmaf(pv[i], v_elem<DT, DH>(vreg[k], e), acc[i][e]);
+      }
+    }
+  }
+  // ---- publish block partials, combine blocks in wave order
+  constexpr int CBS = DH + 1;  // floats per (wave, head)
+  if (nk > 0) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      float* dst = cb + (wave * R + i) * CBS;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) dst[DPL * lane + e] = acc[i][e];
+      if (lane == 0) dst[DH] = lsum[i];
+    }
+  }
+  __syncthreads();
+  const int nb = (n + 63) >> 6;
+  typedef ChunkOut<R, NW, DPL> CO;
+#pragma unroll
+  for (int k = 0; k < CO::ITEMS; ++k) {
+    const int item = tid + NT * k;
+    if (item < R * 64) {
+      const int hi = item >> 6, ln = item & 63;
+      float l = cb[hi * CBS + DH];
+      float a[DPL];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) a[e] = cb[hi * CBS + DPL * ln + e];
+      for (int b = 1; b < nb; ++b) {
+        const float* src = cb + (b * R + hi) * CBS;
+        l = l + src[DH];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) a[e] = a[e] + src[DPL * ln + e];
+      }
+      out.m[k] = m[hi];
+      out.l[k] = l;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) out.acc[k][e] = a[e];
+    }
+  }
+  __syncthreads();  // LDS (p, block partials, K) may be reused by the caller
+}
+
+// Stage this wave's 64 keys of the chunk (keys [j0, j0+n)) of kv head g:
+// K rows into the swizzled LDS block by direct copies, and this lane's V
+// dims into registers.  Keys >= n read key j0 instead (valid memory, never
+// used).  page_size is a multiple of the keys one copy covers and divides 64,
+// so every page index below is wave-uniform and comes from scalar loads.
+template <int DT, int DH, int NW>
+__device__ __forceinline__ void stage_chunk(char* lds, const void* k_pool, const void* v_pool,
+                                            const int32_t* bt, int j0, int n, int g, int h_kv,
+                                            int page_size,
+                                            uint32_t (&vreg)[64][AttnShape<DT, DH>::VW]) {
+  typedef AttnShape<DT, DH> S;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wk0 = 64 * wave;           // first key of this wave in the chunk
+  const int nk = min(64, n - wk0);     // keys of this wave (may be <= 0)
+  const int np = 64 / page_size;       // pages per wave
+  const int pg0 = (j0 + wk0) / page_size;
+  const long hstride = (long)page_size * S::RB;  // bytes per (page, head) block
+  const long pstride = hstride * h_kv;           // bytes per page
+  const char* kp = static_cast<const char*>(k_pool) + g * hstride;
+  const char* vp = static_cast<const char*>(v_pool) + g * hstride;
+  const int pfall = bt[j0 / page_size];  // page of key j0, stands in for missing keys
+  // K: one 1 KiB copy covers KPI consecutive keys of one page
+#pragma unroll
+  for (int inst = 0; inst < 64 / S::KPI; ++inst) {
+    const int k0 = inst * S::KPI;                    // first key of this copy
+    const int pi = k0 / page_size;                   // uniform
+    const int page = (k0 < nk) ? bt[pg0 + pi] : pfall;
+    const int kk = k0 + lane / S::SLOTS;             // key of this lane
+    const int slot = (k0 < nk) ? (kk % page_size) : 0;
+    const int u = wk0 + kk;                          // key index in the chunk
+    const int c = (lane % S::SLOTS) ^ (u & (S::SW - 1));
+    dma16(kp + page * pstride + slot * S::RB + 16 * c, lds + (wk0 + k0) * S::RB);
+  }
+  // V: lane-per-dim, one row per key of this wave, kept packed
+  const long lane_off = (long)lane * S::DPL * S::ES;
+  int page = pfall;
+#pragma unroll
+  for (int k = 0; k < 64; ++k) {
+    if (k % page_size == 0) page = (k < nk) ? bt[pg0 + k / page_size] : pfall;
+    const int slot = (k < nk) ? (k % page_size) : 0;
+    const char* src = vp + page * pstride + slot * S::RB + lane_off;
+    if (S::DPL * S::ES == 2) {
+      vreg[k][0] = *reinterpret_cast<const uint16_t*>(src);
+    } else {
+#pragma unroll
+      for (int e = 0; e < S::VW; ++e) vreg[k][e] = reinterpret_cast<const uint32_t*>(src)[e];
+    }
+  }
+  (void)np;
+}
+
+// q vectors of the R heads of group g of one row -> LDS as fp32
+template <int DT, int DH, int R, int NW>
+__device__ __forceinline__ void stage_q(char* lds, const void* q, long qrow_elem) {
+  typedef AttnLds<DT, DH, R, NW> L;
+  float* qs = reinterpret_cast<float*>(lds + L::Q_OFF);
+  for (int i = threadIdx.x; i < R * DH; i += 64 * NW) qs[i] = Elem<DT>::ld(q, qrow_elem + i);
+}
+
+// ---------------------------------------------------------------------------
+// decode partials: grid (total_chunks, h_kv)
+// ---------------------------------------------------------------------------
+template <int DT, int DH, int R, int NW>
+__global__ __launch_bounds__(64 * NW) void k_decode_partials(
+    const void* __restrict__ q, const void* __restrict__ k_pool, const void* __restrict__ v_pool,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ kv_len,
+    const int32_t* __restrict__ chunk_off, int B, int h, int h_kv, int page_size, int max_pages,
+    float scale, float* __restrict__ part_ml, float* __restrict__ part_acc) {
+  typedef AttnShape<DT, DH> S;
+  typedef ChunkOut<R, NW, S::DPL> CO;
+  constexpr int C = 64 * NW;
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int crow = blockIdx.x, g = blockIdx.y;
+  // request owning this chunk row: largest r with chunk_off[r] <= crow
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (chunk_off[mid] <= crow) lo = mid; else hi = mid - 1;
+  }
+  const int r = lo;
+  const int c = crow - chunk_off[r];
+  const int j0 = c * C;
+  const int n = min(C, kv_len[r] - j0);
+  const int32_t* bt = block_table + (long)r * max_pages;
+
+  uint32_t vreg[64][S::VW];
+  stage_chunk<DT, DH, NW>(lds, k_pool, v_pool, bt, j0, n, g, h_kv, page_size, vreg);
+  stage_q<DT, DH, R, NW>(lds, q, ((long)r * h + g * R) * DH);
+  __syncthreads();
+  CO out;
+  chunk_partial<DT, DH, R, NW>(lds, n, scale, vreg, out);
+#pragma unroll
+  for (int k = 0; k < CO::ITEMS; ++k) {
+    const int item = threadIdx.x + 64 * NW * k;
+    if (item < R * 64) {
+      const int hi2 = item >> 6, ln = item & 63;
+      const long prow = (long)crow * h + g * R + hi2;
+      if (ln == 0) {
+        part_ml[2 * prow] = out.m[k];
+        part_ml[2 * prow + 1] = out.l[k];
+      }
+#pragma unroll
+      for (int e = 0; e < S::DPL; ++e) part_acc[prow * DH + S::DPL * ln + e] = out.acc[k][e];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// serial merge: one wave per (request, head); lane owns DH/64 dims
+// ---------------------------------------------------------------------------
+template <int DH, int OUT_DT>
+__global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part_ml,
+                                               const float* __restrict__ part_acc,
+                                               const int32_t* __restrict__ chunk_off, int B,
+                                               int h, void* __restrict__ out) {
+  constexpr int DPL = DH / 64;
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wid >= B * h) return;
+  const int r = wid / h, hi = wid % h;
+  const int c0 = chunk_off[r], n = chunk_off[r + 1] - c0;
+  long row = (long)c0 * h + hi;
+  float M = part_ml[2 * row], L = part_ml[2 * row + 1];
+  float A[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) A[e] = part_acc[row * DH + DPL * lane + e];
+  for (int c = 1; c < n; ++c) {
+    row += h;
+    const float mc = part_ml[2 * row], lc = part_ml[2 * row + 1];
+    const float Mn = M > mc ? M : mc;
+    const float a = exp_fixed(M - Mn), b = exp_fixed(mc - Mn);
+    L = __builtin_fmaf(lc, b, L * a);
+#pragma unroll
+    for (int e = 0; e < DPL; ++e)
+      A[e] = __builtin_fmaf(part_acc[row * DH + DPL * lane + e], b, A[e] * a);
+    M = Mn;
+  }
+  const long o = ((long)r * h + hi) * DH + DPL * lane;
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) Elem<OUT_DT>::st(out, o + e, A[e] / L);
+}
+
+// ---------------------------------------------------------------------------
+// prefill: grid (ceil(T / QB), h_kv).  A workgroup takes QB consecutive
+// rows of one request (a block never straddles requests: rows are assigned
+// per request in blocks of QB), stages each chunk once and runs every row's
+// partial, merging serially into per-row running state.
+// ---------------------------------------------------------------------------
+template <int DT, int DH, int R, int NW, int QB>
+__global__ __launch_bounds__(64 * NW) void k_prefill(
+    const void* __restrict__ q, const int32_t* __restrict__ q_start,
+    const int32_t* __restrict__ q_pos0, int Rq,
+    const void* __restrict__ k_pool, const void* __restrict__ v_pool,
+    const int32_t* __restrict__ block_table, int h, int h_kv, int page_size, int max_pages,
+    float scale, void* __restrict__ out) {
+  typedef AttnShape<DT, DH> S;
+  typedef ChunkOut<R, NW, S::DPL> CO;
+  constexpr int C = 64 * NW;
+  constexpr int DPL = S::DPL;
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int blk = blockIdx.x, g = blockIdx.y;
+  // request of this block: rows are cut into blocks of QB per request, in
+  // request order; the grid is an upper bound and surplus blocks exit
+  int r = -1, first = 0;
+  for (int i = 0; i < Rq; ++i) {
+    const int nb = (q_start[i + 1] - q_start[i] + QB - 1) / QB;
+    if (blk < first + nb) { r = i; break; }
+    first += nb;
+  }
+  if (r < 0) return;
+  const int t0 = q_start[r] + (blk - first) * QB;
+  const int t1 = min(t0 + QB, q_start[r + 1]);
+  if (t0 >= t1) return;
+  const int pos0 = q_pos0[r] + (t0 - q_start[r]);
+  const int pos_last = pos0 + (t1 - t0) - 1;
+  const int32_t* bt = block_table + (long)r * max_pages;
+
+  float Mr[QB][CO::ITEMS], Lr[QB][CO::ITEMS], Ar[QB][CO::ITEMS][DPL];
+  const int nch = pos_last / C + 1;
+  for (int c = 0; c < nch; ++c) {
+    const int j0 = c * C;
+    const int nmax = min(C, pos_last + 1 - j0);
+    uint32_t vreg[64][S::VW];
+    stage_chunk<DT, DH, NW>(lds, k_pool, v_pool, bt, j0, nmax, g, h_kv, page_size, vreg);
+#pragma unroll
+    for (int qi = 0; qi < QB; ++qi) {
+      const int t = t0 + qi;
+      if (t < t1) {
+        const int pos = pos0 + qi;
+        const int n = pos + 1 - j0;  // keys of this chunk visible to row t
+        if (n > 0) {               // uniform across the workgroup
+          stage_q<DT, DH, R, NW>(lds, q, ((long)t * h + g * R) * DH);
+          __syncthreads();
+          CO co;
+          chunk_partial<DT, DH, R, NW>(lds, min(n, C), scale, vreg, co);
+#pragma unroll
+          for (int k = 0; k < CO::ITEMS; ++k) {
+            if (c == 0) {
+              Mr[qi][k] = co.m[k];
+              Lr[qi][k] = co.l[k];
+#pragma unroll
+              for (int e = 0; e < DPL; ++e) Ar[qi][k][e] = co.acc[k][e];
+            } else {
+              const float M = Mr[qi][k], mc = co.m[k];
+              const float Mn = M > mc ? M : mc;
+              const float a = exp_fixed(M - Mn), b = exp_fixed(mc - Mn);
+              Lr[qi][k] = __builtin_fmaf(co.l[k], b, Lr[qi][k] * a);
+#pragma unroll
+              for (int e = 0; e < DPL; ++e)
+                Ar[qi][k][e] = __builtin_fmaf(co.acc[k][e], b, Ar[qi][k][e] * a);
+              Mr[qi][k] = Mn;
+            }
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int qi = 0; qi < QB; ++qi) {
+    const int t = t0 + qi;
+    if (t < t1) {
+#pragma unroll
+      for (int k = 0; k < CO::ITEMS; ++k) {
+        const int item = threadIdx.x + 64 * NW * k;
+        if (item < R * 64) {
+          const int hi2 = item >> 6, ln = item & 63;
+          const long o = ((long)t * h + g * R + hi2) * DH + DPL * ln;
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) Elem<DT>::st(out, o + e, Ar[qi][k][e] / Lr[qi][k]);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+struct AttnArgsCheck {
+  static bi_status common(const char* who, int h, int h_kv, int d_h, int page_size,
+                          int kv_chunk, int dtype) {
+    BI_REQUIRE(h >= 1 && h_kv >= 1 && h % h_kv == 0, BI_ERR_INVALID,
+               "%s: h=%d must be a positive multiple of h_kv=%d", who, h, h_kv);
+    const int R = h / h_kv;
+    BI_REQUIRE(R == 2 || R == 4, BI_ERR_UNSUPPORTED, "%s: query group size %d not in {2,4}",
+               who, R);
+    BI_REQUIRE(d_h == 64 || d_h == 128, BI_ERR_UNSUPPORTED, "%s: d_h=%d not in {64,128}", who,
+               d_h);
+    BI_REQUIRE(dtype == BI_F32 || dtype == BI_BF16, BI_ERR_UNSUPPORTED, "%s: dtype %d", who,
+               dtype);
+    BI_REQUIRE(kv_chunk == 64 || kv_chunk == 256, BI_ERR_UNSUPPORTED,
+               "%s: kv_chunk=%d not in {64,256}", who, kv_chunk);
+    BI_REQUIRE(page_size == 16 || page_size == 32 || page_size == 64, BI_ERR_UNSUPPORTED,
+               "%s: page_size=%d not in {16,32,64}", who, page_size);
+    return BI_OK;
+  }
+};
+
+template <int DT, int DH, int R, int NW>
+static void launch_decode(const void* q, const void* kp, const void* vp, const int32_t* bt,
+                          const int32_t* kvl, const int32_t* off, int B, int tot, int h,
+                          int h_kv, int ps, int mp, float scale, float* ml, float* acc,
+                          hipStream_t s) {
+  constexpr int lds = AttnLds<DT, DH, R, NW>::BYTES;
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)k_decode_partials<DT, DH, R, NW>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    attr = true;
+  }
+  hipLaunchKernelGGL((k_decode_partials<DT, DH, R, NW>), dim3(tot, h_kv), dim3(64 * NW), lds, s,
+                     q, kp, vp, bt, kvl, off, B, h, h_kv, ps, mp, scale, ml, acc);
+}
+
+template <int DT, int DH, int R>
+static void decode_nw(int nw, const void* q, const void* kp, const void* vp, const int32_t* bt,
+                      const int32_t* kvl, const int32_t* off, int B, int tot, int h, int h_kv,
+                      int ps, int mp, float scale, float* ml, float* acc, hipStream_t s) {
+  if (nw == 1) launch_decode<DT, DH, R, 1>(q, kp, vp, bt, kvl, off, B, tot, h, h_kv, ps, mp, scale, ml, acc, s);
+  else launch_decode<DT, DH, R, 4>(q, kp, vp, bt, kvl, off, B, tot, h, h_kv, ps, mp, scale, ml, acc, s);
+}
+
+template <int DT, int DH>
+static void decode_r(int R, int nw, const void* q, const void* kp, const void* vp,
+                     const int32_t* bt, const int32_t* kvl, const int32_t* off, int B, int tot,
+                     int h, int h_kv, int ps, int mp, float scale, float* ml, float* acc,
+                     hipStream_t s) {
+  if (R == 2) decode_nw<DT, DH, 2>(nw, q, kp, vp, bt, kvl, off, B, tot, h, h_kv, ps, mp, scale, ml, acc, s);
+  else decode_nw<DT, DH, 4>(nw, q, kp, vp, bt, kvl, off, B, tot, h, h_kv, ps, mp, scale, ml, acc, s);
+}
+
+constexpr int kPrefillQB = 8;
+
+template <int DT, int DH, int R, int NW>
+static void launch_prefill(const void* q, const int32_t* qs, const int32_t* qp, int Rq, int T,
+                           const void* kp, const void* vp, const int32_t* bt, int h, int h_kv,
+                           int ps, int mp, float scale, void* out, hipStream_t s) {
+  constexpr int lds = AttnLds<DT, DH, R, NW>::BYTES;
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)k_prefill<DT, DH, R, NW, kPrefillQB>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    attr = true;
+  }
+  const int blocks = (T + kPrefillQB - 1) / kPrefillQB + Rq;
+  hipLaunchKernelGGL((k_prefill<DT, DH, R, NW, kPrefillQB>), dim3(blocks, h_kv), dim3(64 * NW),
+                     lds, s, q, qs, qp, Rq, kp, vp, bt, h, h_kv, ps, mp, scale, out);
+}
+
+template <int DT, int DH, int R>
+static void prefill_nw(int nw, const void* q, const int32_t* qs, const int32_t* qp, int Rq, int T,
+                       const void* kp, const void* vp, const int32_t* bt, int h, int h_kv, int ps,
+                       int mp, float scale, void* out, hipStream_t s) {
+  if (nw == 1) launch_prefill<DT, DH, R, 1>(q, qs, qp, Rq, T, kp, vp, bt, h, h_kv, ps, mp, scale, out, s);
+  else launch_prefill<DT, DH, R, 4>(q, qs, qp, Rq, T, kp, vp, bt, h, h_kv, ps, mp, scale, out, s);
+}
+
+template <int DT, int DH>
+static void prefill_r(int R, int nw, const void* q, const int32_t* qs, const int32_t* qp, int Rq,
+                      int T, const void* kp, const void* vp, const int32_t* bt, int h, int h_kv,
+                      int ps, int mp, float scale, void* out, hipStream_t s) {
+  if (R == 2) prefill_nw<DT, DH, 2>(nw, q, qs, qp, Rq, T, kp, vp, bt, h, h_kv, ps, mp, scale, out, s);
+  else prefill_nw<DT, DH, 4>(nw, q, qs, qp, Rq, T, kp, vp, bt, h, h_kv, ps, mp, scale, out, s);
+}
+
+}  // namespace bi
+
+extern "C" bi_status bi_prefill_attn(const void* q, const int32_t* q_start,
+                                     const int32_t* q_pos0, int R, int T, const void* k_pool,
+                                     const void* v_pool, const int32_t* block_table, int h,
+                                     int h_kv, int d_h, int page_size, int max_pages,
+                                     int kv_chunk, float scale, int dtype, void* out,
+                                     bi_stream stream) {
+  using namespace bi;
+  bi_status st = AttnArgsCheck::common("bi_prefill_attn", h, h_kv, d_h, page_size, kv_chunk,
+                                       dtype);
+  if (st != BI_OK) return st;
+  BI_REQUIRE(R >= 0 && T >= 0 && max_pages >= 1, BI_ERR_INVALID,
+             "bi_prefill_attn: bad sizes R=%d T=%d max_pages=%d", R, T, max_pages);
+  BI_REQUIRE(kv_chunk % page_size == 0, BI_ERR_UNSUPPORTED,
+             "bi_prefill_attn: page_size %d must divide kv_chunk %d", page_size, kv_chunk);
+  if (R == 0 || T == 0) return BI_OK;
+  BI_REQUIRE(q && q_start && q_pos0 && k_pool && v_pool && block_table && out, BI_ERR_INVALID,
+             "bi_prefill_attn: null pointer");
+  BI_REQUIRE(aligned16(q) && aligned16(k_pool) && aligned16(v_pool) && aligned16(out),
+             BI_ERR_INVALID, "bi_prefill_attn: pointers must be 16-byte aligned");
+  BI_REQUIRE((long)T / kPrefillQB + R < 0x7fffffffL && h_kv <= 65535, BI_ERR_INVALID,
+             "bi_prefill_attn: grid too large");
+  const int Rg = h / h_kv, nw = kv_chunk / 64;
+  hipStream_t s = as_stream(stream);
+  if (dtype == BI_BF16) {
+    if (d_h == 128) prefill_r<1, 128>(Rg, nw, q, q_start, q_pos0, R, T, k_pool, v_pool, block_table, h, h_kv, page_size, max_pages, scale, out, s);
+    else prefill_r<1, 64>(Rg, nw, q, q_start, q_pos0, R, T, k_pool, v_pool, block_table, h, h_kv, page_size, max_pages, scale, out, s);
+  } else {
+    if (d_h == 128) prefill_r<0, 128>(Rg, nw, q, q_start, q_pos0, R, T, k_pool, v_pool, block_table, h, h_kv, page_size, max_pages, scale, out, s);
+    else prefill_r<0, 64>(Rg, nw, q, q_start, q_pos0, R, T, k_pool, v_pool, block_table, h, h_kv, page_size, max_pages, scale, out, s);
+  }
+  return launched("bi_prefill_attn");
+}
+
+extern "C" bi_status bi_decode_attn(const void* q, const void* k_pool, const void* v_pool,
+                                    const int32_t* block_table, const int32_t* kv_len,
+                                    const int32_t* chunk_off, int B, int total_chunks, int h,
+                                    int h_kv, int d_h, int page_size, int max_pages,
+                                    int kv_chunk, float scale, int dtype, float* part_ml,
+                                    float* part_acc, bi_stream stream) {
+  using namespace bi;
+  bi_status st = AttnArgsCheck::common("bi_decode_attn", h, h_kv, d_h, page_size, kv_chunk,
+                                       dtype);
+  if (st != BI_OK) return st;
+  BI_REQUIRE(B >= 0 && total_chunks >= 0 && max_pages >= 1, BI_ERR_INVALID,
+             "bi_decode_attn: bad sizes B=%d total_chunks=%d max_pages=%d", B, total_chunks,
+             max_pages);
+  BI_REQUIRE(kv_chunk % page_size == 0, BI_ERR_UNSUPPORTED,
+             "bi_decode_attn: page_size %d must divide kv_chunk %d", page_size, kv_chunk);
+  if (B == 0 || total_chunks == 0) return BI_OK;
+  BI_REQUIRE(total_chunks <= 0x7fffffff / h && h_kv <= 65535, BI_ERR_INVALID,
+             "bi_decode_attn: grid too large");
+  BI_REQUIRE(q && k_pool && v_pool && block_table && kv_len && chunk_off && part_ml && part_acc,
+             BI_ERR_INVALID, "bi_decode_attn: null pointer");
+  BI_REQUIRE(aligned16(q) && aligned16(k_pool) && aligned16(v_pool) && aligned16(part_acc),
+             BI_ERR_INVALID, "bi_decode_attn: pointers must be 16-byte aligned");
+  const int R = h / h_kv, nw = kv_chunk / 64;
+  hipStream_t s = as_stream(stream);
+  if (dtype == BI_BF16) {
+    if (d_h == 128) decode_r<1, 128>(R, nw, q, k_pool, v_pool, block_table, kv_len, chunk_off, B, total_chunks, h, h_kv, page_size, max_pages, scale, part_ml, part_acc, s);
+    else decode_r<1, 64>(R, nw, q, k_pool, v_pool, block_table, kv_len, chunk_off, B, total_chunks, h, h_kv, page_size, max_pages, scale, part_ml, part_acc, s);
+  } else {
+    if (d_h == 128) decode_r<0, 128>(R, nw, q, k_pool, v_pool, block_table, kv_len, chunk_off, B, total_chunks, h, h_kv, page_size, max_pages, scale, part_ml, part_acc, s);
+    else decode_r<0, 64>(R, nw, q, k_pool, v_pool, block_table, kv_len, chunk_off, B, total_chunks, h, h_kv, page_size, max_pages, scale, part_ml, part_acc, s);
+  }
+  return launched("bi_decode_attn");
+}
+
+extern "C" bi_status bi_merge_partials(const float* part_ml, const float* part_acc,
+                                       const int32_t* chunk_off, int B, int h, int d_h,
+                                       void* out, int out_dtype, bi_stream stream) {
+  using namespace bi;
+  BI_REQUIRE(B >= 0 && h >= 1, BI_ERR_INVALID, "bi_merge_partials: bad sizes B=%d h=%d", B, h);
+  BI_REQUIRE(d_h == 64 || d_h == 128, BI_ERR_UNSUPPORTED, "bi_merge_partials: d_h=%d", d_h);
+  BI_REQUIRE(out_dtype == BI_F32 || out_dtype == BI_BF16, BI_ERR_UNSUPPORTED,
+             "bi_merge_partials: dtype %d", out_dtype);
+  if (B == 0) return BI_OK;
+  BI_REQUIRE(part_ml && part_acc && chunk_off && out, BI_ERR_INVALID,
+             "bi_merge_partials: null pointer");
+  BI_REQUIRE((long)B * h <= 0x7fffffffL, BI_ERR_INVALID, "bi_merge_partials: too large");
+  hipStream_t s = as_stream(stream);
+  const dim3 grid((unsigned)(((long)B * h + 3) / 4));
+  if (d_h == 128) {
+    if (out_dtype == BI_BF16) hipLaunchKernelGGL((k_merge<128, 1>), grid, dim3(256), 0, s, part_ml, part_acc, chunk_off, B, h, out);
+    else hipLaunchKernelGGL((k_merge<128, 0>), grid, dim3(256), 0, s, part_ml, part_acc, chunk_off, B, h, out);
+  } else {
+    if (out_dtype == BI_BF16) hipLaunchKernelGGL((k_merge<64, 1>), grid, dim3(256), 0, s, part_ml, part_acc, chunk_off, B, h, out);
+    else hipLaunchKernelGGL((k_merge<64, 0>), grid, dim3(256), 0, s, part_ml, part_acc, chunk_off, B, h, out);
+  }
+  return launched("bi_merge_partials");
+}

@@ -1,0 +1,183 @@
+// Device helpers shared by the kernels of libbi.so (gfx950 only).
+//
+// Numeric contract of the whole library: IEEE binary32 arithmetic with
+// round-to-nearest-even, fma only where __builtin_fmaf is written (the
+// library is built with -ffp-contract=off and without fast-math), division
+// and sqrt correctly rounded (HIP's default lowering), fp32 denormals kept.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bi {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---- bfloat16 <-> binary32 ---------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// binary32 -> bfloat16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u)
+    return (u & 0x007fffffu) ? ((u | 0x00400000u) >> 16) : (u >> 16);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---- element access by dtype (0 = f32, 1 = bf16) -------------------------
+template <int DT> struct Elem;
+template <> struct Elem<0> {
+  typedef float T;
+  static constexpr int bytes = 4;
+  __device__ static __forceinline__ float ld(const void* p, long i) {
+    return static_cast<const float*>(p)[i];
+  }
+  __device__ static __forceinline__ void st(void* p, long i, float v) {
+    static_cast<float*>(p)[i] = v;
+  }
+};
+template <> struct Elem<1> {
+  typedef uint16_t T;
+  static constexpr int bytes = 2;
+  __device__ static __forceinline__ float ld(const void* p, long i) {
+    return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[i]);
+  }
+  __device__ static __forceinline__ void st(void* p, long i, float v) {
+    static_cast<uint16_t*>(p)[i] = (uint16_t)f32_to_bf16_bits(v);
+  }
+};
+
+// Load 8 consecutive elements starting at element index i (16-byte aligned
+// for bf16, 32-byte for f32) as floats.
+template <int DT> __device__ __forceinline__ void load8(const void* p, long i, float* o);
+template <> __device__ __forceinline__ void load8<1>(const void* p, long i, float* o) {
+  uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
+  o[0] = bf16_lo(w.x); o[1] = bf16_hi(w.x); o[2] = bf16_lo(w.y); o[3] = bf16_hi(w.y);
+  o[4] = bf16_lo(w.z); o[5] = bf16_hi(w.z); o[6] = bf16_lo(w.w); o[7] = bf16_hi(w.w);
+}
+template <> __device__ __forceinline__ void load8<0>(const void* p, long i, float* o) {
+  const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+  float4 a = q[0], b = q[1];
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+}
+template <int DT> __device__ __forceinline__ void store8(void* p, long i, const float* v);
+template <> __device__ __forceinline__ void store8<1>(void* p, long i, const float* v) {
+  uint4 w;
+  w.x = pack_bf16x2(v[0], v[1]); w.y = pack_bf16x2(v[2], v[3]);
+  w.z = pack_bf16x2(v[4], v[5]); w.w = pack_bf16x2(v[6], v[7]);
+  *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p) + i) = w;
+}
+template <> __device__ __forceinline__ void store8<0>(void* p, long i, const float* v) {
+  float4* q = reinterpret_cast<float4*>(static_cast<float*>(p) + i);
+  q[0] = make_float4(v[0], v[1], v[2], v[3]);
+  q[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// ---- the library's exp ----------------------------------------------------
+// One fixed binary32 exp for softmax and SiLU, so a result never depends on
+// which hardware approximation a compiler picks: Cody & Waite range
+// reduction ("Software Manual for the Elementary Functions", 1980) with
+// ln 2 split into a 15-bit head and an fp32 tail, then the degree-7 Taylor
+// polynomial of e^r in Horner form with fma, then scaling by 2^n in two
+// exact-power steps.  Below -104 the result is +0, above 88.75 +inf.
+__device__ __forceinline__ float exp_fixed(float x) {
+  if (x != x) return x;
+  if (x > 88.75f) return __builtin_inff();
+  if (x < -104.0f) return 0.0f;
+  const float n = __builtin_rintf(x * 1.44269502162933349609375f);
+  float r = __builtin_fmaf(-n, 0.693145751953125f, x);
+  r = __builtin_fmaf(-n, 1.428606765330187045037746429443359375e-06f, r);
+  float p = 1.0f / 5040.0f;
+  p = __builtin_fmaf(p, r, 1.0f / 720.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 120.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 24.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 6.0f);
+  p = __builtin_fmaf(p, r, 0.5f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  const int ni = (int)n;
+  const int n1 = ni / 2;
+  const int n2 = ni - n1;
+  p = p * __uint_as_float((uint32_t)(n1 + 127) << 23);
+  p = p * __uint_as_float((uint32_t)(n2 + 127) << 23);
+  return p;
+}
+
+// ---- direct global -> LDS copies -----------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One wave copies 64 x 16 bytes: lane l reads 16 bytes at `src` (its own
+// address) and the hardware writes them to LDS at lds_base + 16 * l.
+// lds_base must be wave-uniform.
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// ---- explicit LDS reads --------------------------------------------------
+// The compiler cannot tell LDS reads apart from LDS written by in-flight
+// direct copies and would wait for every outstanding copy before each read,
+// which serialises a copy ring.  Reads of ring slots therefore go through
+// these helpers: one asm statement issues a batch of ds_read_b128 and waits
+// for them (s_waitcnt lgkmcnt(0)) before it ends, so the compiler never sees
+// a register whose load is still in flight.  Ring-slot reuse is ordered by
+// explicit vmcnt waits and s_barrier.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// a[i] = LDS[ba + 1024 i], b[i] = LDS[bb + 1024 i], i = 0..7 (16 bytes each).
+__device__ __forceinline__ void lds_read_8x2_stride1k(u32x4_t (&a)[8], u32x4_t (&b)[8],
+                                                      uint32_t ba, uint32_t bb) {
+  asm volatile(
+      "ds_read_b128 %0, %16\n\tds_read_b128 %1, %16 offset:1024\n\t"
+      "ds_read_b128 %2, %16 offset:2048\n\tds_read_b128 %3, %16 offset:3072\n\t"
+      "ds_read_b128 %4, %16 offset:4096\n\tds_read_b128 %5, %16 offset:5120\n\t"
+      "ds_read_b128 %6, %16 offset:6144\n\tds_read_b128 %7, %16 offset:7168\n\t"
+      "ds_read_b128 %8, %17\n\tds_read_b128 %9, %17 offset:1024\n\t"
+      "ds_read_b128 %10, %17 offset:2048\n\tds_read_b128 %11, %17 offset:3072\n\t"
+      "ds_read_b128 %12, %17 offset:4096\n\tds_read_b128 %13, %17 offset:5120\n\t"
+      "ds_read_b128 %14, %17 offset:6144\n\tds_read_b128 %15, %17 offset:7168\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]),
+        "=&v"(a[6]), "=&v"(a[7]), "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]),
+        "=&v"(b[4]), "=&v"(b[5]), "=&v"(b[6]), "=&v"(b[7])
+      : "v"(ba), "v"(bb)
+      : "memory");
+}
+
+// a[i] = LDS[ba + 2048 i], b[i] = LDS[bb + 2048 i], i = 0..3.
+__device__ __forceinline__ void lds_read_4x2_stride2k(u32x4_t (&a)[4], u32x4_t (&b)[4],
+                                                      uint32_t ba, uint32_t bb) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:2048\n\t"
+      "ds_read_b128 %2, %8 offset:4096\n\tds_read_b128 %3, %8 offset:6144\n\t"
+      "ds_read_b128 %4, %9\n\tds_read_b128 %5, %9 offset:2048\n\t"
+      "ds_read_b128 %6, %9 offset:4096\n\tds_read_b128 %7, %9 offset:6144\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(b[0]), "=&v"(b[1]),
+        "=&v"(b[2]), "=&v"(b[3])
+      : "v"(ba), "v"(bb)
+      : "memory");
+}
+
+// Wait until at most n vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt encoding; lgkm and exp counters left alone).
+#define BI_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 15) | ((((n) >> 4) & 3) << 14) | (7 << 4) | (15 << 8))
+
+}  // namespace bi

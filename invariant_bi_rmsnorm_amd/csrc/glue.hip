@@ -1,0 +1,212 @@
+// Elementwise glue of a Llama-shaped layer: embedding gather, RoPE + KV page
+// append, residual add, SwiGLU, argmax.  None of these reduces across the
+// batch, so each row's result depends on that row alone; argmax is exact
+// (largest value, lowest index on ties) in any evaluation order.
+#include "api.h"
+#include "common.h"
+
+namespace bi {
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_embed(const void* __restrict__ table,
+                                               const int32_t* __restrict__ ids,
+                                               void* __restrict__ out, int d) {
+  const long row = blockIdx.y;
+  const long src = (long)ids[row] * d;
+  const int vecs = d / 8;
+  for (int v = blockIdx.x * 256 + threadIdx.x; v < vecs; v += gridDim.x * 256) {
+    float x[8];
+    load8<DT>(table, src + 8 * v, x);
+    store8<DT>(out, row * d + 8 * v, x);
+  }
+}
+
+// One thread per rotation pair of one head of one row.
+template <int DT>
+__global__ __launch_bounds__(256) void k_rope_kv_append(
+    const void* __restrict__ qkv, int M, int h, int h_kv, int d_h,
+    const int32_t* __restrict__ pos, const float* __restrict__ cos_t,
+    const float* __restrict__ sin_t, const int32_t* __restrict__ slot_mapping, int page_size,
+    void* __restrict__ q_out, void* __restrict__ k_pool, void* __restrict__ v_pool) {
+  const int half = d_h / 2;
+  const int heads = h + 2 * h_kv;
+  const long tid = (long)blockIdx.x * 256 + threadIdx.x;
+  if (tid >= (long)M * heads * half) return;
+  const int i = (int)(tid % half);
+  const long rh = tid / half;
+  const int hh = (int)(rh % heads);
+  const long row = rh / heads;
+  const long in = row * heads * d_h + (long)hh * d_h;
+  const float a = Elem<DT>::ld(qkv, in + i), b = Elem<DT>::ld(qkv, in + i + half);
+  float ya = a, yb = b;
+  if (hh < h + h_kv && cos_t != nullptr) {
+    const long t = (long)pos[row] * half + i;
+    const float c = cos_t[t], s = sin_t[t];
+    ya = __builtin_fmaf(a, c, -(b * s));
+    yb = __builtin_fmaf(b, c, a * s);
+  }
+  long o;
+  void* dst;
+  if (hh < h) {
+    dst = q_out;
+    o = (row * h + hh) * (long)d_h;
+  } else {
+    const int g = hh < h + h_kv ? hh - h : hh - h - h_kv;
+    const long slot = slot_mapping[row];
+    dst = hh < h + h_kv ? k_pool : v_pool;
+    o = (((slot / page_size) * h_kv + g) * page_size + slot % page_size) * (long)d_h;
+  }
+  Elem<DT>::st(dst, o + i, ya);
+  Elem<DT>::st(dst, o + i + half, yb);
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_add(const void* a, const void* b, void* y, long n) {
+  const long nv = n / 8;
+  for (long v = (long)blockIdx.x * 256 + threadIdx.x; v < nv; v += (long)gridDim.x * 256) {
+    float xa[8], xb[8], r[8];
+    load8<DT>(a, 8 * v, xa);
+    load8<DT>(b, 8 * v, xb);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = xa[e] + xb[e];
+    store8<DT>(y, 8 * v, r);
+  }
+  // tail
+  const long t = nv * 8 + (long)blockIdx.x * 256 + threadIdx.x;
+  if (t < n && (long)blockIdx.x * 256 + threadIdx.x < 8)
+    Elem<DT>::st(y, t, Elem<DT>::ld(a, t) + Elem<DT>::ld(b, t));
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_silu_mul(const void* __restrict__ gu,
+                                                  void* __restrict__ y, int F) {
+  const long row = blockIdx.y;
+  const int vecs = F / 8;
+  for (int v = blockIdx.x * 256 + threadIdx.x; v < vecs; v += gridDim.x * 256) {
+    float g[8], u[8], r[8];
+    load8<DT>(gu, row * 2 * F + 8 * v, g);
+    load8<DT>(gu, row * 2 * F + F + 8 * v, u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float s = g[e] / (1.0f + exp_fixed(-g[e]));
+      r[e] = s * u[e];
+    }
+    store8<DT>(y, row * F + 8 * v, r);
+  }
+}
+
+__device__ __forceinline__ void argbest(float& v, int& i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+}
+
+__global__ __launch_bounds__(256) void k_argmax(const float* __restrict__ x,
+                                                int32_t* __restrict__ idx, int V) {
+  const long row = blockIdx.x;
+  const float* xr = x + row * V;
+  float bv = -__builtin_inff();
+  int bi_ = 0x7fffffff;
+  for (int i = threadIdx.x; i < V; i += 256) argbest(bv, bi_, xr[i], i);
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int oi = __shfl_xor(bi_, off);
+    argbest(bv, bi_, ov, oi);
+  }
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = bv; si[threadIdx.x >> 6] = bi_; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 4; ++w) argbest(bv, bi_, sv[w], si[w]);
+    idx[row] = bi_ == 0x7fffffff ? 0 : bi_;
+  }
+}
+
+static unsigned grid_for(long work, long per_block, unsigned cap) {
+  long g = (work + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  return (unsigned)(g > cap ? cap : g);
+}
+
+}  // namespace bi
+
+using namespace bi;
+
+extern "C" bi_status bi_embed(const void* table, const int32_t* ids, void* out, int M, int d,
+                              int dtype, bi_stream stream) {
+  BI_REQUIRE(M >= 0 && d >= 8 && d % 8 == 0, BI_ERR_INVALID,
+             "bi_embed: need M >= 0 and d a positive multiple of 8 (M=%d d=%d)", M, d);
+  BI_REQUIRE(dtype == BI_F32 || dtype == BI_BF16, BI_ERR_UNSUPPORTED, "bi_embed: dtype %d", dtype);
+  if (M == 0) return BI_OK;
+  BI_REQUIRE(table && ids && out && aligned16(table) && aligned16(out), BI_ERR_INVALID,
+             "bi_embed: null or misaligned pointer");
+  BI_REQUIRE(M <= 65535, BI_ERR_INVALID, "bi_embed: M=%d too large", M);
+  const dim3 grid(grid_for(d / 8, 256, 64), M);
+  if (dtype == BI_BF16) hipLaunchKernelGGL(k_embed<1>, grid, dim3(256), 0, as_stream(stream), table, ids, out, d);
+  else hipLaunchKernelGGL(k_embed<0>, grid, dim3(256), 0, as_stream(stream), table, ids, out, d);
+  return launched("bi_embed");
+}
+
+extern "C" bi_status bi_rope_kv_append(const void* qkv, int M, int h, int h_kv, int d_h,
+                                       const int32_t* pos, const float* cos_t,
+                                       const float* sin_t, const int32_t* slot_mapping,
+                                       int page_size, void* q_out, void* k_pool, void* v_pool,
+                                       int dtype, bi_stream stream) {
+  BI_REQUIRE(M >= 0 && h >= 1 && h_kv >= 1 && d_h >= 2 && d_h % 2 == 0 && page_size >= 1,
+             BI_ERR_INVALID, "bi_rope_kv_append: bad sizes");
+  BI_REQUIRE(dtype == BI_F32 || dtype == BI_BF16, BI_ERR_UNSUPPORTED,
+             "bi_rope_kv_append: dtype %d", dtype);
+  BI_REQUIRE((cos_t == nullptr) == (sin_t == nullptr), BI_ERR_INVALID,
+             "bi_rope_kv_append: cos_t and sin_t must both be given or both be NULL");
+  if (M == 0) return BI_OK;
+  BI_REQUIRE(qkv && slot_mapping && q_out && k_pool && v_pool && (pos || !cos_t),
+             BI_ERR_INVALID, "bi_rope_kv_append: null pointer");
+  const long work = (long)M * (h + 2 * h_kv) * (d_h / 2);
+  BI_REQUIRE(work < (1L << 40), BI_ERR_INVALID, "bi_rope_kv_append: too large");
+  const unsigned grid = (unsigned)((work + 255) / 256);
+  if (dtype == BI_BF16)
+    hipLaunchKernelGGL(k_rope_kv_append<1>, dim3(grid), dim3(256), 0, as_stream(stream), qkv, M,
+                       h, h_kv, d_h, pos, cos_t, sin_t, slot_mapping, page_size, q_out, k_pool,
+                       v_pool);
+  else
+    hipLaunchKernelGGL(k_rope_kv_append<0>, dim3(grid), dim3(256), 0, as_stream(stream), qkv, M,
+                       h, h_kv, d_h, pos, cos_t, sin_t, slot_mapping, page_size, q_out, k_pool,
+                       v_pool);
+  return launched("bi_rope_kv_append");
+}
+
+extern "C" bi_status bi_add(const void* a, const void* b, void* y, long n, int dtype,
+                            bi_stream stream) {
+  BI_REQUIRE(n >= 0, BI_ERR_INVALID, "bi_add: n=%ld", n);
+  BI_REQUIRE(dtype == BI_F32 || dtype == BI_BF16, BI_ERR_UNSUPPORTED, "bi_add: dtype %d", dtype);
+  if (n == 0) return BI_OK;
+  BI_REQUIRE(a && b && y && aligned16(a) && aligned16(b) && aligned16(y), BI_ERR_INVALID,
+             "bi_add: null or misaligned pointer");
+  const unsigned grid = grid_for((n + 7) / 8, 256, 4096);
+  if (dtype == BI_BF16) hipLaunchKernelGGL(k_add<1>, dim3(grid), dim3(256), 0, as_stream(stream), a, b, y, n);
+  else hipLaunchKernelGGL(k_add<0>, dim3(grid), dim3(256), 0, as_stream(stream), a, b, y, n);
+  return launched("bi_add");
+}
+
+extern "C" bi_status bi_silu_mul(const void* gu, void* y, int M, int F, int dtype,
+                                 bi_stream stream) {
+  BI_REQUIRE(M >= 0 && F >= 8 && F % 8 == 0, BI_ERR_INVALID,
+             "bi_silu_mul: need F a positive multiple of 8 (F=%d)", F);
+  BI_REQUIRE(dtype == BI_F32 || dtype == BI_BF16, BI_ERR_UNSUPPORTED, "bi_silu_mul: dtype %d",
+             dtype);
+  if (M == 0) return BI_OK;
+  BI_REQUIRE(gu && y && aligned16(gu) && aligned16(y), BI_ERR_INVALID,
+             "bi_silu_mul: null or misaligned pointer");
+  BI_REQUIRE(M <= 65535, BI_ERR_INVALID, "bi_silu_mul: M=%d too large", M);
+  const dim3 grid(grid_for(F / 8, 256, 64), M);
+  if (dtype == BI_BF16) hipLaunchKernelGGL(k_silu_mul<1>, grid, dim3(256), 0, as_stream(stream), gu, y, F);
+  else hipLaunchKernelGGL(k_silu_mul<0>, grid, dim3(256), 0, as_stream(stream), gu, y, F);
+  return launched("bi_silu_mul");
+}
+
+extern "C" bi_status bi_argmax(const float* x, int32_t* idx, int M, int V, bi_stream stream) {
+  BI_REQUIRE(M >= 0 && V >= 1, BI_ERR_INVALID, "bi_argmax: bad sizes M=%d V=%d", M, V);
+  if (M == 0) return BI_OK;
+  BI_REQUIRE(x && idx, BI_ERR_INVALID, "bi_argmax: null pointer");
+  hipLaunchKernelGGL(k_argmax, dim3(M), dim3(256), 0, as_stream(stream), x, idx, V);
+  return launched("bi_argmax");
+}

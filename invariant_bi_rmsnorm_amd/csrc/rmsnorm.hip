@@ -1,0 +1,90 @@
+// bi_rmsnorm: one workgroup of 256 lanes per row, one fixed reduction tree.
+//
+// "Batch invariance and reproducible inference" lists rms_norm among the
+// kernels that run one block per row with no cross-block reduction, so the
+// order cannot follow the batch; "Lockstep", "The fix", asks exactly that of
+// every forward-pass reduction.  The order (vectors of 8, lane-strided fma,
+// xor butterfly per wave, waves added in order) depends on d only.
+#include "api.h"
+#include "common.h"
+
+namespace bi {
+
+template <int DT>
+__global__ __launch_bounds__(256) void k_rmsnorm(const void* x, const void* __restrict__ gamma,
+                                                 void* y, int d, float eps) {
+  const long row = blockIdx.x;
+  const int t = threadIdx.x;
+  const long base = row * (long)d;
+  const int nv = (d + 7) >> 3;
+  const bool vec = (d & 7) == 0;
+
+  float a = 0.0f;
+  for (int v = t; v < nv; v += 256) {
+    float xs[8];
+    const int i0 = v << 3;
+    if (vec) {
+      load8<DT>(x, base + i0, xs);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a = __builtin_fmaf(xs[e], xs[e], a);
+    } else {
+      const int n = min(8, d - i0);
+      for (int e = 0; e < n; ++e) {
+        const float xv = Elem<DT>::ld(x, base + i0 + e);
+        a = __builtin_fmaf(xv, xv, a);
+      }
+    }
+  }
+  // xor butterfly inside the wave: masks 32, 16, 8, 4, 2, 1
+  a = a + __shfl_xor(a, 32);
+  a = a + __shfl_xor(a, 16);
+  a = a + __shfl_xor(a, 8);
+  a = a + __shfl_xor(a, 4);
+  a = a + __shfl_xor(a, 2);
+  a = a + __shfl_xor(a, 1);
+  __shared__ float ws[4];
+  if ((t & 63) == 0) ws[t >> 6] = a;
+  __syncthreads();
+  const float ss = ((ws[0] + ws[1]) + ws[2]) + ws[3];
+  const float mean = ss / (float)d;
+  const float r = 1.0f / sqrtf(mean + eps);
+
+  for (int v = t; v < nv; v += 256) {
+    const int i0 = v << 3;
+    if (vec) {
+      float xs[8], gs[8], ys[8];
+      load8<DT>(x, base + i0, xs);
+      load8<DT>(gamma, i0, gs);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ys[e] = (xs[e] * r) * gs[e];
+      store8<DT>(y, base + i0, ys);
+    } else {
+      const int n = min(8, d - i0);
+      for (int e = 0; e < n; ++e) {
+        const float xv = Elem<DT>::ld(x, base + i0 + e);
+        Elem<DT>::st(y, base + i0 + e, (xv * r) * Elem<DT>::ld(gamma, i0 + e));
+      }
+    }
+  }
+}
+
+}  // namespace bi
+
+extern "C" bi_status bi_rmsnorm(const void* x, const void* gamma, void* y, int M, int d,
+                                float eps, int dtype, bi_stream stream) {
+  using namespace bi;
+  BI_REQUIRE(M >= 0 && d >= 1, BI_ERR_INVALID, "bi_rmsnorm: bad shape M=%d d=%d", M, d);
+  BI_REQUIRE(dtype == BI_F32 || dtype == BI_BF16, BI_ERR_UNSUPPORTED,
+             "bi_rmsnorm: dtype %d not supported", dtype);
+  if (M == 0) return BI_OK;
+  BI_REQUIRE(x && gamma && y, BI_ERR_INVALID, "bi_rmsnorm: null pointer");
+  BI_REQUIRE(aligned16(x) && aligned16(gamma) && aligned16(y), BI_ERR_INVALID,
+             "bi_rmsnorm: pointers must be 16-byte aligned");
+  BI_REQUIRE(eps >= 0.0f, BI_ERR_INVALID, "bi_rmsnorm: eps must be >= 0");
+  hipStream_t s = as_stream(stream);
+  if (dtype == BI_BF16)
+    hipLaunchKernelGGL(k_rmsnorm<1>, dim3(M), dim3(256), 0, s, x, gamma, y, d, eps);
+  else
+    hipLaunchKernelGGL(k_rmsnorm<0>, dim3(M), dim3(256), 0, s, x, gamma, y, d, eps);
+  return launched("bi_rmsnorm");
+}

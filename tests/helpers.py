@@ -1,0 +1,67 @@
+"""Shared helpers for the GPU tests (inputs from synth, comparisons)."""
+import math
+
+import numpy as np
+import torch
+
+import synth
+
+U = 2.0 ** -24
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy()
+
+
+def bits_equal(a, b) -> bool:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    b = np.ascontiguousarray(b, dtype=np.float32)
+    return a.shape == b.shape and np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def mismatch_report(a, b, n=5) -> str:
+    a = np.asarray(a, np.float32).ravel()
+    b = np.asarray(b, np.float32).ravel()
+    bad = np.nonzero(a.view(np.uint32) != b.view(np.uint32))[0]
+    return f"{bad.size} mismatches of {a.size}; first {[(int(i), float(a[i]), float(b[i])) for i in bad[:n]]}"
+
+
+class PagedKV:
+    """Paged K/V pools [pages][h_kv][page_size][d_h] with random scattered
+    placement of each request's pages, filled from synth normals."""
+
+    def __init__(self, kv_len, h_kv, d_h, page_size, seed, dtype, capacity=None, slack=1.25):
+        cap = np.asarray(capacity if capacity is not None else kv_len)
+        self.place = synth.scatter_pages(cap, page_size, seed=seed, slack=slack)
+        shape = (self.place.num_pages, h_kv, page_size, d_h)
+        self.k = synth.normal(shape, seed=seed + 1).to(dtype)
+        self.v = synth.normal(shape, seed=seed + 2).to(dtype)
+        self.bt = torch.from_numpy(self.place.block_table.copy())
+        self.page_size = page_size
+
+    def to(self, device):
+        return self.k.to(device), self.v.to(device), self.bt.to(device)
+
+
+def gemm_bf16_tol(A: np.ndarray, W: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Bound on |gpu - oracle| for bf16 outputs of a K-long fp32 dot: each
+    side's fp32 accumulation is within (K+1) u sum|a w| of the exact value
+    (any summation order), and each side's bf16 rounding moves at most half a
+    bf16 ulp (2^-9 relative)."""
+    K = A.shape[1]
+    s = np.abs(A).astype(np.float64) @ np.abs(W).astype(np.float64).T
+    return 2.0 ** -8 * np.abs(ref) + 2.2 * (K + 1) * U * s + 1e-30
+
+
+def gemm_f32_tol(A: np.ndarray, W: np.ndarray) -> np.ndarray:
+    K = A.shape[1]
+    s = np.abs(A).astype(np.float64) @ np.abs(W).astype(np.float64).T
+    return 2.0 * (K + 1) * U * s + 1e-30
+
+
+def scale_for(d_h: int) -> float:
+    return float(np.float32(1.0 / math.sqrt(d_h)))

@@ -1,0 +1,363 @@
+"""GPU parity of every HIP kernel against the CPU oracle, plus batch
+invariance of the kernels on the GPU itself.  Calls go through the C ABI
+(invariant_bi_rmsnorm_amd._lib).
+
+Bars:
+  - RMSNorm, fp32 GEMM, attention partials / merge / prefill, RoPE, add,
+    SiLU-mul: the kernels evaluate the oracle's order exactly, so results
+    must be bit-identical.
+  - bf16 GEMM (MFMA): bit-identical on integer inputs (every order exact);
+    on general inputs within gemm_bf16_tol (MFMA's internal summation order
+    inside one 32-wide K step is the hardware's).
+  - argmax, embed: exact.
+  - invariance: a request's outputs are bit-identical alone, in any batch,
+    in any row position.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import (PagedKV, bits_equal, dev, gemm_bf16_tol, gemm_f32_tol, mismatch_report,
+                     scale_for, to_np)
+
+pytestmark = pytest.mark.gpu
+
+L = pytest.importorskip("invariant_bi_rmsnorm_amd._lib")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    L.load()
+    yield
+    torch.cuda.synchronize()
+
+
+DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("M,d", [(1, 4096), (7, 4096), (64, 4096), (3, 256), (5, 13), (2, 1),
+                                 (4, 14336), (9, 1000), (1, 8)])
+def test_rmsnorm_bitwise(dt, M, d):
+    x = synth.normal((M, d), seed=M * 31 + d).to(DT[dt])
+    g = synth.normal((d,), seed=d + 7).to(DT[dt])
+    y = torch.empty_like(x, device=dev())
+    L.bi_rmsnorm(x.to(dev()), g.to(dev()), y, 1e-5)
+    ref = oracle.rmsnorm(x, g, 1e-5, round_bf16=(dt == "bf16"))
+    got = to_np(y)
+    assert bits_equal(got, ref), mismatch_report(got, ref)
+
+
+def test_rmsnorm_rows_invariant_and_inplace():
+    x = synth.normal((64, 4096), seed=5).to(torch.bfloat16).to(dev())
+    g = synth.normal((4096,), seed=6).to(torch.bfloat16).to(dev())
+    full = torch.empty_like(x)
+    L.bi_rmsnorm(x, g, full, 1e-5)
+    for idx in ([3], [63, 0, 17], list(range(64))[::-1]):
+        sub = x[idx].contiguous()
+        out = torch.empty_like(sub)
+        L.bi_rmsnorm(sub, g, out, 1e-5)
+        assert torch.equal(out.view(torch.int16), full[idx].view(torch.int16))
+    xi = x.clone()
+    L.bi_rmsnorm(xi, g, xi, 1e-5)   # in place
+    assert torch.equal(xi.view(torch.int16), full.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# GEMM
+# ---------------------------------------------------------------------------
+
+GEMM_SHAPES = [(1, 16, 32), (1, 17, 40), (5, 100, 264), (16, 64, 512), (17, 48, 96),
+               (33, 130, 1024), (64, 64, 256), (64, 257, 4104), (65, 128, 256),
+               (100, 300, 520), (257, 200, 1000)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_gemm_bf16_integer_exact(M, N, K, out):
+    A = synth.integers((M, K), -8, 8, seed=M + K).to(torch.bfloat16)
+    W = synth.integers((N, K), -8, 8, seed=N + K + 1).to(torch.bfloat16)
+    C = torch.empty((M, N), dtype=DT[out], device=dev())
+    L.bi_gemm(A.to(dev()), W.to(dev()), C)
+    ref = oracle.gemm(A, W, round_bf16=(out == "bf16"))
+    got = to_np(C)
+    assert bits_equal(got, ref), mismatch_report(got, ref)
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm_bf16_random_within_tolerance(M, N, K):
+    A = synth.normal((M, K), seed=M).to(torch.bfloat16)
+    W = synth.normal((N, K), seed=N, std=0.02).to(torch.bfloat16)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev())
+    L.bi_gemm(A.to(dev()), W.to(dev()), C)
+    ref = oracle.gemm(A, W, round_bf16=True)
+    tol = gemm_bf16_tol(A.float().numpy(), W.float().numpy(), ref)
+    err = np.abs(to_np(C) - ref)
+    assert np.all(err <= tol), f"max excess {np.max(err - tol)}"
+    Cf = torch.empty((M, N), dtype=torch.float32, device=dev())
+    L.bi_gemm(A.to(dev()), W.to(dev()), Cf)
+    reff = oracle.gemm(A, W, round_bf16=False)
+    assert np.all(np.abs(to_np(Cf) - reff) <= gemm_f32_tol(A.float().numpy(), W.float().numpy()))
+
+
+def test_gemm_rows_invariant_across_M_and_position():
+    K, N = 4096, 6144
+    A = synth.normal((300, K), seed=1).to(torch.bfloat16).to(dev())
+    W = synth.normal((N, K), seed=2, std=0.02).to(torch.bfloat16).to(dev())
+
+    def run(rows):
+        a = A[rows].contiguous()
+        c = torch.empty((len(rows), N), dtype=torch.float32, device=dev())
+        L.bi_gemm(a, W, c)
+        return c
+
+    full = run(list(range(300)))            # tiled kernel
+    rng = np.random.default_rng(0)
+    for M in [1, 2, 7, 16, 17, 33, 64, 65, 128, 200]:
+        rows = list(rng.choice(300, size=M, replace=False))
+        got = run(rows)
+        assert torch.equal(got.view(torch.int32), full[rows].view(torch.int32)), f"M={M}"
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 512, 256), (8, 512, 256), (3, 33, 7), (20, 70, 300)])
+def test_gemm_f32_bitwise(M, N, K):
+    A = synth.normal((M, K), seed=M)
+    W = synth.normal((N, K), seed=N, std=0.02)
+    C = torch.empty((M, N), dtype=torch.float32, device=dev())
+    L.bi_gemm(A.to(dev()), W.to(dev()), C)
+    ref = oracle.gemm(A, W, round_bf16=False)
+    assert bits_equal(to_np(C), ref), mismatch_report(to_np(C), ref)
+
+
+# ---------------------------------------------------------------------------
+# decode attention + merge
+# ---------------------------------------------------------------------------
+
+ATTN_CFGS = [  # dtype, h, h_kv, d_h, chunk
+    ("bf16", 32, 8, 128, 256),
+    ("f32", 4, 2, 64, 64),
+    ("bf16", 8, 4, 64, 64),
+    ("f32", 8, 2, 128, 256),
+]
+LENS = [1, 2, 15, 16, 17, 63, 64, 65, 255, 256, 257, 300, 511, 1000]
+
+
+def _decode(q, kv, kv_len, chunk, scale):
+    B = q.shape[0]
+    off = L.bi_chunk_offsets(kv_len, chunk)
+    tot = int(off[-1])
+    h, d_h = q.shape[1], q.shape[2]
+    k, v, bt = kv.to(dev())
+    ml = torch.full((tot, h, 2), float("nan"), device=dev())
+    acc = torch.full((tot, h, d_h), float("nan"), device=dev())
+    kvl = torch.as_tensor(kv_len, dtype=torch.int32).to(dev())
+    offd = off.to(dev())
+    L.bi_decode_attn(q.to(dev()), k, v, bt, kvl, offd, tot, chunk, scale, ml, acc)
+    out = torch.empty((B, h, d_h), dtype=q.dtype, device=dev())
+    L.bi_merge_partials(ml, acc, offd, out)
+    return ml, acc, out, off
+
+
+@pytest.mark.parametrize("dt,h,h_kv,d_h,chunk", ATTN_CFGS)
+def test_decode_attention_bitwise(dt, h, h_kv, d_h, chunk):
+    kv_len = np.array(LENS, np.int32)
+    kv = PagedKV(kv_len, h_kv, d_h, 16, seed=100 + d_h, dtype=DT[dt])
+    q = synth.normal((len(kv_len), h, d_h), seed=7).to(DT[dt])
+    scale = scale_for(d_h)
+    ml, acc, out, off = _decode(q, kv, kv_len, chunk, scale)
+    rml, racc = oracle.decode_partials(q, kv.k, kv.v, kv.bt, kv_len, off, h_kv, 16, chunk, scale)
+    assert bits_equal(to_np(ml), rml), mismatch_report(to_np(ml), rml)
+    assert bits_equal(to_np(acc), racc), mismatch_report(to_np(acc), racc)
+    rout = oracle.merge_partials(rml, racc, off, round_bf16=(dt == "bf16"))
+    assert bits_equal(to_np(out), rout), mismatch_report(to_np(out), rout)
+
+
+@pytest.mark.parametrize("dt,h,h_kv,d_h,chunk", ATTN_CFGS[:2])
+def test_decode_attention_batch_invariant(dt, h, h_kv, d_h, chunk):
+    kv_len = synth.uniform_lengths(24, 1, 1200, seed=3)
+    kv = PagedKV(kv_len, h_kv, d_h, 16, seed=200, dtype=DT[dt])
+    q = synth.normal((24, h, d_h), seed=8).to(DT[dt])
+    scale = scale_for(d_h)
+    _, _, full, _ = _decode(q, kv, kv_len, chunk, scale)
+    full = to_np(full)
+    rng = np.random.default_rng(4)
+    for trial in range(6):
+        idx = rng.permutation(24)[: rng.integers(1, 25)]
+        sub = PagedKV.__new__(PagedKV)
+        sub.k, sub.v, sub.page_size = kv.k, kv.v, 16
+        sub.bt = kv.bt[idx].contiguous()
+        _, _, out, _ = _decode(q[idx].contiguous(), sub, kv_len[idx], chunk, scale)
+        assert bits_equal(to_np(out), full[idx]), f"trial {trial}"
+
+
+def test_decode_attention_same_result_on_other_pages():
+    # the same request's KV at different physical pages gives the same bits
+    kv_len = np.array([700], np.int32)
+    a = PagedKV(kv_len, 8, 128, 16, seed=300, dtype=torch.bfloat16)
+    b = PagedKV(kv_len, 8, 128, 16, seed=301, dtype=torch.bfloat16, slack=3.0)
+    # copy request's logical KV from a's placement to b's placement
+    for p in range(a.place.block_table.shape[1]):
+        pa, pb = a.place.block_table[0, p], b.place.block_table[0, p]
+        if pa >= 0:
+            b.k[pb] = a.k[pa]
+            b.v[pb] = a.v[pa]
+    q = synth.normal((1, 32, 128), seed=9).to(torch.bfloat16)
+    _, _, oa, _ = _decode(q, a, kv_len, 256, scale_for(128))
+    _, _, ob, _ = _decode(q, b, kv_len, 256, scale_for(128))
+    assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# prefill attention
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt,h,h_kv,d_h,chunk", ATTN_CFGS[:3])
+def test_prefill_bitwise_and_equal_to_decode(dt, h, h_kv, d_h, chunk):
+    # three requests: prompt chunks at various absolute starts
+    lens = [37, 300, 5]
+    pos0 = [0, 200, 517]
+    cap = np.array([p + n for p, n in zip(pos0, lens)], np.int32)
+    kv = PagedKV(cap, h_kv, d_h, 16, seed=400 + d_h, dtype=DT[dt])
+    T = sum(lens)
+    q = synth.normal((T, h, d_h), seed=11).to(DT[dt])
+    q_start = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    scale = scale_for(d_h)
+    k, v, bt = kv.to(dev())
+    out = torch.empty((T, h, d_h), dtype=DT[dt], device=dev())
+    L.bi_prefill_attn(q.to(dev()), torch.from_numpy(q_start).to(dev()),
+                      torch.tensor(pos0, dtype=torch.int32, device=dev()), k, v, bt, chunk, scale,
+                      out)
+    ref = oracle.prefill_attn(q, q_start, np.array(pos0, np.int32), kv.k, kv.v, kv.bt, h_kv, 16,
+                              chunk, scale, round_bf16=(dt == "bf16"))
+    assert bits_equal(to_np(out), ref), mismatch_report(to_np(out), ref)
+    # each prefill row equals the GPU decode of kv_len = pos + 1
+    rows, kvl, btr = [], [], []
+    for r in range(3):
+        for t in range(q_start[r], q_start[r + 1]):
+            rows.append(t)
+            kvl.append(pos0[r] + t - q_start[r] + 1)
+            btr.append(r)
+    sub = PagedKV.__new__(PagedKV)
+    sub.k, sub.v, sub.page_size = kv.k, kv.v, 16
+    sub.bt = kv.bt[btr].contiguous()
+    _, _, dec, _ = _decode(q[rows].contiguous(), sub, np.array(kvl, np.int32), chunk, scale)
+    assert torch.equal(dec.view(torch.int32 if dt == "f32" else torch.int16),
+                       out[rows].view(torch.int32 if dt == "f32" else torch.int16))
+
+
+def test_prefill_invariant_to_chunk_cuts():
+    Lq, h, h_kv, d_h = 700, 32, 8, 128
+    kv = PagedKV(np.array([Lq], np.int32), h_kv, d_h, 16, seed=500, dtype=torch.bfloat16)
+    q = synth.normal((Lq, h, d_h), seed=12).to(torch.bfloat16).to(dev())
+    k, v, bt = kv.to(dev())
+
+    def run(cuts):
+        qs = torch.tensor(cuts, dtype=torch.int32, device=dev())
+        p0 = torch.tensor(cuts[:-1], dtype=torch.int32, device=dev())
+        btr = bt.repeat(len(cuts) - 1, 1).contiguous()
+        out = torch.empty_like(q)
+        L.bi_prefill_attn(q, qs, p0, k, v, btr, 256, scale_for(d_h), out)
+        return out
+
+    whole = run([0, Lq])
+    for cuts in ([0, 1, 256, 257, Lq], [0, 333, 334, 600, Lq], [0, 100, 200, 300, 400, 500, Lq]):
+        assert torch.equal(run(cuts).view(torch.int16), whole.view(torch.int16)), cuts
+
+
+# ---------------------------------------------------------------------------
+# glue
+# ---------------------------------------------------------------------------
+
+def test_rope_kv_append_bitwise():
+    h, h_kv, d_h, ps = 32, 8, 128, 16
+    M = 5
+    qkv = synth.normal((M, (h + 2 * h_kv) * d_h), seed=13).to(torch.bfloat16)
+    pos = np.array([0, 1, 17, 255, 4000], np.int32)
+    cos_t, sin_t = synth.rope_tables(4096, d_h)
+    pages = 12
+    kp = torch.zeros((pages, h_kv, ps, d_h), dtype=torch.bfloat16, device=dev())
+    vp = torch.zeros_like(kp)
+    slots = np.array([3, 16 * 5 + 2, 16 * 11 + 15, 16 * 7, 16 * 2 + 9], np.int32)
+    qo = torch.empty((M, h, d_h), dtype=torch.bfloat16, device=dev())
+    L.bi_rope_kv_append(qkv.to(dev()), h, h_kv, d_h, torch.from_numpy(pos).to(dev()),
+                        cos_t.to(dev()), sin_t.to(dev()), torch.from_numpy(slots).to(dev()), qo,
+                        kp, vp)
+    x = qkv.float().numpy().reshape(M, h + 2 * h_kv, d_h)
+    rq = oracle.rope(x[:, :h], pos, cos_t, sin_t, round_bf16=True)
+    rk = oracle.rope(x[:, h:h + h_kv], pos, cos_t, sin_t, round_bf16=True)
+    assert bits_equal(to_np(qo), rq)
+    kpn, vpn = to_np(kp), to_np(vp)
+    for i, s in enumerate(slots):
+        assert bits_equal(kpn[s // ps, :, s % ps], rk[i])
+        assert bits_equal(vpn[s // ps, :, s % ps], x[i, h + h_kv:])
+    # no tables: plain split and copy
+    qo2 = torch.empty_like(qo)
+    L.bi_rope_kv_append(qkv.to(dev()), h, h_kv, d_h, None, None, None,
+                        torch.from_numpy(slots).to(dev()), qo2, kp, vp)
+    assert bits_equal(to_np(qo2), x[:, :h])
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_add_and_silu_mul_bitwise(dt):
+    a = synth.normal((3, 4104), seed=1).to(DT[dt])
+    b = synth.normal((3, 4104), seed=2).to(DT[dt])
+    y = torch.empty_like(a, device=dev())
+    L.bi_add(a.to(dev()), b.to(dev()), y)
+    assert bits_equal(to_np(y), oracle.add(a, b, round_bf16=(dt == "bf16")))
+    a7 = synth.normal((13,), seed=3).to(DT[dt])  # ragged tail
+    y7 = torch.empty_like(a7, device=dev())
+    L.bi_add(a7.to(dev()), a7.to(dev()), y7)
+    assert bits_equal(to_np(y7), oracle.add(a7, a7, round_bf16=(dt == "bf16")))
+    gu = synth.normal((4, 2 * 1024), seed=4, std=3.0).to(DT[dt])
+    o = torch.empty((4, 1024), dtype=DT[dt], device=dev())
+    L.bi_silu_mul(gu.to(dev()), o)
+    assert bits_equal(to_np(o), oracle.silu_mul(gu, round_bf16=(dt == "bf16")))
+
+
+def test_argmax_and_embed():
+    x = synth.normal((6, 128256), seed=5)
+    x[1, [7, 100000]] = 9.0
+    x[2] = 0.0
+    x[3, [5, 6]] = torch.tensor([-0.0, 0.0])
+    x[3, :5] = -1.0
+    idx = torch.empty(6, dtype=torch.int32, device=dev())
+    L.bi_argmax(x.to(dev()), idx)
+    assert np.array_equal(idx.cpu().numpy(), oracle.argmax(x))
+    table = synth.normal((1000, 4096), seed=6).to(torch.bfloat16)
+    ids = torch.tensor([0, 999, 5, 5], dtype=torch.int32)
+    out = torch.empty((4, 4096), dtype=torch.bfloat16, device=dev())
+    L.bi_embed(table.to(dev()), ids.to(dev()), out)
+    assert torch.equal(out.cpu().view(torch.int16), table[ids.long()].view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# fail-closed argument checks
+# ---------------------------------------------------------------------------
+
+def test_unsupported_configs_fail_closed():
+    q = torch.zeros((1, 6, 128), dtype=torch.bfloat16, device=dev())
+    kp = torch.zeros((4, 2, 16, 128), dtype=torch.bfloat16, device=dev())
+    bt = torch.zeros((1, 4), dtype=torch.int32, device=dev())
+    kvl = torch.ones(1, dtype=torch.int32, device=dev())
+    off = torch.tensor([0, 1], dtype=torch.int32, device=dev())
+    ml = torch.zeros((1, 6, 2), device=dev())
+    acc = torch.zeros((1, 6, 128), device=dev())
+    with pytest.raises(L.BiError) as e:   # group of 3 query heads per kv head
+        L.bi_decode_attn(q, kp, kp, bt, kvl, off, 1, 256, 0.1, ml, acc)
+    assert e.value.status == L.BI_ERR_UNSUPPORTED
+    with pytest.raises(L.BiError) as e:   # chunk 128 not provided
+        L.bi_decode_attn(q[:, :4].contiguous(), kp, kp, bt, kvl, off, 1, 128, 0.1, ml, acc)
+    assert e.value.status == L.BI_ERR_UNSUPPORTED
+    A = torch.zeros((2, 12), dtype=torch.bfloat16, device=dev())
+    with pytest.raises(L.BiError) as e:   # K % 8 != 0
+        L.bi_gemm(A, torch.zeros((4, 12), dtype=torch.bfloat16, device=dev()),
+                  torch.zeros((2, 4), dtype=torch.bfloat16, device=dev()))
+    assert e.value.status == L.BI_ERR_UNSUPPORTED

@@ -1,0 +1,70 @@
+"""Host-side checks of the C-ABI library that need no GPU: it loads, exports
+every function include/bi.h declares, and its host helpers compute what the
+header says."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT, golden
+
+L = pytest.importorskip("invariant_bi_rmsnorm_amd._lib")
+
+
+def declared_functions():
+    names = []
+    for f in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if f.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", f)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names += re.findall(r"^\s*[A-Za-z_][\w \*]*?\b(bi_\w+)\s*\(", src, re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.load()
+    decl = declared_functions()
+    assert len(decl) >= 15
+    missing = [n for n in decl if not hasattr(lib, n)]
+    assert not missing, missing
+    # the binding wraps exactly the declared functions
+    assert sorted(L.SIGNATURES) == decl
+
+
+def test_status_strings_and_version():
+    lib = L.load()
+    assert lib.bi_abi_version() == 1
+    assert lib.bi_status_string(0) == b"ok"
+    assert lib.bi_status_string(2) == b"unsupported configuration"
+    assert lib.bi_status_string(99) == b"unknown status"
+
+
+def test_chunk_offsets_printed_example():
+    g = golden("split_count.txt")
+    off = L.bi_chunk_offsets([int(g["seq_len"])], int(g["split_tile"]))
+    assert off.tolist() == [0, int(g["num_splits"])]
+    assert L.bi_chunk_offsets([1, 256, 257, 0], 256).tolist() == [0, 1, 2, 4, 4]
+    assert L.bi_attn_partials_bytes(10, 32, 128) == 10 * 32 * 130 * 4
+
+
+def test_invalid_arguments_rejected_before_launch():
+    lib = L.load()
+    # M < 0 is rejected on the host; nothing touches a GPU
+    st = lib.bi_rmsnorm(None, None, None, -1, 16, ctypes.c_float(1e-5), 1, None)
+    assert st == L.BI_ERR_INVALID
+    assert b"bad shape" in lib.bi_last_error()
+    st = lib.bi_gemm(None, None, None, 4, 4, 4, 1, 1, None)   # null pointers
+    assert st == L.BI_ERR_INVALID
+    st = lib.bi_gemm(None, None, None, 4, 4, 4, 0, 1, None)   # f32 in, bf16 out
+    assert st == L.BI_ERR_UNSUPPORTED
+    assert lib.bi_rmsnorm(None, None, None, 0, 16, ctypes.c_float(1e-5), 1, None) == L.BI_OK
+
+
+def test_binding_argument_counts_match_header():
+    src = open(os.path.join(ROOT, "include", "bi.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    for m in re.finditer(r"\b(bi_\w+)\s*\(([^)]*)\)\s*;", src):
+        name, params = m.group(1), m.group(2).strip()
+        n = 0 if params in ("", "void") else params.count(",") + 1
+        assert len(L.SIGNATURES[name][1]) == n, name
