@@ -1,0 +1,346 @@
+#!/usr/bin/env python3
+"""Decode throughput of the batch-invariant path on one MI355X.
+
+Workload (one "step"): a decode step of a 32-layer Llama-3-8B-shaped model
+(d 4096, 32/8 heads of 128, SwiGLU 14336, vocab 128256, bf16 weights
+N(0, 0.02) drawn on the device) for a batch of 64 requests whose KV lengths
+are uniform in 32..4096 (seeded), KV history N(0, 1) in 16-token pages
+scattered over a pool 1.25x the live pages.  Every kernel of the step is a
+libbi.so call: per layer RMSNorm, QKV GEMM, RoPE + KV append, split-KV
+decode attention, serial merge, O GEMM, add, RMSNorm, gate/up GEMM,
+SiLU-mul, down GEMM, add; then RMSNorm, LM-head GEMM (fp32 logits), argmax.
+The KV lengths stay fixed across timed steps (each step rewrites the slot of
+the token it decodes), so every step does the same work.
+
+Prints one JSON line.  `value` = decode tokens/s of the whole step (the
+step is captured in a HIP graph and replayed; the graph's logits are
+checked bitwise against an eager step first).  The same step on the
+batch-adaptive twins (bi_*_free) is timed the same way over the same KV
+pool and weights: `invariance_overhead_pct` = invariant step time / twin
+step time - 1.  `sweep` repeats both at other batch sizes (1, 7, 32 by
+default).  `roofline` is for the
+kernel with the largest share of step time, timed with HIP events on the
+launch stream in a second timed region of eager steps; its algorithmic
+bytes are stated in the design doc.  `cpu_baseline` times the CPU oracle on a
+bounded sample (8 of the 64 requests through one decoder layer plus the
+LM head) and scales it to the full step.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # B/s, MI355X
+BF16_PEAK = 2.5e15         # FLOP/s dense MFMA
+METRIC = "decode tokens/s @Llama-3-8B shape, batch 1–64; HBM GB/s % peak; invariance overhead %"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--batch", type=int, default=64)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", default="1,7,32", help="extra batch sizes ('' for none)")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def model_config(args):
+    from dataclasses import replace
+    from invariant_bi_rmsnorm_amd.model import LLAMA3_8B
+    return replace(LLAMA3_8B, layers=args.layers)
+
+
+def build_workload(args, B, torch, dev, w, free=False):
+    """KV pool, engine(s) and the packed decode step for batch B; free=True
+    also builds an engine on the batch-adaptive twins over the same pool."""
+    import synth
+    from invariant_bi_rmsnorm_amd.model import Engine, KVPool, Segment
+    cfg = model_config(args)
+    kv_len = synth.uniform_lengths(B, 32, 4096, seed=args.seed + 11)
+    place = synth.scatter_pages(kv_len, cfg.page_size, seed=args.seed + 12)
+    pool = KVPool(cfg, place.num_pages, dev)
+    g = torch.Generator(device=dev).manual_seed(args.seed + 13)
+    for li in range(cfg.layers):
+        pool.k[li].normal_(generator=g)
+        pool.v[li].normal_(generator=g)
+    eng = Engine(cfg, w, pool, dev, max_rows=B, max_pages_per_req=max(place.max_pages, 257))
+    twin = Engine(cfg, w, pool, dev, max_rows=B, max_pages_per_req=max(place.max_pages, 257),
+                  free=True) if free else None
+    toks = synth.token_ids(B, cfg.vocab, seed=args.seed + 15)
+    segs = []
+    for r in range(B):
+        npg = (int(kv_len[r]) + cfg.page_size - 1) // cfg.page_size
+        segs.append(Segment(pages=[int(p) for p in place.block_table[r, :npg]],
+                            pos0=int(kv_len[r]) - 1, tokens=[int(toks[r])]))
+    meta = eng.upload(eng.pack(segs))
+    return cfg, eng, twin, meta, kv_len, place
+
+
+def algorithmic_bytes(name, cfg, B, kv_len, meta):
+    """Bytes one launch must move at minimum."""
+    if name == "decode_attn":
+        kv = int(sum(kv_len)) * cfg.h_kv * cfg.d_h * 2 * 2
+        q = B * cfg.h * cfg.d_h * 2
+        part = meta["total_chunks"] * cfg.h * (cfg.d_h + 2) * 4
+        return kv + q + part
+    shapes = {"gemm_qkv": (cfg.qkv_out, cfg.d), "gemm_o": (cfg.d, cfg.h * cfg.d_h),
+              "gemm_gate_up": (2 * cfg.ffn, cfg.d), "gemm_down": (cfg.d, cfg.ffn),
+              "gemm_lm_head": (cfg.vocab, cfg.d)}
+    if name in shapes:
+        N, K = shapes[name]
+        out_b = 4 if name == "gemm_lm_head" else 2
+        return 2 * N * K + 2 * B * K + out_b * B * N
+    if name == "merge":
+        return meta["total_chunks"] * cfg.h * (cfg.d_h + 2) * 4 + B * cfg.h * cfg.d_h * 2
+    return None
+
+
+def time_steps(eng, meta, steps, torch, graph):
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            eng.forward(meta)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def capture(eng, meta, torch, warmup):
+    """Eager warmup, then the step captured in a HIP graph; the graph's
+    logits must equal an eager step's bit for bit over several replays with
+    eager work in between, else the eager step is timed."""
+    for _ in range(max(warmup, 1)):
+        ref = eng.forward(meta)
+    torch.cuda.synchronize()
+    ref_logits = ref.logits.clone()
+    try:
+        graph = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(graph, stream=s):
+                out = eng.forward(meta)
+        torch.cuda.current_stream().wait_stream(s)
+        same = True
+        for _ in range(3):
+            graph.replay()
+            torch.cuda.synchronize()
+            same &= bool(torch.equal(out.logits.view(torch.int32), ref_logits.view(torch.int32)))
+            eng.forward(meta)          # eager work between replays
+            torch.cuda.synchronize()
+        if not same:
+            log("graph replay differs from the eager step; timing eager")
+            return None, False
+        return graph, True
+    except Exception as e:  # capture unsupported -> eager timing
+        log(f"graph capture failed ({e}); timing eager")
+        return None, None
+
+
+def per_kernel_times(eng, meta, steps, torch):
+    """Eager steps with a HIP event pair around every kernel, on the stream
+    the kernels are launched on.  A short device spin before each start
+    event keeps the GPU busy while the host enqueues the event and the
+    kernel, so host launch gaps stay out of the measured interval."""
+    events = {}
+
+    spin = getattr(torch.cuda, "_sleep", None)
+
+    def timer(name, fn):
+        if spin is not None:
+            spin(20000)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        events.setdefault(name, []).append((a, b))
+
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        eng.forward(meta, timer=timer)
+    torch.cuda.synchronize()
+    per = {}
+    for name, lst in events.items():
+        ms = [a.elapsed_time(b) for a, b in lst]
+        per[name] = {"launches_per_step": len(ms) // steps, "avg_us": 1e3 * sum(ms) / len(ms),
+                     "total_ms_per_step": sum(ms) / steps}
+    return per
+
+
+def run_batch(args, B, torch, dev, w, want_detail):
+    cfg, eng, twin, meta, kv_len, place = build_workload(args, B, torch, dev, w, free=True)
+    log(f"B={B}: {int(sum(kv_len))} KV tokens, {meta['total_chunks']} chunks")
+    res = {"B": B}
+    for tag, e in (("inv", eng), ("free", twin)):
+        graph, ok = (None, None) if args.no_graph else capture(e, meta, torch, args.warmup)
+        sec = time_steps(e, meta, args.steps, torch, graph)
+        res[tag] = {"ms_per_step": sec * 1e3, "tokens_per_s": B / sec,
+                    "graph": graph is not None, "graph_matches_eager": ok}
+        del graph
+    res["invariance_overhead_pct"] = 100.0 * (res["inv"]["ms_per_step"] /
+                                              res["free"]["ms_per_step"] - 1.0)
+    step_bytes = (cfg.weight_bytes() - 2 * cfg.vocab * cfg.d
+                  + int(sum(kv_len)) * cfg.kv_bytes_per_token())
+    res["step_bytes"] = step_bytes
+    res["hbm_frac_of_step_bound"] = (step_bytes / (res["inv"]["ms_per_step"] * 1e-3)) / HBM_PEAK
+    log(f"B={B}: invariant {res['inv']['ms_per_step']:.3f} ms/step, twins "
+        f"{res['free']['ms_per_step']:.3f} ms/step")
+    if not want_detail:
+        return res, None
+    # second timed region: eager steps, HIP events around every kernel
+    per = per_kernel_times(eng, meta, args.steps, torch)
+    per_free = per_kernel_times(twin, meta, args.steps, torch)
+    detail = {"per_kernel": per, "per_kernel_free": per_free, "cfg": cfg, "kv_len": kv_len,
+              "meta": meta, "eng": eng, "weights": w, "place": place}
+    return res, detail
+
+
+def cpu_baseline(args, detail, B):
+    """Oracle on a bounded sample: S requests through one decoder layer at
+    their own KV lengths, plus final norm + LM head for those rows; scaled to
+    tokens/s of the 32-layer step."""
+    import numpy as np
+    import oracle
+    import synth
+    cfg, kv_len = detail["cfg"], detail["kv_len"]
+    S = min(8, B)
+    idx = list(range(S))
+    lens = kv_len[idx]
+    place = synth.scatter_pages(lens, cfg.page_size, seed=args.seed + 21)
+    shape = (place.num_pages, cfg.h_kv, cfg.page_size, cfg.d_h)
+    kp = synth.normal(shape, seed=args.seed + 22).numpy()
+    vp = synth.normal(shape, seed=args.seed + 23).numpy()
+    lw = detail["weights"].layers[0]
+    W = {k: getattr(lw, k).float().cpu().numpy() for k in
+         ("attn_norm", "wqkv", "wo", "ffn_norm", "wgu", "wdown")}
+    lm = detail["weights"].lm_head.float().cpu().numpy()
+    fn = detail["weights"].final_norm.float().cpu().numpy()
+    cos_t, sin_t = synth.rope_tables(4096 + 16, cfg.d_h, cfg.rope_theta)
+    h = synth.normal((S, cfg.d), seed=args.seed + 24, std=1.0).numpy()
+    pos = lens - 1
+    hd, kvd = cfg.h * cfg.d_h, cfg.h_kv * cfg.d_h
+    t0 = time.perf_counter()
+    x = oracle.rmsnorm(h, W["attn_norm"], cfg.eps, True)
+    qkv = oracle.gemm(x, W["wqkv"], True)
+    q = oracle.rope(qkv[:, :hd].reshape(S, cfg.h, cfg.d_h), pos, cos_t, sin_t, True)
+    k = oracle.rope(qkv[:, hd:hd + kvd].reshape(S, cfg.h_kv, cfg.d_h), pos, cos_t, sin_t, True)
+    for r in range(S):
+        p = int(pos[r])
+        pg = place.block_table[r, p // cfg.page_size]
+        kp[pg, :, p % cfg.page_size] = k[r]
+        vp[pg, :, p % cfg.page_size] = qkv[r, hd + kvd:].reshape(cfg.h_kv, cfg.d_h)
+    a = oracle.decode_attn(q, kp, vp, place.block_table, lens, cfg.h_kv, cfg.page_size,
+                           cfg.kv_chunk, cfg.scale, True)
+    h = oracle.add(h, oracle.gemm(a.reshape(S, hd), W["wo"], True), True)
+    x = oracle.rmsnorm(h, W["ffn_norm"], cfg.eps, True)
+    h = oracle.add(h, oracle.gemm(oracle.silu_mul(oracle.gemm(x, W["wgu"], True), True),
+                                  W["wdown"], True), True)
+    t_layer = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    logits = oracle.gemm(oracle.rmsnorm(h, fn, cfg.eps, True), lm, False)
+    oracle.argmax(logits)
+    t_head = time.perf_counter() - t1
+    per_token = (cfg.layers * t_layer + t_head) / S
+    return {"value": 1.0 / per_token, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{S} of {B} requests (KV lengths {int(lens.min())}..{int(lens.max())}) "
+                      f"through 1 of {cfg.layers} decoder layers ({t_layer:.2f} s) plus final "
+                      f"norm + LM head ({t_head:.2f} s), scaled to {cfg.layers} layers",
+            "sample_seconds": t_layer + t_head}
+
+
+def _rounded(d):
+    return {k: (round(v, 3) if isinstance(v, float) else v) for k, v in d.items()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path is "
+              "data-parallel across GPUs and nothing here uses a second device", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from invariant_bi_rmsnorm_amd import _lib
+    from invariant_bi_rmsnorm_amd.model import init_weights
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    _lib.load()
+    dev = torch.device("cuda:0")
+    cfg = model_config(args)
+    w = init_weights(cfg, args.seed + 14, dev, source="device")
+    log(f"weights drawn ({cfg.weight_bytes() / 1e9:.2f} GB)")
+    B = args.batch
+    res, detail = run_batch(args, B, torch, dev, w, want_detail=True)
+    per, per_free = detail["per_kernel"], detail["per_kernel_free"]
+    kv_len, meta = detail["kv_len"], detail["meta"]
+    for name in per:
+        b = algorithmic_bytes(name, cfg, B, kv_len, meta)
+        if b is not None:
+            per[name]["alg_bytes"] = b
+            per[name]["GBps"] = b / (per[name]["avg_us"] * 1e-6) / 1e9
+            per[name]["hbm_frac"] = per[name]["GBps"] * 1e9 / HBM_PEAK
+    dom = max((n for n in per if "alg_bytes" in per[n]),
+              key=lambda n: per[n]["total_ms_per_step"])
+    b = per[dom]["alg_bytes"]
+    achieved = b / (per[dom]["avg_us"] * 1e-6) / 1e9
+    rl = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK / 1e9,
+          "unit": "GB/s", "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": None,
+          "avg_launch_us": round(per[dom]["avg_us"], 2), "alg_bytes_per_launch": b}
+    out = {
+        "metric": METRIC, "value": round(res["inv"]["tokens_per_s"], 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(res["inv"]["ms_per_step"], 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "llama3-8b-shaped decode step, 32 layers, batch 64, "
+                               "KV lengths uniform 32-4096, kv chunk 256, 16-token pages",
+                   "layers": cfg.layers, "global_batch": B, "kv_tokens": int(sum(kv_len)),
+                   "parallelism": "none (1 GPU)"},
+        "roofline": rl,
+        "step_hbm_frac": round(res["hbm_frac_of_step_bound"], 4),
+        "invariance_overhead_pct": round(res["invariance_overhead_pct"], 2),
+        "twin_tokens_per_s": round(res["free"]["tokens_per_s"], 1),
+        "graph": res["inv"]["graph"], "graph_matches_eager": res["inv"]["graph_matches_eager"],
+        "per_kernel": {k: _rounded(v) for k, v in per.items()},
+        "per_kernel_twin": {k: _rounded(v) for k, v in per_free.items()},
+    }
+    sweep = [int(x) for x in args.sweep.split(",") if x.strip()]
+    if sweep:
+        keep = detail
+        detail = None
+        out["sweep"] = {}
+        for b2 in sweep:
+            r2, _ = run_batch(args, b2, torch, dev, w, want_detail=False)
+            out["sweep"][str(b2)] = {
+                "tokens_per_s": round(r2["inv"]["tokens_per_s"], 1),
+                "ms_per_step": round(r2["inv"]["ms_per_step"], 3),
+                "twin_tokens_per_s": round(r2["free"]["tokens_per_s"], 1),
+                "invariance_overhead_pct": round(r2["invariance_overhead_pct"], 2),
+                "step_hbm_frac": round(r2["hbm_frac_of_step_bound"], 4)}
+            torch.cuda.empty_cache()
+        detail = keep
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(args, detail, B)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -87,6 +87,15 @@ const char *bi_last_error(void);
 bi_status bi_rmsnorm(const void *x, const void *gamma, void *y, int M, int d, float eps,
                      int dtype, bi_stream stream);
 
+/* Twin: when M is too small to fill the device, each row is split over
+ * several workgroups whose partial sums meet through fp32 atomics (order
+ * set by scheduling); otherwise one workgroup per row with a different
+ * tree.  Needs bi_rmsnorm_free_workspace_bytes(M, d) bytes of device
+ * workspace. */
+size_t bi_rmsnorm_free_workspace_bytes(int M, int d);
+bi_status bi_rmsnorm_free(const void *x, const void *gamma, void *y, int M, int d, float eps,
+                          int dtype, void *workspace, size_t workspace_bytes, bi_stream stream);
+
 /* ---------------------------------------------------------------------- */
 /* GEMM  C = A W^T                                                        */
 /* ---------------------------------------------------------------------- */
@@ -107,6 +116,14 @@ bi_status bi_rmsnorm(const void *x, const void *gamma, void *y, int M, int d, fl
  */
 bi_status bi_gemm(const void *A, const void *W, void *C, int M, int N, int K, int in_dtype,
                   int out_dtype, bi_stream stream);
+
+/* Twin: picks its tiling from M and, when M x N offers too few tiles to fill
+ * the device, splits K over workgroups that add fp32 partials with atomics
+ * (order undefined) -- the split-K the pages describe.  Needs
+ * bi_gemm_free_workspace_bytes(M, N, K) bytes of device workspace. */
+size_t bi_gemm_free_workspace_bytes(int M, int N, int K);
+bi_status bi_gemm_free(const void *A, const void *W, void *C, int M, int N, int K, int in_dtype,
+                       int out_dtype, void *workspace, size_t workspace_bytes, bi_stream stream);
 
 /* ---------------------------------------------------------------------- */
 /* split-KV attention over a paged KV cache                               */
@@ -151,8 +168,8 @@ size_t bi_attn_partials_bytes(int total_chunks, int h, int d_h);
  * entry).  Writes part_ml [total_chunks][h][2] and part_acc
  * [total_chunks][h][d_h] (device fp32).
  * Supported (anything else returns BI_ERR_UNSUPPORTED): d_h in {64, 128};
- * h % h_kv == 0 with h/h_kv in {2, 4}; kv_chunk in {64, 256}; page_size in
- * {16, 32, 64}; dtype BI_F32 or BI_BF16.  Every row of q, k and v is
+ * h % h_kv == 0 with h/h_kv in {2, 4}; kv_chunk in {64, 256}; page_size 16;
+ * dtype BI_F32 or BI_BF16.  Every row of q, k and v is
  * 16-byte aligned.
  */
 bi_status bi_decode_attn(const void *q, const void *k_pool, const void *v_pool,
@@ -193,6 +210,35 @@ bi_status bi_prefill_attn(const void *q, const int32_t *q_start, const int32_t *
                           const int32_t *block_table, int h, int h_kv, int d_h, int page_size,
                           int max_pages, int kv_chunk, float scale, int dtype, void *out,
                           bi_stream stream);
+
+/*
+ * Twins.  bi_decode_attn_free picks one split length per request from the
+ * batch, the longest sequence and the device's 256 compute units (the
+ * occupancy policy quoted on "Batch invariance and reproducible
+ * inference", "From batch size to reduction tree": the batch size divides
+ * the core budget, which sets the split count and chunk length), runs the
+ * partials and merges them, writing out [B][h][d_h].  max_kv_len is the
+ * host's bound on kv_len.  Workspace: bi_decode_attn_free_workspace_bytes.
+ * bi_merge_partials_free takes the same arguments as bi_merge_partials but
+ * combines each request's chunks from the last to the first, another fixed
+ * order whose results differ in ulps.  bi_prefill_attn_free splits each row's keys at multiples of a
+ * length chosen from the row count, counted from the start of the prefill
+ * chunk rather than from position 0.
+ */
+size_t bi_decode_attn_free_workspace_bytes(int B, int h, int d_h, int max_kv_len);
+bi_status bi_decode_attn_free(const void *q, const void *k_pool, const void *v_pool,
+                              const int32_t *block_table, const int32_t *kv_len, int B,
+                              int max_kv_len, int h, int h_kv, int d_h, int page_size,
+                              int max_pages, float scale, int dtype, void *workspace,
+                              size_t workspace_bytes, void *out, bi_stream stream);
+bi_status bi_merge_partials_free(const float *part_ml, const float *part_acc,
+                                 const int32_t *chunk_off, int B, int h, int d_h, void *out,
+                                 int out_dtype, bi_stream stream);
+bi_status bi_prefill_attn_free(const void *q, const int32_t *q_start, const int32_t *q_pos0,
+                               int R, int T, const void *k_pool, const void *v_pool,
+                               const int32_t *block_table, int h, int h_kv, int d_h,
+                               int page_size, int max_pages, float scale, int dtype, void *out,
+                               bi_stream stream);
 
 /* ---------------------------------------------------------------------- */
 /* elementwise glue of a Llama-shaped layer (no reductions)               */

@@ -43,6 +43,20 @@ SIGNATURES = {
     "bi_add": (_c_int, [_vp, _vp, _vp, _c_long, _c_int, _vp]),
     "bi_silu_mul": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _vp]),
     "bi_argmax": (_c_int, [_vp, _vp, _c_int, _c_int, _vp]),
+    # batch-adaptive twins
+    "bi_rmsnorm_free_workspace_bytes": (_c_size, [_c_int, _c_int]),
+    "bi_rmsnorm_free": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_float, _c_int, _vp, _c_size,
+                                 _vp]),
+    "bi_gemm_free_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
+    "bi_gemm_free": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _c_size,
+                              _vp]),
+    "bi_decode_attn_free_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
+    "bi_decode_attn_free": (_c_int, [_vp, _vp, _vp, _vp, _vp] + [_c_int] * 7
+                            + [_c_float, _c_int, _vp, _c_size, _vp, _vp]),
+    "bi_merge_partials_free": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _c_int,
+                                        _vp]),
+    "bi_prefill_attn_free": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp]
+                             + [_c_int] * 5 + [_c_float, _c_int, _vp, _vp]),
 }
 
 _lib = None
@@ -206,3 +220,86 @@ def bi_argmax(x, idx, stream=None):
     M, V = x.shape
     _check("bi_argmax", load().bi_argmax(_ptr(x), _i32(idx), M, V, _stream(stream)))
     return idx
+
+
+# ---------------------------------------------------------------------------
+# batch-adaptive twins (same mathematics, split points chosen from the batch)
+# ---------------------------------------------------------------------------
+
+class Workspace:
+    """A grow-only device byte buffer for the twins' workspace arguments."""
+
+    def __init__(self, device=None):
+        self.device = device or torch.device("cuda")
+        self.buf = torch.empty(0, dtype=torch.uint8, device=self.device)
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        if self.buf.numel() < nbytes:
+            self.buf = torch.empty(max(nbytes, 2 * self.buf.numel()), dtype=torch.uint8,
+                                   device=self.device)
+        return self.buf
+
+
+_ws = {}
+
+
+def _workspace(nbytes: int, device) -> tuple:
+    w = _ws.get(str(device))
+    if w is None:
+        w = _ws[str(device)] = Workspace(device)
+    b = w.get(max(nbytes, 1))
+    return ctypes.c_void_p(b.data_ptr()), b.numel()
+
+
+def bi_rmsnorm_free(x, gamma, y, eps: float, stream=None):
+    M, d = x.numel() // x.shape[-1], x.shape[-1]
+    ws, n = _workspace(load().bi_rmsnorm_free_workspace_bytes(M, d), x.device)
+    _check("bi_rmsnorm_free", load().bi_rmsnorm_free(_ptr(x), _ptr(gamma), _ptr(y), M, d, eps,
+                                                     _dt(x), ws, n, _stream(stream)))
+    return y
+
+
+def bi_gemm_free(A, W, C, stream=None):
+    M, K = A.shape
+    N = W.shape[0]
+    if W.shape[1] != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch A{tuple(A.shape)} W{tuple(W.shape)} C{tuple(C.shape)}")
+    ws, n = _workspace(load().bi_gemm_free_workspace_bytes(M, N, K), A.device)
+    _check("bi_gemm_free", load().bi_gemm_free(_ptr(A), _ptr(W), _ptr(C), M, N, K, _dt(A),
+                                               _dt(C), ws, n, _stream(stream)))
+    return C
+
+
+def bi_decode_attn_free(q, k_pool, v_pool, block_table, kv_len, max_kv_len: int, scale: float,
+                        out, stream=None):
+    """Decode attention with the occupancy-driven split policy; writes the
+    merged output directly.  max_kv_len: the host's bound on kv_len."""
+    B, h, d_h = q.shape
+    _, h_kv, page_size, _ = k_pool.shape
+    ws, n = _workspace(load().bi_decode_attn_free_workspace_bytes(B, h, d_h, max_kv_len),
+                       q.device)
+    _check("bi_decode_attn_free", load().bi_decode_attn_free(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _i32(block_table), _i32(kv_len), B, max_kv_len, h,
+        h_kv, d_h, page_size, block_table.shape[1], scale, _dt(q), ws, n, _ptr(out),
+        _stream(stream)))
+    return out
+
+
+def bi_merge_partials_free(part_ml, part_acc, chunk_off, out, stream=None):
+    B, h, d_h = out.shape
+    _check("bi_merge_partials_free", load().bi_merge_partials_free(
+        _ptr(part_ml), _ptr(part_acc), _i32(chunk_off), B, h, d_h, _ptr(out), _dt(out),
+        _stream(stream)))
+    return out
+
+
+def bi_prefill_attn_free(q, q_start, q_pos0, k_pool, v_pool, block_table, scale: float, out,
+                         stream=None):
+    T, h, d_h = q.shape
+    _, h_kv, page_size, _ = k_pool.shape
+    R = q_pos0.numel()
+    _check("bi_prefill_attn_free", load().bi_prefill_attn_free(
+        _ptr(q), _i32(q_start), _i32(q_pos0), R, T, _ptr(k_pool), _ptr(v_pool),
+        _i32(block_table), h, h_kv, d_h, page_size, block_table.shape[1], scale, _dt(q),
+        _ptr(out), _stream(stream)))
+    return out

@@ -22,6 +22,8 @@
 // Prefill runs the same device code per query row and merges the chunks on
 // the fly with the merge kernel's formula, so prefill row t equals a decode
 // of kv_len = t + 1 bit for bit.
+#include <cmath>
+
 #include "api.h"
 #include "common.h"
 
@@ -92,7 +94,8 @@ __device__ __forceinline__ void chunk_partial(char* lds, int n, float scale,
   typedef AttnLds<DT, DH, R, NW> L;
   constexpr int DPL = S::DPL;
   constexpr int NT = 64 * NW;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int u = tid;  // this lane's key within the chunk
   const float* qs = reinterpret_cast<const float*>(lds + L::Q_OFF);
   float* ps = reinterpret_cast<float*>(lds + L::P_OFF);
@@ -239,56 +242,60 @@ __device__ __forceinline__ void chunk_partial(char* lds, int n, float scale,
   __syncthreads();  // LDS (p, block partials, K) may be reused by the caller
 }
 
+// Pages hold kPage tokens (the only page size the kernels are built for).
+constexpr int kPage = 16;
+
 // Stage this wave's 64 keys of the chunk (keys [j0, j0+n)) of kv head g:
 // K rows into the swizzled LDS block by direct copies, and this lane's V
 // dims into registers.  Keys >= n read key j0 instead (valid memory, never
-// used).  page_size is a multiple of the keys one copy covers and divides 64,
-// so every page index below is wave-uniform and comes from scalar loads.
+// used).  j0 and the wave's first key are multiples of the page size, so
+// each copy instruction (<= 16 keys) and each key's page are wave-uniform
+// and come from scalar loads of the block table.
 template <int DT, int DH, int NW>
 __device__ __forceinline__ void stage_chunk(char* lds, const void* k_pool, const void* v_pool,
                                             const int32_t* bt, int j0, int n, int g, int h_kv,
-                                            int page_size,
                                             uint32_t (&vreg)[64][AttnShape<DT, DH>::VW]) {
   typedef AttnShape<DT, DH> S;
+  static_assert(kPage % S::KPI == 0 && 64 % kPage == 0, "page geometry");
+  constexpr int NP = 64 / kPage;                 // pages per wave
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int wk0 = 64 * wave;           // first key of this wave in the chunk
-  const int nk = min(64, n - wk0);     // keys of this wave (may be <= 0)
-  const int np = 64 / page_size;       // pages per wave
-  const int pg0 = (j0 + wk0) / page_size;
-  const long hstride = (long)page_size * S::RB;  // bytes per (page, head) block
+  const int wk0 = 64 * wave;                     // first key of this wave in the chunk
+  const int nk = min(64, n - wk0);               // keys of this wave (may be <= 0)
+  const long hstride = (long)kPage * S::RB;      // bytes per (page, head) block
   const long pstride = hstride * h_kv;           // bytes per page
   const char* kp = static_cast<const char*>(k_pool) + g * hstride;
   const char* vp = static_cast<const char*>(v_pool) + g * hstride;
-  const int pfall = bt[j0 / page_size];  // page of key j0, stands in for missing keys
+  const int pfall = bt[j0 / kPage];              // stands in for pages past the end
+  int page[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) page[p] = (p * kPage < nk) ? bt[(j0 + wk0) / kPage + p] : pfall;
   // K: one 1 KiB copy covers KPI consecutive keys of one page
 #pragma unroll
   for (int inst = 0; inst < 64 / S::KPI; ++inst) {
-    const int k0 = inst * S::KPI;                    // first key of this copy
-    const int pi = k0 / page_size;                   // uniform
-    const int page = (k0 < nk) ? bt[pg0 + pi] : pfall;
-    const int kk = k0 + lane / S::SLOTS;             // key of this lane
-    const int slot = (k0 < nk) ? (kk % page_size) : 0;
-    const int u = wk0 + kk;                          // key index in the chunk
-    const int c = (lane % S::SLOTS) ^ (u & (S::SW - 1));
-    dma16(kp + page * pstride + slot * S::RB + 16 * c, lds + (wk0 + k0) * S::RB);
+    const int k0 = inst * S::KPI;
+    const int kk = k0 + lane / S::SLOTS;         // key of this lane within the wave
+    const int slot = (k0 < nk) ? (kk % kPage) : 0;
+    const int c = (lane % S::SLOTS) ^ ((wk0 + kk) & (S::SW - 1));
+    dma16(kp + page[k0 / kPage] * pstride + slot * S::RB + 16 * c, lds + (wk0 + k0) * S::RB);
   }
   // V: lane-per-dim, one row per key of this wave, kept packed
   const long lane_off = (long)lane * S::DPL * S::ES;
-  int page = pfall;
 #pragma unroll
-  for (int k = 0; k < 64; ++k) {
-    if (k % page_size == 0) page = (k < nk) ? bt[pg0 + k / page_size] : pfall;
-    const int slot = (k < nk) ? (k % page_size) : 0;
-    const char* src = vp + page * pstride + slot * S::RB + lane_off;
-    if (S::DPL * S::ES == 2) {
-      vreg[k][0] = *reinterpret_cast<const uint16_t*>(src);
-    } else {
+  for (int p = 0; p < NP; ++p) {
+    const char* pb = vp + page[p] * pstride + lane_off;
 #pragma unroll
-      for (int e = 0; e < S::VW; ++e) vreg[k][e] = reinterpret_cast<const uint32_t*>(src)[e];
+    for (int s = 0; s < kPage; ++s) {
+      const int k = p * kPage + s;
+      const char* src = pb + ((k < nk) ? s : 0) * S::RB;
+      if (S::DPL * S::ES == 2) {
+        vreg[k][0] = *reinterpret_cast<const uint16_t*>(src);
+      } else {
+#pragma unroll
+        for (int e = 0; e < S::VW; ++e) vreg[k][e] = reinterpret_cast<const uint32_t*>(src)[e];
+      }
     }
   }
-  (void)np;
 }
 
 // q vectors of the R heads of group g of one row -> LDS as fp32
@@ -326,7 +333,7 @@ __global__ __launch_bounds__(64 * NW) void k_decode_partials(
   const int32_t* bt = block_table + (long)r * max_pages;
 
   uint32_t vreg[64][S::VW];
-  stage_chunk<DT, DH, NW>(lds, k_pool, v_pool, bt, j0, n, g, h_kv, page_size, vreg);
+  stage_chunk<DT, DH, NW>(lds, k_pool, v_pool, bt, j0, n, g, h_kv, vreg);
   stage_q<DT, DH, R, NW>(lds, q, ((long)r * h + g * R) * DH);
   __syncthreads();
   CO out;
@@ -350,23 +357,55 @@ __global__ __launch_bounds__(64 * NW) void k_decode_partials(
 // ---------------------------------------------------------------------------
 // serial merge: one wave per (request, head); lane owns DH/64 dims
 // ---------------------------------------------------------------------------
-template <int DH, int OUT_DT>
+// REV (twin only): chunks combined from the last to the first.  The
+// partials of request r start at row chunk_off[r] (chunk_off == nullptr:
+// at row r * fixed_stride, with n_r from the twin's split policy).
+__device__ __forceinline__ int free_splits(int s, int chunk2, int* len) {
+  if (s <= 0) {
+    *len = 0;
+    return 0;
+  }
+  int n = max((s + 255) / 256, (s + chunk2 - 1) / chunk2);
+  int l = (s + n - 1) / n;
+  l = (l + 15) & ~15;
+  *len = l;
+  return (s + l - 1) / l;
+}
+
+template <int DH, int OUT_DT, bool REV = false>
 __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part_ml,
                                                const float* __restrict__ part_acc,
                                                const int32_t* __restrict__ chunk_off, int B,
-                                               int h, void* __restrict__ out) {
+                                               int h, void* __restrict__ out,
+                                               const int32_t* __restrict__ kv_len = nullptr,
+                                               int chunk2 = 0, int stride = 0) {
   constexpr int DPL = DH / 64;
   const int wid = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (wid >= B * h) return;
   const int r = wid / h, hi = wid % h;
-  const int c0 = chunk_off[r], n = chunk_off[r + 1] - c0;
-  long row = (long)c0 * h + hi;
+  int c0, n;
+  if (chunk_off != nullptr) {
+    c0 = chunk_off[r];
+    n = chunk_off[r + 1] - c0;
+  } else {
+    int len;
+    c0 = r * stride;
+    n = min(free_splits(kv_len[r], chunk2, &len), stride);
+  }
+  const long o = ((long)r * h + hi) * DH + DPL * lane;
+  if (n <= 0) {  // no keys: the output is defined as zero
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) Elem<OUT_DT>::st(out, o + e, 0.f);
+    return;
+  }
+  const long step = REV ? -(long)h : (long)h;
+  long row = (long)(REV ? c0 + n - 1 : c0) * h + hi;
   float M = part_ml[2 * row], L = part_ml[2 * row + 1];
   float A[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) A[e] = part_acc[row * DH + DPL * lane + e];
   for (int c = 1; c < n; ++c) {
-    row += h;
+    row += step;
     const float mc = part_ml[2 * row], lc = part_ml[2 * row + 1];
     const float Mn = M > mc ? M : mc;
     const float a = exp_fixed(M - Mn), b = exp_fixed(mc - Mn);
@@ -376,9 +415,53 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part_ml
       A[e] = __builtin_fmaf(part_acc[row * DH + DPL * lane + e], b, A[e] * a);
     M = Mn;
   }
-  const long o = ((long)r * h + hi) * DH + DPL * lane;
 #pragma unroll
   for (int e = 0; e < DPL; ++e) Elem<OUT_DT>::st(out, o + e, A[e] / L);
+}
+
+// ---------------------------------------------------------------------------
+// decode twin: split length per request from the occupancy policy
+// (free_splits: at least ceil(s/256) splits, more when the batch leaves cores
+// idle), so the split points of a request move with the batch.  Same chunk
+// arithmetic as the invariant kernel; partial rows at r * stride + c.
+// ---------------------------------------------------------------------------
+template <int DT, int DH, int R>
+__global__ __launch_bounds__(256) void k_decode_free(
+    const void* __restrict__ q, const void* __restrict__ k_pool, const void* __restrict__ v_pool,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ kv_len, int h, int h_kv,
+    int max_pages, float scale, int chunk2, int stride, float* __restrict__ part_ml,
+    float* __restrict__ part_acc) {
+  typedef AttnShape<DT, DH> S;
+  typedef ChunkOut<R, 4, S::DPL> CO;
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int r = blockIdx.x / stride, c = blockIdx.x % stride, g = blockIdx.y;
+  int len;
+  const int s = kv_len[r];
+  const int n_r = free_splits(s, chunk2, &len);
+  if (c >= n_r) return;  // c < stride by the grid, so rows stay inside the workspace
+  const int j0 = c * len;
+  const int n = min(len, s - j0);
+  const int32_t* bt = block_table + (long)r * max_pages;
+  uint32_t vreg[64][S::VW];
+  stage_chunk<DT, DH, 4>(lds, k_pool, v_pool, bt, j0, n, g, h_kv, vreg);
+  stage_q<DT, DH, R, 4>(lds, q, ((long)r * h + g * R) * DH);
+  __syncthreads();
+  CO out;
+  chunk_partial<DT, DH, R, 4>(lds, n, scale, vreg, out);
+#pragma unroll
+  for (int k = 0; k < CO::ITEMS; ++k) {
+    const int item = threadIdx.x + 256 * k;
+    if (item < R * 64) {
+      const int hi2 = item >> 6, ln = item & 63;
+      const long prow = ((long)r * stride + c) * h + g * R + hi2;
+      if (ln == 0) {
+        part_ml[2 * prow] = out.m[k];
+        part_ml[2 * prow + 1] = out.l[k];
+      }
+#pragma unroll
+      for (int e = 0; e < S::DPL; ++e) part_acc[prow * DH + S::DPL * ln + e] = out.acc[k][e];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -387,7 +470,7 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part_ml
 // per request in blocks of QB), stages each chunk once and runs every row's
 // partial, merging serially into per-row running state.
 // ---------------------------------------------------------------------------
-template <int DT, int DH, int R, int NW, int QB>
+template <int DT, int DH, int R, int NW, int QB, bool REL = false>
 __global__ __launch_bounds__(64 * NW) void k_prefill(
     const void* __restrict__ q, const int32_t* __restrict__ q_start,
     const int32_t* __restrict__ q_pos0, int Rq,
@@ -417,19 +500,26 @@ __global__ __launch_bounds__(64 * NW) void k_prefill(
   const int32_t* bt = block_table + (long)r * max_pages;
 
   float Mr[QB][CO::ITEMS], Lr[QB][CO::ITEMS], Ar[QB][CO::ITEMS][DPL];
-  const int nch = pos_last / C + 1;
+  // Chunk boundaries: absolute multiples of C (REL = false, the invariant
+  // path); the twin (REL = true) starts them at the prefill chunk's first
+  // position (rounded down to a page), so they move with the prompt's cuts.
+  const int shift = REL ? ((q_pos0[r] % C) & ~(kPage - 1)) : 0;
+  auto jstart = [&](int c) { return shift == 0 ? c * C : (c == 0 ? 0 : shift + (c - 1) * C); };
+  const int nch = shift == 0 ? pos_last / C + 1
+                             : (pos_last < shift ? 1 : (pos_last - shift) / C + 2);
   for (int c = 0; c < nch; ++c) {
-    const int j0 = c * C;
-    const int nmax = min(C, pos_last + 1 - j0);
+    const int j0 = jstart(c);
+    const int jend = jstart(c + 1);
+    const int nmax = min(jend, pos_last + 1) - j0;
     uint32_t vreg[64][S::VW];
-    stage_chunk<DT, DH, NW>(lds, k_pool, v_pool, bt, j0, nmax, g, h_kv, page_size, vreg);
+    stage_chunk<DT, DH, NW>(lds, k_pool, v_pool, bt, j0, nmax, g, h_kv, vreg);
 #pragma unroll
     for (int qi = 0; qi < QB; ++qi) {
       const int t = t0 + qi;
       if (t < t1) {
         const int pos = pos0 + qi;
-        const int n = pos + 1 - j0;  // keys of this chunk visible to row t
-        if (n > 0) {               // uniform across the workgroup
+        const int n = min(jend, pos + 1) - j0;  // keys of this chunk visible to row t
+        if (n > 0) {                             // uniform across the workgroup
           stage_q<DT, DH, R, NW>(lds, q, ((long)t * h + g * R) * DH);
           __syncthreads();
           CO co;
@@ -491,8 +581,8 @@ struct AttnArgsCheck {
                dtype);
     BI_REQUIRE(kv_chunk == 64 || kv_chunk == 256, BI_ERR_UNSUPPORTED,
                "%s: kv_chunk=%d not in {64,256}", who, kv_chunk);
-    BI_REQUIRE(page_size == 16 || page_size == 32 || page_size == 64, BI_ERR_UNSUPPORTED,
-               "%s: page_size=%d not in {16,32,64}", who, page_size);
+    BI_REQUIRE(page_size == kPage, BI_ERR_UNSUPPORTED, "%s: page_size=%d (kernels are built "
+               "for %d-token pages)", who, page_size, kPage);
     return BI_OK;
   }
 };
@@ -532,36 +622,75 @@ static void decode_r(int R, int nw, const void* q, const void* kp, const void* v
 
 constexpr int kPrefillQB = 8;
 
-template <int DT, int DH, int R, int NW>
+template <int DT, int DH, int R, int NW, bool REL = false>
 static void launch_prefill(const void* q, const int32_t* qs, const int32_t* qp, int Rq, int T,
                            const void* kp, const void* vp, const int32_t* bt, int h, int h_kv,
                            int ps, int mp, float scale, void* out, hipStream_t s) {
   constexpr int lds = AttnLds<DT, DH, R, NW>::BYTES;
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute((const void*)k_prefill<DT, DH, R, NW, kPrefillQB>,
+    (void)hipFuncSetAttribute((const void*)k_prefill<DT, DH, R, NW, kPrefillQB, REL>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     attr = true;
   }
   const int blocks = (T + kPrefillQB - 1) / kPrefillQB + Rq;
-  hipLaunchKernelGGL((k_prefill<DT, DH, R, NW, kPrefillQB>), dim3(blocks, h_kv), dim3(64 * NW),
-                     lds, s, q, qs, qp, Rq, kp, vp, bt, h, h_kv, ps, mp, scale, out);
+  hipLaunchKernelGGL((k_prefill<DT, DH, R, NW, kPrefillQB, REL>), dim3(blocks, h_kv),
+                     dim3(64 * NW), lds, s, q, qs, qp, Rq, kp, vp, bt, h, h_kv, ps, mp, scale, out);
 }
 
-template <int DT, int DH, int R>
+template <int DT, int DH, int R, bool REL = false>
 static void prefill_nw(int nw, const void* q, const int32_t* qs, const int32_t* qp, int Rq, int T,
                        const void* kp, const void* vp, const int32_t* bt, int h, int h_kv, int ps,
                        int mp, float scale, void* out, hipStream_t s) {
-  if (nw == 1) launch_prefill<DT, DH, R, 1>(q, qs, qp, Rq, T, kp, vp, bt, h, h_kv, ps, mp, scale, out, s);
-  else launch_prefill<DT, DH, R, 4>(q, qs, qp, Rq, T, kp, vp, bt, h, h_kv, ps, mp, scale, out, s);
+  if (nw == 1) launch_prefill<DT, DH, R, 1, REL>(q, qs, qp, Rq, T, kp, vp, bt, h, h_kv, ps, mp, scale, out, s);
+  else launch_prefill<DT, DH, R, 4, REL>(q, qs, qp, Rq, T, kp, vp, bt, h, h_kv, ps, mp, scale, out, s);
 }
 
-template <int DT, int DH>
+template <int DT, int DH, bool REL = false>
 static void prefill_r(int R, int nw, const void* q, const int32_t* qs, const int32_t* qp, int Rq,
                       int T, const void* kp, const void* vp, const int32_t* bt, int h, int h_kv,
                       int ps, int mp, float scale, void* out, hipStream_t s) {
-  if (R == 2) prefill_nw<DT, DH, 2>(nw, q, qs, qp, Rq, T, kp, vp, bt, h, h_kv, ps, mp, scale, out, s);
-  else prefill_nw<DT, DH, 4>(nw, q, qs, qp, Rq, T, kp, vp, bt, h, h_kv, ps, mp, scale, out, s);
+  if (R == 2) prefill_nw<DT, DH, 2, REL>(nw, q, qs, qp, Rq, T, kp, vp, bt, h, h_kv, ps, mp, scale, out, s);
+  else prefill_nw<DT, DH, 4, REL>(nw, q, qs, qp, Rq, T, kp, vp, bt, h, h_kv, ps, mp, scale, out, s);
+}
+
+// ---- twin host plumbing --------------------------------------------------
+// Occupancy policy of the decode twin, on the host: the batch and the longest
+// sequence set a second chunk length from the device's compute units; a
+// request then gets max(ceil(s/256), ceil(s/chunk2)) splits.
+struct FreePolicy {
+  int chunk2, stride;
+};
+static FreePolicy free_policy(int B, int h, int h_kv, int max_kv_len) {
+  constexpr int kCUs = 256, kMaxSplits = 64;
+  const double ext_seq = max_kv_len / 64.0;
+  const int ext_cores = (int)(kCUs * (std::log2(ext_seq) > 1.0 ? std::log2(ext_seq) : 1.0));
+  const int group = h / h_kv;
+  const int block_h = group < 16 ? group : 16;
+  const int token_grid = B * ((h + block_h - 1) / block_h);
+  int ms2 = (ext_cores + token_grid - 1) / token_grid;
+  ms2 = ms2 < kMaxSplits ? ms2 : kMaxSplits;
+  ms2 = ms2 > 1 ? ms2 : 1;
+  FreePolicy p;
+  p.chunk2 = (max_kv_len + ms2 - 1) / ms2;
+  const int a = (max_kv_len + 255) / 256;
+  p.stride = a > kMaxSplits ? a : kMaxSplits;  // >= every request's split count
+  return p;
+}
+
+template <int DT, int DH, int R>
+static void launch_decode_free(const void* q, const void* kp, const void* vp, const int32_t* bt,
+                               const int32_t* kvl, int B, int h, int h_kv, int mp, float scale,
+                               FreePolicy pol, float* ml, float* acc, hipStream_t s) {
+  constexpr int lds = AttnLds<DT, DH, R, 4>::BYTES;
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)k_decode_free<DT, DH, R>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    attr = true;
+  }
+  hipLaunchKernelGGL((k_decode_free<DT, DH, R>), dim3(B * pol.stride, h_kv), dim3(256), lds, s,
+                     q, kp, vp, bt, kvl, h, h_kv, mp, scale, pol.chunk2, pol.stride, ml, acc);
 }
 
 }  // namespace bi
@@ -655,4 +784,112 @@ extern "C" bi_status bi_merge_partials(const float* part_ml, const float* part_a
     else hipLaunchKernelGGL((k_merge<64, 0>), grid, dim3(256), 0, s, part_ml, part_acc, chunk_off, B, h, out);
   }
   return launched("bi_merge_partials");
+}
+
+// ---------------------------------------------------------------------------
+// batch-adaptive twins
+// ---------------------------------------------------------------------------
+
+extern "C" size_t bi_decode_attn_free_workspace_bytes(int B, int h, int d_h, int max_kv_len) {
+  if (B < 0 || h <= 0 || d_h <= 0 || max_kv_len <= 0) return 0;
+  const int a = (max_kv_len + 255) / 256;
+  const long stride = a > 64 ? a : 64;
+  return (size_t)B * stride * h * ((size_t)d_h + 2) * sizeof(float);
+}
+
+extern "C" bi_status bi_decode_attn_free(const void* q, const void* k_pool, const void* v_pool,
+                                         const int32_t* block_table, const int32_t* kv_len, int B,
+                                         int max_kv_len, int h, int h_kv, int d_h, int page_size,
+                                         int max_pages, float scale, int dtype, void* workspace,
+                                         size_t workspace_bytes, void* out, bi_stream stream) {
+  using namespace bi;
+  bi_status st = AttnArgsCheck::common("bi_decode_attn_free", h, h_kv, d_h, page_size, 256,
+                                       dtype);
+  if (st != BI_OK) return st;
+  BI_REQUIRE(B >= 0 && max_kv_len >= 1 && max_pages >= 1, BI_ERR_INVALID,
+             "bi_decode_attn_free: bad sizes");
+  if (B == 0) return BI_OK;
+  BI_REQUIRE(q && k_pool && v_pool && block_table && kv_len && workspace && out, BI_ERR_INVALID,
+             "bi_decode_attn_free: null pointer");
+  const size_t need = bi_decode_attn_free_workspace_bytes(B, h, d_h, max_kv_len);
+  BI_REQUIRE(workspace_bytes >= need, BI_ERR_WORKSPACE,
+             "bi_decode_attn_free: workspace %zu < %zu bytes", workspace_bytes, need);
+  const FreePolicy pol = free_policy(B, h, h_kv, max_kv_len);
+  BI_REQUIRE((long)B * pol.stride <= 0x7fffffffL, BI_ERR_INVALID, "bi_decode_attn_free: grid");
+  float* ml = static_cast<float*>(workspace);
+  float* acc = ml + (size_t)B * pol.stride * h * 2;
+  hipStream_t s = as_stream(stream);
+  const int R = h / h_kv;
+#define BI_DF(dt, dh)                                                                         \
+  do {                                                                                        \
+    if (R == 2) launch_decode_free<dt, dh, 2>(q, k_pool, v_pool, block_table, kv_len, B, h,  \
+                                              h_kv, max_pages, scale, pol, ml, acc, s);      \
+    else launch_decode_free<dt, dh, 4>(q, k_pool, v_pool, block_table, kv_len, B, h, h_kv,   \
+                                       max_pages, scale, pol, ml, acc, s);                   \
+  } while (0)
+  if (dtype == BI_BF16) { if (d_h == 128) BI_DF(1, 128); else BI_DF(1, 64); }
+  else { if (d_h == 128) BI_DF(0, 128); else BI_DF(0, 64); }
+#undef BI_DF
+  st = launched("bi_decode_attn_free");
+  if (st != BI_OK) return st;
+  const dim3 grid((unsigned)(((long)B * h + 3) / 4));
+#define BI_MF(dh, od)                                                                          \
+  hipLaunchKernelGGL((k_merge<dh, od, true>), grid, dim3(256), 0, s, ml, acc, nullptr, B, h,  \
+                     out, kv_len, pol.chunk2, pol.stride)
+  if (d_h == 128) { if (dtype == BI_BF16) BI_MF(128, 1); else BI_MF(128, 0); }
+  else { if (dtype == BI_BF16) BI_MF(64, 1); else BI_MF(64, 0); }
+#undef BI_MF
+  return launched("bi_decode_attn_free");
+}
+
+extern "C" bi_status bi_merge_partials_free(const float* part_ml, const float* part_acc,
+                                            const int32_t* chunk_off, int B, int h, int d_h,
+                                            void* out, int out_dtype, bi_stream stream) {
+  using namespace bi;
+  BI_REQUIRE(B >= 0 && h >= 1, BI_ERR_INVALID, "bi_merge_partials_free: bad sizes");
+  BI_REQUIRE(d_h == 64 || d_h == 128, BI_ERR_UNSUPPORTED, "bi_merge_partials_free: d_h=%d", d_h);
+  BI_REQUIRE(out_dtype == BI_F32 || out_dtype == BI_BF16, BI_ERR_UNSUPPORTED,
+             "bi_merge_partials_free: dtype %d", out_dtype);
+  if (B == 0) return BI_OK;
+  BI_REQUIRE(part_ml && part_acc && chunk_off && out, BI_ERR_INVALID,
+             "bi_merge_partials_free: null pointer");
+  hipStream_t s = as_stream(stream);
+  const dim3 grid((unsigned)(((long)B * h + 3) / 4));
+  if (d_h == 128) {
+    if (out_dtype == BI_BF16) hipLaunchKernelGGL((k_merge<128, 1, true>), grid, dim3(256), 0, s, part_ml, part_acc, chunk_off, B, h, out, nullptr, 0, 0);
+    else hipLaunchKernelGGL((k_merge<128, 0, true>), grid, dim3(256), 0, s, part_ml, part_acc, chunk_off, B, h, out, nullptr, 0, 0);
+  } else {
+    if (out_dtype == BI_BF16) hipLaunchKernelGGL((k_merge<64, 1, true>), grid, dim3(256), 0, s, part_ml, part_acc, chunk_off, B, h, out, nullptr, 0, 0);
+    else hipLaunchKernelGGL((k_merge<64, 0, true>), grid, dim3(256), 0, s, part_ml, part_acc, chunk_off, B, h, out, nullptr, 0, 0);
+  }
+  return launched("bi_merge_partials_free");
+}
+
+extern "C" bi_status bi_prefill_attn_free(const void* q, const int32_t* q_start,
+                                          const int32_t* q_pos0, int R, int T, const void* k_pool,
+                                          const void* v_pool, const int32_t* block_table, int h,
+                                          int h_kv, int d_h, int page_size, int max_pages,
+                                          float scale, int dtype, void* out, bi_stream stream) {
+  using namespace bi;
+  // chunk length from the amount of work: short chunks when the grid is small
+  const long wgs = ((long)T / kPrefillQB + R) * h_kv;
+  const int chunk = wgs < 256 ? 64 : 256;
+  bi_status st = AttnArgsCheck::common("bi_prefill_attn_free", h, h_kv, d_h, page_size, chunk,
+                                       dtype);
+  if (st != BI_OK) return st;
+  BI_REQUIRE(R >= 0 && T >= 0 && max_pages >= 1, BI_ERR_INVALID,
+             "bi_prefill_attn_free: bad sizes");
+  if (R == 0 || T == 0) return BI_OK;
+  BI_REQUIRE(q && q_start && q_pos0 && k_pool && v_pool && block_table && out, BI_ERR_INVALID,
+             "bi_prefill_attn_free: null pointer");
+  const int Rg = h / h_kv, nw = chunk / 64;
+  hipStream_t s = as_stream(stream);
+  if (dtype == BI_BF16) {
+    if (d_h == 128) prefill_r<1, 128, true>(Rg, nw, q, q_start, q_pos0, R, T, k_pool, v_pool, block_table, h, h_kv, page_size, max_pages, scale, out, s);
+    else prefill_r<1, 64, true>(Rg, nw, q, q_start, q_pos0, R, T, k_pool, v_pool, block_table, h, h_kv, page_size, max_pages, scale, out, s);
+  } else {
+    if (d_h == 128) prefill_r<0, 128, true>(Rg, nw, q, q_start, q_pos0, R, T, k_pool, v_pool, block_table, h, h_kv, page_size, max_pages, scale, out, s);
+    else prefill_r<0, 64, true>(Rg, nw, q, q_start, q_pos0, R, T, k_pool, v_pool, block_table, h, h_kv, page_size, max_pages, scale, out, s);
+  }
+  return launched("bi_prefill_attn_free");
 }

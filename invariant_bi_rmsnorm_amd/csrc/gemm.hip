@@ -28,6 +28,7 @@ __device__ __forceinline__ f32x4_t mfma(const u32x4_t& a, const u32x4_t& b, cons
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// OUTF32: 0 = bf16 store, 1 = fp32 store, 2 = fp32 atomic add (split-K twin)
 template <int OUTF32>
 __device__ __forceinline__ void store_tile(void* C, const f32x4_t& acc, int row0, int col0, int M,
                                            int N, int lane) {
@@ -38,7 +39,9 @@ __device__ __forceinline__ void store_tile(void* C, const f32x4_t& acc, int row0
     const int row = row0 + 4 * (lane >> 4) + j;
     if (row < M) {
       const long idx = (long)row * N + col;
-      if (OUTF32)
+      if (OUTF32 == 2)
+        atomicAdd(static_cast<float*>(C) + idx, acc[j]);
+      else if (OUTF32 == 1)
         static_cast<float*>(C)[idx] = acc[j];
       else
         static_cast<uint16_t*>(C)[idx] = (uint16_t)f32_to_bf16_bits(acc[j]);
@@ -46,94 +49,236 @@ __device__ __forceinline__ void store_tile(void* C, const f32x4_t& acc, int row0
   }
 }
 
+// The small-M kernels split roles across waves.  Copy waves only issue
+// direct global->LDS copies of the operand the whole workgroup shares, into
+// an NS-slot ring; compute waves only issue register loads of their private
+// operand and run the MFMAs.  A wave's memory counter then tracks one kind of
+// operation, so copy waves can keep many stages in flight while compute waves
+// wait exactly for their own loads.  Copy and compute waves run separate
+// loops with the same barrier sequence (one s_barrier per stage): after the
+// barrier of stage st, stage st is in LDS and the slot of stage st-1 is free.
+// With K known at compile time the loops unroll into straight-line code.
+constexpr int kCopyWaves = 4;
+
 // ---------------------------------------------------------------------------
-// skinny kernel: M <= 64 (MT row tiles), SB column tiles of 16 per workgroup.
-// 4 waves stream stages of 8 K-tiles (256 k) of A and W through a ring of NS
-// LDS slots with direct global->LDS copies; each (row tile, column tile)
-// pair keeps one accumulator and walks the K-tiles in ascending order.
+// wide kernel (M <= 64, large N): 4 compute waves, each owning one 16-column
+// strip of W (64 columns per workgroup) and all MT row tiles; W streams into
+// a ring of RING stages of registers.  A (shared) goes through the LDS ring.
 // ---------------------------------------------------------------------------
-template <int MT, int SB, int NS, int OUTF32>
-__global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t* __restrict__ A,
-                                                     const uint16_t* __restrict__ W, void* C,
-                                                     int M, int N, int K) {
-  constexpr int KTS = 8;               // K-tiles per stage
-  constexpr int WFR = SB * KTS;        // W fragments per stage
-  constexpr int FPS = (SB + MT) * KTS; // fragments per stage
-  constexpr int PER_WAVE = FPS / 4;    // copies each wave issues per stage
-  constexpr int PAIRS = MT * SB;
-  constexpr int PPW = (PAIRS + 3) / 4; // accumulators per wave
+template <int MT, int OUTF32, int NSTC>
+__global__ __launch_bounds__(512) void k_gemm_wide(const uint16_t* __restrict__ A,
+                                                   const uint16_t* __restrict__ W, void* C,
+                                                   int M, int N, int Ktot, int kslice) {
+  // K slice of this workgroup (one slice covering all of K on the invariant
+  // path; the split-K twin launches several along y).  Rows keep stride Ktot.
+  const int kbeg = blockIdx.y * kslice;
+  const int K = min(kslice, Ktot - kbeg);
+  const long ld = Ktot;
+  A += kbeg;
+  W += kbeg;
+  constexpr int KTS = 4, NS = 4, RING = 4;
+  constexpr int SLOT = 16 * kFrag;           // room for MT * KTS <= 16 fragments
+  constexpr int QA = MT * KTS / kCopyWaves;  // copies per copy wave per stage
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n0 = blockIdx.x * 16 * SB;
-  const int KT = (K + 31) >> 5;
-  const int NST = (KT + KTS - 1) / KTS;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int lrow = lane & 15, lk = (lane >> 4) * 8;
+  const int KT = (K + 31) >> 5;
+  const int NST = NSTC > 0 ? NSTC : (KT + KTS - 1) / KTS;
 
-  auto issue = [&](int st) {
-    char* slot = smem + (st % NS) * FPS * kFrag;
+  if (wave >= 4) {
+    // ---- copy waves: A stages into the ring
+    const int cw = wave - 4;
+    auto issue_a = [&](int st) {
+      char* slot = smem + (st % NS) * SLOT;
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const int f = wave + 4 * i;
-      const int kt = (f < WFR ? f : f - WFR) % KTS;
-      int kk = (st * KTS + kt) * 32 + lk;
-      kk = kk < K ? kk : 0;
-      const uint16_t* src;
-      if (f < WFR) {
-        const int n = min(n0 + (f / KTS) * 16 + lrow, N - 1);
-        src = W + (long)n * K + kk;
-      } else {
-        const int m = min(((f - WFR) / KTS) * 16 + lrow, M - 1);
-        src = A + (long)m * K + kk;
+      for (int i = 0; i < QA; ++i) {
+        const int f = cw + kCopyWaves * i;  // fragment (mt, kt) = divmod(f, KTS)
+        int kk = (st * KTS + f % KTS) * 32 + lk;
+        if (NSTC == 0) kk = kk < K ? kk : 0;
+        dma16(A + (long)min((f / KTS) * 16 + lrow, M - 1) * ld + kk, slot + f * kFrag);
       }
-      dma16(src, slot + f * kFrag);
+    };
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < NST) issue_a(s);
+    auto step = [&](int st, bool steady) {
+      if (steady) BI_WAIT_VMCNT((NS - 2) * QA); else BI_WAIT_VMCNT(0);
+      __builtin_amdgcn_s_barrier();
+      if (st + NS - 1 < NST) issue_a(st + NS - 1);
+    };
+    if constexpr (NSTC > 0) {
+#pragma unroll
+      for (int st = 0; st < NSTC; ++st) step(st, st + NS - 1 <= NSTC);
+    } else {
+      for (int st = 0; st < NST; ++st) step(st, st + NS - 1 <= NST);
+    }
+    return;
+  }
+
+  // ---- compute waves
+  const int ntile = blockIdx.x * 4 + wave;
+  const uint16_t* wrow = W + (long)min(ntile * 16 + lrow, N - 1) * ld;
+  auto load_w = [&](int st, u32x4_t (&dst)[KTS]) {
+    const int stc = st < NST ? st : NST - 1;
+#pragma unroll
+    for (int kt = 0; kt < KTS; ++kt) {
+      int kk = (stc * KTS + kt) * 32 + lk;
+      if (NSTC == 0) kk = kk < K ? kk : 0;
+      dst[kt] = *reinterpret_cast<const u32x4_t*>(wrow + kk);
     }
   };
-
-  f32x4_t acc[PPW];
+  u32x4_t wreg[RING][KTS];
+  f32x4_t acc[MT];
 #pragma unroll
-  for (int p = 0; p < PPW; ++p) acc[p] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // prologue: stages 0 .. NS-2 in flight
+  for (int m = 0; m < MT; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < NST) issue(s);
-
+  for (int r = 0; r < RING; ++r) load_w(r, wreg[r]);
   const uint32_t lds0 = lds_addr(smem) + lane * 16;
-  for (int st = 0; st < NST; ++st) {
-    // this wave's copies of stage st have landed (newer stages may still fly)
-    if (st + NS - 1 <= NST)
-      BI_WAIT_VMCNT(PER_WAVE * (NS - 2));
-    else
-      BI_WAIT_VMCNT(0);
-    __builtin_amdgcn_s_barrier();  // all waves' copies landed; slot (st-1)%NS is free
-    if (st + NS - 1 < NST) issue(st + NS - 1);
-    const uint32_t slot = lds0 + (st % NS) * FPS * kFrag;
-    const int kt_left = KT - st * KTS;  // K-tiles of this stage that exist
+  auto step = [&](int st, int j, bool guarded, bool refill) {
+    __builtin_amdgcn_s_barrier();
+    const uint32_t slot = lds0 + (st % NS) * SLOT;
+    u32x4_t a0[8], a1[8];
+    lds_read_8x2_stride1k(a0, a1, slot, slot + 8 * kFrag);
 #pragma unroll
-    for (int p = 0; p < PPW; ++p) {
-      const int pair = wave + 4 * p;
-      if (pair < PAIRS) {
-        const int mt = pair / SB, sb = pair % SB;
-        static_assert(KTS == 8, "stage = 8 K-tiles");
-        u32x4_t a[KTS], b[KTS];
-        lds_read_8x2_stride1k(a, b, slot + (WFR + mt * KTS) * kFrag, slot + sb * KTS * kFrag);
+    for (int kt = 0; kt < KTS; ++kt) {
+      const int ktg = st * KTS + kt;
+      if (!guarded || ktg < KT) {
+        const bool tail = guarded && ktg * 32 + lk >= K;
+        const u32x4_t z = u32x4_t{0, 0, 0, 0};
+        const u32x4_t b = tail ? z : wreg[j][kt];
 #pragma unroll
-        for (int kt = 0; kt < KTS; ++kt) {
-          if (kt < kt_left) {
-            if ((st * KTS + kt) * 32 + lk >= K) a[kt] = b[kt] = u32x4_t{0, 0, 0, 0};
-            acc[p] = mfma(a[kt], b[kt], acc[p]);
-          }
+        for (int m = 0; m < MT; ++m) {
+          const int f = m * KTS + kt;
+          const u32x4_t a = tail ? z : (f < 8 ? a0[f & 7] : a1[f & 7]);
+          acc[m] = mfma(a, b, acc[m]);
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    if (refill) load_w(st + RING, wreg[j]);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if constexpr (NSTC > 0) {
+#pragma unroll
+    for (int st = 0; st < NSTC; ++st) step(st, st % RING, false, st + RING < NSTC);
+  } else {
+    const int NMAIN = ((KT / KTS) / RING) * RING;  // full stages, whole ring turns
+    for (int st0 = 0; st0 < NMAIN; st0 += RING) {
+#pragma unroll
+      for (int j = 0; j < RING; ++j) step(st0 + j, j, false, true);
+    }
+#pragma unroll
+    for (int j = 0; j < RING; ++j)
+      if (NMAIN + j < NST) step(NMAIN + j, j, true, false);
   }
 #pragma unroll
-  for (int p = 0; p < PPW; ++p) {
-    const int pair = wave + 4 * p;
-    if (pair < PAIRS)
-      store_tile<OUTF32>(C, acc[p], (pair / SB) * 16, n0 + (pair % SB) * 16, M, N, lane);
+  for (int m = 0; m < MT; ++m) store_tile<OUTF32>(C, acc[m], m * 16, ntile * 16, M, N, lane);
+}
+
+// ---------------------------------------------------------------------------
+// narrow kernel (M <= 64, N up to a few thousand): one 16-column strip of W
+// per workgroup, shared through a deep LDS ring filled by the copy waves;
+// compute wave w owns row tile w and streams its A fragments into registers.
+// ---------------------------------------------------------------------------
+template <int MT, int OUTF32, int NSTC>
+__global__ __launch_bounds__((MT + kCopyWaves) * 64) void k_gemm_narrow(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, void* C, int M, int N,
+    int Ktot, int kslice) {
+  const int kbeg = blockIdx.y * kslice;
+  const int K = min(kslice, Ktot - kbeg);
+  const long ld = Ktot;
+  A += kbeg;
+  W += kbeg;
+  constexpr int KTS = 8, NS = 16, RING = 2;
+  constexpr int SLOT = KTS * kFrag;
+  constexpr int QW = KTS / kCopyWaves;  // copies per copy wave per stage
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n0 = blockIdx.x * 16;
+  const int lrow = lane & 15, lk = (lane >> 4) * 8;
+  const int KT = (K + 31) >> 5;
+  const int NST = NSTC > 0 ? NSTC : (KT + KTS - 1) / KTS;
+
+  if (wave >= MT) {
+    // ---- copy waves: W stages into the ring
+    const int cw = wave - MT;
+    const uint16_t* wrow = W + (long)min(n0 + lrow, N - 1) * ld;
+    auto issue_w = [&](int st) {
+      char* slot = smem + (st % NS) * SLOT;
+#pragma unroll
+      for (int i = 0; i < QW; ++i) {
+        const int kt = cw + kCopyWaves * i;
+        int kk = (st * KTS + kt) * 32 + lk;
+        if (NSTC == 0) kk = kk < K ? kk : 0;
+        dma16(wrow + kk, slot + kt * kFrag);
+      }
+    };
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < NST) issue_w(s);
+    auto step = [&](int st, bool steady) {
+      if (steady) BI_WAIT_VMCNT((NS - 2) * QW); else BI_WAIT_VMCNT(0);
+      __builtin_amdgcn_s_barrier();
+      if (st + NS - 1 < NST) issue_w(st + NS - 1);
+    };
+    if constexpr (NSTC > 0) {
+#pragma unroll
+      for (int st = 0; st < NSTC; ++st) step(st, st + NS - 1 <= NSTC);
+    } else {
+      for (int st = 0; st < NST; ++st) step(st, st + NS - 1 <= NST);
+    }
+    return;
   }
+
+  // ---- compute waves
+  const uint16_t* arow = A + (long)min(wave * 16 + lrow, M - 1) * ld;
+  auto load_a = [&](int st, u32x4_t (&dst)[KTS]) {
+    const int stc = st < NST ? st : NST - 1;
+#pragma unroll
+    for (int kt = 0; kt < KTS; ++kt) {
+      int kk = (stc * KTS + kt) * 32 + lk;
+      if (NSTC == 0) kk = kk < K ? kk : 0;
+      dst[kt] = *reinterpret_cast<const u32x4_t*>(arow + kk);
+    }
+  };
+  u32x4_t areg[RING][KTS];
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int r = 0; r < RING; ++r) load_a(r, areg[r]);
+  const uint32_t lds0 = lds_addr(smem) + lane * 16;
+  auto step = [&](int st, int j, bool guarded, bool refill) {
+    __builtin_amdgcn_s_barrier();
+    u32x4_t b[8];
+    lds_read_8_stride1k(b, lds0 + (st % NS) * SLOT);
+#pragma unroll
+    for (int kt = 0; kt < KTS; ++kt) {
+      const int ktg = st * KTS + kt;
+      if (!guarded || ktg < KT) {
+        const bool tail = guarded && ktg * 32 + lk >= K;
+        const u32x4_t z = u32x4_t{0, 0, 0, 0};
+        acc = mfma(tail ? z : areg[j][kt], tail ? z : b[kt], acc);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (refill) load_a(st + RING, areg[j]);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if constexpr (NSTC > 0) {
+#pragma unroll
+    for (int st = 0; st < NSTC; ++st) step(st, st % RING, false, st + RING < NSTC);
+  } else {
+    const int NMAIN = ((KT / KTS) / RING) * RING;
+    for (int st0 = 0; st0 < NMAIN; st0 += RING) {
+#pragma unroll
+      for (int j = 0; j < RING; ++j) step(st0 + j, j, false, true);
+    }
+#pragma unroll
+    for (int j = 0; j < RING; ++j)
+      if (NMAIN + j < NST) step(NMAIN + j, j, true, false);
+  }
+  store_tile<OUTF32>(C, acc, wave * 16, n0, M, N, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -240,42 +385,68 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A,
 // ---------------------------------------------------------------------------
 // launch plumbing
 // ---------------------------------------------------------------------------
-template <int MT, int SB, int NS, int OUTF32>
-static void launch_skinny(const void* A, const void* W, void* C, int M, int N, int K,
-                          hipStream_t s) {
-  constexpr size_t lds = (size_t)NS * (SB + MT) * 8 * kFrag;
-  static_assert(lds <= 160 * 1024, "LDS budget");
+template <int MT, int OUTF32, int NSTC>
+static void launch_wide_k(const void* A, const void* W, void* C, int M, int N, int K,
+                          hipStream_t s, int splits = 1, int kslice = 0) {
+  if (splits == 1) kslice = K;
+  constexpr int lds = 4 * 16 * kFrag;
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute((const void*)k_gemm_skinny<MT, SB, NS, OUTF32>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipFuncSetAttribute((const void*)k_gemm_wide<MT, OUTF32, NSTC>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     attr = true;
   }
-  const int grid = (N + 16 * SB - 1) / (16 * SB);
-  hipLaunchKernelGGL((k_gemm_skinny<MT, SB, NS, OUTF32>), dim3(grid), dim3(256), lds, s,
-                     (const uint16_t*)A, (const uint16_t*)W, C, M, N, K);
+  hipLaunchKernelGGL((k_gemm_wide<MT, OUTF32, NSTC>), dim3((N + 63) / 64, splits), dim3(512),
+                     lds, s, (const uint16_t*)A, (const uint16_t*)W, C, M, N, K, kslice);
 }
 
-// ring depth: as many 8-K-tile stages as fit in ~128 KiB, at most 6
-constexpr int skinny_ns(int MT, int SB) {
-  return (128 / (8 * (SB + MT))) > 6 ? 6 : (128 / (8 * (SB + MT)));
+// K = 4096 runs a fully unrolled pipeline (4 K-tiles per stage)
+template <int MT, int OUTF32>
+static void launch_wide(const void* A, const void* W, void* C, int M, int N, int K,
+                        hipStream_t s) {
+  if (K == 4096) launch_wide_k<MT, OUTF32, 32>(A, W, C, M, N, K, s);
+  else launch_wide_k<MT, OUTF32, 0>(A, W, C, M, N, K, s);
 }
 
+template <int MT, int OUTF32, int NSTC>
+static void launch_narrow_k(const void* A, const void* W, void* C, int M, int N, int K,
+                            hipStream_t s, int splits = 1, int kslice = 0) {
+  if (splits == 1) kslice = K;
+  constexpr int lds = 16 * 8 * kFrag;
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)k_gemm_narrow<MT, OUTF32, NSTC>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    attr = true;
+  }
+  hipLaunchKernelGGL((k_gemm_narrow<MT, OUTF32, NSTC>), dim3((N + 15) / 16, splits),
+                     dim3((MT + kCopyWaves) * 64), lds, s,
+                     (const uint16_t*)A, (const uint16_t*)W, C, M, N, K, kslice);
+}
+
+// K = 4096 and K = 14336 run fully unrolled pipelines (8 K-tiles per stage)
+template <int MT, int OUTF32>
+static void launch_narrow(const void* A, const void* W, void* C, int M, int N, int K,
+                          hipStream_t s) {
+  if (K == 4096) launch_narrow_k<MT, OUTF32, 16>(A, W, C, M, N, K, s);
+  else if (K == 14336) launch_narrow_k<MT, OUTF32, 56>(A, W, C, M, N, K, s);
+  else launch_narrow_k<MT, OUTF32, 0>(A, W, C, M, N, K, s);
+}
+
+// Small M: wide strips (A shared through LDS) when N offers >= 256
+// workgroups of 64 columns, else one strip of 16 columns per workgroup.
 template <int OUTF32>
 static void dispatch_skinny(const void* A, const void* W, void* C, int M, int N, int K,
                             hipStream_t s) {
-  // column tiles per workgroup: widest that still gives >= 256 workgroups
   const int MT = (M + 15) / 16;
-  const int sb = (N >= 4 * 16 * 256) ? 4 : (N >= 2 * 16 * 256) ? 2 : 1;
-#define BI_SKINNY(mt, sbv)                                                              \
-  if (MT == mt && sb == sbv) {                                                         \
-    launch_skinny<mt, sbv, skinny_ns(mt, sbv), OUTF32>(A, W, C, M, N, K, s);           \
-    return;                                                                            \
+  const bool wide = N >= 64 * 256;
+#define BI_SKINNY(mt)                                                   \
+  if (MT == mt) {                                                       \
+    if (wide) launch_wide<mt, OUTF32>(A, W, C, M, N, K, s);             \
+    else launch_narrow<mt, OUTF32>(A, W, C, M, N, K, s);                \
+    return;                                                             \
   }
-  BI_SKINNY(1, 1) BI_SKINNY(1, 2) BI_SKINNY(1, 4)
-  BI_SKINNY(2, 1) BI_SKINNY(2, 2) BI_SKINNY(2, 4)
-  BI_SKINNY(3, 1) BI_SKINNY(3, 2) BI_SKINNY(3, 4)
-  BI_SKINNY(4, 1) BI_SKINNY(4, 2) BI_SKINNY(4, 4)
+  BI_SKINNY(1) BI_SKINNY(2) BI_SKINNY(3) BI_SKINNY(4)
 #undef BI_SKINNY
 }
 
@@ -292,6 +463,34 @@ static void launch_tiled(const void* A, const void* W, void* C, int M, int N, in
   const int tiles_m = (M + 127) / 128, tiles_n = (N + 127) / 128;
   hipLaunchKernelGGL((k_gemm_tiled<OUTF32>), dim3(tiles_m * tiles_n), dim3(256), lds, s,
                      (const uint16_t*)A, (const uint16_t*)W, C, M, N, K, tiles_n);
+}
+
+// Split-K over `splits` workgroup slices of kslice (multiple of 32) columns of
+// K, fp32 partial sums added atomically into C32 (which the caller zeroed).
+// Used only by the batch-adaptive twin.
+void gemm_splitk_atomic(const void* A, const void* W, float* C32, int M, int N, int K,
+                        int splits, int kslice, hipStream_t s) {
+  const int MT = (M + 15) / 16;
+  const bool wide = N >= 64 * 256;
+#define BI_SPLIT(mt)                                                                   \
+  if (MT == mt) {                                                                      \
+    if (wide) launch_wide_k<mt, 2, 0>(A, W, C32, M, N, K, s, splits, kslice);          \
+    else launch_narrow_k<mt, 2, 0>(A, W, C32, M, N, K, s, splits, kslice);             \
+    return;                                                                            \
+  }
+  BI_SPLIT(1) BI_SPLIT(2) BI_SPLIT(3) BI_SPLIT(4)
+#undef BI_SPLIT
+}
+
+void gemm_dispatch(const void* A, const void* W, void* C, int M, int N, int K, int out_f32,
+                   hipStream_t s) {
+  if (M <= 64) {
+    if (out_f32) dispatch_skinny<1>(A, W, C, M, N, K, s);
+    else dispatch_skinny<0>(A, W, C, M, N, K, s);
+  } else {
+    if (out_f32) launch_tiled<1>(A, W, C, M, N, K, s);
+    else launch_tiled<0>(A, W, C, M, N, K, s);
+  }
 }
 
 }  // namespace bi

@@ -99,25 +99,47 @@ __device__ __forceinline__ void argbest(float& v, int& i, float v2, int i2) {
   if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
 }
 
-__global__ __launch_bounds__(256) void k_argmax(const float* __restrict__ x,
-                                                int32_t* __restrict__ idx, int V) {
+// One 1024-thread workgroup per row; four independent candidates per
+// thread over float4 loads, then a tree.  The (largest value, lowest index)
+// pair is the same in any combination order.
+__global__ __launch_bounds__(1024) void k_argmax(const float* __restrict__ x,
+                                                 int32_t* __restrict__ idx, int V) {
   const long row = blockIdx.x;
   const float* xr = x + row * V;
-  float bv = -__builtin_inff();
-  int bi_ = 0x7fffffff;
-  for (int i = threadIdx.x; i < V; i += 256) argbest(bv, bi_, xr[i], i);
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(bv, off);
-    const int oi = __shfl_xor(bi_, off);
-    argbest(bv, bi_, ov, oi);
+  float bv[4];
+  int bi_[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { bv[j] = -__builtin_inff(); bi_[j] = 0x7fffffff; }
+  const bool vec = ((V & 3) == 0) && ((reinterpret_cast<uintptr_t>(xr) & 15) == 0);
+  if (vec) {
+    const float4* x4 = reinterpret_cast<const float4*>(xr);
+    const int n4 = V >> 2;
+    for (int i = threadIdx.x; i < n4; i += 1024) {
+      const float4 t = x4[i];
+      argbest(bv[0], bi_[0], t.x, 4 * i);
+      argbest(bv[1], bi_[1], t.y, 4 * i + 1);
+      argbest(bv[2], bi_[2], t.z, 4 * i + 2);
+      argbest(bv[3], bi_[3], t.w, 4 * i + 3);
+    }
+  } else {
+    for (int i = threadIdx.x; i < V; i += 1024) argbest(bv[i & 3], bi_[i & 3], xr[i], i);
   }
-  __shared__ float sv[4];
-  __shared__ int si[4];
-  if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = bv; si[threadIdx.x >> 6] = bi_; }
+#pragma unroll
+  for (int j = 1; j < 4; ++j) argbest(bv[0], bi_[0], bv[j], bi_[j]);
+  float v = bv[0];
+  int ix = bi_[0];
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(v, off);
+    const int oi = __shfl_xor(ix, off);
+    argbest(v, ix, ov, oi);
+  }
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = v; si[threadIdx.x >> 6] = ix; }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int w = 1; w < 4; ++w) argbest(bv, bi_, sv[w], si[w]);
-    idx[row] = bi_ == 0x7fffffff ? 0 : bi_;
+    for (int w = 1; w < 16; ++w) argbest(v, ix, sv[w], si[w]);
+    idx[row] = ix == 0x7fffffff ? 0 : ix;
   }
 }
 
@@ -207,6 +229,6 @@ extern "C" bi_status bi_argmax(const float* x, int32_t* idx, int M, int V, bi_st
   BI_REQUIRE(M >= 0 && V >= 1, BI_ERR_INVALID, "bi_argmax: bad sizes M=%d V=%d", M, V);
   if (M == 0) return BI_OK;
   BI_REQUIRE(x && idx, BI_ERR_INVALID, "bi_argmax: null pointer");
-  hipLaunchKernelGGL(k_argmax, dim3(M), dim3(256), 0, as_stream(stream), x, idx, V);
+  hipLaunchKernelGGL(k_argmax, dim3(M), dim3(1024), 0, as_stream(stream), x, idx, V);
   return launched("bi_argmax");
 }

@@ -1,0 +1,313 @@
+"""Llama-shaped decoder driven through the C ABI.
+
+Every arithmetic step of a forward pass is a libbi.so call; torch provides
+device memory, streams and integer bookkeeping only.  A step takes packed
+rows from several requests -- single decode rows and multi-row prompt
+chunks -- in one pass:
+
+  embed -> L x [ rmsnorm -> QKV gemm -> RoPE + KV append -> attention
+                 -> O gemm -> add -> rmsnorm -> gate/up gemm -> SiLU-mul
+                 -> down gemm -> add ] -> rmsnorm -> (row gather) -> LM-head
+  gemm (fp32 logits) -> argmax
+
+Attention: decode rows go through bi_decode_attn + bi_merge_partials (split
+over request-aligned KV chunks, parallel over chunks); prompt rows through
+bi_prefill_attn.  Both give the same bits for a row at position t, so the
+split between the two paths never shows in the logits.  Decode rows are
+packed first so both paths write one contiguous attention buffer.
+
+Weight layout follows the GEMM ABI: [out_features][in_features] bf16; the
+fused QKV weight is [q | k | v] rows, gate/up is [gate | up] rows.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+@dataclass
+class ModelConfig:
+    d: int = 4096
+    h: int = 32
+    h_kv: int = 8
+    d_h: int = 128
+    ffn: int = 14336
+    vocab: int = 128256
+    layers: int = 32
+    eps: float = 1e-5
+    rope_theta: float = 500000.0
+    kv_chunk: int = 256
+    page_size: int = 16
+    dtype: torch.dtype = torch.bfloat16
+    rope: bool = True
+
+    @property
+    def qkv_out(self) -> int:
+        return (self.h + 2 * self.h_kv) * self.d_h
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.d_h)))
+
+    def weight_bytes(self) -> int:
+        per_layer = (self.qkv_out * self.d + self.d * self.h * self.d_h
+                     + 2 * self.ffn * self.d + self.d * self.ffn + 2 * self.d)
+        return 2 * (self.layers * per_layer + self.vocab * self.d + self.d)
+
+    def kv_bytes_per_token(self) -> int:
+        return 2 * self.layers * self.h_kv * self.d_h * 2
+
+
+LLAMA3_8B = ModelConfig()
+
+
+@dataclass
+class LayerWeights:
+    attn_norm: torch.Tensor
+    wqkv: torch.Tensor
+    wo: torch.Tensor
+    ffn_norm: torch.Tensor
+    wgu: torch.Tensor
+    wdown: torch.Tensor
+
+
+@dataclass
+class Weights:
+    embed: torch.Tensor
+    layers: list
+    final_norm: torch.Tensor
+    lm_head: torch.Tensor
+
+
+def init_weights(cfg: ModelConfig, seed: int, device, source: str = "device",
+                 std: float = 0.02) -> Weights:
+    """Random-init weights N(0, std^2), norms = 1.  source='device' draws on
+    the GPU (fast, for throughput runs); source='synth' draws each tensor
+    from the seeded CPU generators of `synth` (so the oracle can be handed
+    the same values) and copies it over."""
+    import synth
+
+    dt = cfg.dtype
+    counter = [0]
+
+    def rnd(shape):
+        counter[0] += 1
+        if source == "synth":
+            return synth.normal(shape, seed=seed * 1000 + counter[0], std=std).to(dt).to(device)
+        g = torch.Generator(device=device).manual_seed(seed * 1000 + counter[0])
+        t = torch.empty(shape, dtype=torch.float32, device=device)
+        out = torch.empty(shape, dtype=dt, device=device)
+        # fill in slabs to bound the fp32 temporary
+        flat, oflat = t.view(-1), out.view(-1)
+        step = 1 << 26
+        for i in range(0, flat.numel(), step):
+            n = min(step, flat.numel() - i)
+            oflat[i:i + n] = torch.randn(n, generator=g, device=device).mul_(std).to(dt)
+        del t
+        return out
+
+    def ones(n):
+        return torch.ones(n, dtype=dt, device=device)
+
+    layers = []
+    for _ in range(cfg.layers):
+        layers.append(LayerWeights(
+            attn_norm=ones(cfg.d), wqkv=rnd((cfg.qkv_out, cfg.d)),
+            wo=rnd((cfg.d, cfg.h * cfg.d_h)), ffn_norm=ones(cfg.d),
+            wgu=rnd((2 * cfg.ffn, cfg.d)), wdown=rnd((cfg.d, cfg.ffn))))
+    embed = rnd((cfg.vocab, cfg.d))
+    return Weights(embed=embed, layers=layers, final_norm=ones(cfg.d),
+                   lm_head=rnd((cfg.vocab, cfg.d)))
+
+
+class KVPool:
+    """Paged KV storage for all layers: k, v [layers][pages][h_kv][page][d_h]."""
+
+    def __init__(self, cfg: ModelConfig, num_pages: int, device):
+        shape = (cfg.layers, num_pages, cfg.h_kv, cfg.page_size, cfg.d_h)
+        self.k = torch.zeros(shape, dtype=cfg.dtype, device=device)
+        self.v = torch.zeros(shape, dtype=cfg.dtype, device=device)
+        self.num_pages = num_pages
+        self.page_size = cfg.page_size
+
+
+@dataclass
+class Segment:
+    """Rows of one request in a step: positions pos0 .. pos0 + len(tokens) - 1."""
+    pages: list            # the request's page ids (block-table row), covering pos0+n-1
+    pos0: int
+    tokens: list
+    want_logits: bool = True   # logits of the segment's last row
+
+
+@dataclass
+class StepOutput:
+    logits: torch.Tensor       # [n_segments_with_logits, vocab] fp32 (device)
+    tokens: torch.Tensor       # argmax of each logits row (device int32)
+    seg_index: list = field(default_factory=list)
+
+
+class Engine:
+    """Runs forward steps over packed rows through libbi.so.
+
+    free=True swaps every reduction kernel for its batch-adaptive twin
+    (bi_*_free): the same mathematics with split points chosen from the
+    batch, which prices invariance and serves as the negative control of the
+    schedule fuzzer."""
+
+    def __init__(self, cfg: ModelConfig, weights: Weights, pool: KVPool, device,
+                 max_rows: int = 64, max_pages_per_req: int = 512, free: bool = False):
+        self.cfg, self.w, self.pool, self.dev = cfg, weights, pool, device
+        self.free = free
+        self.max_pages = max_pages_per_req
+        c = cfg
+        if c.rope:
+            import synth
+            cos_t, sin_t = synth.rope_tables(max_pages_per_req * c.page_size, c.d_h, c.rope_theta)
+            self.cos, self.sin = cos_t.to(device), sin_t.to(device)
+        else:
+            self.cos = self.sin = None
+        self._alloc(max_rows)
+
+    def _alloc(self, rows: int):
+        c, d, dt = self.cfg, self.dev, self.cfg.dtype
+        self.cap = rows
+        self.h = torch.empty((rows, c.d), dtype=dt, device=d)
+        self.x = torch.empty((rows, c.d), dtype=dt, device=d)
+        self.qkv = torch.empty((rows, c.qkv_out), dtype=dt, device=d)
+        self.q = torch.empty((rows, c.h, c.d_h), dtype=dt, device=d)
+        self.att = torch.empty((rows, c.h, c.d_h), dtype=dt, device=d)
+        self.o = torch.empty((rows, c.d), dtype=dt, device=d)
+        self.gu = torch.empty((rows, 2 * c.ffn), dtype=dt, device=d)
+        self.act = torch.empty((rows, c.ffn), dtype=dt, device=d)
+
+    # -- host-side packing -------------------------------------------------
+    def pack(self, segs: list):
+        """Order rows decode-first and build the int32 metadata of a step."""
+        c = self.cfg
+        order = [i for i, s in enumerate(segs) if len(s.tokens) == 1] + \
+                [i for i, s in enumerate(segs) if len(s.tokens) > 1]
+        dec = [segs[i] for i in order if len(segs[i].tokens) == 1]
+        pre = [segs[i] for i in order if len(segs[i].tokens) > 1]
+        toks, pos, slots = [], [], []
+        for s in dec + pre:
+            for j, t in enumerate(s.tokens):
+                p = s.pos0 + j
+                toks.append(int(t))
+                pos.append(p)
+                slots.append(int(s.pages[p // c.page_size]) * c.page_size + p % c.page_size)
+        T = len(toks)
+        bt = np.full((len(segs), self.max_pages), 0, np.int32)
+        for k, s in enumerate(dec + pre):
+            bt[k, :len(s.pages)] = s.pages
+        meta = {
+            "order": order, "T": T, "n_dec": len(dec), "n_pre": len(pre),
+            "tokens": torch.tensor(toks, dtype=torch.int32),
+            "pos": torch.tensor(pos, dtype=torch.int32),
+            "slots": torch.tensor(slots, dtype=torch.int32),
+            "bt_dec": torch.from_numpy(bt[:len(dec)].copy()),
+            "bt_pre": torch.from_numpy(bt[len(dec):].copy()),
+            "kv_len_dec": np.array([s.pos0 + 1 for s in dec], np.int32),
+            "q_start_pre": np.concatenate([[len(dec)], len(dec) + np.cumsum(
+                [len(s.tokens) for s in pre])]).astype(np.int32) - len(dec),
+            "pos0_pre": np.array([s.pos0 for s in pre], np.int32),
+        }
+        # rows whose logits are wanted: last row of each segment (packed order)
+        want, row = [], 0
+        for k, s in enumerate(dec + pre):
+            row += len(s.tokens)
+            if s.want_logits:
+                want.append((order[k], row - 1))
+        meta["want"] = want
+        return meta
+
+    def upload(self, meta):
+        d = self.dev
+        m = dict(meta)
+        for key in ("tokens", "pos", "slots", "bt_dec", "bt_pre"):
+            m[key] = meta[key].to(d, non_blocking=False)
+        if meta["n_dec"]:
+            off = L.bi_chunk_offsets(meta["kv_len_dec"], self.cfg.kv_chunk)
+            m["chunk_off"] = off.to(d)
+            m["total_chunks"] = int(off[-1])
+            m["kv_len"] = torch.from_numpy(meta["kv_len_dec"]).to(d)
+            m["max_kv_len"] = int(meta["kv_len_dec"].max())
+            nb = m["total_chunks"]
+            m["ml"] = torch.empty((nb, self.cfg.h, 2), device=d)
+            m["pacc"] = torch.empty((nb, self.cfg.h, self.cfg.d_h), device=d)
+        if meta["n_pre"]:
+            m["q_start"] = torch.from_numpy(meta["q_start_pre"]).to(d)
+            m["pos0"] = torch.from_numpy(meta["pos0_pre"]).to(d)
+        m["want_rows"] = torch.tensor([r for _, r in meta["want"]], dtype=torch.int32, device=d)
+        return m
+
+    # -- the forward pass ------------------------------------------------------
+    def forward(self, m, layers=None, timer=None) -> StepOutput:
+        """One forward pass over the packed rows of `m` (from upload()).
+        `timer`, if given, is called as timer(name, fn) around the kernels it
+        brackets ("decode_attn", "gemm_gate_up", ...)."""
+        c, w, T = self.cfg, self.w, m["T"]
+        run = timer if timer is not None else (lambda name, fn: fn())
+        if T > self.cap:
+            self._alloc(T)
+        h, x, qkv, q, att = self.h[:T], self.x[:T], self.qkv[:T], self.q[:T], self.att[:T]
+        o, gu, act = self.o[:T], self.gu[:T], self.act[:T]
+        nd = m["n_dec"]
+        fr = self.free
+        rms = L.bi_rmsnorm_free if fr else L.bi_rmsnorm
+        gemm = L.bi_gemm_free if fr else L.bi_gemm
+        L.bi_embed(w.embed, m["tokens"], h)
+        for li, lw in enumerate(w.layers[:layers] if layers else w.layers):
+            kp, vp = self.pool.k[li], self.pool.v[li]
+            run("rmsnorm", lambda: rms(h, lw.attn_norm, x, c.eps))
+            run("gemm_qkv", lambda: gemm(x, lw.wqkv, qkv))
+            run("rope_kv_append", lambda: L.bi_rope_kv_append(
+                qkv, c.h, c.h_kv, c.d_h, m["pos"] if c.rope else None, self.cos, self.sin,
+                m["slots"], q, kp, vp))
+            if nd and fr:
+                run("decode_attn", lambda: L.bi_decode_attn_free(
+                    q[:nd], kp, vp, m["bt_dec"], m["kv_len"], m["max_kv_len"], c.scale,
+                    att[:nd]))
+            elif nd:
+                run("decode_attn", lambda: L.bi_decode_attn(
+                    q[:nd], kp, vp, m["bt_dec"], m["kv_len"], m["chunk_off"], m["total_chunks"],
+                    c.kv_chunk, c.scale, m["ml"], m["pacc"]))
+                run("merge", lambda: L.bi_merge_partials(m["ml"], m["pacc"], m["chunk_off"],
+                                                         att[:nd]))
+            if m["n_pre"] and fr:
+                run("prefill_attn", lambda: L.bi_prefill_attn_free(
+                    q[nd:], m["q_start"], m["pos0"], kp, vp, m["bt_pre"], c.scale, att[nd:]))
+            elif m["n_pre"]:
+                run("prefill_attn", lambda: L.bi_prefill_attn(
+                    q[nd:], m["q_start"], m["pos0"], kp, vp, m["bt_pre"], c.kv_chunk, c.scale,
+                    att[nd:]))
+            run("gemm_o", lambda: gemm(att.view(T, c.h * c.d_h), lw.wo, o))
+            run("add", lambda: L.bi_add(h, o, h))
+            run("rmsnorm", lambda: rms(h, lw.ffn_norm, x, c.eps))
+            run("gemm_gate_up", lambda: gemm(x, lw.wgu, gu))
+            run("silu_mul", lambda: L.bi_silu_mul(gu, act))
+            run("gemm_down", lambda: gemm(act, lw.wdown, o))
+            run("add", lambda: L.bi_add(h, o, h))
+        rms(h, w.final_norm, x, c.eps)
+        nw = len(m["want"])
+        if nw == 0:
+            return StepOutput(torch.empty((0, c.vocab), device=self.dev),
+                              torch.empty(0, dtype=torch.int32, device=self.dev), [])
+        if nw == T:
+            hs = x
+        else:
+            hs = torch.empty((nw, c.d), dtype=c.dtype, device=self.dev)
+            L.bi_embed(x, m["want_rows"], hs)      # row gather
+        logits = torch.empty((nw, c.vocab), dtype=torch.float32, device=self.dev)
+        run("gemm_lm_head", lambda: gemm(hs, w.lm_head, logits))
+        toks = torch.empty(nw, dtype=torch.int32, device=self.dev)
+        L.bi_argmax(logits, toks)
+        return StepOutput(logits, toks, [i for i, _ in m["want"]])
+
+    def step(self, segs: list, layers=None) -> StepOutput:
+        return self.forward(self.upload(self.pack(segs)), layers=layers)

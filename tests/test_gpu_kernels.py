@@ -77,7 +77,10 @@ def test_rmsnorm_rows_invariant_and_inplace():
 
 GEMM_SHAPES = [(1, 16, 32), (1, 17, 40), (5, 100, 264), (16, 64, 512), (17, 48, 96),
                (33, 130, 1024), (64, 64, 256), (64, 257, 4104), (65, 128, 256),
-               (100, 300, 520), (257, 200, 1000)]
+               (100, 300, 520), (257, 200, 1000),
+               # compile-time-K pipelines (K = 4096, 14336) and the wide path (N >= 16384)
+               (1, 64, 4096), (16, 130, 4096), (64, 48, 14336), (33, 100, 14336),
+               (3, 16400, 4096), (64, 16448, 4096), (20, 16384, 264)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
@@ -125,6 +128,23 @@ def test_gemm_rows_invariant_across_M_and_position():
         rows = list(rng.choice(300, size=M, replace=False))
         got = run(rows)
         assert torch.equal(got.view(torch.int32), full[rows].view(torch.int32)), f"M={M}"
+
+
+def test_gemm_wide_rows_invariant_across_M():
+    K, N = 4096, 16448
+    A = synth.normal((96, K), seed=3).to(torch.bfloat16).to(dev())
+    W = synth.normal((N, K), seed=4, std=0.02).to(torch.bfloat16).to(dev())
+
+    def run(rows):
+        c = torch.empty((len(rows), N), dtype=torch.float32, device=dev())
+        L.bi_gemm(A[rows].contiguous(), W, c)
+        return c
+
+    full = run(list(range(96)))             # tiled kernel
+    rng = np.random.default_rng(1)
+    for M in [1, 5, 16, 31, 48, 64]:
+        rows = list(rng.choice(96, size=M, replace=False))
+        assert torch.equal(run(rows).view(torch.int32), full[rows].view(torch.int32)), f"M={M}"
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 512, 256), (8, 512, 256), (3, 33, 7), (20, 70, 300)])

@@ -1,0 +1,141 @@
+"""CPU tests of the schedule fuzzer and the verdict core (no GPU).
+
+The runner drives a deterministic mock backend that keeps a paged "KV"
+state: the value stored for position p is a hash of the token at p and the
+value at p-1, and a step's logits row is derived from the value at the
+row's position.  Invariant by construction -- unless its divergence knob
+mixes the step's batch size into the logits, which must turn the verdict
+RED.  Preemption with swap and with recompute must reproduce the same state.
+"""
+import hashlib
+import json
+import os
+
+import numpy as np
+import pytest
+
+from invariant_bi_rmsnorm_amd import harness as H
+
+
+class MockBackend:
+    page_size = 4
+
+    def __init__(self, num_pages=400, divergence=False):
+        self.num_pages = num_pages
+        self.kv = np.zeros((num_pages, self.page_size), dtype=np.uint64)
+        self.divergence = divergence
+        self.steps = 0
+        self.batch_sizes = []
+
+    def _h(self, *vals):
+        d = hashlib.blake2b(repr(vals).encode(), digest_size=8).digest()
+        return np.uint64(int.from_bytes(d, "little"))
+
+    def step(self, segs):
+        self.steps += 1
+        self.batch_sizes.append(len(segs))
+        rows, toks = [], []
+        for s in segs:
+            for j, t in enumerate(s.tokens):
+                p = s.pos0 + j
+                prev = np.uint64(0) if p == 0 else self.kv[s.pages[(p - 1) // 4], (p - 1) % 4]
+                self.kv[s.pages[p // 4], p % 4] = self._h(int(t), p, int(prev))
+            if s.want_logits:
+                p = s.pos0 + len(s.tokens) - 1
+                v = int(self.kv[s.pages[p // 4], p % 4])
+                logits = np.frombuffer(hashlib.sha256(v.to_bytes(8, "little")).digest(),
+                                       dtype=np.uint8).astype(np.float32)
+                if self.divergence and len(segs) > 1:
+                    logits[0] += 1.0   # a batch-dependent rounding, caricatured
+                rows.append(logits.tobytes())
+                toks.append(int(np.argmax(logits)) % 50)
+        return rows, toks
+
+    def swap_out(self, pages):
+        return self.kv[pages].copy()
+
+    def swap_in(self, blob, pages):
+        self.kv[pages[:len(blob)]] = blob
+
+
+def make_reqs(n=8, seed=0):
+    rng = np.random.default_rng(seed)
+    return [H.Request(i, list(rng.integers(0, 50, size=int(rng.integers(1, 30)))),
+                      int(rng.integers(1, 12))) for i in range(n)]
+
+
+def test_verdict_core_pure():
+    base = {0: {3: "a", 4: "b"}, 1: {1: "c"}}
+    same = [{0: {3: "a", 4: "b"}, 1: {1: "c"}}] * 3
+    rep = H.diff_runs(base, same)
+    assert rep["divergent"] == {} and rep["compared"] == 9 and rep["unique_samples_max"] == 1
+    out = H.decide(rep, {0: 2, 1: 1}, {0: True, 1: True}, 2)
+    assert out["verdict"] == H.GREEN and out["rule_of_three_upper"] == pytest.approx(3 / 9)
+    bad = [{0: {3: "a", 4: "x"}, 1: {1: "c"}}]
+    rep = H.diff_runs(base, bad)
+    assert rep["divergent"] == {0: 1} and rep["unique_samples_max"] == 2
+    assert H.decide(rep, {0: 1, 1: 1}, {0: True, 1: True}, 2)["verdict"] == H.RED
+    # a clean run that never co-batched a request earns nothing
+    rep = H.diff_runs(base, same)
+    assert H.decide(rep, {0: 1, 1: 0}, {0: True, 1: True}, 2)["verdict"] == H.UNVERIFIED
+    # an incomplete request earns nothing
+    assert H.decide(rep, {0: 1, 1: 1}, {0: True, 1: False}, 2)["verdict"] == H.UNVERIFIED
+    # missing records earn nothing
+    rep = H.diff_runs(base, [{0: {3: "a"}, 1: {1: "c"}}])
+    assert H.decide(rep, {0: 1, 1: 1}, {0: True, 1: True}, 2)["verdict"] == H.UNVERIFIED
+
+
+def test_fuzzed_schedules_green_on_invariant_backend(tmp_path):
+    reqs = make_reqs(10, seed=1)
+    path = os.path.join(tmp_path, "cert.json")
+    fz = H.FuzzConfig(seed=7, max_rows=24, max_reqs=6, p_preempt=0.3, p_swap=0.5)
+    out = H.verify(lambda: MockBackend(), reqs, n_schedules=6, fuzz=fz, report_path=path)
+    assert out["verdict"] == H.GREEN, out
+    assert out["cobatch_frac"] == 1.0 and out["completion_frac"] == 1.0
+    assert out["rerecord_mismatch"] == 0
+    with open(path) as f:
+        assert json.load(f)["verdict"] == H.GREEN
+
+
+def test_fuzzed_schedules_red_on_batch_dependent_backend():
+    reqs = make_reqs(8, seed=2)
+    fz = H.FuzzConfig(seed=3, max_rows=24, max_reqs=6, p_preempt=0.2)
+    out = H.verify(lambda: MockBackend(divergence=True), reqs, n_schedules=3, fuzz=fz)
+    assert out["verdict"] == H.RED
+    assert out["divergent_requests"] > 0
+
+
+def test_schedules_actually_vary_and_preempt():
+    reqs = make_reqs(10, seed=4)
+    sizes, preempts, cuts = set(), 0, set()
+    for seed in range(5):
+        be = MockBackend()
+        runner = H.Runner(be, reqs, H.FuzzConfig(seed=seed, max_rows=24, max_reqs=6,
+                                                 p_preempt=0.4))
+        orig = runner._preempt
+        count = [0]
+
+        def spy(r, orig=orig, count=count):
+            count[0] += 1
+            orig(r)
+        runner._preempt = spy
+        runner.run()
+        sizes |= set(be.batch_sizes)
+        preempts += count[0]
+    assert len(sizes) >= 4          # compositions of several sizes
+    assert preempts > 0             # preemption (swap or recompute) happened
+
+
+def test_alone_baseline_runs_one_request_per_step():
+    be = MockBackend()
+    H.Runner(be, make_reqs(5, seed=5), H.FuzzConfig(alone=True, prefill_whole=True)).run()
+    assert set(be.batch_sizes) == {1}
+
+
+def test_report_write_is_atomic(tmp_path):
+    p = os.path.join(tmp_path, "sub", "r.json")
+    H.write_report(p, {"verdict": "GREEN", "n": 1})
+    H.write_report(p, {"verdict": "RED", "n": 2})
+    with open(p) as f:
+        assert json.load(f) == {"verdict": "RED", "n": 2}
+    assert [x for x in os.listdir(os.path.dirname(p)) if x.endswith(".tmp")] == []
