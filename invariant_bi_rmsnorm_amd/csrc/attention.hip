@@ -673,8 +673,12 @@ static FreePolicy free_policy(int B, int h, int h_kv, int max_kv_len) {
   ms2 = ms2 > 1 ? ms2 : 1;
   FreePolicy p;
   p.chunk2 = (max_kv_len + ms2 - 1) / ms2;
-  const int a = (max_kv_len + 255) / 256;
-  p.stride = a > kMaxSplits ? a : kMaxSplits;  // >= every request's split count
+  // max(ceil(s/256), ceil(s/chunk2)) grows with s and bounds the split
+  // count free_splits gives a request of length s, so its value at the
+  // longest request bounds every request's count.  Partial rows of request
+  // r start at r * stride.
+  const int a = (max_kv_len + 255) / 256, b = (max_kv_len + p.chunk2 - 1) / p.chunk2;
+  p.stride = a > b ? a : b;
   return p;
 }
 
@@ -816,6 +820,9 @@ extern "C" bi_status bi_decode_attn_free(const void* q, const void* k_pool, cons
              "bi_decode_attn_free: workspace %zu < %zu bytes", workspace_bytes, need);
   const FreePolicy pol = free_policy(B, h, h_kv, max_kv_len);
   BI_REQUIRE((long)B * pol.stride <= 0x7fffffffL, BI_ERR_INVALID, "bi_decode_attn_free: grid");
+  // the workspace query's bound (ceil(max/256) or 64 splits) covers pol.stride
+  BI_REQUIRE(pol.stride <= ((max_kv_len + 255) / 256 > 64 ? (max_kv_len + 255) / 256 : 64),
+             BI_ERR_INVALID, "bi_decode_attn_free: split policy exceeds its bound");
   float* ml = static_cast<float*>(workspace);
   float* acc = ml + (size_t)B * pol.stride * h * 2;
   hipStream_t s = as_stream(stream);
