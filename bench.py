@@ -53,6 +53,11 @@ def parse():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", default="1,7,32", help="extra batch sizes ('' for none)")
+    ap.add_argument("--only", default="",
+                    help="time one kernel of the step instead (decode_attn, gemm_qkv, ..., or "
+                         "'copy' for a plain 1 GiB device copy), e.g. under rocprofv3 --pmc")
+    ap.add_argument("--twin", action="store_true", help="with --only: the twin's kernel")
+    ap.add_argument("--launches", type=int, default=50)
     return ap.parse_args()
 
 
@@ -276,6 +281,80 @@ def cpu_baseline(args, detail, B, budget_s=10.0):
             "sample_seconds": round(t_layers + t_head, 2)}
 
 
+def prefill_gemm(torch, dev, M=8192, N=14336, K=4096, launches=20):
+    """The chunked-prefill GEMM: M rows (prefill chunks plus decode rows),
+    K 4096 -> N 14336, bf16 in and out, fp32 accumulation.  Timed with HIP
+    events on its stream; 2MNK flops against the dense bf16 MFMA peak."""
+    from invariant_bi_rmsnorm_amd import _lib as L
+    g = torch.Generator(device=dev).manual_seed(7)
+    A = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
+    W = (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        L.bi_gemm(A, W, C)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(launches):
+        L.bi_gemm(A, W, C)
+    b.record()
+    torch.cuda.synchronize()
+    us = 1e3 * a.elapsed_time(b) / launches
+    tf = 2.0 * M * N * K / us / 1e6
+    return {"kernel": "bi_gemm prefill", "M": M, "N": N, "K": K, "avg_us": round(us, 1),
+            "TFLOPs": round(tf, 1), "peak": BF16_PEAK / 1e12, "frac": round(tf * 1e12 / BF16_PEAK, 4)}
+
+
+def only_kernel(args, torch, dev):
+    """Launch one kernel of the step (the last layer's instance) --launches
+    times back to back and report its average duration from HIP events on
+    its stream.  'copy' copies 1 GiB device to device (the yardstick that
+    calibrates HBM byte counters)."""
+    if args.only == "copy":
+        n = 1 << 28
+        src = torch.empty(n, device=dev).normal_()
+        dst = torch.empty_like(src)
+        fn, alg, label = (lambda: dst.copy_(src)), 2 * 4 * n, "copy 1 GiB"
+    elif args.only == "prefill_gemm":
+        print(json.dumps(prefill_gemm(torch, dev, launches=args.launches)), flush=True)
+        return
+    else:
+        from invariant_bi_rmsnorm_amd.model import init_weights
+        cfg = model_config(args)
+        w = init_weights(cfg, args.seed + 14, dev, source="device")
+        _, eng, twin, meta, kv_len, _ = build_workload(args, args.batch, torch, dev, w,
+                                                       free=args.twin)
+        e = twin if args.twin else eng
+        grab = {}
+
+        def keep(name, f):
+            grab[name] = f
+            f()
+
+        e.forward(meta, timer=keep)
+        torch.cuda.synchronize()
+        if args.only not in grab:
+            raise SystemExit(f"--only {args.only}: not a kernel of the step ({sorted(grab)})")
+        fn = grab[args.only]
+        alg = algorithmic_bytes(args.only, cfg, args.batch, kv_len, meta)
+        label = f"{args.only}{' (twin)' if args.twin else ''}, batch {args.batch}"
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.launches):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    us = 1e3 * a.elapsed_time(b) / args.launches
+    out = {"kernel": label, "launches": args.launches, "avg_us": round(us, 2)}
+    if alg:
+        out.update(alg_bytes=alg, GBps=round(alg / us / 1e3, 1),
+                   hbm_frac=round(alg / us / 1e3 / (HBM_PEAK / 1e9), 4))
+    print(json.dumps(out), flush=True)
+
+
 def _rounded(d):
     return {k: (round(v, 3) if isinstance(v, float) else v) for k, v in d.items()}
 
@@ -294,6 +373,9 @@ def main():
         sys.exit(1)
     _lib.load()
     dev = torch.device("cuda:0")
+    if args.only:
+        only_kernel(args, torch, dev)
+        return
     cfg = model_config(args)
     w = init_weights(cfg, args.seed + 14, dev, source="device")
     log(f"weights drawn ({cfg.weight_bytes() / 1e9:.2f} GB)")
@@ -346,6 +428,7 @@ def main():
                 "step_hbm_frac": round(r2["hbm_frac_of_step_bound"], 4)}
             torch.cuda.empty_cache()
         detail = keep
+    out["prefill_gemm"] = prefill_gemm(torch, dev)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(args, detail, B)

@@ -50,10 +50,10 @@ __device__ __forceinline__ int kswz(int u, int c) {
 }
 
 // LDS layout of one attention workgroup
-template <int DT, int DH, int R, int NW>
+template <int DT, int DH, int R, int NW, bool KLDS = true>
 struct AttnLds {
   static constexpr int KEYS = 64 * NW;
-  static constexpr int K_BYTES = KEYS * AttnShape<DT, DH>::RB;
+  static constexpr int K_BYTES = KLDS ? KEYS * AttnShape<DT, DH>::RB : 0;
   static constexpr int Q_OFF = K_BYTES;                        // fp32 q [R][DH]
   static constexpr int P_OFF = Q_OFF + R * DH * 4;             // fp32 p [KEYS][R]
   static constexpr int MX_OFF = P_OFF + KEYS * R * 4;          // fp32 [NW][R]
@@ -86,18 +86,30 @@ __device__ __forceinline__ float v_elem(const uint32_t* v, int e) {
   return __uint_as_float(v[e]);
 }
 
-template <int DT, int DH, int R, int NW>
-__device__ __forceinline__ void chunk_partial(char* lds, int n, float scale,
-                                              const uint32_t (&vreg)[64][AttnShape<DT, DH>::VW],
-                                              ChunkOut<R, NW, AttnShape<DT, DH>::DPL>& out) {
+struct NoHook {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+// KSrc(c) returns this lane's 16-byte column c of its key's K row (from the
+// LDS block, or from registers in the pipelined kernel).  after_qk runs once
+// every K read of the chunk is done, after_pv once every V register is
+// consumed: the pipelined kernel issues the next chunk's loads there.
+template <int DT, int DH, int R, int NW, bool KLDS = true, bool FINAL_SYNC = true, class KSrc,
+          class H1 = NoHook, class H2 = NoHook>
+__device__ __forceinline__ void chunk_partial_k(char* lds, int n, float scale, const KSrc& ksrc,
+                                                const uint32_t (&vreg)[64][AttnShape<DT, DH>::VW],
+                                                ChunkOut<R, NW, AttnShape<DT, DH>::DPL>& out,
+                                                const H1& after_qk = H1(),
+                                                const H2& after_pv = H2(),
+                                                int q_off = AttnLds<DT, DH, R, NW, KLDS>::Q_OFF) {
   typedef AttnShape<DT, DH> S;
-  typedef AttnLds<DT, DH, R, NW> L;
+  typedef AttnLds<DT, DH, R, NW, KLDS> L;
   constexpr int DPL = S::DPL;
   constexpr int NT = 64 * NW;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int u = tid;  // this lane's key within the chunk
-  const float* qs = reinterpret_cast<const float*>(lds + L::Q_OFF);
+  const float* qs = reinterpret_cast<const float*>(lds + q_off);
   float* ps = reinterpret_cast<float*>(lds + L::P_OFF);
   float* mx = reinterpret_cast<float*>(lds + L::MX_OFF);
   float* cb = reinterpret_cast<float*>(lds + L::CB_OFF);
@@ -108,10 +120,9 @@ __device__ __forceinline__ void chunk_partial(char* lds, int n, float scale,
   for (int i = 0; i < R; ++i) sc[i] = 0.0f;
   const bool valid = u < n;
   if (valid) {
-    const char* krow = lds;
 #pragma unroll
     for (int c = 0; c < S::SLOTS; ++c) {
-      const uint4 w = *reinterpret_cast<const uint4*>(krow + kswz<DT, DH>(u, c));
+      const uint4 w = ksrc(c);
       float kv[S::EPS];
       if (DT == 1) {
         kv[0] = bf16_lo(w.x); kv[1] = bf16_hi(w.x); kv[2] = bf16_lo(w.y); kv[3] = bf16_hi(w.y);
@@ -136,6 +147,7 @@ __device__ __forceinline__ void chunk_partial(char* lds, int n, float scale,
 #pragma unroll
     for (int i = 0; i < R; ++i) sc[i] = sc[i] * scale;
   }
+  after_qk();
   // ---- chunk max (exact in any order)
   float m[R];
 #pragma unroll
@@ -204,6 +216,7 @@ __device__ __forceinline__ void chunk_partial(char* lds, int n, float scale,
       }
     }
   }
+  after_pv();
   // ---- publish block partials, combine blocks in wave order
   constexpr int CBS = DH + 1;  // floats per (wave, head)
   if (nk > 0) {
@@ -239,7 +252,16 @@ __device__ __forceinline__ void chunk_partial(char* lds, int n, float scale,
       for (int e = 0; e < DPL; ++e) out.acc[k][e] = a[e];
     }
   }
-  __syncthreads();  // LDS (p, block partials, K) may be reused by the caller
+  if (FINAL_SYNC) __syncthreads();  // LDS (p, block partials, K) may be reused by the caller
+}
+
+template <int DT, int DH, int R, int NW>
+__device__ __forceinline__ void chunk_partial(char* lds, int n, float scale,
+                                              const uint32_t (&vreg)[64][AttnShape<DT, DH>::VW],
+                                              ChunkOut<R, NW, AttnShape<DT, DH>::DPL>& out) {
+  const int u = threadIdx.x;
+  auto kl = [&](int c) { return *reinterpret_cast<const uint4*>(lds + kswz<DT, DH>(u, c)); };
+  chunk_partial_k<DT, DH, R, NW, true>(lds, n, scale, kl, vreg, out);
 }
 
 // Pages hold kPage tokens (the only page size the kernels are built for).
@@ -351,6 +373,192 @@ __global__ __launch_bounds__(64 * NW) void k_decode_partials(
 #pragma unroll
       for (int e = 0; e < S::DPL; ++e) part_acc[prow * DH + S::DPL * ln + e] = out.acc[k][e];
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// decode partials, persistent and software-pipelined (bf16 KV, 256-key
+// chunks, 4 waves).  Same per-chunk arithmetic as k_decode_partials, so the
+// partials are bit-identical; only the schedule differs.  Work items are
+// (chunk row, kv head) pairs; each workgroup of a grid sized to the device
+// takes a contiguous run of them.  Each lane keeps its key's K row in
+// registers (no LDS copy, so a small LDS footprint) and its V dims of the
+// wave's 64 keys in registers.  The next item's K is issued as soon as the
+// QK loop has read the current one, its V as soon as the PV loop has; the
+// one wait sits at the top of the next item, so HBM traffic overlaps the
+// current item's softmax, PV and merge and the other workgroup on the CU.
+// ---------------------------------------------------------------------------
+template <int DH>
+struct PipeRegs {
+  typedef AttnShape<1, DH> S;
+  uint4 k[S::SLOTS];          // this lane's key row
+  uint32_t q;                 // one packed pair of q (bf16) per thread
+};
+template <int DH>
+struct PipeV {
+  uint32_t v[64][AttnShape<1, DH>::VW];  // this lane's V dims of the wave's 64 keys
+};
+
+// Cursor over the workgroup's run of items.  Items are (chunk row, kv head)
+// with the head fastest, so consecutive items share the chunk row (and its
+// pages) and the request index only ever moves forward.
+struct PipeItem {
+  int it, crow, g, r, j0, n;
+  int pg0, pg1, pg2, pg3;  // pages of this wave's 64 keys (scalars, never indexed)
+};
+
+template <int DH, int R>
+__global__ __launch_bounds__(256, 2) void k_decode_pipe(
+    const void* __restrict__ q, const void* __restrict__ k_pool, const void* __restrict__ v_pool,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ kv_len,
+    const int32_t* __restrict__ chunk_off, int B, int h, int h_kv, int max_pages, float scale,
+    float* __restrict__ part_ml, float* __restrict__ part_acc, int n_items) {
+  constexpr int DT = 1, NW = 4, C = 256;
+  typedef AttnShape<DT, DH> S;
+  typedef AttnLds<DT, DH, R, NW, false> L;
+  typedef ChunkOut<R, NW, S::DPL> CO;
+  static_assert((R * DH) % 2 == 0 && R * DH / 2 <= 256, "q staging");
+  constexpr int QB0 = L::Q_OFF, QB1 = L::BYTES;  // two q slots: L's own and one past it
+  __shared__ __attribute__((aligned(16))) char lds[L::BYTES + R * DH * 4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const long hstride = (long)kPage * S::RB, pstride = hstride * h_kv;
+
+  // this workgroup's contiguous run [it_beg, it_end)
+  const int per = n_items / (int)gridDim.x, rem = n_items % (int)gridDim.x;
+  const int bid = blockIdx.x;
+  const int it_beg = bid * per + (bid < rem ? bid : rem);
+  const int it_end = it_beg + per + (bid < rem ? 1 : 0);
+  if (it_beg >= it_end) return;
+
+  // The cursor is wave-uniform; readfirstlane keeps it in scalar registers so
+  // its loads (chunk_off, kv_len, block table) are scalar loads that do not
+  // count against the vector memory counter the pipeline waits on.
+  auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+  auto set_row = [&](PipeItem& x) {
+    x.j0 = uni((x.crow - chunk_off[x.r]) * C);
+    x.n = uni(min(C, kv_len[x.r] - x.j0));
+    const int32_t* bt = block_table + (long)x.r * max_pages;
+    const int first = uni(bt[x.j0 / kPage]);
+    const int k0 = 64 * wave;  // pages past the chunk's end stand in with its first page
+    const int b0 = (x.j0 + k0) / kPage;
+    x.pg0 = k0 < x.n ? uni(bt[b0]) : first;
+    x.pg1 = k0 + kPage < x.n ? uni(bt[b0 + 1]) : first;
+    x.pg2 = k0 + 2 * kPage < x.n ? uni(bt[b0 + 2]) : first;
+    x.pg3 = k0 + 3 * kPage < x.n ? uni(bt[b0 + 3]) : first;
+  };
+  auto first_item = [&](int it) {
+    PipeItem x;
+    x.it = uni(it);
+    x.crow = uni(it / h_kv);
+    x.g = uni(it - x.crow * h_kv);
+    int lo = 0, hi = B - 1;                  // largest r with chunk_off[r] <= crow
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (uni(chunk_off[mid]) <= x.crow) lo = mid; else hi = mid - 1;
+    }
+    x.r = uni(lo);
+    set_row(x);
+    return x;
+  };
+  auto next_item = [&](const PipeItem& c) {
+    PipeItem x = c;
+    x.it = c.it + 1;
+    if (++x.g == h_kv) {
+      x.g = 0;
+      ++x.crow;
+      while (x.r + 1 < B && uni(chunk_off[x.r + 1]) <= x.crow) x.r = uni(x.r + 1);
+      set_row(x);
+    }
+    return x;
+  };
+  auto issue_k = [&](const PipeItem& x, PipeRegs<DH>& R_) {
+    // this lane's page, picked with masks (a select chain over the fields
+    // gets turned into an indexed load from a stack copy of the cursor)
+    const int p = lane >> 4;
+    const int page = (x.pg0 & -(p == 0)) | (x.pg1 & -(p == 1)) | (x.pg2 & -(p == 2)) |
+                     (x.pg3 & -(p == 3));
+    const char* row = static_cast<const char*>(k_pool) + x.g * hstride + page * pstride +
+                      (lane & (kPage - 1)) * S::RB;
+#pragma unroll
+    for (int c = 0; c < S::SLOTS; ++c) R_.k[c] = reinterpret_cast<const uint4*>(row)[c];
+  };
+  auto issue_v = [&](const PipeItem& x, PipeV<DH>& R_) {
+    const char* base = static_cast<const char*>(v_pool) + x.g * hstride + lane * S::DPL * 2;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int page = p == 0 ? x.pg0 : p == 1 ? x.pg1 : p == 2 ? x.pg2 : x.pg3;
+      const char* pb = base + page * pstride;
+#pragma unroll
+      for (int s = 0; s < kPage; ++s) {
+        if (S::DPL == 2) {
+          R_.v[p * kPage + s][0] = *reinterpret_cast<const uint32_t*>(pb + s * S::RB);
+        } else {
+          R_.v[p * kPage + s][0] = *reinterpret_cast<const uint16_t*>(pb + s * S::RB);
+        }
+      }
+    }
+  };
+  auto issue_q = [&](const PipeItem& x, PipeRegs<DH>& R_) {
+    const uint32_t* qs = reinterpret_cast<const uint32_t*>(
+        static_cast<const uint16_t*>(q) + ((long)x.r * h + x.g * R) * DH);
+    R_.q = tid < R * DH / 2 ? qs[tid] : 0u;
+  };
+  auto put_q = [&](const PipeRegs<DH>& R_, int off) {
+    float* dst = reinterpret_cast<float*>(lds + off);
+    if (tid < R * DH / 2) {
+      dst[2 * tid] = bf16_lo(R_.q);
+      dst[2 * tid + 1] = bf16_hi(R_.q);
+    }
+  };
+
+  PipeItem cur = first_item(it_beg);
+  PipeRegs<DH> rg;
+  PipeV<DH> vr;
+  issue_q(cur, rg);
+  issue_k(cur, rg);
+  issue_v(cur, vr);
+  put_q(rg, QB0);
+  __syncthreads();
+  // One item, its q in LDS slot qc.  The next item's q is issued first
+  // thing, its K once QK has read the current K, its V once PV has read the
+  // current V (then its q moves to slot qn; the merge's barrier publishes it).
+  // The loads are unconditional, so the compiler can count them exactly and
+  // never needs a full wait inside the item; after the last item they
+  // re-read the current item, which is still in L2.
+  auto step = [&](int qc, int qn) {
+    BI_WAIT_VMCNT(0);
+    const bool more = cur.it + 1 < it_end;
+    const PipeItem nxt = more ? next_item(cur) : cur;
+    issue_q(nxt, rg);
+    auto ks = [&](int c) { return rg.k[c]; };
+    auto h1 = [&]() { issue_k(nxt, rg); };
+    auto h2 = [&]() {
+      put_q(rg, qn);
+      issue_v(nxt, vr);
+    };
+    CO out;
+    chunk_partial_k<DT, DH, R, NW, false, false>(lds, cur.n, scale, ks, vr.v, out, h1, h2, qc);
+#pragma unroll
+    for (int k = 0; k < CO::ITEMS; ++k) {
+      const int item = tid + 256 * k;
+      if (item < R * 64) {
+        const int hi2 = item >> 6, ln = item & 63;
+        const long prow = (long)cur.crow * h + cur.g * R + hi2;
+        if (ln == 0) {
+          part_ml[2 * prow] = out.m[k];
+          part_ml[2 * prow + 1] = out.l[k];
+        }
+#pragma unroll
+        for (int e = 0; e < S::DPL; ++e) part_acc[prow * DH + S::DPL * ln + e] = out.acc[k][e];
+      }
+    }
+    cur = nxt;
+    return more;
+  };
+  for (;;) {
+    if (!step(QB0, QB1)) break;
+    if (!step(QB1, QB0)) break;
   }
 }
 
@@ -603,11 +811,33 @@ static void launch_decode(const void* q, const void* kp, const void* vp, const i
                      q, kp, vp, bt, kvl, off, B, h, h_kv, ps, mp, scale, ml, acc);
 }
 
+// Persistent grid of the pipelined kernel: as many workgroups as the device
+// keeps resident (queried once per instantiation), never more than items.
+template <int DH, int R>
+static void launch_decode_pipe(const void* q, const void* kp, const void* vp, const int32_t* bt,
+                               const int32_t* kvl, const int32_t* off, int B, int tot, int h,
+                               int h_kv, int mp, float scale, float* ml, float* acc,
+                               hipStream_t s) {
+  static int resident = 0;
+  if (resident == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    (void)hipGetDevice(&dev);
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_pipe<DH, R>, 256, 0);
+    resident = (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
+  }
+  const long items = (long)tot * h_kv;
+  const int grid = (int)(items < resident ? items : resident);
+  hipLaunchKernelGGL((k_decode_pipe<DH, R>), dim3(grid), dim3(256), 0, s, q, kp, vp, bt, kvl,
+                     off, B, h, h_kv, mp, scale, ml, acc, (int)items);
+}
+
 template <int DT, int DH, int R>
 static void decode_nw(int nw, const void* q, const void* kp, const void* vp, const int32_t* bt,
                       const int32_t* kvl, const int32_t* off, int B, int tot, int h, int h_kv,
                       int ps, int mp, float scale, float* ml, float* acc, hipStream_t s) {
   if (nw == 1) launch_decode<DT, DH, R, 1>(q, kp, vp, bt, kvl, off, B, tot, h, h_kv, ps, mp, scale, ml, acc, s);
+  else if (DT == 1) launch_decode_pipe<DH, R>(q, kp, vp, bt, kvl, off, B, tot, h, h_kv, mp, scale, ml, acc, s);
   else launch_decode<DT, DH, R, 4>(q, kp, vp, bt, kvl, off, B, tot, h, h_kv, ps, mp, scale, ml, acc, s);
 }
 

@@ -190,7 +190,7 @@ __global__ __launch_bounds__((MT + kCopyWaves) * 64) void k_gemm_narrow(
   const long ld = Ktot;
   A += kbeg;
   W += kbeg;
-  constexpr int KTS = 8, NS = 16, RING = 2;
+  constexpr int KTS = 8, NS = 16, RING = 4;
   constexpr int SLOT = KTS * kFrag;
   constexpr int QW = KTS / kCopyWaves;  // copies per copy wave per stage
   extern __shared__ __attribute__((aligned(1024))) char smem[];
