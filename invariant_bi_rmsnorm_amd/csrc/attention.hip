@@ -94,14 +94,18 @@ struct NoHook {
 // LDS block, or from registers in the pipelined kernel).  after_qk runs once
 // every K read of the chunk is done, after_pv once every V register is
 // consumed: the pipelined kernel issues the next chunk's loads there.
-template <int DT, int DH, int R, int NW, bool KLDS = true, bool FINAL_SYNC = true, class KSrc,
-          class H1 = NoHook, class H2 = NoHook>
+// QG: q is read from global memory (bf16, qg = this kv head's first query
+// head, wave-uniform) instead of the fp32 copy in LDS; same values.
+template <int DT, int DH, int R, int NW, bool KLDS = true, bool FINAL_SYNC = true,
+          bool QG = false, class KSrc, class H1 = NoHook, class H2 = NoHook>
 __device__ __forceinline__ void chunk_partial_k(char* lds, int n, float scale, const KSrc& ksrc,
                                                 const uint32_t (&vreg)[64][AttnShape<DT, DH>::VW],
                                                 ChunkOut<R, NW, AttnShape<DT, DH>::DPL>& out,
                                                 const H1& after_qk = H1(),
                                                 const H2& after_pv = H2(),
-                                                int q_off = AttnLds<DT, DH, R, NW, KLDS>::Q_OFF) {
+                                                int q_off = AttnLds<DT, DH, R, NW, KLDS>::Q_OFF,
+                                                const uint16_t* __restrict__ qg = nullptr) {
+  static_assert(!QG || DT == 1, "global q path is for bf16");
   typedef AttnShape<DT, DH> S;
   typedef AttnLds<DT, DH, R, NW, KLDS> L;
   constexpr int DPL = S::DPL;
@@ -133,15 +137,24 @@ __device__ __forceinline__ void chunk_partial_k(char* lds, int n, float scale, c
       }
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        const float4* qv = reinterpret_cast<const float4*>(qs + i * DH + c * S::EPS);
+        float qv[S::EPS];
+        if constexpr (QG) {
+          // q straight from global memory at a wave-uniform address: scalar
+          // loads into SGPRs (bf16 widened by shifts), no LDS traffic
+          const uint4 w4 = *reinterpret_cast<const uint4*>(qg + i * DH + c * S::EPS);
+          qv[0] = bf16_lo(w4.x); qv[1] = bf16_hi(w4.x); qv[2] = bf16_lo(w4.y);
+          qv[3] = bf16_hi(w4.y); qv[4] = bf16_lo(w4.z); qv[5] = bf16_hi(w4.z);
+          qv[6] = bf16_lo(w4.w); qv[7] = bf16_hi(w4.w);
+        } else {
+          const float4* q4p = reinterpret_cast<const float4*>(qs + i * DH + c * S::EPS);
 #pragma unroll
-        for (int e4 = 0; e4 < S::EPS / 4; ++e4) {
-          const float4 q4 = qv[e4];
-          sc[i] = __builtin_fmaf(q4.x, kv[4 * e4 + 0], sc[i]);
-          sc[i] = __builtin_fmaf(q4.y, kv[4 * e4 + 1], sc[i]);
-          sc[i] = __builtin_fmaf(q4.z, kv[4 * e4 + 2], sc[i]);
-          sc[i] = __builtin_fmaf(q4.w, kv[4 * e4 + 3], sc[i]);
+          for (int e4 = 0; e4 < S::EPS / 4; ++e4) {
+            const float4 q4 = q4p[e4];
+            qv[4 * e4] = q4.x; qv[4 * e4 + 1] = q4.y; qv[4 * e4 + 2] = q4.z; qv[4 * e4 + 3] = q4.w;
+          }
         }
+#pragma unroll
+        for (int e = 0; e < S::EPS; ++e) sc[i] = __builtin_fmaf(qv[e], kv[e], sc[i]);
       }
     }
 #pragma unroll
@@ -383,16 +396,16 @@ __global__ __launch_bounds__(64 * NW) void k_decode_partials(
 // (chunk row, kv head) pairs; each workgroup of a grid sized to the device
 // takes a contiguous run of them.  Each lane keeps its key's K row in
 // registers (no LDS copy, so a small LDS footprint) and its V dims of the
-// wave's 64 keys in registers.  The next item's K is issued as soon as the
-// QK loop has read the current one, its V as soon as the PV loop has; the
-// one wait sits at the top of the next item, so HBM traffic overlaps the
-// current item's softmax, PV and merge and the other workgroup on the CU.
+// wave's 64 keys in registers; q comes from scalar loads (SGPRs), so the QK
+// loop touches no LDS.  The next item's K is issued as soon as the QK loop
+// has read the current one, its V as soon as the PV loop has; the one wait
+// sits at the top of the next item, so HBM traffic overlaps the current
+// item's softmax, PV and merge and the other workgroup on the CU.
 // ---------------------------------------------------------------------------
 template <int DH>
 struct PipeRegs {
   typedef AttnShape<1, DH> S;
   uint4 k[S::SLOTS];          // this lane's key row
-  uint32_t q;                 // one packed pair of q (bf16) per thread
 };
 template <int DH>
 struct PipeV {
@@ -417,9 +430,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_pipe(
   typedef AttnShape<DT, DH> S;
   typedef AttnLds<DT, DH, R, NW, false> L;
   typedef ChunkOut<R, NW, S::DPL> CO;
-  static_assert((R * DH) % 2 == 0 && R * DH / 2 <= 256, "q staging");
-  constexpr int QB0 = L::Q_OFF, QB1 = L::BYTES;  // two q slots: L's own and one past it
-  __shared__ __attribute__((aligned(16))) char lds[L::BYTES + R * DH * 4];
+  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long hstride = (long)kPage * S::RB, pstride = hstride * h_kv;
@@ -499,46 +510,33 @@ __global__ __launch_bounds__(256, 2) void k_decode_pipe(
       }
     }
   };
-  auto issue_q = [&](const PipeItem& x, PipeRegs<DH>& R_) {
-    const uint32_t* qs = reinterpret_cast<const uint32_t*>(
-        static_cast<const uint16_t*>(q) + ((long)x.r * h + x.g * R) * DH);
-    R_.q = tid < R * DH / 2 ? qs[tid] : 0u;
-  };
-  auto put_q = [&](const PipeRegs<DH>& R_, int off) {
-    float* dst = reinterpret_cast<float*>(lds + off);
-    if (tid < R * DH / 2) {
-      dst[2 * tid] = bf16_lo(R_.q);
-      dst[2 * tid + 1] = bf16_hi(R_.q);
-    }
-  };
-
   PipeItem cur = first_item(it_beg);
   PipeRegs<DH> rg;
   PipeV<DH> vr;
-  issue_q(cur, rg);
   issue_k(cur, rg);
   issue_v(cur, vr);
-  put_q(rg, QB0);
-  __syncthreads();
-  // One item, its q in LDS slot qc.  The next item's q is issued first
-  // thing, its K once QK has read the current K, its V once PV has read the
-  // current V (then its q moves to slot qn; the merge's barrier publishes it).
-  // The loads are unconditional, so the compiler can count them exactly and
-  // never needs a full wait inside the item; after the last item they
-  // re-read the current item, which is still in L2.
-  auto step = [&](int qc, int qn) {
+  // One item.  Its K is issued once the QK loop has read the current K, its
+  // V once PV has read the current V.  The loads are unconditional, so the
+  // compiler can count them exactly and never needs a full wait inside the
+  // item; after the last item they read one page of the current item again
+  // (just fetched, so a cache hit).  q is read by the QK loop itself with
+  // scalar loads.
+  for (;;) {
     BI_WAIT_VMCNT(0);
     const bool more = cur.it + 1 < it_end;
-    const PipeItem nxt = more ? next_item(cur) : cur;
-    issue_q(nxt, rg);
+    PipeItem nxt = cur;
+    if (more) {
+      nxt = next_item(cur);
+    } else {
+      nxt.pg1 = nxt.pg2 = nxt.pg3 = nxt.pg0;
+    }
+    const uint16_t* qg = static_cast<const uint16_t*>(q) + ((long)cur.r * h + cur.g * R) * DH;
     auto ks = [&](int c) { return rg.k[c]; };
     auto h1 = [&]() { issue_k(nxt, rg); };
-    auto h2 = [&]() {
-      put_q(rg, qn);
-      issue_v(nxt, vr);
-    };
+    auto h2 = [&]() { issue_v(nxt, vr); };
     CO out;
-    chunk_partial_k<DT, DH, R, NW, false, false>(lds, cur.n, scale, ks, vr.v, out, h1, h2, qc);
+    chunk_partial_k<DT, DH, R, NW, false, false, true>(lds, cur.n, scale, ks, vr.v, out, h1, h2,
+                                                       0, qg);
 #pragma unroll
     for (int k = 0; k < CO::ITEMS; ++k) {
       const int item = tid + 256 * k;
@@ -553,12 +551,8 @@ __global__ __launch_bounds__(256, 2) void k_decode_pipe(
         for (int e = 0; e < S::DPL; ++e) part_acc[prow * DH + S::DPL * ln + e] = out.acc[k][e];
       }
     }
+    if (!more) break;
     cur = nxt;
-    return more;
-  };
-  for (;;) {
-    if (!step(QB0, QB1)) break;
-    if (!step(QB1, QB0)) break;
   }
 }
 
