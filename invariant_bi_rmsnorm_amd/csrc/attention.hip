@@ -390,173 +390,6 @@ __global__ __launch_bounds__(64 * NW) void k_decode_partials(
 }
 
 // ---------------------------------------------------------------------------
-// decode partials, persistent and software-pipelined (bf16 KV, 256-key
-// chunks, 4 waves).  Same per-chunk arithmetic as k_decode_partials, so the
-// partials are bit-identical; only the schedule differs.  Work items are
-// (chunk row, kv head) pairs; each workgroup of a grid sized to the device
-// takes a contiguous run of them.  Each lane keeps its key's K row in
-// registers (no LDS copy, so a small LDS footprint) and its V dims of the
-// wave's 64 keys in registers; q comes from scalar loads (SGPRs), so the QK
-// loop touches no LDS.  The next item's K is issued as soon as the QK loop
-// has read the current one, its V as soon as the PV loop has; the one wait
-// sits at the top of the next item, so HBM traffic overlaps the current
-// item's softmax, PV and merge and the other workgroup on the CU.
-// ---------------------------------------------------------------------------
-template <int DH>
-struct PipeRegs {
-  typedef AttnShape<1, DH> S;
-  uint4 k[S::SLOTS];          // this lane's key row
-};
-template <int DH>
-struct PipeV {
-  uint32_t v[64][AttnShape<1, DH>::VW];  // this lane's V dims of the wave's 64 keys
-};
-
-// Cursor over the workgroup's run of items.  Items are (chunk row, kv head)
-// with the head fastest, so consecutive items share the chunk row (and its
-// pages) and the request index only ever moves forward.
-struct PipeItem {
-  int it, crow, g, r, j0, n;
-  int pg0, pg1, pg2, pg3;  // pages of this wave's 64 keys (scalars, never indexed)
-};
-
-template <int DH, int R>
-__global__ __launch_bounds__(256, 2) void k_decode_pipe(
-    const void* __restrict__ q, const void* __restrict__ k_pool, const void* __restrict__ v_pool,
-    const int32_t* __restrict__ block_table, const int32_t* __restrict__ kv_len,
-    const int32_t* __restrict__ chunk_off, int B, int h, int h_kv, int max_pages, float scale,
-    float* __restrict__ part_ml, float* __restrict__ part_acc, int n_items) {
-  constexpr int DT = 1, NW = 4, C = 256;
-  typedef AttnShape<DT, DH> S;
-  typedef AttnLds<DT, DH, R, NW, false> L;
-  typedef ChunkOut<R, NW, S::DPL> CO;
-  __shared__ __attribute__((aligned(16))) char lds[L::BYTES];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const long hstride = (long)kPage * S::RB, pstride = hstride * h_kv;
-
-  // this workgroup's contiguous run [it_beg, it_end)
-  const int per = n_items / (int)gridDim.x, rem = n_items % (int)gridDim.x;
-  const int bid = blockIdx.x;
-  const int it_beg = bid * per + (bid < rem ? bid : rem);
-  const int it_end = it_beg + per + (bid < rem ? 1 : 0);
-  if (it_beg >= it_end) return;
-
-  // The cursor is wave-uniform; readfirstlane keeps it in scalar registers so
-  // its loads (chunk_off, kv_len, block table) are scalar loads that do not
-  // count against the vector memory counter the pipeline waits on.
-  auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
-  auto set_row = [&](PipeItem& x) {
-    x.j0 = uni((x.crow - chunk_off[x.r]) * C);
-    x.n = uni(min(C, kv_len[x.r] - x.j0));
-    const int32_t* bt = block_table + (long)x.r * max_pages;
-    const int first = uni(bt[x.j0 / kPage]);
-    const int k0 = 64 * wave;  // pages past the chunk's end stand in with its first page
-    const int b0 = (x.j0 + k0) / kPage;
-    x.pg0 = k0 < x.n ? uni(bt[b0]) : first;
-    x.pg1 = k0 + kPage < x.n ? uni(bt[b0 + 1]) : first;
-    x.pg2 = k0 + 2 * kPage < x.n ? uni(bt[b0 + 2]) : first;
-    x.pg3 = k0 + 3 * kPage < x.n ? uni(bt[b0 + 3]) : first;
-  };
-  auto first_item = [&](int it) {
-    PipeItem x;
-    x.it = uni(it);
-    x.crow = uni(it / h_kv);
-    x.g = uni(it - x.crow * h_kv);
-    int lo = 0, hi = B - 1;                  // largest r with chunk_off[r] <= crow
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (uni(chunk_off[mid]) <= x.crow) lo = mid; else hi = mid - 1;
-    }
-    x.r = uni(lo);
-    set_row(x);
-    return x;
-  };
-  auto next_item = [&](const PipeItem& c) {
-    PipeItem x = c;
-    x.it = c.it + 1;
-    if (++x.g == h_kv) {
-      x.g = 0;
-      ++x.crow;
-      while (x.r + 1 < B && uni(chunk_off[x.r + 1]) <= x.crow) x.r = uni(x.r + 1);
-      set_row(x);
-    }
-    return x;
-  };
-  auto issue_k = [&](const PipeItem& x, PipeRegs<DH>& R_) {
-    // this lane's page, picked with masks (a select chain over the fields
-    // gets turned into an indexed load from a stack copy of the cursor)
-    const int p = lane >> 4;
-    const int page = (x.pg0 & -(p == 0)) | (x.pg1 & -(p == 1)) | (x.pg2 & -(p == 2)) |
-                     (x.pg3 & -(p == 3));
-    const char* row = static_cast<const char*>(k_pool) + x.g * hstride + page * pstride +
-                      (lane & (kPage - 1)) * S::RB;
-#pragma unroll
-    for (int c = 0; c < S::SLOTS; ++c) R_.k[c] = reinterpret_cast<const uint4*>(row)[c];
-  };
-  auto issue_v = [&](const PipeItem& x, PipeV<DH>& R_) {
-    const char* base = static_cast<const char*>(v_pool) + x.g * hstride + lane * S::DPL * 2;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int page = p == 0 ? x.pg0 : p == 1 ? x.pg1 : p == 2 ? x.pg2 : x.pg3;
-      const char* pb = base + page * pstride;
-#pragma unroll
-      for (int s = 0; s < kPage; ++s) {
-        if (S::DPL == 2) {
-          R_.v[p * kPage + s][0] = *reinterpret_cast<const uint32_t*>(pb + s * S::RB);
-        } else {
-          R_.v[p * kPage + s][0] = *reinterpret_cast<const uint16_t*>(pb + s * S::RB);
-        }
-      }
-    }
-  };
-  PipeItem cur = first_item(it_beg);
-  PipeRegs<DH> rg;
-  PipeV<DH> vr;
-  issue_k(cur, rg);
-  issue_v(cur, vr);
-  // One item.  Its K is issued once the QK loop has read the current K, its
-  // V once PV has read the current V.  The loads are unconditional, so the
-  // compiler can count them exactly and never needs a full wait inside the
-  // item; after the last item they read one page of the current item again
-  // (just fetched, so a cache hit).  q is read by the QK loop itself with
-  // scalar loads.
-  for (;;) {
-    BI_WAIT_VMCNT(0);
-    const bool more = cur.it + 1 < it_end;
-    PipeItem nxt = cur;
-    if (more) {
-      nxt = next_item(cur);
-    } else {
-      nxt.pg1 = nxt.pg2 = nxt.pg3 = nxt.pg0;
-    }
-    const uint16_t* qg = static_cast<const uint16_t*>(q) + ((long)cur.r * h + cur.g * R) * DH;
-    auto ks = [&](int c) { return rg.k[c]; };
-    auto h1 = [&]() { issue_k(nxt, rg); };
-    auto h2 = [&]() { issue_v(nxt, vr); };
-    CO out;
-    chunk_partial_k<DT, DH, R, NW, false, false, true>(lds, cur.n, scale, ks, vr.v, out, h1, h2,
-                                                       0, qg);
-#pragma unroll
-    for (int k = 0; k < CO::ITEMS; ++k) {
-      const int item = tid + 256 * k;
-      if (item < R * 64) {
-        const int hi2 = item >> 6, ln = item & 63;
-        const long prow = (long)cur.crow * h + cur.g * R + hi2;
-        if (ln == 0) {
-          part_ml[2 * prow] = out.m[k];
-          part_ml[2 * prow + 1] = out.l[k];
-        }
-#pragma unroll
-        for (int e = 0; e < S::DPL; ++e) part_acc[prow * DH + S::DPL * ln + e] = out.acc[k][e];
-      }
-    }
-    if (!more) break;
-    cur = nxt;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // serial merge: one wave per (request, head); lane owns DH/64 dims
 // ---------------------------------------------------------------------------
 // REV (twin only): chunks combined from the last to the first.  The
@@ -767,6 +600,432 @@ __global__ __launch_bounds__(64 * NW) void k_prefill(
 }
 
 // ---------------------------------------------------------------------------
+// bf16 KV: the chunk on matrix cores.
+//
+// Per chunk (keys j0 .. j0 + n - 1, n <= C) of one kv head, for a tile of up
+// to 16 rows, each a (query row, query head) pair:
+//   S = q K^T by v_mfma_f32_16x16x32_bf16, one accumulation chain over the
+//       d_h in steps of 32 (ascending); s = S * scale;
+//   m = max of s over the row's visible keys, plus 0;
+//   p = exp(s - m) for visible keys, 0 otherwise; P = bf16(p);
+//   l = P . 1 and acc = P V, each one MFMA chain over the chunk's keys in
+//       steps of 32 (ascending).
+// Every step depends only on the row's own q and the chunk's keys: a row's
+// results do not depend on the other rows of its tile (decode and prefill
+// rows give the same bits), on the batch, or on physical pages.
+//
+// Layout: wave w computes S for the chunk's keys 64w .. 64w + 63 (four key
+// tiles of 16); its K fragments come straight from global memory (a tile is
+// one 16-token page).  V of the whole chunk is copied to LDS (rows of d_h
+// bf16, 16-byte pieces XOR-swizzled by the key) and read back as MFMA B
+// fragments by transposing reads; P goes through LDS as bf16 [row][key]
+// (8-key blocks swizzled by the row).  Wave w then owns d_h / 16 / NW
+// 16-dim tiles of the output.  Keys past n read valid memory and are masked;
+// their V rows are zeroed so that no stale value can reach the sum.
+// ---------------------------------------------------------------------------
+template <int DH, int C, int MT>
+struct MfmaLds {
+  static constexpr int NW = C / 64;
+  static constexpr int RB = DH * 2;                       // bytes per V row
+  static constexpr int V_OFF = 0;                         // bf16 V [C][DH]
+  static constexpr int P_OFF = C * RB;                    // bf16 P [MT * 16][C]
+  static constexpr int MX_OFF = P_OFF + MT * 16 * C * 2;  // fp32 [NW][MT * 16]
+  static constexpr int BYTES = MX_OFF + NW * MT * 16 * 4;
+  static constexpr int PM = (C / 8 < 16 ? C / 8 : 16) - 1;  // P block swizzle mask
+};
+
+template <int DH>
+__device__ __forceinline__ uint32_t vswz(int key, int piece) {
+  return (uint32_t)(key * DH * 2 + 16 * (piece ^ (key & 7)));
+}
+
+// Copies V rows of this wave's 64 keys (absolute keys j0 + 64w + k) into the
+// chunk's LDS block, one 1 KiB copy per instruction, page ids per 16 keys.
+template <int DH>
+__device__ __forceinline__ void mfma_stage_v(char* lds, const char* vbase, long pstride,
+                                             const int (&pg)[4], int wave) {
+  constexpr int RB = DH * 2, SLOTS = RB / 16, KPI = 1024 / RB;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int inst = 0; inst < 64 / KPI; ++inst) {
+    const int k = inst * KPI + lane / SLOTS;       // key within the wave
+    const int slot = lane % SLOTS;
+    const int key = 64 * wave + k;                 // key within the chunk
+    const int page = pg[k / kPage];
+    const char* src = vbase + page * pstride + (k % kPage) * RB + 16 * (slot ^ (key & 7));
+    dma16(src, lds + (64 * wave + inst * KPI) * RB);
+  }
+}
+
+// K fragments (B operand of QK) of this wave's four key tiles.
+template <int DH>
+__device__ __forceinline__ void mfma_load_k(u32x4_t (&kf)[4][DH / 32], const char* kbase,
+                                            long pstride, const int (&pg)[4]) {
+  constexpr int RB = DH * 2;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const char* row = kbase + pg[t] * pstride + (lane & 15) * RB + 16 * (lane >> 4);
+#pragma unroll
+    for (int s = 0; s < DH / 32; ++s) kf[t][s] = *reinterpret_cast<const u32x4_t*>(row + 64 * s);
+  }
+}
+
+// Zero V rows n .. of this wave's keys (keys past the chunk's end).
+template <int DH>
+__device__ __forceinline__ void mfma_zero_v_tail(char* lds, int n, int wave) {
+  constexpr int RB = DH * 2, SLOTS = RB / 16;
+  const int lane = threadIdx.x & 63;
+  const int k0 = max(n, 64 * wave), k1 = 64 * wave + 64;
+  for (int i = lane; i < (k1 - k0) * SLOTS; i += 64)
+    *reinterpret_cast<uint4*>(lds + (k0 + i / SLOTS) * RB + 16 * (i % SLOTS)) =
+        make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The chunk for MT row tiles.  qf: A fragments of q; kf: this wave's K
+// fragments; key abs position of (wave, tile t, lane) = j0 + 64w + 16t +
+// (l & 15); lastpos[mt][j]: last visible absolute key of row 4 (l >> 4) + j
+// of tile mt (-1 for rows that are not used).  Only rows with j < RJ may be
+// used (decode puts its query heads on rows 0, 4, 8, 12 and passes RJ = 1);
+// P rows of the other j must already hold zeros.  V must be staged (and the
+// tail zeroed) by every wave before the call.  Outputs for this lane's rows
+// and this wave's dim tiles; m = -inf marks a row with no visible key.
+template <int DH, int C, int MT, int RJ = 4>
+__device__ __forceinline__ void mfma_chunk(char* lds, const u32x4_t (&qf)[MT][DH / 32],
+                                           const u32x4_t (&kf)[4][DH / 32], int j0,
+                                           const int (&lastpos)[MT][4], float scale,
+                                           float (&m_out)[MT][4], float (&l_out)[MT][4],
+                                           f32x4_t (&acc)[MT][DH / 16 / (C / 64)]) {
+  typedef MfmaLds<DH, C, MT> L;
+  constexpr int NW = L::NW, KS = DH / 32, DPW = DH / 16 / NW;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g4 = lane >> 4, col = lane & 15;
+  float* mx = reinterpret_cast<float*>(lds + L::MX_OFF);
+  char* pl = lds + L::P_OFF;
+
+  // ---- S = q K^T, scaled and masked
+  float sv[MT][4][4];  // [row tile][key tile][j]
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x4_t c = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) c = mfma16(qf[mt][s], kf[t][s], c);
+      const int key = j0 + 64 * wave + 16 * t + col;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sv[mt][t][j] = (j < RJ && key <= lastpos[mt][j]) ? c[j] * scale : -__builtin_inff();
+    }
+  }
+  // ---- row maxima: in lane over the key tiles, over the 16 lanes of the
+  // row group, then over the waves
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) {
+      float v = fmaxf(fmaxf(sv[mt][0][j], sv[mt][1][j]), fmaxf(sv[mt][2][j], sv[mt][3][j]));
+      v = row16_max(v);
+      if (col == 0) mx[wave * MT * 16 + mt * 16 + 4 * g4 + j] = v;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) {
+      float v = mx[mt * 16 + 4 * g4 + j];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) v = fmaxf(v, mx[w * MT * 16 + mt * 16 + 4 * g4 + j]);
+      m_out[mt][j] = v + 0.0f;
+    }
+  }
+  // ---- P = bf16(exp(s - m)) into LDS [row][key]
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int key = 64 * wave + 16 * t + col;  // within the chunk
+#pragma unroll
+      for (int j = 0; j < RJ; ++j) {
+        const int row = 4 * g4 + j;
+        const float mm = m_out[mt][j];
+        const float p = (sv[mt][t][j] == -__builtin_inff()) ? 0.0f : exp_fixed(sv[mt][t][j] - mm);
+        const uint32_t off = (uint32_t)((mt * 16 + row) * C * 2 +
+                                        16 * ((key >> 3) ^ (row & L::PM)) + 2 * (key & 7));
+        *reinterpret_cast<uint16_t*>(pl + off) = (uint16_t)f32_to_bf16_bits(p);
+      }
+    }
+  }
+  __syncthreads();
+  // ---- l = P . 1 and acc = P V over the chunk's keys, 32 at a time
+  const u32x4_t ones = u32x4_t{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+  f32x4_t lacc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    lacc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int d = 0; d < DPW; ++d) acc[mt][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const int e = col >> 2, c4 = col & 3;  // this lane as a transposing-read source
+#pragma unroll
+  for (int ks = 0; ks < C / 32; ++ks) {
+    u32x4_t a[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int row = col;
+      const uint32_t off = (uint32_t)((mt * 16 + row) * C * 2 +
+                                      16 * ((4 * ks + g4) ^ (row & L::PM)));
+      a[mt] = *reinterpret_cast<const u32x4_t*>(pl + off);
+      lacc[mt] = mfma16(a[mt], ones, lacc[mt]);
+    }
+#pragma unroll
+    for (int d = 0; d < DPW; ++d) {
+      const int dt = wave * DPW + d;                       // 16-dim tile
+      const int piece = 2 * dt + (c4 >> 1);
+      const int k0 = 32 * ks + 8 * g4 + e;
+      const uint2 lo = lds_read_tr16(lds, vswz<DH>(k0, piece) + 8 * (c4 & 1));
+      const uint2 hi = lds_read_tr16(lds, vswz<DH>(k0 + 4, piece) + 8 * (c4 & 1));
+      const u32x4_t b = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt][d] = mfma16(a[mt], b, acc[mt][d]);
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) l_out[mt][j] = lacc[mt][j];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = RJ; j < 4; ++j) m_out[mt][j] = -__builtin_inff();
+}
+
+// Decode partials on matrix cores, C / 64 waves.  FREE = false: grid (chunk
+// rows, h_kv), chunks of C keys at absolute multiples of C.  FREE = true (the
+// twin): grid (B * stride, h_kv), request r's split c of the length the
+// occupancy policy gives it (free_splits), partial row r * stride + c.
+template <int DH, int R, int C, bool FREE = false>
+__global__ __launch_bounds__(C) void k_decode_mfma(
+    const void* __restrict__ q, const void* __restrict__ k_pool, const void* __restrict__ v_pool,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ kv_len,
+    const int32_t* __restrict__ chunk_off, int B, int h, int h_kv, int max_pages, float scale,
+    float* __restrict__ part_ml, float* __restrict__ part_acc, int chunk2 = 0, int stride = 0) {
+  typedef MfmaLds<DH, C, 1> L;
+  constexpr int KS = DH / 32, DPW = DH / 16 / L::NW;
+  static_assert(R <= 4, "one row group holds the query heads of a kv head");
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = blockIdx.y;
+  int r, j0, n, len;
+  long crow;
+  if (FREE) {
+    r = blockIdx.x / stride;
+    const int c = blockIdx.x % stride;
+    len = kv_len[r];
+    int slen;
+    const int nr = free_splits(len, chunk2, &slen);
+    if (c >= nr) return;
+    j0 = c * slen;
+    n = min(slen, len - j0);
+    crow = (long)r * stride + c;
+  } else {
+    crow = blockIdx.x;
+    int lo = 0, hi = B - 1;  // request owning this chunk row
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (chunk_off[mid] <= (int)crow) lo = mid; else hi = mid - 1;
+    }
+    r = lo;
+    j0 = ((int)crow - chunk_off[r]) * C;
+    len = kv_len[r];
+    n = min(C, len - j0);
+  }
+  const int32_t* bt = block_table + (long)r * max_pages;
+  int pg[4];
+  const int first = bt[j0 / kPage];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int k0 = 64 * wave + kPage * p;
+    pg[p] = k0 < n ? bt[(j0 + k0) / kPage] : first;
+  }
+  const long hstride = (long)kPage * DH * 2, pstride = hstride * h_kv;
+  const char* kbase = static_cast<const char*>(k_pool) + g * hstride;
+  const char* vbase = static_cast<const char*>(v_pool) + g * hstride;
+  u32x4_t kf[4][KS];
+  mfma_load_k<DH>(kf, kbase, pstride, pg);
+  mfma_stage_v<DH>(lds, vbase, pstride, pg, wave);
+  // query head hd sits on A row 4 hd, so each row group of the score tile
+  // (lanes 16 G .. 16 G + 15, j = 0) holds one head: every lane has a real
+  // score per key tile
+  u32x4_t qf[1][KS];
+  const int col = lane & 15, g4 = lane >> 4;
+  const bool qreal = (col & 3) == 0 && (col >> 2) < R;
+  const uint16_t* qrow =
+      static_cast<const uint16_t*>(q) + ((long)r * h + g * R + (qreal ? col >> 2 : 0)) * DH;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qrow + 8 * g4 + 32 * s);
+    qf[0][s] = qreal ? v : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  // P rows that are not 4 hd stay zero (the chunk writes rows 4 hd only)
+  {
+    char* pl = lds + L::P_OFF;
+    for (int i = threadIdx.x; i < 16 * C * 2 / 16; i += C) {
+      const int row = i / (C * 2 / 16);
+      if ((row & 3) != 0) *reinterpret_cast<uint4*>(pl + 16 * i) = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  BI_WAIT_VMCNT(0);
+  if (n < C) mfma_zero_v_tail<DH>(lds, n, wave);
+  int lastpos[1][4];
+  lastpos[0][0] = g4 < R ? j0 + n - 1 : -1;
+  lastpos[0][1] = lastpos[0][2] = lastpos[0][3] = -1;
+  float m[1][4], l[1][4];
+  f32x4_t acc[1][DPW];
+  mfma_chunk<DH, C, 1, 1>(lds, qf, kf, j0, lastpos, scale, m, l, acc);
+  if (g4 < R) {  // row 4 g4 = query head g4, in every lane of row group g4
+    const long prow = crow * h + g * R + g4;
+    if (col == 0 && wave == 0) {
+      part_ml[2 * prow] = m[0][0];
+      part_ml[2 * prow + 1] = l[0][0];
+    }
+#pragma unroll
+    for (int d = 0; d < DPW; ++d) part_acc[prow * DH + 16 * (wave * DPW + d) + col] = acc[0][d][0];
+  }
+}
+
+// Prefill on matrix cores: grid (blocks of QB = 16 MT / R query rows of one
+// request, h_kv), C / 64 waves.  Each chunk of keys is staged once for the
+// block's rows; each row merges the chunks' partials in chunk order with the
+// rule of the decode merge, so row t equals the decode of kv_len = t + 1.
+// REL (twin): chunk boundaries start at the prompt cut (rounded down to a
+// page) instead of at absolute multiples of C.
+template <int DH, int R, int C, int MT, bool REL = false>
+__global__ __launch_bounds__(C) void k_prefill_mfma(
+    const void* __restrict__ q, const int32_t* __restrict__ q_start,
+    const int32_t* __restrict__ q_pos0, int Rq, const void* __restrict__ k_pool,
+    const void* __restrict__ v_pool, const int32_t* __restrict__ block_table, int h, int h_kv,
+    int max_pages, float scale, void* __restrict__ out) {
+  typedef MfmaLds<DH, C, MT> L;
+  constexpr int KS = DH / 32, DPW = DH / 16 / L::NW, QB = MT * 16 / R;
+  static_assert((MT * 16) % R == 0, "row tiles hold whole query rows");
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, g4 = lane >> 4;
+  const int blk = blockIdx.x, g = blockIdx.y;
+  int r = -1, firstb = 0;  // request of this block: blocks of QB rows, request by request
+  for (int i = 0; i < Rq; ++i) {
+    const int nb = (q_start[i + 1] - q_start[i] + QB - 1) / QB;
+    if (blk < firstb + nb) { r = i; break; }
+    firstb += nb;
+  }
+  if (r < 0) return;
+  const int t0 = q_start[r] + (blk - firstb) * QB;
+  const int t1 = min(t0 + QB, q_start[r + 1]);
+  if (t0 >= t1) return;
+  const int nrows = t1 - t0;
+  const int pos0 = q_pos0[r] + (t0 - q_start[r]);
+  const int pos_last = pos0 + nrows - 1;
+  const int32_t* bt = block_table + (long)r * max_pages;
+  const long hstride = (long)kPage * DH * 2, pstride = hstride * h_kv;
+  const char* kbase = static_cast<const char*>(k_pool) + g * hstride;
+  const char* vbase = static_cast<const char*>(v_pool) + g * hstride;
+
+  // q fragments: A row mt * 16 + col is query row (that / R), head (that % R)
+  u32x4_t qf[MT][KS];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int rr = mt * 16 + col, rho = rr / R, hd = rr % R;
+    const bool real = rho < nrows;
+    const uint16_t* qrow =
+        static_cast<const uint16_t*>(q) + ((long)(t0 + (real ? rho : 0)) * h + g * R + hd) * DH;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qrow + 8 * g4 + 32 * s);
+      qf[mt][s] = real ? v : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+  int rowpos[MT][4];  // this lane's rows: absolute position, or -1
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rho = (mt * 16 + 4 * g4 + j) / R;
+      rowpos[mt][j] = rho < nrows ? pos0 + rho : -1;
+    }
+
+  const int shift = REL ? ((q_pos0[r] % C) & ~(kPage - 1)) : 0;
+  auto jstart = [&](int c) { return shift == 0 ? c * C : (c == 0 ? 0 : shift + (c - 1) * C); };
+  const int nch = shift == 0 ? pos_last / C + 1
+                             : (pos_last < shift ? 1 : (pos_last - shift) / C + 2);
+  float M[MT][4], Lr[MT][4];
+  f32x4_t A[MT][DPW];
+  for (int c = 0; c < nch; ++c) {
+    const int j0 = jstart(c);
+    const int n = min(jstart(c + 1), pos_last + 1) - j0;
+    int pg[4];
+    const int first = bt[j0 / kPage];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int k0 = 64 * wave + kPage * p;
+      pg[p] = k0 < n ? bt[(j0 + k0) / kPage] : first;
+    }
+    if (c > 0) __syncthreads();  // the previous chunk's V and P are no longer read
+    u32x4_t kf[4][KS];
+    mfma_load_k<DH>(kf, kbase, pstride, pg);
+    mfma_stage_v<DH>(lds, vbase, pstride, pg, wave);
+    BI_WAIT_VMCNT(0);
+    if (n < C) mfma_zero_v_tail<DH>(lds, n, wave);
+    int lastpos[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lastpos[mt][j] = min(rowpos[mt][j], j0 + n - 1);
+    float m[MT][4], l[MT][4];
+    f32x4_t acc[MT][DPW];
+    mfma_chunk<DH, C, MT>(lds, qf, kf, j0, lastpos, scale, m, l, acc);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (c == 0) {
+          M[mt][j] = m[mt][j];
+          Lr[mt][j] = l[mt][j];
+#pragma unroll
+          for (int d = 0; d < DPW; ++d) A[mt][d][j] = acc[mt][d][j];
+        } else if (m[mt][j] != -__builtin_inff()) {  // the row sees keys of this chunk
+          const float Mo = M[mt][j], mc = m[mt][j];
+          const float Mn = Mo > mc ? Mo : mc;
+          const float a = exp_fixed(Mo - Mn), b = exp_fixed(mc - Mn);
+          Lr[mt][j] = __builtin_fmaf(l[mt][j], b, Lr[mt][j] * a);
+#pragma unroll
+          for (int d = 0; d < DPW; ++d)
+            A[mt][d][j] = __builtin_fmaf(acc[mt][d][j], b, A[mt][d][j] * a);
+          M[mt][j] = Mn;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rr = mt * 16 + 4 * g4 + j, rho = rr / R, hd = rr % R;
+      if (rho < nrows) {
+        const long o = ((long)(t0 + rho) * h + g * R + hd) * DH;
+#pragma unroll
+        for (int d = 0; d < DPW; ++d)
+          Elem<1>::st(out, o + 16 * (wave * DPW + d) + col, A[mt][d][j] / Lr[mt][j]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 struct AttnArgsCheck {
@@ -805,34 +1064,51 @@ static void launch_decode(const void* q, const void* kp, const void* vp, const i
                      q, kp, vp, bt, kvl, off, B, h, h_kv, ps, mp, scale, ml, acc);
 }
 
-// Persistent grid of the pipelined kernel: as many workgroups as the device
-// keeps resident (queried once per instantiation), never more than items.
-template <int DH, int R>
-static void launch_decode_pipe(const void* q, const void* kp, const void* vp, const int32_t* bt,
-                               const int32_t* kvl, const int32_t* off, int B, int tot, int h,
-                               int h_kv, int mp, float scale, float* ml, float* acc,
-                               hipStream_t s) {
-  static int resident = 0;
-  if (resident == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    (void)hipGetDevice(&dev);
-    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_pipe<DH, R>, 256, 0);
-    resident = (cus > 0 ? cus : 256) * (per_cu > 0 ? per_cu : 1);
+// bf16 KV: matrix-core kernels, chunk length C = 64 nw.
+template <int DH, int R, int C, bool FREE = false>
+static void launch_decode_mfma(dim3 grid, const void* q, const void* kp, const void* vp,
+                               const int32_t* bt, const int32_t* kvl, const int32_t* off, int B,
+                               int h, int h_kv, int mp, float scale, float* ml, float* acc,
+                               hipStream_t s, int chunk2 = 0, int stride = 0) {
+  constexpr int lds = MfmaLds<DH, C, 1>::BYTES;
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)k_decode_mfma<DH, R, C, FREE>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    attr = true;
   }
-  const long items = (long)tot * h_kv;
-  const int grid = (int)(items < resident ? items : resident);
-  hipLaunchKernelGGL((k_decode_pipe<DH, R>), dim3(grid), dim3(256), 0, s, q, kp, vp, bt, kvl,
-                     off, B, h, h_kv, mp, scale, ml, acc, (int)items);
+  hipLaunchKernelGGL((k_decode_mfma<DH, R, C, FREE>), grid, dim3(C), lds, s, q, kp, vp, bt, kvl,
+                     off, B, h, h_kv, mp, scale, ml, acc, chunk2, stride);
+}
+
+template <int DH, int R, int C, bool REL>
+static void launch_prefill_mfma(const void* q, const int32_t* qs, const int32_t* qp, int Rq,
+                                int T, const void* kp, const void* vp, const int32_t* bt, int h,
+                                int h_kv, int mp, float scale, void* out, hipStream_t s) {
+  constexpr int lds = MfmaLds<DH, C, 1>::BYTES, QB = 16 / R;
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)k_prefill_mfma<DH, R, C, 1, REL>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    attr = true;
+  }
+  const int blocks = (T + QB - 1) / QB + Rq;
+  hipLaunchKernelGGL((k_prefill_mfma<DH, R, C, 1, REL>), dim3(blocks, h_kv), dim3(C), lds, s, q,
+                     qs, qp, Rq, kp, vp, bt, h, h_kv, mp, scale, out);
 }
 
 template <int DT, int DH, int R>
 static void decode_nw(int nw, const void* q, const void* kp, const void* vp, const int32_t* bt,
                       const int32_t* kvl, const int32_t* off, int B, int tot, int h, int h_kv,
                       int ps, int mp, float scale, float* ml, float* acc, hipStream_t s) {
-  if (nw == 1) launch_decode<DT, DH, R, 1>(q, kp, vp, bt, kvl, off, B, tot, h, h_kv, ps, mp, scale, ml, acc, s);
-  else if (DT == 1) launch_decode_pipe<DH, R>(q, kp, vp, bt, kvl, off, B, tot, h, h_kv, mp, scale, ml, acc, s);
-  else launch_decode<DT, DH, R, 4>(q, kp, vp, bt, kvl, off, B, tot, h, h_kv, ps, mp, scale, ml, acc, s);
+  if constexpr (DT == 1) {
+    const dim3 grid(tot, h_kv);
+    if (nw == 1) launch_decode_mfma<DH, R, 64>(grid, q, kp, vp, bt, kvl, off, B, h, h_kv, mp, scale, ml, acc, s);
+    else launch_decode_mfma<DH, R, 256>(grid, q, kp, vp, bt, kvl, off, B, h, h_kv, mp, scale, ml, acc, s);
+  } else {
+    if (nw == 1) launch_decode<DT, DH, R, 1>(q, kp, vp, bt, kvl, off, B, tot, h, h_kv, ps, mp, scale, ml, acc, s);
+    else launch_decode<DT, DH, R, 4>(q, kp, vp, bt, kvl, off, B, tot, h, h_kv, ps, mp, scale, ml, acc, s);
+  }
 }
 
 template <int DT, int DH>
@@ -866,8 +1142,13 @@ template <int DT, int DH, int R, bool REL = false>
 static void prefill_nw(int nw, const void* q, const int32_t* qs, const int32_t* qp, int Rq, int T,
                        const void* kp, const void* vp, const int32_t* bt, int h, int h_kv, int ps,
                        int mp, float scale, void* out, hipStream_t s) {
-  if (nw == 1) launch_prefill<DT, DH, R, 1, REL>(q, qs, qp, Rq, T, kp, vp, bt, h, h_kv, ps, mp, scale, out, s);
-  else launch_prefill<DT, DH, R, 4, REL>(q, qs, qp, Rq, T, kp, vp, bt, h, h_kv, ps, mp, scale, out, s);
+  if constexpr (DT == 1) {
+    if (nw == 1) launch_prefill_mfma<DH, R, 64, REL>(q, qs, qp, Rq, T, kp, vp, bt, h, h_kv, mp, scale, out, s);
+    else launch_prefill_mfma<DH, R, 256, REL>(q, qs, qp, Rq, T, kp, vp, bt, h, h_kv, mp, scale, out, s);
+  } else {
+    if (nw == 1) launch_prefill<DT, DH, R, 1, REL>(q, qs, qp, Rq, T, kp, vp, bt, h, h_kv, ps, mp, scale, out, s);
+    else launch_prefill<DT, DH, R, 4, REL>(q, qs, qp, Rq, T, kp, vp, bt, h, h_kv, ps, mp, scale, out, s);
+  }
 }
 
 template <int DT, int DH, bool REL = false>
@@ -910,15 +1191,21 @@ template <int DT, int DH, int R>
 static void launch_decode_free(const void* q, const void* kp, const void* vp, const int32_t* bt,
                                const int32_t* kvl, int B, int h, int h_kv, int mp, float scale,
                                FreePolicy pol, float* ml, float* acc, hipStream_t s) {
-  constexpr int lds = AttnLds<DT, DH, R, 4>::BYTES;
-  static bool attr = false;
-  if (!attr) {
-    (void)hipFuncSetAttribute((const void*)k_decode_free<DT, DH, R>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    attr = true;
+  if constexpr (DT == 1) {
+    launch_decode_mfma<DH, R, 256, true>(dim3(B * pol.stride, h_kv), q, kp, vp, bt, kvl, nullptr,
+                                         B, h, h_kv, mp, scale, ml, acc, s, pol.chunk2,
+                                         pol.stride);
+  } else {
+    constexpr int lds = AttnLds<DT, DH, R, 4>::BYTES;
+    static bool attr = false;
+    if (!attr) {
+      (void)hipFuncSetAttribute((const void*)k_decode_free<DT, DH, R>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      attr = true;
+    }
+    hipLaunchKernelGGL((k_decode_free<DT, DH, R>), dim3(B * pol.stride, h_kv), dim3(256), lds, s,
+                       q, kp, vp, bt, kvl, h, h_kv, mp, scale, pol.chunk2, pol.stride, ml, acc);
   }
-  hipLaunchKernelGGL((k_decode_free<DT, DH, R>), dim3(B * pol.stride, h_kv), dim3(256), lds, s,
-                     q, kp, vp, bt, kvl, h, h_kv, mp, scale, pol.chunk2, pol.stride, ml, acc);
 }
 
 }  // namespace bi

@@ -92,11 +92,11 @@ template <> __device__ __forceinline__ void store8<0>(void* p, long i, const flo
 // polynomial of e^r in Horner form with fma, then scaling by 2^n in two
 // exact-power steps.  Below -104 the result is +0, above 88.75 +inf.
 __device__ __forceinline__ float exp_fixed(float x) {
-  if (x != x) return x;
-  if (x > 88.75f) return __builtin_inff();
-  if (x < -104.0f) return 0.0f;
-  const float n = __builtin_rintf(x * 1.44269502162933349609375f);
-  float r = __builtin_fmaf(-n, 0.693145751953125f, x);
+  // branch-free: the polynomial runs on x clamped into range, the special
+  // cases are selected at the end (same values as testing them first)
+  const float xc = __builtin_fminf(__builtin_fmaxf(x, -104.0f), 88.75f);
+  const float n = __builtin_rintf(xc * 1.44269502162933349609375f);
+  float r = __builtin_fmaf(-n, 0.693145751953125f, xc);
   r = __builtin_fmaf(-n, 1.428606765330187045037746429443359375e-06f, r);
   float p = 1.0f / 5040.0f;
   p = __builtin_fmaf(p, r, 1.0f / 720.0f);
@@ -111,7 +111,23 @@ __device__ __forceinline__ float exp_fixed(float x) {
   const int n2 = ni - n1;
   p = p * __uint_as_float((uint32_t)(n1 + 127) << 23);
   p = p * __uint_as_float((uint32_t)(n2 + 127) << 23);
-  return p;
+  p = x < -104.0f ? 0.0f : p;
+  p = x > 88.75f ? __builtin_inff() : p;
+  return x != x ? x : p;
+}
+
+// Maximum over the 16 lanes of each row of the wave (DPP row rotations;
+// max is exact, so the order of the steps does not matter).
+__device__ __forceinline__ float row16_max(float v) {
+  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(
+                             0, __float_as_int(v), 0x128, 0xf, 0xf, false)));  // row_ror:8
+  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(
+                             0, __float_as_int(v), 0x124, 0xf, 0xf, false)));  // row_ror:4
+  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(
+                             0, __float_as_int(v), 0x122, 0xf, 0xf, false)));  // row_ror:2
+  v = __builtin_fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(
+                             0, __float_as_int(v), 0x121, 0xf, 0xf, false)));  // row_ror:1
+  return v;
 }
 
 // ---- direct global -> LDS copies -----------------------------------------
@@ -187,6 +203,29 @@ __device__ __forceinline__ void lds_read_4x2_stride2k(u32x4_t (&a)[4], u32x4_t (
         "=&v"(b[2]), "=&v"(b[3])
       : "v"(ba), "v"(bb)
       : "memory");
+}
+
+// ---- matrix cores -----------------------------------------------------------
+// v_mfma_f32_16x16x32_bf16.  Operand layout: lane l holds 8 bf16 of A row
+// (l & 15) and of B column (l & 15), both for k = 8 (l >> 4) .. 8 (l >> 4) + 7;
+// the 16 x 16 fp32 result gives lane l column (l & 15), rows 4 (l >> 4) + j,
+// j = 0..3.  A result row depends only on its own A row and B.
+__device__ __forceinline__ f32x4_t mfma16(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i = 4e + c gives the address of 4 consecutive 16-bit elements; lane
+// j = 4c + d receives element d of the segments of lanes c, c + 4, c + 8 and
+// c + 12, in that order (returned as two packed dwords).
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+__device__ __forceinline__ uint2 lds_read_tr16(const void* lds_base, uint32_t byte_off) {
+  const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16_t*)((lds_char_t*)lds_base + byte_off));
+  return __builtin_bit_cast(uint2, r);
 }
 
 // Wait until at most n vector-memory operations of this wave are in flight

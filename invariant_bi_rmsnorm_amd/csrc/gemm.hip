@@ -24,8 +24,7 @@ namespace bi {
 constexpr int kFrag = 1024;  // bytes per operand fragment
 
 __device__ __forceinline__ f32x4_t mfma(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  return mfma16(a, b, c);
 }
 
 // OUTF32: 0 = bf16 store, 1 = fp32 store, 2 = fp32 atomic add (split-K twin)

@@ -43,11 +43,11 @@ def _load():
         "oracle_gemm": (None, [_F, _F, _F, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                ctypes.c_int]),
         "oracle_decode_partials": (None, [_F, _F, _F, _I, _I, _I] + [ctypes.c_int] * 7
-                                   + [ctypes.c_float, _F, _F]),
+                                   + [ctypes.c_float, _F, _F, ctypes.c_int]),
         "oracle_merge_partials": (None, [_F, _F, _I, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          _F, ctypes.c_int]),
         "oracle_prefill_attn": (None, [_F, _I, _I, ctypes.c_int, _F, _F, _I] + [ctypes.c_int] * 6
-                                + [ctypes.c_float, _F, ctypes.c_int]),
+                                + [ctypes.c_float, _F, ctypes.c_int, ctypes.c_int]),
         "oracle_rope": (None, [_F, _I, _F, _F, _F, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                ctypes.c_int]),
         "oracle_add": (None, [_F, _F, _F, ctypes.c_long, ctypes.c_int]),
@@ -144,7 +144,7 @@ def chunk_offsets(kv_len, chunk: int) -> np.ndarray:
 
 
 def decode_partials(q, k_pool, v_pool, block_table, kv_len, chunk_off, h_kv: int,
-                    page_size: int, chunk: int, scale: float):
+                    page_size: int, chunk: int, scale: float, p_bf16: bool = False):
     q = _f32(q)
     B, h, d_h = q.shape
     kp, vp = _f32(k_pool), _f32(v_pool)
@@ -156,7 +156,7 @@ def decode_partials(q, k_pool, v_pool, block_table, kv_len, chunk_off, h_kv: int
     acc = np.zeros((rows, h, d_h), dtype=np.float32)
     _load().oracle_decode_partials(_pf(q), _pf(kp), _pf(vp), _pi(bt), _pi(kv), _pi(off), B, h,
                                    h_kv, d_h, page_size, bt.shape[1], chunk, scale, _pf(ml),
-                                   _pf(acc))
+                                   _pf(acc), int(p_bf16))
     return ml, acc
 
 
@@ -171,16 +171,17 @@ def merge_partials(part_ml, part_acc, chunk_off, round_bf16: bool) -> np.ndarray
 
 
 def decode_attn(q, k_pool, v_pool, block_table, kv_len, h_kv, page_size, chunk, scale,
-                round_bf16: bool):
-    """Decode attention = partials + serial merge."""
+                round_bf16: bool, p_bf16: bool = False):
+    """Decode attention = partials + serial merge.  p_bf16: softmax weights
+    rounded to bf16 before the sums (bf16 KV on matrix cores)."""
     off = chunk_offsets(kv_len, chunk)
     ml, acc = decode_partials(q, k_pool, v_pool, block_table, kv_len, off, h_kv, page_size,
-                              chunk, scale)
+                              chunk, scale, p_bf16)
     return merge_partials(ml, acc, off, round_bf16)
 
 
 def prefill_attn(q, q_start, q_pos0, k_pool, v_pool, block_table, h_kv: int, page_size: int,
-                 chunk: int, scale: float, round_bf16: bool) -> np.ndarray:
+                 chunk: int, scale: float, round_bf16: bool, p_bf16: bool = False) -> np.ndarray:
     q = _f32(q)
     T, h, d_h = q.shape
     qs, qp, bt = _i32(q_start), _i32(q_pos0), _i32(block_table)
@@ -189,7 +190,7 @@ def prefill_attn(q, q_start, q_pos0, k_pool, v_pool, block_table, h_kv: int, pag
     out = np.empty_like(q)
     _load().oracle_prefill_attn(_pf(q), _pi(qs), _pi(qp), R, _pf(kp), _pf(vp), _pi(bt), h, h_kv,
                                 d_h, page_size, bt.shape[1], chunk, scale, _pf(out),
-                                int(round_bf16))
+                                int(round_bf16), int(p_bf16))
     return out
 
 

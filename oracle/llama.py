@@ -6,6 +6,9 @@ request is processed on its own: the oracle has no batch, so its output for
 a request cannot depend on one.  KV lives in the oracle's own paged pools
 (numpy), written at the same (page, slot) addresses.
 
+The model is bf16 throughout, so attention takes the bf16-weight form
+(p rounded to bf16 before the sums, as matrix cores consume it).
+
 Layer (pre-norm, SwiGLU, RoPE on q and k):
   x = rmsnorm(h) ; qkv = x W_qkv^T ; q,k = rope(q,k) ; append k,v
   a = attention(q) ; h = h + a W_o^T ; x = rmsnorm(h)
@@ -74,11 +77,11 @@ class OracleModel:
             self.v[li, pg, :, pos % c.page_size] = v
             if n == 1:
                 a = decode_attn(q, self.k[li], self.v[li], bt, np.array([pos0 + 1], np.int32),
-                                c.h_kv, c.page_size, c.kv_chunk, c.scale, True)
+                                c.h_kv, c.page_size, c.kv_chunk, c.scale, True, p_bf16=True)
             else:
                 a = prefill_attn(q, np.array([0, n], np.int32), np.array([pos0], np.int32),
                                  self.k[li], self.v[li], bt, c.h_kv, c.page_size, c.kv_chunk,
-                                 c.scale, True)
+                                 c.scale, True, p_bf16=True)
             h = add(h, self.gemm(a.reshape(n, hd), lw["wo"], True), True)
             x = rmsnorm(h, lw["ffn_norm"], c.eps, True)
             act = silu_mul(self.gemm(x, lw["wgu"], True), True)

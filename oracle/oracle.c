@@ -260,6 +260,10 @@ static const float *kv_row(const float *pool, const int32_t *bt, int j,
  *   S_u = fl(dot(q, k_u)) * scale, dot serial over d = 0 .. d_h-1 in fma;
  *   m   = max_u S_u, then m + 0 (turns -0 into +0);
  *   p_u = exp(S_u - m)                        (oracle_exp);
+ *   with p_bf16, p_u = bf16(p_u): the weights a matrix-core PV product
+ *     consumes (the multiply-accumulate order below is then the oracle's own;
+ *     a matrix core sums in its hardware order, so parity is the derived
+ *     tolerance, or exact where every partial sum is exact);
  *   keys in blocks of 64 (u = 0..63, 64..127, ...): inside block b,
  *     L_b = serial sum of p_u (L = L + p_u from +0), and
  *     A_b[d] = serial fma(p_u, v_u[d], A_b[d]) from +0, u ascending;
@@ -269,7 +273,7 @@ static void attn_chunk_partial(const float *q, const float *k_pool, const float 
                                const int32_t *bt, int g, int h_kv, int page_size, int d_h,
                                int j0, int n, float scale,
                                float *m_out, float *l_out, float *acc_out,
-                               float *S, float *blk /* [d_h] scratch */)
+                               float *S, float *blk /* [d_h] scratch */, int p_bf16)
 {
     for (int u = 0; u < n; ++u) {
         const float *k = kv_row(k_pool, bt, j0 + u, g, h_kv, page_size, d_h);
@@ -281,6 +285,8 @@ static void attn_chunk_partial(const float *q, const float *k_pool, const float 
     for (int u = 1; u < n; ++u) if (S[u] > m) m = S[u];
     m = m + 0.0f;
     for (int u = 0; u < n; ++u) S[u] = oracle_exp(S[u] - m);   /* S now holds p */
+    if (p_bf16)  /* weights carried in bf16 (matrix-core PV): P = bf16(p) */
+        for (int u = 0; u < n; ++u) S[u] = oracle_bf16_rne(S[u]);
 
     float l = 0.0f;
     for (int b = 0; b * 64 < n; ++b) {
@@ -325,7 +331,7 @@ void oracle_decode_partials(const float *q, const float *k_pool, const float *v_
                             const int32_t *block_table, const int32_t *kv_len,
                             const int32_t *chunk_off, int B, int h, int h_kv, int d_h,
                             int page_size, int max_pages, int chunk, float scale,
-                            float *part_ml, float *part_acc)
+                            float *part_ml, float *part_acc, int p_bf16)
 {
     int group = h / h_kv;
 #pragma omp parallel for collapse(2) schedule(dynamic)
@@ -342,7 +348,7 @@ void oracle_decode_partials(const float *q, const float *k_pool, const float *v_
                 attn_chunk_partial(q + ((size_t)r * h + hi) * d_h, k_pool, v_pool, bt,
                                    hi / group, h_kv, page_size, d_h, j0, n, scale,
                                    &part_ml[2 * row], &part_ml[2 * row + 1],
-                                   &part_acc[row * d_h], S, blk);
+                                   &part_acc[row * d_h], S, blk, p_bf16);
             }
             free(S);
             free(blk);
@@ -409,7 +415,7 @@ void oracle_merge_partials(const float *part_ml, const float *part_acc,
 void oracle_prefill_attn(const float *q, const int32_t *q_start, const int32_t *q_pos0, int R,
                          const float *k_pool, const float *v_pool, const int32_t *block_table,
                          int h, int h_kv, int d_h, int page_size, int max_pages, int chunk,
-                         float scale, float *out, int round_bf16)
+                         float scale, float *out, int round_bf16, int p_bf16)
 {
     int group = h / h_kv;
     int T = q_start[R];
@@ -432,7 +438,8 @@ void oracle_prefill_attn(const float *q, const int32_t *q_start, const int32_t *
                 size_t row = (size_t)c * h + hi;
                 attn_chunk_partial(q + ((size_t)t * h + hi) * d_h, k_pool, v_pool, bt,
                                    hi / group, h_kv, page_size, d_h, j0, n, scale,
-                                   &ml[2 * row], &ml[2 * row + 1], &acc[row * d_h], S, blk);
+                                   &ml[2 * row], &ml[2 * row + 1], &acc[row * d_h], S, blk,
+                                   p_bf16);
             }
             merge_one(ml + 2 * hi, acc + (size_t)hi * d_h, nch, h, d_h,
                       out + ((size_t)t * h + hi) * d_h, round_bf16);

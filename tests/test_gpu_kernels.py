@@ -186,8 +186,13 @@ def _decode(q, kv, kv_len, chunk, scale):
     return ml, acc, out, off
 
 
-@pytest.mark.parametrize("dt,h,h_kv,d_h,chunk", ATTN_CFGS)
+F32_CFGS = [c for c in ATTN_CFGS if c[0] == "f32"]
+BF16_CFGS = [c for c in ATTN_CFGS if c[0] == "bf16"]
+
+
+@pytest.mark.parametrize("dt,h,h_kv,d_h,chunk", F32_CFGS)
 def test_decode_attention_bitwise(dt, h, h_kv, d_h, chunk):
+    # fp32 KV runs the serial VALU chunk: bit for bit the oracle's order
     kv_len = np.array(LENS, np.int32)
     kv = PagedKV(kv_len, h_kv, d_h, 16, seed=100 + d_h, dtype=DT[dt])
     q = synth.normal((len(kv_len), h, d_h), seed=7).to(DT[dt])
@@ -196,8 +201,57 @@ def test_decode_attention_bitwise(dt, h, h_kv, d_h, chunk):
     rml, racc = oracle.decode_partials(q, kv.k, kv.v, kv.bt, kv_len, off, h_kv, 16, chunk, scale)
     assert bits_equal(to_np(ml), rml), mismatch_report(to_np(ml), rml)
     assert bits_equal(to_np(acc), racc), mismatch_report(to_np(acc), racc)
-    rout = oracle.merge_partials(rml, racc, off, round_bf16=(dt == "bf16"))
+    rout = oracle.merge_partials(rml, racc, off, round_bf16=False)
     assert bits_equal(to_np(out), rout), mismatch_report(to_np(out), rout)
+
+
+def _exact_case(kv_len, h, h_kv, d_h, seed, nnz=4):
+    """bf16 inputs on which every partial sum is exact in fp32: q has nnz
+    entries of +-1 per head, keys are in {-1, 0, 1} (integer scores of at
+    most nnz), values are integers in [-2, 2]; with scale 1/4 the weights
+    exp(s - m) are >= e^-2, so P = bf16(p) are multiples of 2^-10 and every
+    l and acc sum, in any order, is exact.  The matrix-core path must then
+    equal the oracle (p_bf16) bit for bit."""
+    rng = np.random.default_rng(seed)
+    kv = PagedKV(kv_len, h_kv, d_h, 16, seed=seed, dtype=torch.bfloat16)
+    kv.k = torch.from_numpy(rng.integers(-1, 2, size=tuple(kv.k.shape)).astype(np.float32)).to(
+        torch.bfloat16)
+    kv.v = torch.from_numpy(rng.integers(-2, 3, size=tuple(kv.v.shape)).astype(np.float32)).to(
+        torch.bfloat16)
+    q = np.zeros((len(kv_len), h, d_h), np.float32)
+    for r in range(len(kv_len)):
+        for i in range(h):
+            idx = rng.choice(d_h, size=nnz, replace=False)
+            q[r, i, idx] = rng.choice([-1.0, 1.0], size=nnz)
+    return torch.from_numpy(q).to(torch.bfloat16), kv
+
+
+@pytest.mark.parametrize("dt,h,h_kv,d_h,chunk", BF16_CFGS)
+def test_decode_attention_bf16_exact_inputs_bitwise(dt, h, h_kv, d_h, chunk):
+    kv_len = np.array(LENS, np.int32)
+    q, kv = _exact_case(kv_len, h, h_kv, d_h, seed=110 + d_h)
+    ml, acc, out, off = _decode(q, kv, kv_len, chunk, 0.25)
+    rml, racc = oracle.decode_partials(q, kv.k, kv.v, kv.bt, kv_len, off, h_kv, 16, chunk, 0.25,
+                                       p_bf16=True)
+    assert bits_equal(to_np(ml), rml), mismatch_report(to_np(ml), rml)
+    assert bits_equal(to_np(acc), racc), mismatch_report(to_np(acc), racc)
+    rout = oracle.merge_partials(rml, racc, off, round_bf16=True)
+    assert bits_equal(to_np(out), rout), mismatch_report(to_np(out), rout)
+
+
+@pytest.mark.parametrize("dt,h,h_kv,d_h,chunk", BF16_CFGS)
+def test_decode_attention_bf16_within_bound(dt, h, h_kv, d_h, chunk):
+    from oracle.bounds import attn_bound
+    kv_len = np.array(LENS, np.int32)
+    kv = PagedKV(kv_len, h_kv, d_h, 16, seed=100 + d_h, dtype=DT[dt])
+    q = synth.normal((len(kv_len), h, d_h), seed=7).to(DT[dt])
+    scale = scale_for(d_h)
+    _, _, out, _ = _decode(q, kv, kv_len, chunk, scale)
+    ref = oracle.decode_attn(q, kv.k, kv.v, kv.bt, kv_len, h_kv, 16, chunk, scale,
+                             round_bf16=True, p_bf16=True)
+    bound = attn_bound(q, kv.k, kv.v, kv.bt, kv_len, h_kv, 16, chunk, scale, out_bf16=True)
+    err = np.abs(to_np(out) - ref)
+    assert np.all(err <= bound), f"worst {np.max(err / (bound + 1e-30)):.3g}x of the bound"
 
 
 @pytest.mark.parametrize("dt,h,h_kv,d_h,chunk", ATTN_CFGS[:2])
@@ -239,28 +293,33 @@ def test_decode_attention_same_result_on_other_pages():
 # prefill attention
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("dt,h,h_kv,d_h,chunk", ATTN_CFGS[:3])
-def test_prefill_bitwise_and_equal_to_decode(dt, h, h_kv, d_h, chunk):
-    # three requests: prompt chunks at various absolute starts
+def _prefill_case(dt, h, h_kv, d_h, seed, exact=False):
     lens = [37, 300, 5]
     pos0 = [0, 200, 517]
     cap = np.array([p + n for p, n in zip(pos0, lens)], np.int32)
-    kv = PagedKV(cap, h_kv, d_h, 16, seed=400 + d_h, dtype=DT[dt])
     T = sum(lens)
-    q = synth.normal((T, h, d_h), seed=11).to(DT[dt])
+    if exact:
+        q, kv = _exact_case(cap, h, h_kv, d_h, seed=seed)
+        q = torch.cat([q[r:r + 1].expand(n, h, d_h) for r, n in enumerate(lens)]).contiguous()
+    else:
+        kv = PagedKV(cap, h_kv, d_h, 16, seed=seed, dtype=DT[dt])
+        q = synth.normal((T, h, d_h), seed=11).to(DT[dt])
     q_start = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
-    scale = scale_for(d_h)
+    return lens, pos0, kv, q, q_start, T
+
+
+def _gpu_prefill(q, q_start, pos0, kv, chunk, scale, dt):
     k, v, bt = kv.to(dev())
-    out = torch.empty((T, h, d_h), dtype=DT[dt], device=dev())
+    out = torch.empty(q.shape, dtype=DT[dt], device=dev())
     L.bi_prefill_attn(q.to(dev()), torch.from_numpy(q_start).to(dev()),
                       torch.tensor(pos0, dtype=torch.int32, device=dev()), k, v, bt, chunk, scale,
                       out)
-    ref = oracle.prefill_attn(q, q_start, np.array(pos0, np.int32), kv.k, kv.v, kv.bt, h_kv, 16,
-                              chunk, scale, round_bf16=(dt == "bf16"))
-    assert bits_equal(to_np(out), ref), mismatch_report(to_np(out), ref)
-    # each prefill row equals the GPU decode of kv_len = pos + 1
+    return out
+
+
+def _check_equal_to_decode(q, q_start, pos0, lens, kv, chunk, scale, out, dt):
     rows, kvl, btr = [], [], []
-    for r in range(3):
+    for r in range(len(lens)):
         for t in range(q_start[r], q_start[r + 1]):
             rows.append(t)
             kvl.append(pos0[r] + t - q_start[r] + 1)
@@ -269,8 +328,45 @@ def test_prefill_bitwise_and_equal_to_decode(dt, h, h_kv, d_h, chunk):
     sub.k, sub.v, sub.page_size = kv.k, kv.v, 16
     sub.bt = kv.bt[btr].contiguous()
     _, _, dec, _ = _decode(q[rows].contiguous(), sub, np.array(kvl, np.int32), chunk, scale)
-    assert torch.equal(dec.view(torch.int32 if dt == "f32" else torch.int16),
-                       out[rows].view(torch.int32 if dt == "f32" else torch.int16))
+    iv = torch.int32 if dt == "f32" else torch.int16
+    assert torch.equal(dec.view(iv), out[rows].view(iv))
+
+
+@pytest.mark.parametrize("dt,h,h_kv,d_h,chunk", F32_CFGS[:1])
+def test_prefill_bitwise_and_equal_to_decode(dt, h, h_kv, d_h, chunk):
+    # three requests: prompt chunks at various absolute starts
+    lens, pos0, kv, q, q_start, T = _prefill_case(dt, h, h_kv, d_h, seed=400 + d_h)
+    scale = scale_for(d_h)
+    out = _gpu_prefill(q, q_start, pos0, kv, chunk, scale, dt)
+    ref = oracle.prefill_attn(q, q_start, np.array(pos0, np.int32), kv.k, kv.v, kv.bt, h_kv, 16,
+                              chunk, scale, round_bf16=False)
+    assert bits_equal(to_np(out), ref), mismatch_report(to_np(out), ref)
+    # each prefill row equals the GPU decode of kv_len = pos + 1
+    _check_equal_to_decode(q, q_start, pos0, lens, kv, chunk, scale, out, dt)
+
+
+@pytest.mark.parametrize("dt,h,h_kv,d_h,chunk", BF16_CFGS)
+def test_prefill_bf16_equal_to_decode_and_oracle(dt, h, h_kv, d_h, chunk):
+    from oracle.bounds import attn_bound
+    scale = scale_for(d_h)
+    lens, pos0, kv, q, q_start, T = _prefill_case(dt, h, h_kv, d_h, seed=400 + d_h)
+    out = _gpu_prefill(q, q_start, pos0, kv, chunk, scale, dt)
+    _check_equal_to_decode(q, q_start, pos0, lens, kv, chunk, scale, out, dt)
+    ref = oracle.prefill_attn(q, q_start, np.array(pos0, np.int32), kv.k, kv.v, kv.bt, h_kv, 16,
+                              chunk, scale, round_bf16=True, p_bf16=True)
+    rows_bt = np.repeat(np.arange(len(lens)), lens)
+    positions = np.concatenate([np.arange(p, p + n) for p, n in zip(pos0, lens)])
+    bound = attn_bound(q, kv.k, kv.v, kv.bt, None, h_kv, 16, chunk, scale, True,
+                       positions=positions, rows_bt=rows_bt)
+    err = np.abs(to_np(out) - ref)
+    assert np.all(err <= bound), f"worst {np.max(err / (bound + 1e-30)):.3g}x of the bound"
+    # exact inputs: bit for bit the oracle
+    lens, pos0, kv, q, q_start, T = _prefill_case(dt, h, h_kv, d_h, seed=450 + d_h, exact=True)
+    out = _gpu_prefill(q, q_start, pos0, kv, chunk, 0.25, dt)
+    ref = oracle.prefill_attn(q, q_start, np.array(pos0, np.int32), kv.k, kv.v, kv.bt, h_kv, 16,
+                              chunk, 0.25, round_bf16=True, p_bf16=True)
+    assert bits_equal(to_np(out), ref), mismatch_report(to_np(out), ref)
+    _check_equal_to_decode(q, q_start, pos0, lens, kv, chunk, 0.25, out, dt)
 
 
 def test_prefill_invariant_to_chunk_cuts():

@@ -264,6 +264,62 @@ def test_decode_attention_vs_fp64(h, h_kv, d_h, chunk):
     assert np.max(np.abs(out[-1] - ref_drop[-1])) > 3 * tol
 
 
+def _sparse_int_case(kv_len, h, h_kv, d_h, ps, seed, nnz=4):
+    """q with nnz entries of +-1 per head, keys in {-1, 0, 1}: every score is
+    an exact small integer, so with a power-of-two scale the weights are
+    known to fp64."""
+    rng = np.random.default_rng(seed)
+    place = synth.scatter_pages(kv_len, ps, seed=seed + 1)
+    shape = (place.num_pages, h_kv, ps, d_h)
+    kp = rng.integers(-1, 2, size=shape).astype(np.float32)
+    vp = synth.normal(shape, seed=seed + 2).to(torch.bfloat16).float().numpy()
+    q = np.zeros((len(kv_len), h, d_h), np.float32)
+    for r in range(len(kv_len)):
+        for i in range(h):
+            idx = rng.choice(d_h, size=nnz, replace=False)
+            q[r, i, idx] = rng.choice([-1.0, 1.0], size=nnz)
+    return q, kp, vp, place
+
+
+def test_decode_attention_bf16_weights_pin():
+    # p_bf16: the softmax weights are rounded to bf16 before the sums.  With
+    # exact integer scores and a power-of-two scale, P = bf16(exp(s - m_chunk))
+    # is fixed by fp64 (the check below makes sure no weight sits within a few
+    # fp32 ulps of a bf16 rounding boundary, where the oracle's 1-ulp exp
+    # could round the other way), so the merged output is known to within
+    # the fp32 sum and merge error.  Without the rounding it moves far more.
+    h, h_kv, d_h, ps, chunk = 4, 2, 64, 16, 64
+    kv_len = np.array([1, 17, 64, 65, 200, 300], np.int32)
+    q, kp, vp, place = _sparse_int_case(kv_len, h, h_kv, d_h, ps, seed=61)
+    scale = 0.25
+    out = oracle.decode_attn(q, kp, vp, place.block_table, kv_len, h_kv, ps, chunk, scale,
+                             round_bf16=False, p_bf16=True)
+    raw = oracle.decode_attn(q, kp, vp, place.block_table, kv_len, h_kv, ps, chunk, scale,
+                             round_bf16=False, p_bf16=False)
+    worst_gap = 0.0
+    for r, n in enumerate(kv_len):
+        for i in range(h):
+            g = i // (h // h_kv)
+            K = _gather(kp, place.block_table[r], int(n), g, ps)
+            V = _gather(vp, place.block_table[r], int(n), g, ps)
+            s = K @ q[r, i].astype(np.float64) * scale
+            nch = -(-int(n) // chunk)
+            m = np.array([s[c * chunk:(c + 1) * chunk].max() for c in range(nch)])
+            p64 = np.concatenate([np.exp(s[c * chunk:(c + 1) * chunk] - m[c])
+                                  for c in range(nch)])
+            p32 = torch.from_numpy(p64.astype(np.float32))
+            P = p32.to(torch.bfloat16).double().numpy()
+            for k in (-4, 4):  # rounding stable under a few fp32 ulps
+                moved = (p32.view(torch.int32) + k).view(torch.float32)
+                assert np.array_equal(moved.to(torch.bfloat16).double().numpy(), P)
+            w = np.repeat(np.exp(m - m.max()), chunk)[:int(n)]
+            ref = (w * P) @ V / (w * P).sum()
+            tol = 16 * (int(n) + nch + 4) * U * np.abs(V).max()
+            assert np.max(np.abs(out[r, i] - ref)) <= tol
+            worst_gap = max(worst_gap, float(np.max(np.abs(raw[r, i] - ref))))
+    assert worst_gap > 1e-4   # the rounding is really applied
+
+
 def test_decode_single_token_returns_v_exactly():
     kv_len = np.array([1, 1, 1], np.int32)
     q, kp, vp, place = _paged_case(kv_len, 8, 2, 128, 16, seed=7)
@@ -409,3 +465,25 @@ def test_argmax_lowest_index_on_ties():
     idx = oracle.argmax(x)
     assert np.array_equal(idx, np.argmax(x, axis=1))
     assert idx[0] == 5 and idx[1] == 0
+
+
+def test_attention_bound_covers_weight_rounding_and_catches_a_dropped_key():
+    # the bound used for matrix-core attention: two valid evaluations (weights
+    # in fp32 and weights rounded to bf16) stay inside it; dropping a key of a
+    # short request does not
+    from oracle.bounds import attn_bound
+    h, h_kv, d_h, ps, chunk = 4, 2, 64, 16, 64
+    kv_len = np.array([5, 17, 64, 65, 130], np.int32)
+    q, kp, vp, place = _paged_case(kv_len, h, h_kv, d_h, ps, seed=71)
+    scale = float(np.float32(1.0 / math.sqrt(d_h)))
+    a = oracle.decode_attn(q, kp, vp, place.block_table, kv_len, h_kv, ps, chunk, scale, False,
+                           p_bf16=True)
+    b = oracle.decode_attn(q, kp, vp, place.block_table, kv_len, h_kv, ps, chunk, scale, False,
+                           p_bf16=False)
+    bound = attn_bound(q, kp, vp, place.block_table, kv_len, h_kv, ps, chunk, scale, False)
+    assert np.all(np.abs(a - b) <= bound)
+    short = kv_len.copy()
+    short[0] -= 1
+    c = oracle.decode_attn(q, kp, vp, place.block_table, short, h_kv, ps, chunk, scale, False,
+                           p_bf16=True)
+    assert np.any(np.abs(c[0] - a[0]) > bound[0])
