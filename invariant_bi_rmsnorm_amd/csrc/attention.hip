@@ -690,12 +690,13 @@ __device__ __forceinline__ void mfma_zero_v_tail(char* lds, int n, int wave) {
 // P rows of the other j must already hold zeros.  V must be staged (and the
 // tail zeroed) by every wave before the call.  Outputs for this lane's rows
 // and this wave's dim tiles; m = -inf marks a row with no visible key.
-template <int DH, int C, int MT, int RJ = 4>
+template <int DH, int C, int MT, int RJ = 4, class H1 = NoHook>
 __device__ __forceinline__ void mfma_chunk(char* lds, const u32x4_t (&qf)[MT][DH / 32],
                                            const u32x4_t (&kf)[4][DH / 32], int j0,
                                            const int (&lastpos)[MT][4], float scale,
                                            float (&m_out)[MT][4], float (&l_out)[MT][4],
-                                           f32x4_t (&acc)[MT][DH / 16 / (C / 64)]) {
+                                           f32x4_t (&acc)[MT][DH / 16 / (C / 64)],
+                                           const H1& after_qk = H1()) {
   typedef MfmaLds<DH, C, MT> L;
   constexpr int NW = L::NW, KS = DH / 32, DPW = DH / 16 / NW;
   const int lane = threadIdx.x & 63;
@@ -719,6 +720,7 @@ __device__ __forceinline__ void mfma_chunk(char* lds, const u32x4_t (&qf)[MT][DH
         sv[mt][t][j] = (j < RJ && key <= lastpos[mt][j]) ? c[j] * scale : -__builtin_inff();
     }
   }
+  after_qk();  // the K fragments are free
   // ---- row maxima: in lane over the key tiles, over the 16 lanes of the
   // row group, then over the waves
 #pragma unroll
@@ -833,12 +835,17 @@ __global__ __launch_bounds__(C) void k_decode_mfma(
     crow = (long)r * stride + c;
   } else {
     crow = blockIdx.x;
-    int lo = 0, hi = B - 1;  // request owning this chunk row
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (chunk_off[mid] <= (int)crow) lo = mid; else hi = mid - 1;
+    // request owning this chunk row: the number of r >= 1 with chunk_off[r]
+    // <= crow (chunk_off ascends), counted 64 requests per vector load
+    r = 0;
+    for (int b0 = 1; b0 < B; b0 += 64) {
+      const int i = b0 + lane;
+      const bool le = i < B && chunk_off[i] <= (int)crow;
+      const int cnt = __builtin_popcountll(__ballot(le));
+      r += cnt;
+      if (cnt < 64) break;
     }
-    r = lo;
+    r = __builtin_amdgcn_readfirstlane(r);
     j0 = ((int)crow - chunk_off[r]) * C;
     len = kv_len[r];
     n = min(C, len - j0);
