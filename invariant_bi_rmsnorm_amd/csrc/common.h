@@ -190,6 +190,42 @@ __device__ __forceinline__ void lds_read_8_stride1k(u32x4_t (&a)[8], uint32_t ba
       : "memory");
 }
 
+// a[i] = LDS[ba + 2048 i], i = 0..7.
+__device__ __forceinline__ void lds_read_8_stride2k(u32x4_t (&a)[8], uint32_t ba) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:2048\n\t"
+      "ds_read_b128 %2, %8 offset:4096\n\tds_read_b128 %3, %8 offset:6144\n\t"
+      "ds_read_b128 %4, %8 offset:8192\n\tds_read_b128 %5, %8 offset:10240\n\t"
+      "ds_read_b128 %6, %8 offset:12288\n\tds_read_b128 %7, %8 offset:14336\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]),
+        "=&v"(a[6]), "=&v"(a[7])
+      : "v"(ba)
+      : "memory");
+}
+
+// a[i] = LDS[ba + 2048 i], i = 0..3.
+__device__ __forceinline__ void lds_read_4_stride2k(u32x4_t (&a)[4], uint32_t ba) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:2048\n\t"
+      "ds_read_b128 %2, %4 offset:4096\n\tds_read_b128 %3, %4 offset:6144\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+      : "v"(ba)
+      : "memory");
+}
+
+// a[i] = LDS[ba + 1024 i], i = 0..3.
+__device__ __forceinline__ void lds_read_4_stride1k(u32x4_t (&a)[4], uint32_t ba) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
+      "ds_read_b128 %2, %4 offset:2048\n\tds_read_b128 %3, %4 offset:3072\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+      : "v"(ba)
+      : "memory");
+}
+
 // a[i] = LDS[ba + 2048 i], b[i] = LDS[bb + 2048 i], i = 0..3.
 __device__ __forceinline__ void lds_read_4x2_stride2k(u32x4_t (&a)[4], u32x4_t (&b)[4],
                                                       uint32_t ba, uint32_t bb) {

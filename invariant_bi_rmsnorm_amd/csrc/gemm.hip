@@ -464,6 +464,123 @@ static void launch_tiled(const void* A, const void* W, void* C, int M, int N, in
                      (const uint16_t*)A, (const uint16_t*)W, C, M, N, K, tiles_n);
 }
 
+// ---------------------------------------------------------------------------
+// large tiles for large M (chunked prefill): 256 x 256 output tile per
+// workgroup, 8 waves as 2 (M) x 4 (N), each 128 x 64 (8 x 4 MFMA tiles).
+// Two K-tiles per stage, two stages of A and W rows in LDS by direct copies
+// of whole 128-byte lines.  Same MFMA chain per output element as every
+// other path.  Workgroups are mapped so that each XCD (blockIdx % 8) takes a
+// contiguous range of tiles in grouped order (4 row-blocks at a time), so
+// the tiles resident on one XCD share A rows and W columns in its L2.
+// ---------------------------------------------------------------------------
+template <int OUTF32>
+__global__ __launch_bounds__(512) void k_gemm_big(const uint16_t* __restrict__ A,
+                                                  const uint16_t* __restrict__ W, void* C,
+                                                  int M, int N, int K, int tiles_m, int tiles_n) {
+  // Stage = 2 K-tiles (64 columns of K = one 128-byte line per row).  LDS
+  // stage layout is line-major: A rows 0..255 then W rows 0..255, 8 rows
+  // (8 lines) per 1 KiB block; the 16-byte unit u of row r sits at slot
+  // u ^ (r & 7).  Each direct copy moves 8 whole lines (128-byte requests);
+  // a fragment (16 rows x 32 K) is read back with per-lane addresses.
+  constexpr int NS = 2, BLK = 64, PER_WAVE = BLK / 8;  // 1 KiB blocks per stage
+  constexpr int STAGE = BLK * 1024;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int nt = tiles_m * tiles_n, b = blockIdx.x;
+  const int xcd = b % 8, idx = b / 8;
+  const int per = nt / 8, rem = nt % 8;
+  const int t = xcd * per + (xcd < rem ? xcd : rem) + idx;
+  // grouped order inside that range: GM row-blocks at a time, row fastest,
+  // so the XCD's resident workgroups form a GM x (32 / GM) block of tiles
+  // sharing A rows and W columns in its L2
+  constexpr int GM = 4;
+  const int grp = t / (GM * tiles_n), first = grp * GM;
+  const int gm = min(GM, tiles_m - first);
+  const int tm = first + (t % (GM * tiles_n)) % gm, tn = (t % (GM * tiles_n)) / gm;
+  const int m0 = tm * 256, n0 = tn * 256;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int KT = (K + 31) >> 5;
+  const int NST = (KT + 1) >> 1;
+
+  // copy lane: row (lane >> 3) of its block, slot (lane & 7) holds unit
+  // slot ^ (row & 7) of that row's 128-byte span
+  const int crow = lane >> 3, cunit = (lane & 7) ^ crow;
+  auto issue = [&](int st) {
+    char* slot = smem + (st % NS) * STAGE;
+    int kk = st * 64 + cunit * 8;
+    kk = kk < K ? kk : 0;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int blk = wave + 8 * i;  // 0..31 A row blocks, 32..63 W row blocks
+      const uint16_t* src = blk < 32
+          ? A + (long)min(m0 + blk * 8 + crow, M - 1) * K + kk
+          : W + (long)min(n0 + (blk - 32) * 8 + crow, N - 1) * K + kk;
+      dma16(src, slot + blk * 1024);
+    }
+  };
+  // read lane: row (lane & 15) of a 16-row tile, unit 4 kt + (lane >> 4)
+  auto rd_off = [&](int kt) {
+    const int r = lane & 15, u = 4 * kt + (lane >> 4);
+    return (uint32_t)(((r >> 3) & 1) * 1024 + (r & 7) * 128 + 16 * (u ^ (r & 7)));
+  };
+  const uint32_t off0 = rd_off(0), off1 = rd_off(1);
+
+  f32x4_t acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  issue(0);
+  const uint32_t lds0 = lds_addr(smem);
+  for (int st = 0; st < NST; ++st) {
+    BI_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+    if (st + 1 < NST) issue(st + 1);
+    const uint32_t sb = lds0 + (st % NS) * STAGE;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int ktg = 2 * st + kt;
+      if (ktg < KT) {
+        const uint32_t off = kt ? off1 : off0;
+        u32x4_t a[8], bw[4];
+        // A row tiles 8 wm .. 8 wm + 7 (tile t at blocks 2t, 2t + 1: stride
+        // 2 KiB), W column tiles 4 wn .. 4 wn + 3
+        lds_read_8_stride2k(a, sb + (8 * wm) * 2048 + off);
+        lds_read_4_stride2k(bw, sb + 32 * 1024 + (4 * wn) * 2048 + off);
+        if (ktg * 32 + 8 * (lane >> 4) >= K) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) a[i] = u32x4_t{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = mfma(a[i], bw[j], acc[i][j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      store_tile<OUTF32>(C, acc[i][j], m0 + (8 * wm + i) * 16, n0 + (4 * wn + j) * 16, M, N,
+                         lane);
+}
+
+template <int OUTF32>
+static void launch_big(const void* A, const void* W, void* C, int M, int N, int K,
+                       hipStream_t s) {
+  constexpr size_t lds = 2 * 64 * 1024;
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)k_gemm_big<OUTF32>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    attr = true;
+  }
+  const int tiles_m = (M + 255) / 256, tiles_n = (N + 255) / 256;
+  hipLaunchKernelGGL((k_gemm_big<OUTF32>), dim3(tiles_m * tiles_n), dim3(512), lds, s,
+                     (const uint16_t*)A, (const uint16_t*)W, C, M, N, K, tiles_m, tiles_n);
+}
+
 // Split-K over `splits` workgroup slices of kslice (multiple of 32) columns of
 // K, fp32 partial sums added atomically into C32 (which the caller zeroed).
 // Used only by the batch-adaptive twin.
@@ -486,6 +603,9 @@ void gemm_dispatch(const void* A, const void* W, void* C, int M, int N, int K, i
   if (M <= 64) {
     if (out_f32) dispatch_skinny<1>(A, W, C, M, N, K, s);
     else dispatch_skinny<0>(A, W, C, M, N, K, s);
+  } else if (M >= 1024 && N >= 2048) {
+    if (out_f32) launch_big<1>(A, W, C, M, N, K, s);
+    else launch_big<0>(A, W, C, M, N, K, s);
   } else {
     if (out_f32) launch_tiled<1>(A, W, C, M, N, K, s);
     else launch_tiled<0>(A, W, C, M, N, K, s);
@@ -517,16 +637,6 @@ extern "C" bi_status bi_gemm(const void* A, const void* W, void* C, int M, int N
     return launched("bi_gemm");
   }
   BI_REQUIRE(K % 8 == 0, BI_ERR_UNSUPPORTED, "bi_gemm: bf16 needs K %% 8 == 0 (K=%d)", K);
-  if (M <= 64) {
-    if (out_dtype == BI_F32)
-      dispatch_skinny<1>(A, W, C, M, N, K, s);
-    else
-      dispatch_skinny<0>(A, W, C, M, N, K, s);
-  } else {
-    if (out_dtype == BI_F32)
-      launch_tiled<1>(A, W, C, M, N, K, s);
-    else
-      launch_tiled<0>(A, W, C, M, N, K, s);
-  }
+  gemm_dispatch(A, W, C, M, N, K, out_dtype == BI_F32, s);
   return launched("bi_gemm");
 }

@@ -477,3 +477,26 @@ def test_unsupported_configs_fail_closed():
         L.bi_gemm(A, torch.zeros((4, 12), dtype=torch.bfloat16, device=dev()),
                   torch.zeros((2, 4), dtype=torch.bfloat16, device=dev()))
     assert e.value.status == L.BI_ERR_UNSUPPORTED
+
+
+def test_gemm_large_tile_rows_equal_small_M_rows():
+    # chunked-prefill GEMM (M = 2048 + 5 rows, 256 x 256 tiles, ragged in M
+    # and N) against the skinny and 128-tile paths, bit for bit per row; and
+    # the integer-exact case against the oracle
+    K, N = 4096, 2304 + 40
+    M = 2053
+    A = synth.normal((M, K), seed=21).to(torch.bfloat16).to(dev())
+    W = synth.normal((N, K), seed=22, std=0.02).to(torch.bfloat16).to(dev())
+    big = torch.empty((M, N), dtype=torch.float32, device=dev())
+    L.bi_gemm(A, W, big)
+    rng = np.random.default_rng(3)
+    for m in [1, 37, 64, 300]:
+        rows = sorted(rng.choice(M, size=m, replace=False).tolist())
+        c = torch.empty((m, N), dtype=torch.float32, device=dev())
+        L.bi_gemm(A[rows].contiguous(), W, c)
+        assert torch.equal(c.view(torch.int32), big[rows].view(torch.int32)), f"m={m}"
+    Ai = synth.integers((M, 512), -8, 8, seed=23).to(torch.bfloat16)
+    Wi = synth.integers((N, 512), -8, 8, seed=24).to(torch.bfloat16)
+    ci = torch.empty((M, N), dtype=torch.float32, device=dev())
+    L.bi_gemm(Ai.to(dev()), Wi.to(dev()), ci)
+    assert bits_equal(to_np(ci), oracle.gemm(Ai, Wi, round_bf16=False))
