@@ -138,7 +138,7 @@ extern "C" bi_status bi_gemm_free(const void* A, const void* W, void* C, int M, 
   // Workgroups the small-M kernels would launch along N; split K until the
   // device holds a target that grows as the batch shrinks (fewer rows leave
   // each workgroup less work to hide its latency behind).
-  const long tiles = N >= 64 * kCUs ? (N + 63) / 64 : (N + 15) / 16;
+  const long tiles = (N + 15) / 16;
   const long target = (M <= 16 ? 4L : 2L) * kCUs;
   if (tiles >= target || K < 1024)
     return bi_gemm(A, W, C, M, N, K, in_dtype, out_dtype, stream);

@@ -13,9 +13,12 @@
 //
 // Operand "fragments": 64 lanes x 16 bytes; lane l holds 8 consecutive k of
 // row (l % 16) at offset 8 * (l / 16) inside the 32-wide K-tile -- exactly
-// the operand layout of v_mfma_f32_16x16x32_bf16, so a fragment copied to
-// LDS by one direct global->LDS instruction is read back by the same lane
-// with one conflict-free ds_read_b128.
+// the operand layout of v_mfma_f32_16x16x32_bf16.  A 16-byte unit of k that
+// lies past K (K % 32 != 0) enters both operands as zeros in every kernel.
+// The tiled kernel copies fragments to LDS in that layout (one direct
+// global->LDS instruction per fragment, read back by the same lane); the
+// small-M and large-tile kernels copy whole 128-byte row lines and read
+// fragments back through a swizzled line-major layout.
 #include "api.h"
 #include "common.h"
 
@@ -48,236 +51,178 @@ __device__ __forceinline__ void store_tile(void* C, const f32x4_t& acc, int row0
   }
 }
 
-// The small-M kernels split roles across waves.  Copy waves only issue
-// direct global->LDS copies of the operand the whole workgroup shares, into
-// an NS-slot ring; compute waves only issue register loads of their private
-// operand and run the MFMAs.  A wave's memory counter then tracks one kind of
-// operation, so copy waves can keep many stages in flight while compute waves
-// wait exactly for their own loads.  Copy and compute waves run separate
-// loops with the same barrier sequence (one s_barrier per stage): after the
-// barrier of stage st, stage st is in LDS and the slot of stage st-1 is free.
-// With K known at compile time the loops unroll into straight-line code.
-constexpr int kCopyWaves = 4;
+// ---------------------------------------------------------------------------
+// small-M kernel (M <= 64): one workgroup per CT 16-column strips of W and all
+// rows of A.  Per CU the bytes to move are A plus the workgroup's strips of
+// W, so both ride the fastest path into a CU: direct global->LDS copies of
+// whole 128-byte lines (8 rows x 128 bytes per instruction).  One wave
+// sustains only a fraction of a CU's copy rate, so eight copy waves issue the
+// copies; four compute waves read fragments with ds_read_b128 and run the
+// MFMAs.  A stage holds KS K-tiles (LPS = KS / 2 lines of each row, about
+// 24 KiB in all, so one barrier covers enough bytes); its LDS layout
+// is line-major, [line][8-row block][row][16-byte unit], with unit u of row r
+// at slot u ^ (r & 7), so fragment reads are conflict-free.  A is MB 8-row
+// blocks (M <= 8 * MB); a 16-row tile whose second block lies past the copied
+// rows reads other data there, which only reaches output rows >= M (an MFMA
+// output row depends on its own A row alone) and is never stored.
+//
+// All waves pass the same s_barrier once per stage: after the barrier of
+// stage st, stage st is in LDS and the slot of stage st - 1 is free.
+// ---------------------------------------------------------------------------
+constexpr int kSmallCopyWaves = 8, kSmallComputeWaves = 4;
+constexpr int kSmallThreads = (kSmallCopyWaves + kSmallComputeWaves) * 64;
 
-// ---------------------------------------------------------------------------
-// wide kernel (M <= 64, large N): 4 compute waves, each owning one 16-column
-// strip of W (64 columns per workgroup) and all MT row tiles; W streams into
-// a ring of RING stages of registers.  A (shared) goes through the LDS ring.
-// ---------------------------------------------------------------------------
-template <int MT, int OUTF32, int NSTC>
-__global__ __launch_bounds__(512) void k_gemm_wide(const uint16_t* __restrict__ A,
-                                                   const uint16_t* __restrict__ W, void* C,
-                                                   int M, int N, int Ktot, int kslice) {
-  // K slice of this workgroup (one slice covering all of K on the invariant
-  // path; the split-K twin launches several along y).  Rows keep stride Ktot.
+template <int MB, int CT>
+struct SmallCfg {
+  static constexpr int MT = (MB + 1) / 2;                // 16-row tiles
+  static constexpr int BLK = MB + 2 * CT;                // 8-row blocks per line
+  static constexpr int LPS0 = 24 / BLK;                  // lines of each row per stage:
+  static constexpr int LPS = LPS0 < 1 ? 1 : LPS0 > 8 ? 8 : LPS0;   // about 24 KiB a stage
+  static constexpr int KS = 2 * LPS;                     // K-tiles per stage
+  static constexpr int ITEMS = BLK * LPS;                // copies per stage
+  static constexpr int STAGE = ITEMS * 1024;             // bytes per stage
+  static constexpr int QB = ITEMS / kSmallCopyWaves;     // copies per copy wave,
+  static constexpr int XR = ITEMS % kSmallCopyWaves;     // plus one for the first XR
+  static constexpr int QMAX = QB + (XR > 0);
+  static constexpr int D_LDS = (160 * 1024) / STAGE;
+  static constexpr int D_CNT = 1 + 63 / QMAX;            // vmcnt holds at most 63
+  static constexpr int D0 = D_LDS < D_CNT ? D_LDS : D_CNT;
+  static constexpr int D = D0 < 16 ? D0 : 16;            // ring slots
+  static constexpr int LDS = D * STAGE;
+  static constexpr int WN = CT >= 4 ? 4 : CT;            // compute waves along N
+  static constexpr int WM = 4 / WN;                      // ... and along M
+  static constexpr int IM = (MT + WM - 1) / WM;          // row tiles per wave
+  static constexpr int JN = CT / WN;                     // column tiles per wave
+  static_assert(D >= 3, "ring too shallow");
+  static_assert(CT % WN == 0, "tiling");
+};
+
+template <int MB, int CT, int OUTF32>
+__global__ __launch_bounds__(kSmallThreads) void k_gemm_small(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, void* C, int M, int N,
+    int Ktot, int kslice) {
+  using G = SmallCfg<MB, CT>;
+  constexpr int BLK = G::BLK, KS = G::KS, STAGE = G::STAGE, D = G::D, MT = G::MT;
+  // K slice of this workgroup (all of K on the invariant path; the split-K
+  // twin launches several along y).  Rows keep stride Ktot.
   const int kbeg = blockIdx.y * kslice;
   const int K = min(kslice, Ktot - kbeg);
   const long ld = Ktot;
-  A += kbeg;
-  W += kbeg;
-  constexpr int KTS = 4, NS = 4, RING = 4;
-  constexpr int SLOT = 16 * kFrag;           // room for MT * KTS <= 16 fragments
-  constexpr int QA = MT * KTS / kCopyWaves;  // copies per copy wave per stage
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int lrow = lane & 15, lk = (lane >> 4) * 8;
+  const int n0 = blockIdx.x * (16 * CT);
   const int KT = (K + 31) >> 5;
-  const int NST = NSTC > 0 ? NSTC : (KT + KTS - 1) / KTS;
+  const int NST = (KT + KS - 1) / KS;
 
-  if (wave >= 4) {
-    // ---- copy waves: A stages into the ring
-    const int cw = wave - 4;
-    auto issue_a = [&](int st) {
-      char* slot = smem + (st % NS) * SLOT;
+  if (wave >= kSmallComputeWaves) {
+    // ---- copy waves.  Item j = line * BLK + block of a stage goes to LDS
+    // offset j KiB; copy wave cw takes items cw, cw + 8, ...  Lane: row
+    // (lane >> 3) of the block, slot (lane & 7) <- unit (lane & 7) ^ row.
+    const int cw = wave - kSmallComputeWaves;
+    const bool extra = cw < G::XR;
+    const int crow = lane >> 3, koff = ((lane & 7) ^ crow) * 8;
+    const uint16_t* src[G::QMAX];
 #pragma unroll
-      for (int i = 0; i < QA; ++i) {
-        const int f = cw + kCopyWaves * i;  // fragment (mt, kt) = divmod(f, KTS)
-        int kk = (st * KTS + f % KTS) * 32 + lk;
-        if (NSTC == 0) kk = kk < K ? kk : 0;
-        dma16(A + (long)min((f / KTS) * 16 + lrow, M - 1) * ld + kk, slot + f * kFrag);
+    for (int i = 0; i < G::QMAX; ++i) {
+      const int j = min(cw + kSmallCopyWaves * i, G::ITEMS - 1), b = j % BLK, line = j / BLK;
+      const uint16_t* row = b < MB
+          ? A + (long)min(b * 8 + crow, M - 1) * ld
+          : W + (long)min(n0 + (b - MB) * 8 + crow, N - 1) * ld;
+      src[i] = row + kbeg + line * 64 + koff;
+    }
+    auto issue = [&](int st) {
+      char* slot = smem + (st % D) * STAGE;
+#pragma unroll
+      for (int i = 0; i < G::QMAX; ++i) {
+        if (i < G::QB || extra) {
+          const int j = cw + kSmallCopyWaves * i, line = j / BLK;
+          const int k = st * (32 * KS) + line * 64 + koff;   // this lane's first k
+          dma16(k < K ? src[i] + st * (32 * KS) : src[i] - line * 64 - koff, slot + j * 1024);
+        }
       }
     };
 #pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-      if (s < NST) issue_a(s);
-    auto step = [&](int st, bool steady) {
-      if (steady) BI_WAIT_VMCNT((NS - 2) * QA); else BI_WAIT_VMCNT(0);
+    for (int s = 0; s < D - 1; ++s)
+      if (s < NST) issue(s);
+    for (int st = 0; st < NST; ++st) {
+      if (st + D - 1 > NST) BI_WAIT_VMCNT(0);
+      else if (extra) BI_WAIT_VMCNT((D - 2) * G::QMAX);
+      else BI_WAIT_VMCNT((D - 2) * G::QB);
       __builtin_amdgcn_s_barrier();
-      if (st + NS - 1 < NST) issue_a(st + NS - 1);
-    };
-    if constexpr (NSTC > 0) {
-#pragma unroll
-      for (int st = 0; st < NSTC; ++st) step(st, st + NS - 1 <= NSTC);
-    } else {
-      for (int st = 0; st < NST; ++st) step(st, st + NS - 1 <= NST);
+      if (st + D - 1 < NST) issue(st + D - 1);
     }
     return;
   }
 
-  // ---- compute waves
-  const int ntile = blockIdx.x * 4 + wave;
-  const uint16_t* wrow = W + (long)min(ntile * 16 + lrow, N - 1) * ld;
-  auto load_w = [&](int st, u32x4_t (&dst)[KTS]) {
-    const int stc = st < NST ? st : NST - 1;
+  // ---- compute waves: wave (wm, wn) owns row tiles wm + WM i (< MT) and
+  // column tiles wn + WN j.  A wave whose first row tile lies past MT idles.
+  const int wn = wave % G::WN, wm = wave / G::WN;
+  const bool active = wm < MT;
+  const int r = lane & 15, g = lane >> 4;
+  // fragment offset of row r, K-tile parity h inside a 16-row tile
+  const uint32_t off0 = ((r >> 3) << 10) + ((r & 7) << 7) + ((g ^ (r & 7)) << 4);
+  const uint32_t off1 = ((r >> 3) << 10) + ((r & 7) << 7) + (((4 + g) ^ (r & 7)) << 4);
+  uint32_t aoff[G::IM], boff[G::JN];
 #pragma unroll
-    for (int kt = 0; kt < KTS; ++kt) {
-      int kk = (stc * KTS + kt) * 32 + lk;
-      if (NSTC == 0) kk = kk < K ? kk : 0;
-      dst[kt] = *reinterpret_cast<const u32x4_t*>(wrow + kk);
+  for (int i = 0; i < G::IM; ++i) aoff[i] = min(wm + G::WM * i, MT - 1) * 2048;
+#pragma unroll
+  for (int j = 0; j < G::JN; ++j) boff[j] = (MB + 2 * (wn + G::WN * j)) * 1024;
+  f32x4_t acc[G::IM][G::JN];
+#pragma unroll
+  for (int i = 0; i < G::IM; ++i)
+#pragma unroll
+    for (int j = 0; j < G::JN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // one stage: read every fragment of its (up to) KS K-tiles, then the MFMAs
+  // in ascending K-tile order.  A unit past K enters both operands as zeros.
+  auto stage = [&](const char* slot, int st, int nkt) {
+    u32x4_t a[KS][G::IM], b[KS][G::JN];
+#pragma unroll
+    for (int kt = 0; kt < KS; ++kt) {
+      if (kt < nkt) {
+        const char* base = slot + (kt >> 1) * (BLK * 1024) + ((kt & 1) ? off1 : off0);
+#pragma unroll
+        for (int i = 0; i < G::IM; ++i) a[kt][i] = *reinterpret_cast<const u32x4_t*>(base + aoff[i]);
+#pragma unroll
+        for (int j = 0; j < G::JN; ++j) b[kt][j] = *reinterpret_cast<const u32x4_t*>(base + boff[j]);
+      }
     }
-  };
-  u32x4_t wreg[RING][KTS];
-  f32x4_t acc[MT];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int kt = 0; kt < KS; ++kt) {
+      if (kt < nkt) {
+        const bool tail = (st * KS + kt) * 32 + 8 * g >= K;
 #pragma unroll
-  for (int r = 0; r < RING; ++r) load_w(r, wreg[r]);
-  const uint32_t lds0 = lds_addr(smem) + lane * 16;
-  auto step = [&](int st, int j, bool guarded, bool refill) {
-    __builtin_amdgcn_s_barrier();
-    const uint32_t slot = lds0 + (st % NS) * SLOT;
-    u32x4_t a0[8], a1[8];
-    lds_read_8x2_stride1k(a0, a1, slot, slot + 8 * kFrag);
+        for (int i = 0; i < G::IM; ++i) {
+          const u32x4_t av = tail ? u32x4_t{0, 0, 0, 0} : a[kt][i];
 #pragma unroll
-    for (int kt = 0; kt < KTS; ++kt) {
-      const int ktg = st * KTS + kt;
-      if (!guarded || ktg < KT) {
-        const bool tail = guarded && ktg * 32 + lk >= K;
-        const u32x4_t z = u32x4_t{0, 0, 0, 0};
-        const u32x4_t b = tail ? z : wreg[j][kt];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          const int f = m * KTS + kt;
-          const u32x4_t a = tail ? z : (f < 8 ? a0[f & 7] : a1[f & 7]);
-          acc[m] = mfma(a, b, acc[m]);
+          for (int j = 0; j < G::JN; ++j)
+            acc[i][j] = mfma(av, tail ? u32x4_t{0, 0, 0, 0} : b[kt][j], acc[i][j]);
         }
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    if (refill) load_w(st + RING, wreg[j]);
-    __builtin_amdgcn_sched_barrier(0);
   };
-  if constexpr (NSTC > 0) {
-#pragma unroll
-    for (int st = 0; st < NSTC; ++st) step(st, st % RING, false, st + RING < NSTC);
-  } else {
-    const int NMAIN = ((KT / KTS) / RING) * RING;  // full stages, whole ring turns
-    for (int st0 = 0; st0 < NMAIN; st0 += RING) {
-#pragma unroll
-      for (int j = 0; j < RING; ++j) step(st0 + j, j, false, true);
-    }
-#pragma unroll
-    for (int j = 0; j < RING; ++j)
-      if (NMAIN + j < NST) step(NMAIN + j, j, true, false);
-  }
-#pragma unroll
-  for (int m = 0; m < MT; ++m) store_tile<OUTF32>(C, acc[m], m * 16, ntile * 16, M, N, lane);
-}
-
-// ---------------------------------------------------------------------------
-// narrow kernel (M <= 64, N up to a few thousand): one 16-column strip of W
-// per workgroup, shared through a deep LDS ring filled by the copy waves;
-// compute wave w owns row tile w and streams its A fragments into registers.
-// ---------------------------------------------------------------------------
-template <int MT, int OUTF32, int NSTC>
-__global__ __launch_bounds__((MT + kCopyWaves) * 64) void k_gemm_narrow(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, void* C, int M, int N,
-    int Ktot, int kslice) {
-  const int kbeg = blockIdx.y * kslice;
-  const int K = min(kslice, Ktot - kbeg);
-  const long ld = Ktot;
-  A += kbeg;
-  W += kbeg;
-  constexpr int KTS = 8, NS = 16, RING = 4;
-  constexpr int SLOT = KTS * kFrag;
-  constexpr int QW = KTS / kCopyWaves;  // copies per copy wave per stage
-  extern __shared__ __attribute__((aligned(1024))) char smem[];
-
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int n0 = blockIdx.x * 16;
-  const int lrow = lane & 15, lk = (lane >> 4) * 8;
-  const int KT = (K + 31) >> 5;
-  const int NST = NSTC > 0 ? NSTC : (KT + KTS - 1) / KTS;
-
-  if (wave >= MT) {
-    // ---- copy waves: W stages into the ring
-    const int cw = wave - MT;
-    const uint16_t* wrow = W + (long)min(n0 + lrow, N - 1) * ld;
-    auto issue_w = [&](int st) {
-      char* slot = smem + (st % NS) * SLOT;
-#pragma unroll
-      for (int i = 0; i < QW; ++i) {
-        const int kt = cw + kCopyWaves * i;
-        int kk = (st * KTS + kt) * 32 + lk;
-        if (NSTC == 0) kk = kk < K ? kk : 0;
-        dma16(wrow + kk, slot + kt * kFrag);
-      }
-    };
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-      if (s < NST) issue_w(s);
-    auto step = [&](int st, bool steady) {
-      if (steady) BI_WAIT_VMCNT((NS - 2) * QW); else BI_WAIT_VMCNT(0);
-      __builtin_amdgcn_s_barrier();
-      if (st + NS - 1 < NST) issue_w(st + NS - 1);
-    };
-    if constexpr (NSTC > 0) {
-#pragma unroll
-      for (int st = 0; st < NSTC; ++st) step(st, st + NS - 1 <= NSTC);
-    } else {
-      for (int st = 0; st < NST; ++st) step(st, st + NS - 1 <= NST);
-    }
-    return;
-  }
-
-  // ---- compute waves
-  const uint16_t* arow = A + (long)min(wave * 16 + lrow, M - 1) * ld;
-  auto load_a = [&](int st, u32x4_t (&dst)[KTS]) {
-    const int stc = st < NST ? st : NST - 1;
-#pragma unroll
-    for (int kt = 0; kt < KTS; ++kt) {
-      int kk = (stc * KTS + kt) * 32 + lk;
-      if (NSTC == 0) kk = kk < K ? kk : 0;
-      dst[kt] = *reinterpret_cast<const u32x4_t*>(arow + kk);
-    }
-  };
-  u32x4_t areg[RING][KTS];
-  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int r = 0; r < RING; ++r) load_a(r, areg[r]);
-  const uint32_t lds0 = lds_addr(smem) + lane * 16;
-  auto step = [&](int st, int j, bool guarded, bool refill) {
+  for (int st = 0; st < NST; ++st) {
     __builtin_amdgcn_s_barrier();
-    u32x4_t b[8];
-    lds_read_8_stride1k(b, lds0 + (st % NS) * SLOT);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    const char* slot = smem + (st % D) * STAGE;
+    const int nkt = KT - st * KS;
+    if (active) {
+      if (nkt >= KS) {
+        stage(slot, st, KS);
+      } else {
 #pragma unroll
-    for (int kt = 0; kt < KTS; ++kt) {
-      const int ktg = st * KTS + kt;
-      if (!guarded || ktg < KT) {
-        const bool tail = guarded && ktg * 32 + lk >= K;
-        const u32x4_t z = u32x4_t{0, 0, 0, 0};
-        acc = mfma(tail ? z : areg[j][kt], tail ? z : b[kt], acc);
+        for (int n = 1; n < KS; ++n)
+          if (nkt == n) stage(slot, st, n);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    if (refill) load_a(st + RING, areg[j]);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  if constexpr (NSTC > 0) {
-#pragma unroll
-    for (int st = 0; st < NSTC; ++st) step(st, st % RING, false, st + RING < NSTC);
-  } else {
-    const int NMAIN = ((KT / KTS) / RING) * RING;
-    for (int st0 = 0; st0 < NMAIN; st0 += RING) {
-#pragma unroll
-      for (int j = 0; j < RING; ++j) step(st0 + j, j, false, true);
-    }
-#pragma unroll
-    for (int j = 0; j < RING; ++j)
-      if (NMAIN + j < NST) step(NMAIN + j, j, true, false);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   }
-  store_tile<OUTF32>(C, acc, wave * 16, n0, M, N, lane);
+#pragma unroll
+  for (int i = 0; i < G::IM; ++i)
+#pragma unroll
+    for (int j = 0; j < G::JN; ++j) {
+      const int m = wm + G::WM * i, c = wn + G::WN * j;
+      if (m < MT) store_tile<OUTF32>(C, acc[i][j], m * 16, n0 + c * 16, M, N, lane);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -384,69 +329,52 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A,
 // ---------------------------------------------------------------------------
 // launch plumbing
 // ---------------------------------------------------------------------------
-template <int MT, int OUTF32, int NSTC>
-static void launch_wide_k(const void* A, const void* W, void* C, int M, int N, int K,
-                          hipStream_t s, int splits = 1, int kslice = 0) {
-  if (splits == 1) kslice = K;
-  constexpr int lds = 4 * 16 * kFrag;
+template <int MB, int CT, int OUTF32>
+static void launch_small_k(const void* A, const void* W, void* C, int M, int N, int K,
+                           hipStream_t s, int splits, int kslice) {
+  constexpr int lds = SmallCfg<MB, CT>::LDS;
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute((const void*)k_gemm_wide<MT, OUTF32, NSTC>,
+    (void)hipFuncSetAttribute((const void*)k_gemm_small<MB, CT, OUTF32>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     attr = true;
   }
-  hipLaunchKernelGGL((k_gemm_wide<MT, OUTF32, NSTC>), dim3((N + 63) / 64, splits), dim3(512),
-                     lds, s, (const uint16_t*)A, (const uint16_t*)W, C, M, N, K, kslice);
-}
-
-// K = 4096 runs a fully unrolled pipeline (4 K-tiles per stage)
-template <int MT, int OUTF32>
-static void launch_wide(const void* A, const void* W, void* C, int M, int N, int K,
-                        hipStream_t s) {
-  if (K == 4096) launch_wide_k<MT, OUTF32, 32>(A, W, C, M, N, K, s);
-  else launch_wide_k<MT, OUTF32, 0>(A, W, C, M, N, K, s);
-}
-
-template <int MT, int OUTF32, int NSTC>
-static void launch_narrow_k(const void* A, const void* W, void* C, int M, int N, int K,
-                            hipStream_t s, int splits = 1, int kslice = 0) {
-  if (splits == 1) kslice = K;
-  constexpr int lds = 16 * 8 * kFrag;
-  static bool attr = false;
-  if (!attr) {
-    (void)hipFuncSetAttribute((const void*)k_gemm_narrow<MT, OUTF32, NSTC>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    attr = true;
-  }
-  hipLaunchKernelGGL((k_gemm_narrow<MT, OUTF32, NSTC>), dim3((N + 15) / 16, splits),
-                     dim3((MT + kCopyWaves) * 64), lds, s,
+  hipLaunchKernelGGL((k_gemm_small<MB, CT, OUTF32>),
+                     dim3((N + 16 * CT - 1) / (16 * CT), splits),
+                     dim3(kSmallThreads), lds, s,
                      (const uint16_t*)A, (const uint16_t*)W, C, M, N, K, kslice);
 }
 
-// K = 4096 and K = 14336 run fully unrolled pipelines (8 K-tiles per stage)
-template <int MT, int OUTF32>
-static void launch_narrow(const void* A, const void* W, void* C, int M, int N, int K,
-                          hipStream_t s) {
-  if (K == 4096) launch_narrow_k<MT, OUTF32, 16>(A, W, C, M, N, K, s);
-  else if (K == 14336) launch_narrow_k<MT, OUTF32, 56>(A, W, C, M, N, K, s);
-  else launch_narrow_k<MT, OUTF32, 0>(A, W, C, M, N, K, s);
+// Column tiles per workgroup, chosen from N (and the rows copied): every
+// workgroup moves A plus its strips of W, one workgroup per CU at a time, so
+// the time goes with rounds * (A blocks + W blocks).
+static int small_ct(int MB, int N) {
+  const int tiles = (N + 15) / 16;
+  int best = 1;
+  long best_cost = -1;
+  for (int ct : {1, 2, 4, 8}) {
+    const long wgs = (tiles + ct - 1) / ct;
+    const long cost = ((wgs + 255) / 256) * (MB + 2 * ct);
+    if (best_cost < 0 || cost < best_cost) best = ct, best_cost = cost;
+  }
+  return best;
 }
 
-// Small M: wide strips (A shared through LDS) when N offers >= 256
-// workgroups of 64 columns, else one strip of 16 columns per workgroup.
 template <int OUTF32>
-static void dispatch_skinny(const void* A, const void* W, void* C, int M, int N, int K,
-                            hipStream_t s) {
-  const int MT = (M + 15) / 16;
-  const bool wide = N >= 64 * 256;
-#define BI_SKINNY(mt)                                                   \
-  if (MT == mt) {                                                       \
-    if (wide) launch_wide<mt, OUTF32>(A, W, C, M, N, K, s);             \
-    else launch_narrow<mt, OUTF32>(A, W, C, M, N, K, s);                \
-    return;                                                             \
+static void dispatch_small(const void* A, const void* W, void* C, int M, int N, int K,
+                           hipStream_t s, int splits = 1, int kslice = 0) {
+  if (splits == 1) kslice = K;
+  const int MB = M <= 8 ? 1 : M <= 16 ? 2 : M <= 32 ? 4 : M <= 48 ? 6 : 8;
+  const int CT = small_ct(MB, N);
+#define BI_SMALL(mb, ct)                                                        \
+  if (MB == mb && CT == ct) {                                                   \
+    launch_small_k<mb, ct, OUTF32>(A, W, C, M, N, K, s, splits, kslice);        \
+    return;                                                                     \
   }
-  BI_SKINNY(1) BI_SKINNY(2) BI_SKINNY(3) BI_SKINNY(4)
-#undef BI_SKINNY
+#define BI_SMALL_M(mb) BI_SMALL(mb, 1) BI_SMALL(mb, 2) BI_SMALL(mb, 4) BI_SMALL(mb, 8)
+  BI_SMALL_M(1) BI_SMALL_M(2) BI_SMALL_M(4) BI_SMALL_M(6) BI_SMALL_M(8)
+#undef BI_SMALL_M
+#undef BI_SMALL
 }
 
 template <int OUTF32>
@@ -550,6 +478,8 @@ __global__ __launch_bounds__(512) void k_gemm_big(const uint16_t* __restrict__ A
         if (ktg * 32 + 8 * (lane >> 4) >= K) {
 #pragma unroll
           for (int i = 0; i < 8; ++i) a[i] = u32x4_t{0, 0, 0, 0};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) bw[j] = u32x4_t{0, 0, 0, 0};
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -586,23 +516,14 @@ static void launch_big(const void* A, const void* W, void* C, int M, int N, int 
 // Used only by the batch-adaptive twin.
 void gemm_splitk_atomic(const void* A, const void* W, float* C32, int M, int N, int K,
                         int splits, int kslice, hipStream_t s) {
-  const int MT = (M + 15) / 16;
-  const bool wide = N >= 64 * 256;
-#define BI_SPLIT(mt)                                                                   \
-  if (MT == mt) {                                                                      \
-    if (wide) launch_wide_k<mt, 2, 0>(A, W, C32, M, N, K, s, splits, kslice);          \
-    else launch_narrow_k<mt, 2, 0>(A, W, C32, M, N, K, s, splits, kslice);             \
-    return;                                                                            \
-  }
-  BI_SPLIT(1) BI_SPLIT(2) BI_SPLIT(3) BI_SPLIT(4)
-#undef BI_SPLIT
+  dispatch_small<2>(A, W, C32, M, N, K, s, splits, kslice);
 }
 
 void gemm_dispatch(const void* A, const void* W, void* C, int M, int N, int K, int out_f32,
                    hipStream_t s) {
   if (M <= 64) {
-    if (out_f32) dispatch_skinny<1>(A, W, C, M, N, K, s);
-    else dispatch_skinny<0>(A, W, C, M, N, K, s);
+    if (out_f32) dispatch_small<1>(A, W, C, M, N, K, s);
+    else dispatch_small<0>(A, W, C, M, N, K, s);
   } else if (M >= 1024 && N >= 2048) {
     if (out_f32) launch_big<1>(A, W, C, M, N, K, s);
     else launch_big<0>(A, W, C, M, N, K, s);

@@ -78,8 +78,10 @@ def test_rmsnorm_rows_invariant_and_inplace():
 GEMM_SHAPES = [(1, 16, 32), (1, 17, 40), (5, 100, 264), (16, 64, 512), (17, 48, 96),
                (33, 130, 1024), (64, 64, 256), (64, 257, 4104), (65, 128, 256),
                (100, 300, 520), (257, 200, 1000),
-               # compile-time-K pipelines (K = 4096, 14336) and the wide path (N >= 16384)
+               # long K (4096, 14336) and every small-M strip width: 1, 2, 4 and 8
+               # column tiles per workgroup (chosen from N), with ragged K tails
                (1, 64, 4096), (16, 130, 4096), (64, 48, 14336), (33, 100, 14336),
+               (48, 6144, 264), (7, 9000, 1000), (64, 14336, 512),
                (3, 16400, 4096), (64, 16448, 4096), (20, 16384, 264)]
 
 
@@ -130,8 +132,9 @@ def test_gemm_rows_invariant_across_M_and_position():
         assert torch.equal(got.view(torch.int32), full[rows].view(torch.int32)), f"M={M}"
 
 
-def test_gemm_wide_rows_invariant_across_M():
-    K, N = 4096, 16448
+@pytest.mark.parametrize("N", [16448, 14336])
+def test_gemm_wide_rows_invariant_across_M(N):
+    K = 4096
     A = synth.normal((96, K), seed=3).to(torch.bfloat16).to(dev())
     W = synth.normal((N, K), seed=4, std=0.02).to(torch.bfloat16).to(dev())
 
