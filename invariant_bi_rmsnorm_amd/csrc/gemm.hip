@@ -59,50 +59,98 @@ __device__ __forceinline__ void store_tile(void* C, const f32x4_t& acc, int row0
 // sustains only a fraction of a CU's copy rate, so eight copy waves issue the
 // copies; four compute waves read fragments with ds_read_b128 and run the
 // MFMAs.  A stage holds KS K-tiles (LPS = KS / 2 lines of each row, about
-// 24 KiB in all, so one barrier covers enough bytes); its LDS layout
-// is line-major, [line][8-row block][row][16-byte unit], with unit u of row r
-// at slot u ^ (r & 7), so fragment reads are conflict-free.  A is MB 8-row
-// blocks (M <= 8 * MB); a 16-row tile whose second block lies past the copied
-// rows reads other data there, which only reaches output rows >= M (an MFMA
-// output row depends on its own A row alone) and is never stored.
+// 24 KiB in all, so one barrier covers enough bytes).  A and W have rings of
+// their own, each fed by four copy waves: A (re-read by every workgroup)
+// stays in L2 and needs only a few stages in flight, while W comes from HBM
+// and its ring runs as many stages ahead as LDS allows.  Ring layout per
+// stage is line-major, [line][8-row block][row][16-byte unit], with unit u of
+// row r at slot u ^ (r & 7), so fragment reads are conflict-free.  A is MB
+// 8-row blocks (M <= 8 * MB); a 16-row tile whose second block lies past the
+// copied rows reads other data there, which only reaches output rows >= M
+// (an MFMA output row depends on its own A row alone) and is never stored.
 //
 // All waves pass the same s_barrier once per stage: after the barrier of
-// stage st, stage st is in LDS and the slot of stage st - 1 is free.
+// stage st, stage st of both rings is in LDS and the slots of stage st - 1
+// are free.
 // ---------------------------------------------------------------------------
-constexpr int kSmallCopyWaves = 8, kSmallComputeWaves = 4;
+constexpr int kSmallCopyWaves = 8, kSmallComputeWaves = 4, kSmallGroupWaves = 4;
 constexpr int kSmallThreads = (kSmallCopyWaves + kSmallComputeWaves) * 64;
 
 template <int MB, int CT>
 struct SmallCfg {
   static constexpr int MT = (MB + 1) / 2;                // 16-row tiles
   static constexpr int BLK = MB + 2 * CT;                // 8-row blocks per line
-  static constexpr int LPS0 = 24 / BLK;                  // lines of each row per stage:
-  static constexpr int LPS = LPS0 < 1 ? 1 : LPS0 > 8 ? 8 : LPS0;   // about 24 KiB a stage
+  static constexpr int LPS0 = 24 / BLK;                  // lines of each row per stage
+  static constexpr int LPS = LPS0 < 1 ? 1 : LPS0 > 8 ? 8 : LPS0;
   static constexpr int KS = 2 * LPS;                     // K-tiles per stage
-  static constexpr int ITEMS = BLK * LPS;                // copies per stage
-  static constexpr int STAGE = ITEMS * 1024;             // bytes per stage
-  static constexpr int QB = ITEMS / kSmallCopyWaves;     // copies per copy wave,
-  static constexpr int XR = ITEMS % kSmallCopyWaves;     // plus one for the first XR
-  static constexpr int QMAX = QB + (XR > 0);
-  static constexpr int D_LDS = (160 * 1024) / STAGE;
-  static constexpr int D_CNT = 1 + 63 / QMAX;            // vmcnt holds at most 63
-  static constexpr int D0 = D_LDS < D_CNT ? D_LDS : D_CNT;
-  static constexpr int D = D0 < 16 ? D0 : 16;            // ring slots
-  static constexpr int LDS = D * STAGE;
+  static constexpr int A_ITEMS = MB * LPS, W_ITEMS = 2 * CT * LPS;   // KiB per stage
+  static constexpr int QA = (A_ITEMS + kSmallGroupWaves - 1) / kSmallGroupWaves;
+  static constexpr int QW = (W_ITEMS + kSmallGroupWaves - 1) / kSmallGroupWaves;
+  static constexpr int AD0 = 96 / A_ITEMS;
+  static constexpr int AD1 = AD0 < 3 ? 3 : AD0 > 6 ? 6 : AD0;
+  static constexpr int AD = AD1 < 1 + 63 / QA ? AD1 : 1 + 63 / QA;   // A ring slots
+  static constexpr int A_RING = AD * A_ITEMS * 1024;
+  static constexpr int WD0 = (160 * 1024 - A_RING) / (W_ITEMS * 1024);
+  static constexpr int WD1 = WD0 < 16 ? WD0 : 16;
+  static constexpr int WD = WD1 < 1 + 63 / QW ? WD1 : 1 + 63 / QW;   // W ring slots
+  static constexpr int LDS = A_RING + WD * W_ITEMS * 1024;
   static constexpr int WN = CT >= 4 ? 4 : CT;            // compute waves along N
   static constexpr int WM = 4 / WN;                      // ... and along M
   static constexpr int IM = (MT + WM - 1) / WM;          // row tiles per wave
   static constexpr int JN = CT / WN;                     // column tiles per wave
-  static_assert(D >= 3, "ring too shallow");
+  static_assert(AD >= 3 && WD >= 3 && LDS <= 160 * 1024, "rings");
   static_assert(CT % WN == 0, "tiling");
 };
+
+// One group of four copy waves feeding one ring of RD slots: NB 8-row blocks
+// (rows row0 + 8 b + 0..7, clamped to rmax) times LPS lines per stage; item
+// j = line * NB + b of a stage goes to slot offset j KiB and group wave gw
+// takes items gw, gw + 4, ...  Lane: row (lane >> 3) of the block, LDS slot
+// (lane & 7) <- 16-byte unit (lane & 7) ^ row.  Before the barrier of stage
+// st, the wave waits for its own copies of stage st.
+template <int NB, int LPS, int RD>
+__device__ __forceinline__ void small_copy_ring(const uint16_t* __restrict__ base, long ld,
+                                                int row0, int rmax, int kbeg, int K, int NST,
+                                                char* ring, int gw, int lane) {
+  constexpr int NIT = NB * LPS, QB = NIT / kSmallGroupWaves, XR = NIT % kSmallGroupWaves;
+  constexpr int QMAX = QB + (XR > 0), KS = 2 * LPS;
+  const bool extra = gw < XR;
+  const int crow = lane >> 3, koff = ((lane & 7) ^ crow) * 8;
+  const uint16_t* src[QMAX];
+#pragma unroll
+  for (int i = 0; i < QMAX; ++i) {
+    const int j = min(gw + kSmallGroupWaves * i, NIT - 1), b = j % NB, line = j / NB;
+    src[i] = base + (long)min(row0 + b * 8 + crow, rmax) * ld + kbeg + line * 64 + koff;
+  }
+  auto issue = [&](int st) {
+    char* slot = ring + (st % RD) * (NIT * 1024);
+#pragma unroll
+    for (int i = 0; i < QMAX; ++i) {
+      if (i < QB || extra) {
+        const int j = gw + kSmallGroupWaves * i, line = j / NB;
+        const int k = st * (32 * KS) + line * 64 + koff;   // this lane's first k
+        dma16(k < K ? src[i] + st * (32 * KS) : src[i] - line * 64 - koff, slot + j * 1024);
+      }
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < RD - 1; ++s)
+    if (s < NST) issue(s);
+  for (int st = 0; st < NST; ++st) {
+    if (st + RD - 1 > NST) BI_WAIT_VMCNT(0);
+    else if (extra) BI_WAIT_VMCNT((RD - 2) * QMAX);
+    else BI_WAIT_VMCNT((RD - 2) * QB);
+    __builtin_amdgcn_s_barrier();
+    if (st + RD - 1 < NST) issue(st + RD - 1);
+  }
+}
 
 template <int MB, int CT, int OUTF32>
 __global__ __launch_bounds__(kSmallThreads) void k_gemm_small(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, void* C, int M, int N,
     int Ktot, int kslice) {
   using G = SmallCfg<MB, CT>;
-  constexpr int BLK = G::BLK, KS = G::KS, STAGE = G::STAGE, D = G::D, MT = G::MT;
+  constexpr int KS = G::KS, LPS = G::LPS, MT = G::MT;
   // K slice of this workgroup (all of K on the invariant path; the split-K
   // twin launches several along y).  Rows keep stride Ktot.
   const int kbeg = blockIdx.y * kslice;
@@ -115,42 +163,12 @@ __global__ __launch_bounds__(kSmallThreads) void k_gemm_small(
   const int NST = (KT + KS - 1) / KS;
 
   if (wave >= kSmallComputeWaves) {
-    // ---- copy waves.  Item j = line * BLK + block of a stage goes to LDS
-    // offset j KiB; copy wave cw takes items cw, cw + 8, ...  Lane: row
-    // (lane >> 3) of the block, slot (lane & 7) <- unit (lane & 7) ^ row.
     const int cw = wave - kSmallComputeWaves;
-    const bool extra = cw < G::XR;
-    const int crow = lane >> 3, koff = ((lane & 7) ^ crow) * 8;
-    const uint16_t* src[G::QMAX];
-#pragma unroll
-    for (int i = 0; i < G::QMAX; ++i) {
-      const int j = min(cw + kSmallCopyWaves * i, G::ITEMS - 1), b = j % BLK, line = j / BLK;
-      const uint16_t* row = b < MB
-          ? A + (long)min(b * 8 + crow, M - 1) * ld
-          : W + (long)min(n0 + (b - MB) * 8 + crow, N - 1) * ld;
-      src[i] = row + kbeg + line * 64 + koff;
-    }
-    auto issue = [&](int st) {
-      char* slot = smem + (st % D) * STAGE;
-#pragma unroll
-      for (int i = 0; i < G::QMAX; ++i) {
-        if (i < G::QB || extra) {
-          const int j = cw + kSmallCopyWaves * i, line = j / BLK;
-          const int k = st * (32 * KS) + line * 64 + koff;   // this lane's first k
-          dma16(k < K ? src[i] + st * (32 * KS) : src[i] - line * 64 - koff, slot + j * 1024);
-        }
-      }
-    };
-#pragma unroll
-    for (int s = 0; s < D - 1; ++s)
-      if (s < NST) issue(s);
-    for (int st = 0; st < NST; ++st) {
-      if (st + D - 1 > NST) BI_WAIT_VMCNT(0);
-      else if (extra) BI_WAIT_VMCNT((D - 2) * G::QMAX);
-      else BI_WAIT_VMCNT((D - 2) * G::QB);
-      __builtin_amdgcn_s_barrier();
-      if (st + D - 1 < NST) issue(st + D - 1);
-    }
+    if (cw < kSmallGroupWaves)
+      small_copy_ring<MB, LPS, G::AD>(A, ld, 0, M - 1, kbeg, K, NST, smem, cw, lane);
+    else
+      small_copy_ring<2 * CT, LPS, G::WD>(W, ld, n0, N - 1, kbeg, K, NST, smem + G::A_RING,
+                                          cw - kSmallGroupWaves, lane);
     return;
   }
 
@@ -166,7 +184,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_gemm_small(
 #pragma unroll
   for (int i = 0; i < G::IM; ++i) aoff[i] = min(wm + G::WM * i, MT - 1) * 2048;
 #pragma unroll
-  for (int j = 0; j < G::JN; ++j) boff[j] = (MB + 2 * (wn + G::WN * j)) * 1024;
+  for (int j = 0; j < G::JN; ++j) boff[j] = (wn + G::WN * j) * 2048;
   f32x4_t acc[G::IM][G::JN];
 #pragma unroll
   for (int i = 0; i < G::IM; ++i)
@@ -174,16 +192,18 @@ __global__ __launch_bounds__(kSmallThreads) void k_gemm_small(
     for (int j = 0; j < G::JN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // one stage: read every fragment of its (up to) KS K-tiles, then the MFMAs
   // in ascending K-tile order.  A unit past K enters both operands as zeros.
-  auto stage = [&](const char* slot, int st, int nkt) {
+  auto stage = [&](const char* aslot, const char* wslot, int st, int nkt) {
     u32x4_t a[KS][G::IM], b[KS][G::JN];
 #pragma unroll
     for (int kt = 0; kt < KS; ++kt) {
       if (kt < nkt) {
-        const char* base = slot + (kt >> 1) * (BLK * 1024) + ((kt & 1) ? off1 : off0);
+        const uint32_t off = (kt & 1) ? off1 : off0;
+        const char* abase = aslot + (kt >> 1) * (MB * 1024) + off;
+        const char* wbase = wslot + (kt >> 1) * (2 * CT * 1024) + off;
 #pragma unroll
-        for (int i = 0; i < G::IM; ++i) a[kt][i] = *reinterpret_cast<const u32x4_t*>(base + aoff[i]);
+        for (int i = 0; i < G::IM; ++i) a[kt][i] = *reinterpret_cast<const u32x4_t*>(abase + aoff[i]);
 #pragma unroll
-        for (int j = 0; j < G::JN; ++j) b[kt][j] = *reinterpret_cast<const u32x4_t*>(base + boff[j]);
+        for (int j = 0; j < G::JN; ++j) b[kt][j] = *reinterpret_cast<const u32x4_t*>(wbase + boff[j]);
       }
     }
 #pragma unroll
@@ -203,15 +223,16 @@ __global__ __launch_bounds__(kSmallThreads) void k_gemm_small(
   for (int st = 0; st < NST; ++st) {
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    const char* slot = smem + (st % D) * STAGE;
+    const char* aslot = smem + (st % G::AD) * (G::A_ITEMS * 1024);
+    const char* wslot = smem + G::A_RING + (st % G::WD) * (G::W_ITEMS * 1024);
     const int nkt = KT - st * KS;
     if (active) {
       if (nkt >= KS) {
-        stage(slot, st, KS);
+        stage(aslot, wslot, st, KS);
       } else {
 #pragma unroll
         for (int n = 1; n < KS; ++n)
-          if (nkt == n) stage(slot, st, n);
+          if (nkt == n) stage(aslot, wslot, st, n);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
