@@ -58,6 +58,9 @@ def parse():
                          "'copy' for a plain 1 GiB device copy), e.g. under rocprofv3 --pmc")
     ap.add_argument("--twin", action="store_true", help="with --only: the twin's kernel")
     ap.add_argument("--launches", type=int, default=50)
+    ap.add_argument("--traffic-summary", default="",
+                    help="summarise rocprofv3 --pmc runs (FETCH_SIZE / WRITE_SIZE of --only "
+                         "decode_attn and of --only copy) found under this directory")
     return ap.parse_args()
 
 
@@ -174,7 +177,7 @@ def per_kernel_times(eng, meta, steps, torch):
 
     def timer(name, fn):
         if spin is not None:
-            spin(20000)
+            spin(200000)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
@@ -305,6 +308,85 @@ def prefill_gemm(torch, dev, M=8192, N=14336, K=4096, launches=20):
             "TFLOPs": round(tf, 1), "peak": BF16_PEAK / 1e12, "frac": round(tf * 1e12 / BF16_PEAK, 4)}
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_attn_traffic_llama3_8b_b64.md")
+TRAFFIC_SOURCES = ("invariant_bi_rmsnorm_amd/csrc/attention.hip",
+                   "invariant_bi_rmsnorm_amd/csrc/common.h")
+
+
+def kernel_source_hash():
+    """sha256 over the sources the decode-attention kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _counter_rows(d, counter, match):
+    """Per-dispatch values of `counter` for kernels whose name contains
+    `match`, from a rocprofv3 --output-format csv run under directory d."""
+    import csv
+    import glob
+    vals = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter and match in r["Kernel_Name"]:
+                    vals.append(float(r["Counter_Value"]))
+    return vals
+
+
+def traffic_summary(d):
+    """HBM bytes per decode-attention launch from four rocprofv3 --pmc runs
+    (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, for `--only decode_attn`
+    and for `--only copy`).  Each counter is scaled by bytes / counter of the
+    1 GiB copy (it reads 1 GiB and writes 1 GiB).  Prints a markdown summary
+    whose `traffic-record:` line bench.py reads back."""
+    import statistics
+    gib = float(1 << 30)
+    cf = _counter_rows(os.path.join(d, "copy_fetch"), "FETCH_SIZE", "copy")
+    cw = _counter_rows(os.path.join(d, "copy_write"), "WRITE_SIZE", "copy")
+    af = _counter_rows(os.path.join(d, "attn_fetch"), "FETCH_SIZE", "k_decode")
+    aw = _counter_rows(os.path.join(d, "attn_write"), "WRITE_SIZE", "k_decode")
+    if not (cf and cw and af and aw):
+        raise SystemExit(f"missing counter rows under {d}: {len(cf)} {len(cw)} {len(af)} {len(aw)}")
+    f_scale = gib / (max(cf) * 1024.0)      # the largest copy dispatch is the 1 GiB one
+    w_scale = gib / (max(cw) * 1024.0)
+    fetch = statistics.median(af) * 1024.0 * f_scale
+    write = statistics.median(aw) * 1024.0 * w_scale
+    rec = {"kernel": "decode_attn", "hbm_bytes_per_launch": round(fetch + write),
+           "fetch_bytes": round(fetch), "write_bytes": round(write),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "dispatches": [len(af), len(aw)], "source_sha256": kernel_source_hash()}
+    print("| quantity | value |\n|---|---|")
+    print(f"| FETCH_SIZE, decode attention (KiB/dispatch, median of {len(af)}) | {statistics.median(af):.0f} |")
+    print(f"| WRITE_SIZE, decode attention (KiB/dispatch, median of {len(aw)}) | {statistics.median(aw):.0f} |")
+    print(f"| FETCH_SIZE, 1 GiB copy (KiB) | {max(cf):.0f} |")
+    print(f"| WRITE_SIZE, 1 GiB copy (KiB) | {max(cw):.0f} |")
+    print(f"| fetch scale (bytes per counted byte) | {f_scale:.4f} |")
+    print(f"| write scale | {w_scale:.4f} |")
+    print(f"| HBM bytes per decode-attention launch | {fetch + write:.4g} |")
+    print()
+    print("traffic-record: " + json.dumps(rec))
+
+
+def measured_traffic():
+    """HBM bytes per decode-attention launch from the committed counter
+    summary, or None when the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            lines = [ln for ln in f if ln.startswith("traffic-record: ")]
+    except OSError:
+        return None
+    if not lines:
+        return None
+    rec = json.loads(lines[-1][len("traffic-record: "):])
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec
+
+
 def only_kernel(args, torch, dev):
     """Launch one kernel of the step (the last layer's instance) --launches
     times back to back and report its average duration from HIP events on
@@ -361,6 +443,9 @@ def _rounded(d):
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        traffic_summary(args.traffic_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path is "
               "data-parallel across GPUs and nothing here uses a second device", file=sys.stderr)
@@ -396,6 +481,10 @@ def main():
     rl = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK / 1e9,
           "unit": "GB/s", "frac": round(achieved * 1e9 / HBM_PEAK, 4), "traffic": None,
           "avg_launch_us": round(per[dom]["avg_us"], 2), "alg_bytes_per_launch": b}
+    rec = measured_traffic() if dom == "decode_attn" else None
+    if rec is not None:
+        rl["traffic"] = rec["hbm_bytes_per_launch"]
+        rl["traffic_frac_of_alg"] = round(rec["hbm_bytes_per_launch"] / b, 4)
     out = {
         "metric": METRIC, "value": round(res["inv"]["tokens_per_s"], 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
