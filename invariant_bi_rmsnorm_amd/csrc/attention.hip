@@ -804,9 +804,11 @@ __device__ __forceinline__ void mfma_chunk(char* lds, const u32x4_t (&qf)[MT][DH
     for (int j = RJ; j < 4; ++j) m_out[mt][j] = -__builtin_inff();
 }
 
-// Decode partials on matrix cores, C / 64 waves.  FREE = false: grid (chunk
-// rows, h_kv), chunks of C keys at absolute multiples of C.  FREE = true (the
-// twin): grid (B * stride, h_kv), request r's split c of the length the
+// Decode partials on matrix cores, C / 64 waves.  One workgroup per (row,
+// kv head), kv head fastest: blockIdx.x = row * h_kv + g, so the h_kv
+// workgroups that read the same pages run side by side.  FREE = false: rows
+// are chunk rows, chunks of C keys at absolute multiples of C.  FREE = true
+// (the twin): B * stride rows, request r's split c of the length the
 // occupancy policy gives it (free_splits), partial row r * stride + c.
 template <int DH, int R, int C, bool FREE = false>
 __global__ __launch_bounds__(C) void k_decode_mfma(
@@ -820,12 +822,12 @@ __global__ __launch_bounds__(C) void k_decode_mfma(
   extern __shared__ __attribute__((aligned(1024))) char lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = blockIdx.y;
+  const int g = blockIdx.x % h_kv, row = blockIdx.x / h_kv;
   int r, j0, n, len;
   long crow;
   if (FREE) {
-    r = blockIdx.x / stride;
-    const int c = blockIdx.x % stride;
+    r = row / stride;
+    const int c = row % stride;
     len = kv_len[r];
     int slen;
     const int nr = free_splits(len, chunk2, &slen);
@@ -834,7 +836,7 @@ __global__ __launch_bounds__(C) void k_decode_mfma(
     n = min(slen, len - j0);
     crow = (long)r * stride + c;
   } else {
-    crow = blockIdx.x;
+    crow = row;
     // request owning this chunk row: the number of r >= 1 with chunk_off[r]
     // <= crow (chunk_off ascends), counted 64 requests per vector load
     r = 0;
@@ -1109,7 +1111,7 @@ static void decode_nw(int nw, const void* q, const void* kp, const void* vp, con
                       const int32_t* kvl, const int32_t* off, int B, int tot, int h, int h_kv,
                       int ps, int mp, float scale, float* ml, float* acc, hipStream_t s) {
   if constexpr (DT == 1) {
-    const dim3 grid(tot, h_kv);
+    const dim3 grid((unsigned)tot * h_kv);
     if (nw == 1) launch_decode_mfma<DH, R, 64>(grid, q, kp, vp, bt, kvl, off, B, h, h_kv, mp, scale, ml, acc, s);
     else launch_decode_mfma<DH, R, 256>(grid, q, kp, vp, bt, kvl, off, B, h, h_kv, mp, scale, ml, acc, s);
   } else {
@@ -1199,7 +1201,7 @@ static void launch_decode_free(const void* q, const void* kp, const void* vp, co
                                const int32_t* kvl, int B, int h, int h_kv, int mp, float scale,
                                FreePolicy pol, float* ml, float* acc, hipStream_t s) {
   if constexpr (DT == 1) {
-    launch_decode_mfma<DH, R, 256, true>(dim3(B * pol.stride, h_kv), q, kp, vp, bt, kvl, nullptr,
+    launch_decode_mfma<DH, R, 256, true>(dim3((unsigned)B * pol.stride * h_kv), q, kp, vp, bt, kvl, nullptr,
                                          B, h, h_kv, mp, scale, ml, acc, s, pol.chunk2,
                                          pol.stride);
   } else {
