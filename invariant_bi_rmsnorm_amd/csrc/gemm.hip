@@ -52,9 +52,11 @@ __device__ __forceinline__ void store_tile(void* C, const f32x4_t& acc, int row0
 }
 
 // ---------------------------------------------------------------------------
-// small-M kernel (M <= 64): one workgroup per CT 16-column strips of W and all
-// rows of A.  Per CU the bytes to move are A plus the workgroup's strips of
-// W, so both ride the fastest path into a CU: direct global->LDS copies of
+// small-M kernel (M <= 64): one workgroup per CT 16-column strips of W and one
+// group of 8 MB rows of A (blockIdx.z; MB and CT are chosen from M and N so
+// that rows x columns per workgroup balance).  Per CU the bytes to move are
+// its rows of A plus its strips of W, so both ride the fastest path into a
+// CU: direct global->LDS copies of
 // whole 128-byte lines (8 rows x 128 bytes per instruction).  One wave
 // sustains only a fraction of a CU's copy rate, so eight copy waves issue the
 // copies; four compute waves read fragments with ds_read_b128 and run the
@@ -158,14 +160,15 @@ __global__ __launch_bounds__(kSmallThreads) void k_gemm_small(
   const long ld = Ktot;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int n0 = blockIdx.x * (16 * CT);
+  const int n0 = blockIdx.x * (16 * CT), m0 = blockIdx.z * (8 * MB);
+  const int mend = min(M, m0 + 8 * MB);  // rows of this workgroup: m0 .. mend - 1
   const int KT = (K + 31) >> 5;
   const int NST = (KT + KS - 1) / KS;
 
   if (wave >= kSmallComputeWaves) {
     const int cw = wave - kSmallComputeWaves;
     if (cw < kSmallGroupWaves)
-      small_copy_ring<MB, LPS, G::AD>(A, ld, 0, M - 1, kbeg, K, NST, smem, cw, lane);
+      small_copy_ring<MB, LPS, G::AD>(A, ld, m0, mend - 1, kbeg, K, NST, smem, cw, lane);
     else
       small_copy_ring<2 * CT, LPS, G::WD>(W, ld, n0, N - 1, kbeg, K, NST, smem + G::A_RING,
                                           cw - kSmallGroupWaves, lane);
@@ -242,7 +245,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_gemm_small(
 #pragma unroll
     for (int j = 0; j < G::JN; ++j) {
       const int m = wm + G::WM * i, c = wn + G::WN * j;
-      if (m < MT) store_tile<OUTF32>(C, acc[i][j], m * 16, n0 + c * 16, M, N, lane);
+      if (m < MT) store_tile<OUTF32>(C, acc[i][j], m0 + m * 16, n0 + c * 16, mend, N, lane);
     }
 }
 
@@ -361,22 +364,29 @@ static void launch_small_k(const void* A, const void* W, void* C, int M, int N, 
     attr = true;
   }
   hipLaunchKernelGGL((k_gemm_small<MB, CT, OUTF32>),
-                     dim3((N + 16 * CT - 1) / (16 * CT), splits),
+                     dim3((N + 16 * CT - 1) / (16 * CT), splits, (M + 8 * MB - 1) / (8 * MB)),
                      dim3(kSmallThreads), lds, s,
                      (const uint16_t*)A, (const uint16_t*)W, C, M, N, K, kslice);
 }
 
-// Column tiles per workgroup, chosen from N (and the rows copied): every
-// workgroup moves A plus its strips of W, one workgroup per CU at a time, so
-// the time goes with rounds * (A blocks + W blocks).
-static int small_ct(int MB, int N) {
-  const int tiles = (N + 15) / 16;
-  int best = 1;
-  long best_cost = -1;
-  for (int ct : {1, 2, 4, 8}) {
-    const long wgs = (tiles + ct - 1) / ct;
-    const long cost = ((wgs + 255) / 256) * (MB + 2 * ct);
-    if (best_cost < 0 || cost < best_cost) best = ct, best_cost = cost;
+// Rows (8 MB) and 16-column strips (CT) per workgroup, chosen from M and N:
+// a workgroup moves its rows of A plus its strips of W, one workgroup per CU
+// at a time, so the time goes with rounds * (MB + 2 CT) (KiB per 32 k).
+struct SmallShape {
+  int mb, ct;
+};
+static SmallShape small_shape(int M, int N) {
+  const long tiles = (N + 15) / 16;
+  SmallShape best{8, 1};
+  long best_cost = -1, best_wgs = 0;
+  for (int mb : {1, 2, 4, 6, 8}) {
+    const long rg = (M + 8 * mb - 1) / (8 * mb);
+    for (int ct : {1, 2, 3, 4, 8}) {
+      const long wgs = rg * ((tiles + ct - 1) / ct);
+      const long cost = ((wgs + 255) / 256) * (mb + 2 * ct);
+      if (best_cost < 0 || cost < best_cost || (cost == best_cost && wgs < best_wgs))
+        best = SmallShape{mb, ct}, best_cost = cost, best_wgs = wgs;
+    }
   }
   return best;
 }
@@ -385,14 +395,14 @@ template <int OUTF32>
 static void dispatch_small(const void* A, const void* W, void* C, int M, int N, int K,
                            hipStream_t s, int splits = 1, int kslice = 0) {
   if (splits == 1) kslice = K;
-  const int MB = M <= 8 ? 1 : M <= 16 ? 2 : M <= 32 ? 4 : M <= 48 ? 6 : 8;
-  const int CT = small_ct(MB, N);
-#define BI_SMALL(mb, ct)                                                        \
-  if (MB == mb && CT == ct) {                                                   \
-    launch_small_k<mb, ct, OUTF32>(A, W, C, M, N, K, s, splits, kslice);        \
+  const SmallShape sh = small_shape(M, N);
+#define BI_SMALL(MB_, CT_)                                                      \
+  if (sh.mb == MB_ && sh.ct == CT_) {                                           \
+    launch_small_k<MB_, CT_, OUTF32>(A, W, C, M, N, K, s, splits, kslice);      \
     return;                                                                     \
   }
-#define BI_SMALL_M(mb) BI_SMALL(mb, 1) BI_SMALL(mb, 2) BI_SMALL(mb, 4) BI_SMALL(mb, 8)
+#define BI_SMALL_M(MB_) \
+  BI_SMALL(MB_, 1) BI_SMALL(MB_, 2) BI_SMALL(MB_, 3) BI_SMALL(MB_, 4) BI_SMALL(MB_, 8)
   BI_SMALL_M(1) BI_SMALL_M(2) BI_SMALL_M(4) BI_SMALL_M(6) BI_SMALL_M(8)
 #undef BI_SMALL_M
 #undef BI_SMALL
