@@ -87,6 +87,17 @@ const char *bi_last_error(void);
 bi_status bi_rmsnorm(const void *x, const void *gamma, void *y, int M, int d, float eps,
                      int dtype, bi_stream stream);
 
+/* Residual add fused with the RMSNorm that follows it (the transformer's
+ * "h = h + sublayer(x); x = norm(h)"): h[i][j] = round(h[i][j] + o[i][j]) is
+ * written back to h, then y = bi_rmsnorm(h) with the same tree.  The result
+ * equals bi_add followed by bi_rmsnorm bit for bit; one launch instead of
+ * two, one pass over h.
+ *   h : device [M][d] of `dtype`, read and written;  o : device [M][d];
+ *   gamma : device [d];  y : device [M][d], must not alias h or o.
+ *   Same shapes, dtypes and errors as bi_rmsnorm. */
+bi_status bi_add_rmsnorm(void *h, const void *o, const void *gamma, void *y, int M, int d,
+                         float eps, int dtype, bi_stream stream);
+
 /* Twin: when M is too small to fill the device, each row is split over
  * several workgroups whose partial sums meet through fp32 atomics (order
  * set by scheduling); otherwise one workgroup per row with a different

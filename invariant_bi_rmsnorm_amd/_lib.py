@@ -31,6 +31,7 @@ SIGNATURES = {
     "bi_chunk_offsets": (_c_int, [_i32p, _c_int, _c_int, _i32p]),
     "bi_attn_partials_bytes": (_c_size, [_c_int, _c_int, _c_int]),
     "bi_rmsnorm": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_float, _c_int, _vp]),
+    "bi_add_rmsnorm": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_float, _c_int, _vp]),
     "bi_gemm": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
     "bi_decode_attn": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp] + [_c_int] * 8
                        + [_c_float, _c_int, _vp, _vp, _vp]),
@@ -145,6 +146,16 @@ def bi_rmsnorm(x, gamma, y, eps: float, stream=None):
     M, d = (x.shape[0], x.shape[-1]) if x.dim() == 2 else (x.numel() // x.shape[-1], x.shape[-1])
     _check("bi_rmsnorm", load().bi_rmsnorm(_ptr(x), _ptr(gamma), _ptr(y), M, d, eps, _dt(x),
                                            _stream(stream)))
+    return y
+
+
+def bi_add_rmsnorm(h, o, gamma, y, eps: float, stream=None):
+    """h += o (rounded to h's dtype), then y = RMSNorm(h) * gamma."""
+    M, d = (h.shape[0], h.shape[-1]) if h.dim() == 2 else (h.numel() // h.shape[-1], h.shape[-1])
+    if tuple(o.shape) != tuple(h.shape) or tuple(y.shape) != tuple(h.shape):
+        raise ValueError(f"shape mismatch h{tuple(h.shape)} o{tuple(o.shape)} y{tuple(y.shape)}")
+    _check("bi_add_rmsnorm", load().bi_add_rmsnorm(_ptr(h), _ptr(o), _ptr(gamma), _ptr(y), M, d,
+                                                   eps, _dt(h), _stream(stream)))
     return y
 
 

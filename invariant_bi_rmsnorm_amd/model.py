@@ -262,9 +262,17 @@ class Engine:
         rms = L.bi_rmsnorm_free if fr else L.bi_rmsnorm
         gemm = L.bi_gemm_free if fr else L.bi_gemm
         L.bi_embed(w.embed, m["tokens"], h)
-        for li, lw in enumerate(w.layers[:layers] if layers else w.layers):
+        lws = w.layers[:layers] if layers else w.layers
+        # invariant path: each residual add runs fused with the RMSNorm after
+        # it (the next sublayer's, or the final norm); the twins keep them apart
+        fuse = not fr
+        if fuse:
+            run("rmsnorm", lambda: rms(h, lws[0].attn_norm, x, c.eps))
+        for li, lw in enumerate(lws):
             kp, vp = self.pool.k[li], self.pool.v[li]
-            run("rmsnorm", lambda: rms(h, lw.attn_norm, x, c.eps))
+            nxt = lws[li + 1].attn_norm if li + 1 < len(lws) else w.final_norm
+            if not fuse:
+                run("rmsnorm", lambda: rms(h, lw.attn_norm, x, c.eps))
             run("gemm_qkv", lambda: gemm(x, lw.wqkv, qkv))
             run("rope_kv_append", lambda: L.bi_rope_kv_append(
                 qkv, c.h, c.h_kv, c.d_h, m["pos"] if c.rope else None, self.cos, self.sin,
@@ -287,13 +295,20 @@ class Engine:
                     q[nd:], m["q_start"], m["pos0"], kp, vp, m["bt_pre"], c.kv_chunk, c.scale,
                     att[nd:]))
             run("gemm_o", lambda: gemm(att.view(T, c.h * c.d_h), lw.wo, o))
-            run("add", lambda: L.bi_add(h, o, h))
-            run("rmsnorm", lambda: rms(h, lw.ffn_norm, x, c.eps))
+            if fuse:
+                run("add_rmsnorm", lambda: L.bi_add_rmsnorm(h, o, lw.ffn_norm, x, c.eps))
+            else:
+                run("add", lambda: L.bi_add(h, o, h))
+                run("rmsnorm", lambda: rms(h, lw.ffn_norm, x, c.eps))
             run("gemm_gate_up", lambda: gemm(x, lw.wgu, gu))
             run("silu_mul", lambda: L.bi_silu_mul(gu, act))
             run("gemm_down", lambda: gemm(act, lw.wdown, o))
-            run("add", lambda: L.bi_add(h, o, h))
-        rms(h, w.final_norm, x, c.eps)
+            if fuse:
+                run("add_rmsnorm", lambda: L.bi_add_rmsnorm(h, o, nxt, x, c.eps))
+            else:
+                run("add", lambda: L.bi_add(h, o, h))
+        if not fuse:
+            rms(h, w.final_norm, x, c.eps)
         nw = len(m["want"])
         if nw == 0:
             return StepOutput(torch.empty((0, c.vocab), device=self.dev),

@@ -71,6 +71,27 @@ def test_rmsnorm_rows_invariant_and_inplace():
     assert torch.equal(xi.view(torch.int16), full.view(torch.int16))
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("M,d", [(1, 4096), (7, 4096), (64, 4096), (3, 1000), (5, 13)])
+def test_add_rmsnorm_equals_add_then_rmsnorm_and_oracle(dt, M, d):
+    h0 = synth.normal((M, d), seed=M * 17 + d).to(DT[dt])
+    o = synth.normal((M, d), seed=M * 19 + d, std=0.5).to(DT[dt])
+    g = synth.normal((d,), seed=d + 11).to(DT[dt])
+    h, og, gg = h0.to(dev()), o.to(dev()), g.to(dev())
+    y = torch.empty_like(h)
+    L.bi_add_rmsnorm(h, og, gg, y, 1e-5)
+    h2 = h0.to(dev())
+    y2 = torch.empty_like(h2)
+    L.bi_add(h2, og, h2)
+    L.bi_rmsnorm(h2, gg, y2, 1e-5)
+    assert bits_equal(to_np(h), to_np(h2)) and bits_equal(to_np(y), to_np(y2))
+    rb = dt == "bf16"
+    rh = oracle.add(h0, o, round_bf16=rb)
+    ry = oracle.rmsnorm(rh, g, 1e-5, round_bf16=rb)
+    assert bits_equal(to_np(h), rh), mismatch_report(to_np(h), rh)
+    assert bits_equal(to_np(y), ry), mismatch_report(to_np(y), ry)
+
+
 # ---------------------------------------------------------------------------
 # GEMM
 # ---------------------------------------------------------------------------
