@@ -653,7 +653,7 @@ __device__ __forceinline__ void mfma_stage_v(char* lds, const char* vbase, long 
     const int key = 64 * wave + k;                 // key within the chunk
     const int page = pg[k / kPage];
     const char* src = vbase + page * pstride + (k % kPage) * RB + 16 * (slot ^ (key & 7));
-    dma16(src, lds + (64 * wave + inst * KPI) * RB);
+    dma16_nt(src, lds + (64 * wave + inst * KPI) * RB);
   }
 }
 
@@ -667,7 +667,8 @@ __device__ __forceinline__ void mfma_load_k(u32x4_t (&kf)[4][DH / 32], const cha
   for (int t = 0; t < 4; ++t) {
     const char* row = kbase + pg[t] * pstride + (lane & 15) * RB + 16 * (lane >> 4);
 #pragma unroll
-    for (int s = 0; s < DH / 32; ++s) kf[t][s] = *reinterpret_cast<const u32x4_t*>(row + 64 * s);
+    for (int s = 0; s < DH / 32; ++s)   // read once: non-temporal
+      kf[t][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + 64 * s));
   }
 }
 

@@ -140,6 +140,13 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
   __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_base, 16, 0, 0);
 }
 
+// The same copy marked non-temporal (cache policy NT), for data that is read
+// once (the weights of a skinny GEMM, KV pages): the L2 then keeps its room for
+// the operands that other workgroups re-read.
+__device__ __forceinline__ void dma16_nt(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds_base, 16, 0, 2);
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // ---- explicit LDS reads --------------------------------------------------

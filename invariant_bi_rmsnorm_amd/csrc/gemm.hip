@@ -83,24 +83,26 @@ struct SmallCfg {
   static constexpr int MT = (MB + 1) / 2;                // 16-row tiles
   static constexpr int BLK = MB + 2 * CT;                // 8-row blocks per line
   static constexpr int LPS0 = 24 / BLK;                  // lines of each row per stage
-  static constexpr int LPS = LPS0 < 1 ? 1 : LPS0 > 8 ? 8 : LPS0;
+  static constexpr int LPS_MAX = MB == 1 ? 4 : 8;         // MB = 1: registers for two per CU
+  static constexpr int LPS = LPS0 < 1 ? 1 : LPS0 > LPS_MAX ? LPS_MAX : LPS0;
   static constexpr int KS = 2 * LPS;                     // K-tiles per stage
   static constexpr int A_ITEMS = MB * LPS, W_ITEMS = 2 * CT * LPS;   // KiB per stage
   static constexpr int QA = (A_ITEMS + kSmallGroupWaves - 1) / kSmallGroupWaves;
   static constexpr int QW = (W_ITEMS + kSmallGroupWaves - 1) / kSmallGroupWaves;
-  static constexpr int AD0 = 96 / A_ITEMS;
+  static constexpr int AD0 = (MB == 1 ? 24 : 96) / A_ITEMS;
   static constexpr int AD1 = AD0 < 3 ? 3 : AD0 > 6 ? 6 : AD0;
   static constexpr int AD = AD1 < 1 + 63 / QA ? AD1 : 1 + 63 / QA;   // A ring slots
   static constexpr int A_RING = AD * A_ITEMS * 1024;
-  static constexpr int WD0 = (160 * 1024 - A_RING) / (W_ITEMS * 1024);
+  static constexpr int BUDGET = (MB == 1 ? 80 : 160) * 1024;   // MB = 1: two per CU
+  static constexpr int WD0 = (BUDGET - A_RING) / (W_ITEMS * 1024);
   static constexpr int WD1 = WD0 < 16 ? WD0 : 16;
   static constexpr int WD = WD1 < 1 + 63 / QW ? WD1 : 1 + 63 / QW;   // W ring slots
   static constexpr int LDS = A_RING + WD * W_ITEMS * 1024;
-  static constexpr int WN = CT >= 4 ? 4 : CT;            // compute waves along N
+  static constexpr int WN = CT % 4 == 0 ? 4 : CT % 3 == 0 ? 3 : CT % 2 == 0 ? 2 : 1;  // along N
   static constexpr int WM = 4 / WN;                      // ... and along M
   static constexpr int IM = (MT + WM - 1) / WM;          // row tiles per wave
   static constexpr int JN = CT / WN;                     // column tiles per wave
-  static_assert(AD >= 3 && WD >= 3 && LDS <= 160 * 1024, "rings");
+  static_assert(AD >= 3 && WD >= 3 && LDS <= BUDGET, "rings");
   static_assert(CT % WN == 0, "tiling");
 };
 
@@ -110,7 +112,7 @@ struct SmallCfg {
 // takes items gw, gw + 4, ...  Lane: row (lane >> 3) of the block, LDS slot
 // (lane & 7) <- 16-byte unit (lane & 7) ^ row.  Before the barrier of stage
 // st, the wave waits for its own copies of stage st.
-template <int NB, int LPS, int RD>
+template <int NB, int LPS, int RD, bool NT>
 __device__ __forceinline__ void small_copy_ring(const uint16_t* __restrict__ base, long ld,
                                                 int row0, int rmax, int kbeg, int K, int NST,
                                                 char* ring, int gw, int lane) {
@@ -131,7 +133,9 @@ __device__ __forceinline__ void small_copy_ring(const uint16_t* __restrict__ bas
       if (i < QB || extra) {
         const int j = gw + kSmallGroupWaves * i, line = j / NB;
         const int k = st * (32 * KS) + line * 64 + koff;   // this lane's first k
-        dma16(k < K ? src[i] + st * (32 * KS) : src[i] - line * 64 - koff, slot + j * 1024);
+        const uint16_t* p = k < K ? src[i] + st * (32 * KS) : src[i] - line * 64 - koff;
+        if (NT) dma16_nt(p, slot + j * 1024);
+        else dma16(p, slot + j * 1024);
       }
     }
   };
@@ -168,10 +172,10 @@ __global__ __launch_bounds__(kSmallThreads) void k_gemm_small(
   if (wave >= kSmallComputeWaves) {
     const int cw = wave - kSmallComputeWaves;
     if (cw < kSmallGroupWaves)
-      small_copy_ring<MB, LPS, G::AD>(A, ld, m0, mend - 1, kbeg, K, NST, smem, cw, lane);
+      small_copy_ring<MB, LPS, G::AD, false>(A, ld, m0, mend - 1, kbeg, K, NST, smem, cw, lane);
     else
-      small_copy_ring<2 * CT, LPS, G::WD>(W, ld, n0, N - 1, kbeg, K, NST, smem + G::A_RING,
-                                          cw - kSmallGroupWaves, lane);
+      small_copy_ring<2 * CT, LPS, G::WD, true>(W, ld, n0, N - 1, kbeg, K, NST, smem + G::A_RING,
+                                                cw - kSmallGroupWaves, lane);
     return;
   }
 
@@ -371,7 +375,10 @@ static void launch_small_k(const void* A, const void* W, void* C, int M, int N, 
 
 // Rows (8 MB) and 16-column strips (CT) per workgroup, chosen from M and N:
 // a workgroup moves its rows of A plus its strips of W, one workgroup per CU
-// at a time, so the time goes with rounds * (MB + 2 CT) (KiB per 32 k).
+// at a time, so the time goes with rounds * (MB + 2 CT) (KiB per 32 k).  One
+// 8-row block (M <= 8) always takes single strips: A is then negligible, two
+// such workgroups share a CU, and HBM streams best when each CU sweeps few
+// rows of W at a time.
 struct SmallShape {
   int mb, ct;
 };
@@ -381,7 +388,8 @@ static SmallShape small_shape(int M, int N) {
   long best_cost = -1, best_wgs = 0;
   for (int mb : {1, 2, 4, 6, 8}) {
     const long rg = (M + 8 * mb - 1) / (8 * mb);
-    for (int ct : {1, 2, 3, 4, 8}) {
+    for (int ct : {1, 2, 3, 4, 7, 8}) {
+      if (mb == 1 && ct != 1) continue;   // one 8-row block: 16-row strips, two per CU
       const long wgs = rg * ((tiles + ct - 1) / ct);
       const long cost = ((wgs + 255) / 256) * (mb + 2 * ct);
       if (best_cost < 0 || cost < best_cost || (cost == best_cost && wgs < best_wgs))
@@ -402,7 +410,8 @@ static void dispatch_small(const void* A, const void* W, void* C, int M, int N, 
     return;                                                                     \
   }
 #define BI_SMALL_M(MB_) \
-  BI_SMALL(MB_, 1) BI_SMALL(MB_, 2) BI_SMALL(MB_, 3) BI_SMALL(MB_, 4) BI_SMALL(MB_, 8)
+  BI_SMALL(MB_, 1) BI_SMALL(MB_, 2) BI_SMALL(MB_, 3) BI_SMALL(MB_, 4) BI_SMALL(MB_, 7)          \
+  BI_SMALL(MB_, 8)
   BI_SMALL_M(1) BI_SMALL_M(2) BI_SMALL_M(4) BI_SMALL_M(6) BI_SMALL_M(8)
 #undef BI_SMALL_M
 #undef BI_SMALL
