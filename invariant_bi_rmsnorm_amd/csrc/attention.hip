@@ -623,12 +623,12 @@ __global__ __launch_bounds__(64 * NW) void k_prefill(
 // 16-dim tiles of the output.  Keys past n read valid memory and are masked;
 // their V rows are zeroed so that no stale value can reach the sum.
 // ---------------------------------------------------------------------------
-template <int DH, int C, int MT>
+template <int DH, int C, int MT, int VH = 1>
 struct MfmaLds {
   static constexpr int NW = C / 64;
   static constexpr int RB = DH * 2;                       // bytes per V row
-  static constexpr int V_OFF = 0;                         // bf16 V [C][DH]
-  static constexpr int P_OFF = C * RB;                    // bf16 P [MT * 16][C]
+  static constexpr int V_OFF = 0;                         // bf16 V [C / VH][DH]
+  static constexpr int P_OFF = C / VH * RB;               // bf16 P [MT * 16][C]
   static constexpr int MX_OFF = P_OFF + MT * 16 * C * 2;  // fp32 [NW][MT * 16]
   static constexpr int BYTES = MX_OFF + NW * MT * 16 * 4;
   static constexpr int PM = (C / 8 < 16 ? C / 8 : 16) - 1;  // P block swizzle mask
@@ -683,6 +683,37 @@ __device__ __forceinline__ void mfma_zero_v_tail(char* lds, int n, int wave) {
         make_uint4(0u, 0u, 0u, 0u);
 }
 
+// V in two halves through one buffer of C / 2 rows: wave w copies keys
+// C / 2 * half + 32 w .. + 31 of the chunk (page ids vpg, one per 16 keys) to
+// rows 32 w .. 32 w + 31.
+template <int DH, int C>
+__device__ __forceinline__ void mfma_stage_v_half(char* lds, const char* vbase, long pstride,
+                                                  const int (&vpg)[2], int wave) {
+  constexpr int RB = DH * 2, SLOTS = RB / 16, KPI = 1024 / RB, KW = C / 2 / (C / 64);
+  static_assert(KW == 32, "32 keys per wave and half");
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int inst = 0; inst < KW / KPI; ++inst) {
+    const int k = inst * KPI + lane / SLOTS;       // key within the wave's 32
+    const int slot = lane % SLOTS;
+    const int row = KW * wave + k;                 // row of the half buffer
+    const char* src = vbase + vpg[k / kPage] * pstride + (k % kPage) * RB +
+                      16 * (slot ^ (row & 7));
+    dma16_nt(src, lds + (KW * wave + inst * KPI) * RB);
+  }
+}
+
+// Zero the rows of this wave's 32 keys of the half that lie at or past n.
+template <int DH, int C>
+__device__ __forceinline__ void mfma_zero_v_half_tail(char* lds, int n, int half, int wave) {
+  constexpr int RB = DH * 2, SLOTS = RB / 16, KW = 32;
+  const int lane = threadIdx.x & 63;
+  const int first = max(n - C / 2 * half, KW * wave), end = KW * wave + KW;   // rows
+  for (int i = lane; i < (end - first) * SLOTS; i += 64)
+    *reinterpret_cast<uint4*>(lds + (first + i / SLOTS) * RB + 16 * (i % SLOTS)) =
+        make_uint4(0u, 0u, 0u, 0u);
+}
+
 // The chunk for MT row tiles.  qf: A fragments of q; kf: this wave's K
 // fragments; key abs position of (wave, tile t, lane) = j0 + 64w + 16t +
 // (l & 15); lastpos[mt][j]: last visible absolute key of row 4 (l >> 4) + j
@@ -691,14 +722,16 @@ __device__ __forceinline__ void mfma_zero_v_tail(char* lds, int n, int wave) {
 // P rows of the other j must already hold zeros.  V must be staged (and the
 // tail zeroed) by every wave before the call.  Outputs for this lane's rows
 // and this wave's dim tiles; m = -inf marks a row with no visible key.
-template <int DH, int C, int MT, int RJ = 4, class H1 = NoHook>
+template <int DH, int C, int MT, int RJ = 4, int VH = 1, class H1 = NoHook, class H2 = NoHook>
 __device__ __forceinline__ void mfma_chunk(char* lds, const u32x4_t (&qf)[MT][DH / 32],
                                            const u32x4_t (&kf)[4][DH / 32], int j0,
                                            const int (&lastpos)[MT][4], float scale,
                                            float (&m_out)[MT][4], float (&l_out)[MT][4],
                                            f32x4_t (&acc)[MT][DH / 16 / (C / 64)],
-                                           const H1& after_qk = H1()) {
-  typedef MfmaLds<DH, C, MT> L;
+                                           const H1& after_qk = H1(),
+                                           const H2& next_v_half = H2()) {
+  typedef MfmaLds<DH, C, MT, VH> L;
+  static_assert(VH == 1 || VH == 2, "V resident whole or in two halves");
   constexpr int NW = L::NW, KS = DH / 32, DPW = DH / 16 / NW;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -774,6 +807,9 @@ __device__ __forceinline__ void mfma_chunk(char* lds, const u32x4_t (&qf)[MT][DH
   const int e = col >> 2, c4 = col & 3;  // this lane as a transposing-read source
 #pragma unroll
   for (int ks = 0; ks < C / 32; ++ks) {
+    // second half of the keys: the caller refills the V buffer
+    if (VH == 2 && ks == C / 64) next_v_half();
+    const int vrow0 = (VH == 2 && ks >= C / 64) ? C / 2 : 0;   // first key in the buffer
     u32x4_t a[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -787,7 +823,7 @@ __device__ __forceinline__ void mfma_chunk(char* lds, const u32x4_t (&qf)[MT][DH
     for (int d = 0; d < DPW; ++d) {
       const int dt = wave * DPW + d;                       // 16-dim tile
       const int piece = 2 * dt + (c4 >> 1);
-      const int k0 = 32 * ks + 8 * g4 + e;
+      const int k0 = 32 * ks + 8 * g4 + e - vrow0;
       const uint2 lo = lds_read_tr16(lds, vswz<DH>(k0, piece) + 8 * (c4 & 1));
       const uint2 hi = lds_read_tr16(lds, vswz<DH>(k0 + 4, piece) + 8 * (c4 & 1));
       const u32x4_t b = u32x4_t{lo.x, lo.y, hi.x, hi.y};
@@ -817,7 +853,7 @@ __global__ __launch_bounds__(C) void k_decode_mfma(
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ kv_len,
     const int32_t* __restrict__ chunk_off, int B, int h, int h_kv, int max_pages, float scale,
     float* __restrict__ part_ml, float* __restrict__ part_acc, int chunk2 = 0, int stride = 0) {
-  typedef MfmaLds<DH, C, 1> L;
+  typedef MfmaLds<DH, C, 1, 2> L;   // V through LDS in two halves
   constexpr int KS = DH / 32, DPW = DH / 16 / L::NW;
   static_assert(R <= 4, "one row group holds the query heads of a kv head");
   extern __shared__ __attribute__((aligned(1024))) char lds[];
@@ -839,34 +875,56 @@ __global__ __launch_bounds__(C) void k_decode_mfma(
   } else {
     crow = row;
     // request owning this chunk row: the number of r >= 1 with chunk_off[r]
-    // <= crow (chunk_off ascends), counted 64 requests per vector load
+    // <= crow, counted 64 requests per vector load.  chunk_off ascends
+    // strictly, so the lanes that pass form a prefix and the last of them
+    // holds chunk_off[r] (chunk_off[0] = 0).
     r = 0;
+    int base = 0;
     for (int b0 = 1; b0 < B; b0 += 64) {
       const int i = b0 + lane;
-      const bool le = i < B && chunk_off[i] <= (int)crow;
-      const int cnt = __builtin_popcountll(__ballot(le));
+      const int v = i < B ? chunk_off[i] : 0x7fffffff;
+      const int cnt = __builtin_popcountll(__ballot(v <= (int)crow));
       r += cnt;
+      if (cnt > 0) base = __builtin_amdgcn_readlane(v, cnt - 1);
       if (cnt < 64) break;
     }
     r = __builtin_amdgcn_readfirstlane(r);
-    j0 = ((int)crow - chunk_off[r]) * C;
-    len = kv_len[r];
-    n = min(C, len - j0);
+    base = __builtin_amdgcn_readfirstlane(base);
+    j0 = ((int)crow - base) * C;
   }
+  // page ids: loaded with clamped indices before kv_len (so the loads go out
+  // together), then every page past the chunk's last key replaced by its
+  // first (a valid page)
   const int32_t* bt = block_table + (long)r * max_pages;
   int pg[4];
   const int first = bt[j0 / kPage];
+  int ids[4], vids[2][2];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int k0 = 64 * wave + kPage * p;
-    pg[p] = k0 < n ? bt[(j0 + k0) / kPage] : first;
+  for (int p = 0; p < 4; ++p)
+    ids[p] = bt[min((j0 + 64 * wave + kPage * p) / kPage, max_pages - 1)];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      vids[hf][p] = bt[min((j0 + C / 2 * hf + 32 * wave + kPage * p) / kPage, max_pages - 1)];
+  if (!FREE) {
+    len = kv_len[r];
+    n = min(C, len - j0);
   }
+  int vpg[2][2];   // V pages of this wave's 32 keys of each half
+#pragma unroll
+  for (int p = 0; p < 4; ++p) pg[p] = 64 * wave + kPage * p < n ? ids[p] : first;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      vpg[hf][p] = C / 2 * hf + 32 * wave + kPage * p < n ? vids[hf][p] : first;
   const long hstride = (long)kPage * DH * 2, pstride = hstride * h_kv;
   const char* kbase = static_cast<const char*>(k_pool) + g * hstride;
   const char* vbase = static_cast<const char*>(v_pool) + g * hstride;
   u32x4_t kf[4][KS];
   mfma_load_k<DH>(kf, kbase, pstride, pg);
-  mfma_stage_v<DH>(lds, vbase, pstride, pg, wave);
+  mfma_stage_v_half<DH, C>(lds, vbase, pstride, vpg[0], wave);
   // query head hd sits on A row 4 hd, so each row group of the score tile
   // (lanes 16 G .. 16 G + 15, j = 0) holds one head: every lane has a real
   // score per key tile
@@ -889,13 +947,23 @@ __global__ __launch_bounds__(C) void k_decode_mfma(
     }
   }
   BI_WAIT_VMCNT(0);
-  if (n < C) mfma_zero_v_tail<DH>(lds, n, wave);
+  if (n < C / 2) mfma_zero_v_half_tail<DH, C>(lds, n, 0, wave);
   int lastpos[1][4];
   lastpos[0][0] = g4 < R ? j0 + n - 1 : -1;
   lastpos[0][1] = lastpos[0][2] = lastpos[0][3] = -1;
   float m[1][4], l[1][4];
   f32x4_t acc[1][DPW];
-  mfma_chunk<DH, C, 1, 1>(lds, qf, kf, j0, lastpos, scale, m, l, acc);
+  // between the halves of P V: every wave is done with the first half of V;
+  // copy the second (keys past n only zeroed) and wait for all of it
+  auto v_second_half = [&]() {
+    __syncthreads();
+    if (n > C / 2) mfma_stage_v_half<DH, C>(lds, vbase, pstride, vpg[1], wave);
+    BI_WAIT_VMCNT(0);
+    if (n < C) mfma_zero_v_half_tail<DH, C>(lds, n, 1, wave);
+    __syncthreads();
+  };
+  mfma_chunk<DH, C, 1, 1, 2>(lds, qf, kf, j0, lastpos, scale, m, l, acc, NoHook(),
+                             v_second_half);
   if (g4 < R) {  // row 4 g4 = query head g4, in every lane of row group g4
     const long prow = crow * h + g * R + g4;
     if (col == 0 && wave == 0) {
@@ -1080,7 +1148,7 @@ static void launch_decode_mfma(dim3 grid, const void* q, const void* kp, const v
                                const int32_t* bt, const int32_t* kvl, const int32_t* off, int B,
                                int h, int h_kv, int mp, float scale, float* ml, float* acc,
                                hipStream_t s, int chunk2 = 0, int stride = 0) {
-  constexpr int lds = MfmaLds<DH, C, 1>::BYTES;
+  constexpr int lds = MfmaLds<DH, C, 1, 2>::BYTES;
   static bool attr = false;
   if (!attr) {
     (void)hipFuncSetAttribute((const void*)k_decode_mfma<DH, R, C, FREE>,
