@@ -623,13 +623,13 @@ __global__ __launch_bounds__(64 * NW) void k_prefill(
 // 16-dim tiles of the output.  Keys past n read valid memory and are masked;
 // their V rows are zeroed so that no stale value can reach the sum.
 // ---------------------------------------------------------------------------
-template <int DH, int C, int MT, int VH = 1>
+template <int DH, int C, int MT, int VH = 1, int PR = 16>
 struct MfmaLds {
   static constexpr int NW = C / 64;
   static constexpr int RB = DH * 2;                       // bytes per V row
   static constexpr int V_OFF = 0;                         // bf16 V [C / VH][DH]
-  static constexpr int P_OFF = C / VH * RB;               // bf16 P [MT * 16][C]
-  static constexpr int MX_OFF = P_OFF + MT * 16 * C * 2;  // fp32 [NW][MT * 16]
+  static constexpr int P_OFF = C / VH * RB;               // bf16 P [MT * PR][C]
+  static constexpr int MX_OFF = P_OFF + MT * PR * C * 2;  // fp32 [NW][MT * 16]
   static constexpr int BYTES = MX_OFF + NW * MT * 16 * 4;
   static constexpr int PM = (C / 8 < 16 ? C / 8 : 16) - 1;  // P block swizzle mask
 };
@@ -718,10 +718,12 @@ __device__ __forceinline__ void mfma_zero_v_half_tail(char* lds, int n, int half
 // fragments; key abs position of (wave, tile t, lane) = j0 + 64w + 16t +
 // (l & 15); lastpos[mt][j]: last visible absolute key of row 4 (l >> 4) + j
 // of tile mt (-1 for rows that are not used).  Only rows with j < RJ may be
-// used (decode puts its query heads on rows 0, 4, 8, 12 and passes RJ = 1);
-// P rows of the other j must already hold zeros.  V must be staged (and the
-// tail zeroed) by every wave before the call.  Outputs for this lane's rows
-// and this wave's dim tiles; m = -inf marks a row with no visible key.
+// used (decode puts its query heads on rows 0, 4, 8, 12 and passes RJ = 1;
+// P then keeps those four rows only and the other rows enter P V as zeros).
+// V must be staged (and the tail zeroed) by every wave before the call; with
+// VH = 2 the buffer holds the first C / 2 keys and next_v_half() refills it
+// with the rest once P V reaches them.  Outputs for this lane's rows and this
+// wave's dim tiles; m = -inf marks a row with no visible key.
 template <int DH, int C, int MT, int RJ = 4, int VH = 1, class H1 = NoHook, class H2 = NoHook>
 __device__ __forceinline__ void mfma_chunk(char* lds, const u32x4_t (&qf)[MT][DH / 32],
                                            const u32x4_t (&kf)[4][DH / 32], int j0,
@@ -730,8 +732,11 @@ __device__ __forceinline__ void mfma_chunk(char* lds, const u32x4_t (&qf)[MT][DH
                                            f32x4_t (&acc)[MT][DH / 16 / (C / 64)],
                                            const H1& after_qk = H1(),
                                            const H2& next_v_half = H2()) {
-  typedef MfmaLds<DH, C, MT, VH> L;
+  // RJ = 1 keeps only P rows 4 i (the others are zero): 4 rows per tile
+  constexpr int PR = RJ == 1 ? 4 : 16;
+  typedef MfmaLds<DH, C, MT, VH, PR> L;
   static_assert(VH == 1 || VH == 2, "V resident whole or in two halves");
+  static_assert(RJ == 1 || RJ == 4, "all rows of a tile, or rows 4 i");
   constexpr int NW = L::NW, KS = DH / 32, DPW = DH / 16 / NW;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -788,7 +793,8 @@ __device__ __forceinline__ void mfma_chunk(char* lds, const u32x4_t (&qf)[MT][DH
         const int row = 4 * g4 + j;
         const float mm = m_out[mt][j];
         const float p = (sv[mt][t][j] == -__builtin_inff()) ? 0.0f : exp_fixed(sv[mt][t][j] - mm);
-        const uint32_t off = (uint32_t)((mt * 16 + row) * C * 2 +
+        const int prow = PR == 16 ? row : row >> 2;   // row 4 g4 when PR = 4
+        const uint32_t off = (uint32_t)((mt * PR + prow) * C * 2 +
                                         16 * ((key >> 3) ^ (row & L::PM)) + 2 * (key & 7));
         *reinterpret_cast<uint16_t*>(pl + off) = (uint16_t)f32_to_bf16_bits(p);
       }
@@ -814,9 +820,16 @@ __device__ __forceinline__ void mfma_chunk(char* lds, const u32x4_t (&qf)[MT][DH
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int row = col;
-      const uint32_t off = (uint32_t)((mt * 16 + row) * C * 2 +
-                                      16 * ((4 * ks + g4) ^ (row & L::PM)));
-      a[mt] = *reinterpret_cast<const u32x4_t*>(pl + off);
+      if (PR == 16) {
+        const uint32_t off = (uint32_t)((mt * 16 + row) * C * 2 +
+                                        16 * ((4 * ks + g4) ^ (row & L::PM)));
+        a[mt] = *reinterpret_cast<const u32x4_t*>(pl + off);
+      } else {   // rows 4 i from LDS, zeros for the rest
+        const uint32_t off = (uint32_t)((mt * PR + (row >> 2)) * C * 2 +
+                                        16 * ((4 * ks + g4) ^ (row & L::PM)));
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(pl + off);
+        a[mt] = (row & 3) == 0 ? v : u32x4_t{0u, 0u, 0u, 0u};
+      }
       lacc[mt] = mfma16(a[mt], ones, lacc[mt]);
     }
 #pragma unroll
@@ -853,7 +866,7 @@ __global__ __launch_bounds__(C) void k_decode_mfma(
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ kv_len,
     const int32_t* __restrict__ chunk_off, int B, int h, int h_kv, int max_pages, float scale,
     float* __restrict__ part_ml, float* __restrict__ part_acc, int chunk2 = 0, int stride = 0) {
-  typedef MfmaLds<DH, C, 1, 2> L;   // V through LDS in two halves
+  typedef MfmaLds<DH, C, 1, 2, 4> L;   // V through LDS in two halves, P rows 4 i
   constexpr int KS = DH / 32, DPW = DH / 16 / L::NW;
   static_assert(R <= 4, "one row group holds the query heads of a kv head");
   extern __shared__ __attribute__((aligned(1024))) char lds[];
@@ -937,14 +950,6 @@ __global__ __launch_bounds__(C) void k_decode_mfma(
   for (int s = 0; s < KS; ++s) {
     const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qrow + 8 * g4 + 32 * s);
     qf[0][s] = qreal ? v : u32x4_t{0u, 0u, 0u, 0u};
-  }
-  // P rows that are not 4 hd stay zero (the chunk writes rows 4 hd only)
-  {
-    char* pl = lds + L::P_OFF;
-    for (int i = threadIdx.x; i < 16 * C * 2 / 16; i += C) {
-      const int row = i / (C * 2 / 16);
-      if ((row & 3) != 0) *reinterpret_cast<uint4*>(pl + 16 * i) = make_uint4(0u, 0u, 0u, 0u);
-    }
   }
   BI_WAIT_VMCNT(0);
   if (n < C / 2) mfma_zero_v_half_tail<DH, C>(lds, n, 0, wave);
@@ -1148,7 +1153,7 @@ static void launch_decode_mfma(dim3 grid, const void* q, const void* kp, const v
                                const int32_t* bt, const int32_t* kvl, const int32_t* off, int B,
                                int h, int h_kv, int mp, float scale, float* ml, float* acc,
                                hipStream_t s, int chunk2 = 0, int stride = 0) {
-  constexpr int lds = MfmaLds<DH, C, 1, 2>::BYTES;
+  constexpr int lds = MfmaLds<DH, C, 1, 2, 4>::BYTES;
   static bool attr = false;
   if (!attr) {
     (void)hipFuncSetAttribute((const void*)k_decode_mfma<DH, R, C, FREE>,
