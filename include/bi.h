@@ -128,6 +128,18 @@ bi_status bi_rmsnorm_free(const void *x, const void *gamma, void *y, int M, int 
 bi_status bi_gemm(const void *A, const void *W, void *C, int M, int N, int K, int in_dtype,
                   int out_dtype, bi_stream stream);
 
+/* SwiGLU projection of a decode batch in one pass: act[i][j] =
+ * round(g / (1 + exp(-g)) * u) with g = C[i][j], u = C[i][I + j] of
+ * C = A W^T as bi_gemm computes it (bf16 out), so the result is bit-identical
+ * to bi_gemm into [M][2I] followed by bi_silu_mul, without the [M][2I]
+ * intermediate.  A: device bf16 [M][K]; W: device bf16 [2I][K], the I gate
+ * rows then the I up rows; act: device bf16 [M][I].  The K reduction is the
+ * same chain as bi_gemm's ("2 . Cross-block accumulation").  0 <= M <= 64
+ * (larger M: bi_gemm then bi_silu_mul), I % 8 == 0, K % 8 == 0, pointers
+ * 16-byte aligned; anything else returns BI_ERR_INVALID and launches nothing. */
+bi_status bi_gemm_swiglu(const void *A, const void *W, void *act, int M, int I, int K,
+                         bi_stream stream);
+
 /* Twin: picks its tiling from M and, when M x N offers too few tiles to fill
  * the device, splits K over workgroups that add fp32 partials with atomics
  * (order undefined) -- the split-K the pages describe.  Needs

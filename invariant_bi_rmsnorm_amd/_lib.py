@@ -33,6 +33,7 @@ SIGNATURES = {
     "bi_rmsnorm": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_float, _c_int, _vp]),
     "bi_add_rmsnorm": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_float, _c_int, _vp]),
     "bi_gemm": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
+    "bi_gemm_swiglu": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp]),
     "bi_decode_attn": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp] + [_c_int] * 8
                        + [_c_float, _c_int, _vp, _vp, _vp]),
     "bi_merge_partials": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _c_int, _vp]),
@@ -167,6 +168,17 @@ def bi_gemm(A, W, C, stream=None):
     _check("bi_gemm", load().bi_gemm(_ptr(A), _ptr(W), _ptr(C), M, N, K, _dt(A), _dt(C),
                                      _stream(stream)))
     return C
+
+
+def bi_gemm_swiglu(A, W, act, stream=None):
+    """act = silu(g) * u of [g | u] = A W^T (gate rows then up rows of W)."""
+    M, K = A.shape
+    I = act.shape[1]
+    if tuple(W.shape) != (2 * I, K) or act.shape[0] != M:
+        raise ValueError(f"shape mismatch A{tuple(A.shape)} W{tuple(W.shape)} act{tuple(act.shape)}")
+    _check("bi_gemm_swiglu", load().bi_gemm_swiglu(_ptr(A), _ptr(W), _ptr(act), M, I, K,
+                                                   _stream(stream)))
+    return act
 
 
 def bi_decode_attn(q, k_pool, v_pool, block_table, kv_len, chunk_off, total_chunks: int,

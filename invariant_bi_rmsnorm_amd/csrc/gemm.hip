@@ -51,6 +51,29 @@ __device__ __forceinline__ void store_tile(void* C, const f32x4_t& acc, int row0
   }
 }
 
+// SwiGLU epilogue of a pair tile: MFMA columns 0..7 are gate columns a0 .. a0
+// + 7, columns 8..15 the matching up columns.  Each is rounded to bf16 as the
+// GEMM's own output would be, then act = bf16(g / (1 + exp(-g)) * u) with the
+// arithmetic of bi_silu_mul, so the pair equals the GEMM followed by it.
+__device__ __forceinline__ void store_swiglu(void* act, const f32x4_t& acc, int row0, int a0,
+                                             int M, int I, int lane) {
+  float up[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) up[j] = __shfl_xor(acc[j], 8);   // lane l + 8 holds the up column
+  const int c = lane & 15, col = a0 + c;
+  if (c >= 8 || col >= I) return;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = row0 + 4 * (lane >> 4) + j;
+    if (row < M) {
+      const float g = bf16_bits_to_f32((uint16_t)f32_to_bf16_bits(acc[j]));
+      const float u = bf16_bits_to_f32((uint16_t)f32_to_bf16_bits(up[j]));
+      const float sg = g / (1.0f + exp_fixed(-g));
+      static_cast<uint16_t*>(act)[(long)row * I + col] = (uint16_t)f32_to_bf16_bits(sg * u);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // small-M kernel (M <= 64): one workgroup per CT 16-column strips of W and one
 // group of 8 MB rows of A (blockIdx.z; MB and CT are chosen from M and N so
@@ -115,7 +138,7 @@ struct SmallCfg {
 template <int NB, int LPS, int RD, bool NT>
 __device__ __forceinline__ void small_copy_ring(const uint16_t* __restrict__ base, long ld,
                                                 int row0, int rmax, int kbeg, int K, int NST,
-                                                char* ring, int gw, int lane) {
+                                                char* ring, int gw, int lane, int half = 0) {
   constexpr int NIT = NB * LPS, QB = NIT / kSmallGroupWaves, XR = NIT % kSmallGroupWaves;
   constexpr int QMAX = QB + (XR > 0), KS = 2 * LPS;
   const bool extra = gw < XR;
@@ -124,7 +147,11 @@ __device__ __forceinline__ void small_copy_ring(const uint16_t* __restrict__ bas
 #pragma unroll
   for (int i = 0; i < QMAX; ++i) {
     const int j = min(gw + kSmallGroupWaves * i, NIT - 1), b = j % NB, line = j / NB;
-    src[i] = base + (long)min(row0 + b * 8 + crow, rmax) * ld + kbeg + line * 64 + koff;
+    // half > 0 (SwiGLU pairs): block 2p is gate rows row0 + 8p .., block 2p + 1
+    // the up rows `half` further on
+    const int row = half > 0 ? (b & 1) * half + min(row0 + (b >> 1) * 8 + crow, rmax)
+                             : min(row0 + b * 8 + crow, rmax);
+    src[i] = base + (long)row * ld + kbeg + line * 64 + koff;
   }
   auto issue = [&](int st) {
     char* slot = ring + (st % RD) * (NIT * 1024);
@@ -174,8 +201,10 @@ __global__ __launch_bounds__(kSmallThreads) void k_gemm_small(
     if (cw < kSmallGroupWaves)
       small_copy_ring<MB, LPS, G::AD, false>(A, ld, m0, mend - 1, kbeg, K, NST, smem, cw, lane);
     else
-      small_copy_ring<2 * CT, LPS, G::WD, true>(W, ld, n0, N - 1, kbeg, K, NST, smem + G::A_RING,
-                                                cw - kSmallGroupWaves, lane);
+      // OUTF32 3 (SwiGLU): N = 2 I; strip x holds pair tiles CT x .. CT x + CT - 1
+      small_copy_ring<2 * CT, LPS, G::WD, true>(
+          W, ld, OUTF32 == 3 ? n0 / 2 : n0, (OUTF32 == 3 ? N / 2 : N) - 1, kbeg, K, NST,
+          smem + G::A_RING, cw - kSmallGroupWaves, lane, OUTF32 == 3 ? N / 2 : 0);
     return;
   }
 
@@ -249,7 +278,11 @@ __global__ __launch_bounds__(kSmallThreads) void k_gemm_small(
 #pragma unroll
     for (int j = 0; j < G::JN; ++j) {
       const int m = wm + G::WM * i, c = wn + G::WN * j;
-      if (m < MT) store_tile<OUTF32>(C, acc[i][j], m0 + m * 16, n0 + c * 16, mend, N, lane);
+      if constexpr (OUTF32 == 3) {   // every lane joins the exchange
+        if (m < MT) store_swiglu(C, acc[i][j], m0 + m * 16, n0 / 2 + c * 8, mend, N / 2, lane);
+      } else if (m < MT) {
+        store_tile<OUTF32>(C, acc[i][j], m0 + m * 16, n0 + c * 16, mend, N, lane);
+      }
     }
 }
 
@@ -600,4 +633,19 @@ extern "C" bi_status bi_gemm(const void* A, const void* W, void* C, int M, int N
   BI_REQUIRE(K % 8 == 0, BI_ERR_UNSUPPORTED, "bi_gemm: bf16 needs K %% 8 == 0 (K=%d)", K);
   gemm_dispatch(A, W, C, M, N, K, out_dtype == BI_F32, s);
   return launched("bi_gemm");
+}
+
+extern "C" bi_status bi_gemm_swiglu(const void* A, const void* W, void* act, int M, int I, int K,
+                                    bi_stream stream) {
+  using namespace bi;
+  BI_REQUIRE(M >= 0 && M <= 64 && I >= 8 && I % 8 == 0 && K >= 8 && K % 8 == 0,
+             BI_ERR_INVALID, "bi_gemm_swiglu: need 0 <= M <= 64, I %% 8 == 0, K %% 8 == 0 "
+             "(M=%d I=%d K=%d)", M, I, K);
+  if (M == 0) return BI_OK;
+  BI_REQUIRE(A && W && act, BI_ERR_INVALID, "bi_gemm_swiglu: null pointer");
+  BI_REQUIRE(aligned16(A) && aligned16(W) && aligned16(act), BI_ERR_INVALID,
+             "bi_gemm_swiglu: pointers must be 16-byte aligned");
+  BI_REQUIRE(2L * I * K < (1L << 40), BI_ERR_INVALID, "bi_gemm_swiglu: tensor too large");
+  dispatch_small<3>(A, W, act, M, 2 * I, K, as_stream(stream));
+  return launched("bi_gemm_swiglu");
 }

@@ -300,6 +300,8 @@ class Engine:
             else:
                 run("add", lambda: L.bi_add(h, o, h))
                 run("rmsnorm", lambda: rms(h, lw.ffn_norm, x, c.eps))
+            # bi_gemm_swiglu gives the same bits in one pass, but on this
+            # step it measured no faster (slower at 7 and 64 rows)
             run("gemm_gate_up", lambda: gemm(x, lw.wgu, gu))
             run("silu_mul", lambda: L.bi_silu_mul(gu, act))
             run("gemm_down", lambda: gemm(act, lw.wdown, o))

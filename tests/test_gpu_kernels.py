@@ -106,6 +106,50 @@ GEMM_SHAPES = [(1, 16, 32), (1, 17, 40), (5, 100, 264), (16, 64, 512), (17, 48, 
                (3, 16400, 4096), (64, 16448, 4096), (20, 16384, 264)]
 
 
+SWIGLU_SHAPES = [(1, 14336, 4096), (64, 14336, 4096), (7, 1000, 264), (33, 8, 40),
+                 (16, 1024, 4104), (64, 56, 4096), (2, 6144, 1000), (48, 2056, 512)]
+
+
+@pytest.mark.parametrize("M,I,K", SWIGLU_SHAPES)
+def test_gemm_swiglu_equals_gemm_then_silu_mul(M, I, K):
+    A = synth.normal((M, K), seed=M + 3 * K).to(torch.bfloat16)
+    W = synth.normal((2 * I, K), seed=I + K, std=0.05).to(torch.bfloat16)
+    Ad, Wd = A.to(dev()), W.to(dev())
+    act = torch.empty((M, I), dtype=torch.bfloat16, device=dev())
+    L.bi_gemm_swiglu(Ad, Wd, act)
+    gu = torch.empty((M, 2 * I), dtype=torch.bfloat16, device=dev())
+    L.bi_gemm(Ad, Wd, gu)
+    act2 = torch.empty_like(act)
+    L.bi_silu_mul(gu, act2)
+    assert bits_equal(to_np(act), to_np(act2))
+    # the epilogue is the oracle's silu_mul of the GEMM's bf16 output
+    assert bits_equal(to_np(act), oracle.silu_mul(to_np(gu), round_bf16=True))
+
+
+@pytest.mark.parametrize("M,I,K", [(1, 1000, 264), (64, 14336, 4096), (9, 48, 40)])
+def test_gemm_swiglu_integer_exact_vs_oracle(M, I, K):
+    # integer operands: the GEMM is exact in fp32, so the whole pair is the
+    # oracle's to the bit
+    A = synth.integers((M, K), -3, 3, seed=M + K).to(torch.bfloat16)
+    W = synth.integers((2 * I, K), -3, 3, seed=I + K + 1).to(torch.bfloat16)
+    act = torch.empty((M, I), dtype=torch.bfloat16, device=dev())
+    L.bi_gemm_swiglu(A.to(dev()), W.to(dev()), act)
+    ref = oracle.silu_mul(oracle.gemm(A, W, round_bf16=True), round_bf16=True)
+    assert bits_equal(to_np(act), ref), mismatch_report(to_np(act), ref)
+
+
+def test_gemm_swiglu_rejects_bad_shapes():
+    A = torch.zeros((65, 64), dtype=torch.bfloat16, device=dev())
+    W = torch.zeros((32, 64), dtype=torch.bfloat16, device=dev())
+    act = torch.empty((65, 16), dtype=torch.bfloat16, device=dev())
+    with pytest.raises(L.BiError):
+        L.bi_gemm_swiglu(A, W, act)          # M > 64
+    W12 = torch.zeros((24, 64), dtype=torch.bfloat16, device=dev())
+    act12 = torch.empty((1, 12), dtype=torch.bfloat16, device=dev())
+    with pytest.raises(L.BiError):
+        L.bi_gemm_swiglu(A[:1], W12, act12)  # I % 8 != 0
+
+
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 def test_gemm_bf16_integer_exact(M, N, K, out):
