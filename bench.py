@@ -54,8 +54,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", default="1,7,32", help="extra batch sizes ('' for none)")
     ap.add_argument("--only", default="",
-                    help="time one kernel of the step instead (decode_attn, gemm_qkv, ..., or "
-                         "'copy' for a plain 1 GiB device copy), e.g. under rocprofv3 --pmc")
+                    help="time one kernel of the step instead (decode_attn, gemm_qkv, ..., "
+                         "'log_softmax' for logprobs of the batch's logits, or 'copy' for a "
+                         "plain 1 GiB device copy), e.g. under rocprofv3 --pmc")
     ap.add_argument("--twin", action="store_true", help="with --only: the twin's kernel")
     ap.add_argument("--launches", type=int, default=50)
     ap.add_argument("--traffic-summary", default="",
@@ -400,6 +401,15 @@ def only_kernel(args, torch, dev):
     elif args.only == "prefill_gemm":
         print(json.dumps(prefill_gemm(torch, dev, launches=args.launches)), flush=True)
         return
+    elif args.only == "log_softmax":
+        # logprobs of a decode batch: fp32 logits [batch, vocab], read once and
+        # written once (the second and third passes over a row hit L2)
+        from invariant_bi_rmsnorm_amd import _lib
+        V = model_config(args).vocab
+        x = torch.empty((args.batch, V), device=dev).normal_(std=3.0)
+        y = torch.empty_like(x)
+        fn, alg = (lambda: _lib.bi_log_softmax(x, y)), 2 * 4 * args.batch * V
+        label = f"log_softmax, batch {args.batch}"
     else:
         from invariant_bi_rmsnorm_amd.model import init_weights
         cfg = model_config(args)

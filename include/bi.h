@@ -287,6 +287,21 @@ bi_status bi_rope_kv_append(const void *qkv, int M, int h, int h_kv, int d_h,
 /* y = round(a + b) elementwise over n elements (y may alias a or b). */
 bi_status bi_add(const void *a, const void *b, void *y, long n, int dtype, bi_stream stream);
 
+/* Log-softmax of fp32 rows (logprobs): y[i][j] = (x[i][j] - m_i) -
+ * log(sum_j exp(x[i][j] - m_i)), m_i the row maximum.  One
+ * workgroup per row whatever M is, each row reduced in one fixed order (a
+ * thread's strided elements serially, an xor butterfly per wave, the waves in
+ * order), with the library's own exp and log -- "Batch invariance and
+ * reproducible inference": the dispatcher's replacement log_softmax (one
+ * block per row, no cross-block reduction, after "4 . Unsorted top-k in MoE
+ * routing") and "Mathematically equivalent is not bitwise equivalent"
+ * (logprobs come from this one kernel for prefill and decode rows alike, so
+ * equal logit rows give equal logprob rows).  x, y: device fp32 [M][V]; y may
+ * be x (in place) but must not partly overlap it.  A row with no entry above
+ * -inf gives -inf throughout; NaN entries never win the maximum.  M >= 0 (0 is
+ * a no-op), V >= 1; errors return BI_ERR_INVALID and launch nothing. */
+bi_status bi_log_softmax(const float *x, float *y, int M, int V, bi_stream stream);
+
 /* SwiGLU: gu [M][2F] = [gate | up]; y[i][j] = round(g / (1 + exp(-g)) * u). */
 bi_status bi_silu_mul(const void *gu, void *y, int M, int F, int dtype, bi_stream stream);
 

@@ -45,6 +45,7 @@ SIGNATURES = {
     "bi_add": (_c_int, [_vp, _vp, _vp, _c_long, _c_int, _vp]),
     "bi_silu_mul": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _vp]),
     "bi_argmax": (_c_int, [_vp, _vp, _c_int, _c_int, _vp]),
+    "bi_log_softmax": (_c_int, [_vp, _vp, _c_int, _c_int, _vp]),
     # batch-adaptive twins
     "bi_rmsnorm_free_workspace_bytes": (_c_size, [_c_int, _c_int]),
     "bi_rmsnorm_free": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_float, _c_int, _vp, _c_size,
@@ -236,6 +237,16 @@ def bi_add(a, b, y, stream=None):
 def bi_silu_mul(gu, y, stream=None):
     M, F = y.shape
     _check("bi_silu_mul", load().bi_silu_mul(_ptr(gu), _ptr(y), M, F, _dt(gu), _stream(stream)))
+    return y
+
+
+def bi_log_softmax(x, y, stream=None):
+    """y = log_softmax(x) row by row (fp32 [M, V]); y may be x."""
+    M, V = x.shape
+    if tuple(y.shape) != (M, V) or x.dtype != torch.float32 or y.dtype != torch.float32:
+        raise ValueError(f"bi_log_softmax: need fp32 x, y of one shape, got {tuple(x.shape)} "
+                         f"{x.dtype} and {tuple(y.shape)} {y.dtype}")
+    _check("bi_log_softmax", load().bi_log_softmax(_ptr(x), _ptr(y), M, V, _stream(stream)))
     return y
 
 

@@ -116,6 +116,37 @@ __device__ __forceinline__ float exp_fixed(float x) {
   return x != x ? x : p;
 }
 
+// ---- the library's log ----------------------------------------------------
+// One fixed binary32 log for the log-softmax, for the same reason: x = 2^e m
+// with m in [sqrt(1/2), sqrt(2)] (exponent and mantissa taken from the bits),
+// log m = 2 atanh(s) with s = (m - 1) / (m + 1), |s| <= 0.172, by the odd
+// series 2 s (1 + z/3 + z^2/5 + ... + z^6/13), z = s^2, in Horner form with
+// fma (the first omitted term is below 2^-39 relative), then e ln 2 added with
+// ln 2 split into the exp's head and tail.  For positive normal x; +inf and
+// NaN pass through.
+__device__ __forceinline__ float log_fixed(float x) {
+  const uint32_t b = __float_as_uint(x);
+  int e = (int)((b >> 23) & 0xff) - 127;
+  float m = __uint_as_float((b & 0x7fffffu) | 0x3f800000u);        // [1, 2)
+  const bool big = m > 1.41421353816986083984375f;                  // fp32(sqrt 2)
+  m = big ? 0.5f * m : m;
+  e = big ? e + 1 : e;
+  const float s = (m - 1.0f) / (m + 1.0f);
+  const float z = s * s;
+  float q = 1.0f / 13.0f;
+  q = __builtin_fmaf(q, z, 1.0f / 11.0f);
+  q = __builtin_fmaf(q, z, 1.0f / 9.0f);
+  q = __builtin_fmaf(q, z, 1.0f / 7.0f);
+  q = __builtin_fmaf(q, z, 1.0f / 5.0f);
+  q = __builtin_fmaf(q, z, 1.0f / 3.0f);
+  q = __builtin_fmaf(q, z, 1.0f);
+  const float lm = (s + s) * q;
+  const float fe = (float)e;
+  const float r = __builtin_fmaf(fe, 0.693145751953125f,
+                                 __builtin_fmaf(fe, 1.428606765330187045037746429443359375e-06f, lm));
+  return (x != x || x == __builtin_inff()) ? x : r;
+}
+
 // Maximum over the 16 lanes of each row of the wave (DPP row rotations;
 // max is exact, so the order of the steps does not matter).
 __device__ __forceinline__ float row16_max(float v) {

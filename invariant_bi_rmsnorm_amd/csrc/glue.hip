@@ -95,6 +95,64 @@ __global__ __launch_bounds__(256) void k_silu_mul(const void* __restrict__ gu,
   }
 }
 
+// Log-softmax: one 1024-thread workgroup per row whatever the number of rows.
+// Thread t takes elements t, t + 1024, ... in ascending order: first their
+// maximum m (entries that are NaN never win), then a serial fp32 sum of
+// exp(x - m); the 64 sums of a wave meet in an xor butterfly (masks 32 .. 1)
+// and the 16 wave sums are added in wave order.  y = (x - m) - log(sum)
+// (all -inf when no entry is above -inf).  y may alias x.
+__global__ __launch_bounds__(1024) void k_log_softmax(const float* x, float* y, int V) {
+  const long row = blockIdx.x;
+  const float* xr = x + row * V;
+  float* yr = y + row * V;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  __shared__ float red[16];
+  // each loop takes U of the thread's elements per trip: the loads go out
+  // together, then the elements are used in ascending order
+  constexpr int U = 8;
+  float m = -__builtin_inff();
+  for (int i0 = t; i0 < V; i0 += 1024 * U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = xr[min(i0 + 1024 * u, V - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u) m = (i0 + 1024 * u < V && v[u] > m) ? v[u] : m;
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float o = __shfl_xor(m, off);
+    m = o > m ? o : m;
+  }
+  if (lane == 0) red[w] = m;
+  __syncthreads();
+  m = red[0];
+  for (int k = 1; k < 16; ++k) m = red[k] > m ? red[k] : m;
+  __syncthreads();   // red is reused for the sums
+  float a = 0.0f;
+  for (int i0 = t; i0 < V; i0 += 1024 * U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = xr[min(i0 + 1024 * u, V - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i0 + 1024 * u < V) a = a + exp_fixed(v[u] - m);
+  }
+  for (int off = 32; off >= 1; off >>= 1) a = a + __shfl_xor(a, off);
+  if (lane == 0) red[w] = a;
+  __syncthreads();
+  float sum = red[0];
+  for (int k = 1; k < 16; ++k) sum = sum + red[k];
+  const bool none = m == -__builtin_inff();
+  const float ls = log_fixed(sum);
+  for (int i0 = t; i0 < V; i0 += 1024 * U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = xr[min(i0 + 1024 * u, V - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (i0 + 1024 * u < V) yr[i0 + 1024 * u] = none ? -__builtin_inff() : (v[u] - m) - ls;
+  }
+}
+
 __device__ __forceinline__ void argbest(float& v, int& i, float v2, int i2) {
   if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
 }
@@ -223,6 +281,16 @@ extern "C" bi_status bi_silu_mul(const void* gu, void* y, int M, int F, int dtyp
   if (dtype == BI_BF16) hipLaunchKernelGGL(k_silu_mul<1>, grid, dim3(256), 0, as_stream(stream), gu, y, F);
   else hipLaunchKernelGGL(k_silu_mul<0>, grid, dim3(256), 0, as_stream(stream), gu, y, F);
   return launched("bi_silu_mul");
+}
+
+extern "C" bi_status bi_log_softmax(const float* x, float* y, int M, int V, bi_stream stream) {
+  BI_REQUIRE(M >= 0 && V >= 1, BI_ERR_INVALID, "bi_log_softmax: bad sizes M=%d V=%d", M, V);
+  if (M == 0) return BI_OK;
+  BI_REQUIRE(x && y, BI_ERR_INVALID, "bi_log_softmax: null pointer");
+  BI_REQUIRE(y == x || y + (long)M * V <= x || x + (long)M * V <= y, BI_ERR_INVALID,
+             "bi_log_softmax: y must be x or not overlap it");
+  hipLaunchKernelGGL(k_log_softmax, dim3(M), dim3(1024), 0, as_stream(stream), x, y, V);
+  return launched("bi_log_softmax");
 }
 
 extern "C" bi_status bi_argmax(const float* x, int32_t* idx, int M, int V, bi_stream stream) {

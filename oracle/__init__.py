@@ -53,6 +53,9 @@ def _load():
         "oracle_add": (None, [_F, _F, _F, ctypes.c_long, ctypes.c_int]),
         "oracle_silu_mul": (None, [_F, _F, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
         "oracle_argmax": (None, [_F, _I, ctypes.c_int, ctypes.c_int]),
+        "oracle_log": (ctypes.c_float, [ctypes.c_float]),
+        "oracle_log_vec": (None, [_F, _F, ctypes.c_long]),
+        "oracle_log_softmax": (None, [_F, _F, ctypes.c_int, ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -224,3 +227,20 @@ def argmax(x) -> np.ndarray:
     idx = np.empty(M, dtype=np.int32)
     _load().oracle_argmax(_pf(x), _pi(idx), M, V)
     return idx
+
+
+def log(x) -> np.ndarray:
+    """The fixed binary32 log (oracle.c: oracle_log), elementwise."""
+    x = _f32(np.atleast_1d(x))
+    y = np.empty_like(x)
+    _load().oracle_log_vec(_pf(x), _pf(y), x.size)
+    return y
+
+
+def log_softmax(x) -> np.ndarray:
+    """Row-wise log-softmax of fp32 rows in the fixed order of oracle.c."""
+    x = _f32(x)
+    M, V = x.shape
+    y = np.empty_like(x)
+    _load().oracle_log_softmax(_pf(x), _pf(y), M, V)
+    return y

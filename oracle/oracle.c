@@ -508,3 +508,83 @@ void oracle_argmax(const float *x, int32_t *idx, int M, int V)
         idx[row] = best;
     }
 }
+
+/* ------------------------------------------------------------------ */
+/* log-softmax (logprobs)                                              */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Natural log in binary32, fixed for the same reason as the exp (the pages
+ * name no log routine; both sides of the parity check must evaluate the same
+ * one).  x = 2^e * m with e and m taken from the bits, m in [1, 2); if m >
+ * fp32(sqrt 2) then m = m / 2 and e = e + 1, so m lies in [sqrt(1/2),
+ * sqrt(2)].  log m = 2 atanh(s), s = (m - 1) / (m + 1), |s| <= 0.1716, by the
+ * series 2 s sum_{k=0..6} s^(2k) / (2k + 1) in Horner form in z = s^2 with
+ * fma (the first omitted term, z^7 / 15, is below 2^-39 relative); then
+ * log x = fma(e, LN2_HI, fma(e, LN2_LO, log m)) with the exp's split of ln 2.
+ * Defined for positive normal x; +inf and NaN pass through.
+ */
+float oracle_log(float x)
+{
+    if (x != x || x == INFINITY) return x;
+    uint32_t b = f2u(x);
+    int e = (int)((b >> 23) & 0xffu) - 127;
+    float m = u2f((b & 0x7fffffu) | 0x3f800000u);
+    if (m > 1.41421353816986083984375f) { m = 0.5f * m; e = e + 1; }
+    float s = (m - 1.0f) / (m + 1.0f);
+    float z = s * s;
+    float q = 1.0f / 13.0f;
+    q = fmaf(q, z, 1.0f / 11.0f);
+    q = fmaf(q, z, 1.0f / 9.0f);
+    q = fmaf(q, z, 1.0f / 7.0f);
+    q = fmaf(q, z, 1.0f / 5.0f);
+    q = fmaf(q, z, 1.0f / 3.0f);
+    q = fmaf(q, z, 1.0f);
+    float lm = (s + s) * q;
+    float fe = (float)e;
+    return fmaf(fe, EXP_LN2_HI, fmaf(fe, EXP_LN2_LO, lm));
+}
+
+void oracle_log_vec(const float *x, float *y, long n)
+{
+#pragma omp parallel for schedule(static)
+    for (long i = 0; i < n; ++i) y[i] = oracle_log(x[i]);
+}
+
+/*
+ * y = (x - m) - log(sum exp(x - m)) per row, m the row maximum
+ * ("Batch invariance and reproducible inference": the replacement
+ * log_softmax of the dispatcher overrides, one block per row looping the row
+ * serially; "Mathematically equivalent is not bitwise equivalent" for why
+ * logprobs come from it).  The order is the one a block of 1024 threads
+ * gives: thread t takes elements t, t + 1024, ... ascending -- their maximum
+ * (a NaN never wins: v > m is false), then a serial binary32 sum of
+ * exp(x - m); each wave of 64 threads adds its sums with the xor butterfly
+ * (masks 32 .. 1) and the 16 wave sums are added in wave order.  A row with
+ * no entry above -inf gives -inf throughout.
+ */
+void oracle_log_softmax(const float *x, float *y, int M, int V)
+{
+    static const int masks[6] = {32, 16, 8, 4, 2, 1};
+#pragma omp parallel for schedule(dynamic)
+    for (int row = 0; row < M; ++row) {
+        const float *xr = x + (size_t)row * V;
+        float *yr = y + (size_t)row * V;
+        float m = -INFINITY;
+        for (int i = 0; i < V; ++i) if (xr[i] > m) m = xr[i];
+        float lane[1024];
+        for (int t = 0; t < 1024; ++t) {
+            float a = 0.0f;
+            for (int i = t; i < V; i += 1024) a = a + oracle_exp(xr[i] - m);
+            lane[t] = a;
+        }
+        float sum = 0.0f;
+        for (int w = 0; w < 16; ++w) {
+            float ws = xor_butterfly(lane + 64 * w, 64, masks, 6);
+            sum = (w == 0) ? ws : sum + ws;
+        }
+        int none = (m == -INFINITY);
+        float ls = oracle_log(sum);
+        for (int i = 0; i < V; ++i) yr[i] = none ? -INFINITY : (xr[i] - m) - ls;
+    }
+}

@@ -522,6 +522,40 @@ def test_argmax_and_embed():
     assert torch.equal(out.cpu().view(torch.int16), table[ids.long()].view(torch.int16))
 
 
+@pytest.mark.parametrize("M,V", [(1, 1), (3, 7), (5, 1000), (2, 4097), (64, 128256)])
+def test_log_softmax_bitwise_oracle_and_batch_invariant(M, V):
+    x = synth.normal((M, V), seed=M * 7 + V, std=3.0)
+    if V > 8:
+        x[0, 3] = float("-inf")       # a masked entry
+        x[-1, :V // 2] += 40.0        # large logits: the maximum comes out first
+    xd = x.to(dev())
+    y = torch.empty_like(xd)
+    L.bi_log_softmax(xd, y)
+    ref = oracle.log_softmax(x)
+    assert bits_equal(to_np(y), ref), mismatch_report(to_np(y), ref)
+    # each row alone equals its row in the batch
+    for r in range(min(M, 4)):
+        yr = torch.empty((1, V), device=dev())
+        L.bi_log_softmax(xd[r:r + 1].contiguous(), yr)
+        assert bits_equal(to_np(yr)[0], to_np(y)[r])
+    # in place
+    L.bi_log_softmax(xd, xd)
+    assert bits_equal(to_np(xd), ref)
+
+
+def test_log_softmax_masked_rows_and_overlap_check():
+    x = torch.full((2, 300), float("-inf"))
+    x[1, 17] = 2.5
+    xd = x.to(dev())
+    y = torch.empty_like(xd)
+    L.bi_log_softmax(xd, y)
+    got = to_np(y)
+    assert np.all(got[0] == -np.inf) and got[1, 17] == 0.0 and np.sum(got[1] == -np.inf) == 299
+    big = torch.zeros((3, 300), device=dev())
+    with pytest.raises(L.BiError):
+        L.bi_log_softmax(big[:2], big[1:])   # partial overlap is refused
+
+
 # ---------------------------------------------------------------------------
 # fail-closed argument checks
 # ---------------------------------------------------------------------------

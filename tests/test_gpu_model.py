@@ -195,6 +195,34 @@ def test_engine_logits_match_oracle_model():
         assert e <= max(2e-3, 2.0 * s), f"step {i}: rel err {e} vs order spread {s}"
 
 
+def test_logprobs_prefill_equal_decode():
+    """Logprobs of position p: from the last row of a prefill chunk ending at
+    p, and from a decode step at p after a prefill of the rest -- one kernel
+    for both ("Mathematically equivalent is not bitwise equivalent"), so the
+    rows agree bit for bit, whatever the chunk cuts before p."""
+    cfg = SMALL
+    eng, _ = _engine(cfg, seed=21)
+    rng = np.random.default_rng(22)
+    pages = [int(p) for p in rng.permutation(512)[:8]]
+    prompt = [int(t) for t in synth.token_ids(75, cfg.vocab, seed=23)]
+    rows = []
+    for cuts in ([75], [40, 35], [74, 1], [10, 64, 1]):
+        p0, last = 0, None
+        for n in cuts:
+            out = eng.step([Segment(pages=pages, pos0=p0, tokens=prompt[p0:p0 + n],
+                                    want_logits=True)])
+            last = out.logits[0:1].contiguous()
+            p0 += n
+        lp = torch.empty_like(last)
+        L.bi_log_softmax(last, lp)
+        rows.append(to_np(lp)[0])
+    for r in rows[1:]:
+        assert bits_equal(r, rows[0])
+    assert abs(np.exp(rows[0].astype(np.float64)).sum() - 1.0) < 1e-5
+    # and it is the oracle's log-softmax of the same logits, bit for bit
+    assert bits_equal(rows[0], oracle.log_softmax(last.cpu().numpy())[0])
+
+
 # ---------------------------------------------------------------------------
 # schedule fuzzing on the GPU engine
 # ---------------------------------------------------------------------------

@@ -487,3 +487,93 @@ def test_attention_bound_covers_weight_rounding_and_catches_a_dropped_key():
     c = oracle.decode_attn(q, kp, vp, place.block_table, short, h_kv, ps, chunk, scale, False,
                            p_bf16=True)
     assert np.any(np.abs(c[0] - a[0]) > bound[0])
+
+
+# --------------------------------------------------------------------------
+# log and log-softmax (logprobs)
+# --------------------------------------------------------------------------
+
+def _ulps(a, b):
+    """Distance in binary32 ulps between fp32 arrays a and b (same sign)."""
+    ia = np.asarray(a, np.float32).view(np.int32).astype(np.int64)
+    ib = np.asarray(b, np.float32).view(np.int32).astype(np.int64)
+    return np.abs(ia - ib)
+
+
+def test_log_within_two_ulps_of_fp64():
+    rng = np.random.default_rng(31)
+    x = np.exp(rng.uniform(-87.0, 88.0, 200000)).astype(np.float32)
+    x = x[(x > 0) & np.isfinite(x) & (x >= np.finfo(np.float32).tiny)]
+    x = np.concatenate([x, np.float32([1.0, 2.0, 0.5, 3.0, 1.4142135, 1.4142137, 0.70710677,
+                                       np.finfo(np.float32).tiny, np.finfo(np.float32).max])])
+    got = oracle.log(x)
+    ref = np.log(x.astype(np.float64)).astype(np.float32)
+    # near log = 0 the ulp scale shrinks; compare there in absolute terms
+    far = np.abs(ref) > 1e-3
+    assert _ulps(got[far], ref[far]).max() <= 2
+    assert np.abs(got[~far].astype(np.float64) - np.log(x[~far].astype(np.float64))).max() < 1e-9
+    assert oracle.log(np.float32([1.0]))[0] == 0.0
+    k = np.arange(-126, 128)
+    p = np.float32(2.0) ** k.astype(np.float32)
+    assert _ulps(oracle.log(p)[k != 0], (k[k != 0] * math.log(2.0)).astype(np.float32)).max() <= 1
+    assert np.isnan(oracle.log(np.float32([np.nan]))[0])
+    assert oracle.log(np.float32([np.inf]))[0] == np.inf
+
+
+def test_log_softmax_vs_fp64_and_closed_forms():
+    rng = np.random.default_rng(32)
+    x = (rng.standard_normal((4, 5003)) * 4.0).astype(np.float32)
+    y = oracle.log_softmax(x)
+    x64 = x.astype(np.float64)
+    ref = x64 - (x64.max(1, keepdims=True) +
+                 np.log(np.exp(x64 - x64.max(1, keepdims=True)).sum(1, keepdims=True)))
+    assert np.abs(y - ref).max() < 4e-6
+    # probabilities sum to one
+    assert np.abs(np.exp(y.astype(np.float64)).sum(1) - 1.0).max() < 1e-5
+    # one entry: log 1 = 0 exactly; two entries: -log(1 + e^(b - a))
+    assert np.all(oracle.log_softmax(np.float32([[3.5], [-7.0]])) == 0.0)
+    a, b = np.float32(1.25), np.float32(-0.5)
+    y2 = oracle.log_softmax(np.float32([[a, b]]))[0].astype(np.float64)
+    assert abs(y2[0] + math.log1p(math.exp(float(b) - float(a)))) < 3e-7
+    assert abs(y2[1] - (float(b) - float(a)) + math.log1p(math.exp(float(b) - float(a)))) < 3e-7
+    # large logits: the maximum is taken out before the exp (no overflow)
+    big = oracle.log_softmax(np.float32([[1000.0, 999.0, 998.0]]))[0]
+    ref3 = np.array([0.0, -1.0, -2.0]) - math.log(1 + math.exp(-1) + math.exp(-2))
+    assert np.all(np.isfinite(big)) and np.abs(big - ref3).max() < 1e-6
+    # masked entries: -inf stays -inf, a lone finite entry gets 0; all -inf: -inf
+    mm = oracle.log_softmax(np.float32([[-np.inf, 2.0, -np.inf], [-np.inf, -np.inf, -np.inf]]))
+    assert mm[0, 1] == 0.0 and mm[0, 0] == -np.inf and np.all(mm[1] == -np.inf)
+
+
+def test_log_softmax_sums_in_the_stated_order():
+    """The sum of exp runs lane-serially over the strided elements, then an
+    xor butterfly per 64 lanes, then the 16 wave sums in order: a row whose
+    terms straddle several lanes and waves reproduces bit for bit from the
+    oracle's own exp and log composed in that order in binary32."""
+    rng = np.random.default_rng(33)
+    x = (rng.standard_normal(20000) * 3.0).astype(np.float32)
+    m = x.max()
+    e = np.array([oracle.exp(float(np.float32(v - m))) for v in x], np.float32)
+    lane = np.zeros(1024, np.float32)
+    for t in range(1024):
+        a = np.float32(0.0)
+        for i in range(t, x.size, 1024):
+            a = np.float32(a + e[i])
+        lane[t] = a
+    waves = []
+    for w in range(16):
+        v = lane[64 * w:64 * w + 64].copy()
+        for msk in (32, 16, 8, 4, 2, 1):
+            v = np.float32(v + v[np.arange(64) ^ msk])
+        waves.append(v[0])
+    s = np.float32(waves[0])
+    for w in range(1, 16):
+        s = np.float32(s + waves[w])
+    ls = oracle.log(np.float32([s]))[0]
+    y = oracle.log_softmax(x[None, :])[0]
+    assert np.array_equal(y.view(np.int32), ((x - m) - ls).astype(np.float32).view(np.int32))
+    # and a serial sum of the same terms is a different binary32 value here
+    ser = np.float32(0.0)
+    for v in e:
+        ser = np.float32(ser + v)
+    assert ser != s
