@@ -223,6 +223,66 @@ def test_logprobs_prefill_equal_decode():
     assert bits_equal(rows[0], oracle.log_softmax(last.cpu().numpy())[0])
 
 
+PREFIX_CFG = replace(SMALL, kv_chunk=256)
+
+
+def _run(eng, pages, pos0, tokens, decode_steps, chunk=256):
+    """Prefill `tokens` from pos0 in chunks of at most `chunk` rows, then greedy
+    decode; returns the fp32 logit rows (last prefill row, then each step)."""
+    rows, p, toks = [], pos0, list(tokens)
+    for i in range(0, len(toks), chunk):
+        part = toks[i:i + chunk]
+        out = eng.step([Segment(pages=pages, pos0=p, tokens=part, want_logits=True)])
+        p += len(part)
+    rows.append(out.logits[0].cpu().numpy())
+    nxt = int(out.tokens[0])
+    for _ in range(decode_steps):
+        out = eng.step([Segment(pages=pages, pos0=p, tokens=[nxt], want_logits=True)])
+        rows.append(out.logits[0].cpu().numpy())
+        nxt, p = int(out.tokens[0]), p + 1
+    return rows
+
+
+@pytest.mark.parametrize("n_prefix", [1, 255, 256, 257, 4097])
+def test_prefix_reuse_bitwise_equal_to_recompute(n_prefix):
+    """Prefix caching under invariance: request B reuses the KV pages that
+    request A wrote for their shared prefix (whole pages shared, the partial
+    last page copied, as a copy-on-write cache does) and computes only its
+    own suffix from position n_prefix.  With chunks at absolute multiples of
+    C = 256, B's logits -- suffix prefill and decode steps -- equal B run from
+    scratch on fresh pages, bit for bit, for prefixes around the chunk edge."""
+    cfg = PREFIX_CFG
+    ps = cfg.page_size
+    w = init_weights(cfg, 31, dev(), source="synth")
+    total = n_prefix + 40 + 4
+    npg = (total + ps - 1) // ps
+    pool = KVPool(cfg, 3 * npg + 2, dev())
+    eng = Engine(cfg, w, pool, dev(), max_rows=256, max_pages_per_req=npg + 1)
+    prefix = [int(t) for t in synth.token_ids(n_prefix, cfg.vocab, seed=32)]
+    suf_a = [int(t) for t in synth.token_ids(30, cfg.vocab, seed=33)]
+    suf_b = [int(t) for t in synth.token_ids(40, cfg.vocab, seed=34)]
+    pages_a = list(range(0, npg))
+    pages_b = list(range(npg, 2 * npg))
+    pages_c = list(range(2 * npg, 3 * npg))
+    _run(eng, pages_a, 0, prefix + suf_a, 0)                       # A writes the prefix
+    full = n_prefix // ps
+    reuse = pages_a[:full] + pages_b[full:]
+    if n_prefix % ps:                                               # copy the partial page
+        for li in range(cfg.layers):
+            pool.k[li, reuse[full]] = pool.k[li, pages_a[full]]
+            pool.v[li, reuse[full]] = pool.v[li, pages_a[full]]
+    shared = _run(eng, reuse, n_prefix, suf_b, 4)                  # B on the shared prefix
+    alone = _run(eng, pages_c, 0, prefix + suf_b, 4)               # B from scratch
+    assert len(shared) == len(alone) == 5
+    for i, (a, b) in enumerate(zip(shared, alone)):
+        assert bits_equal(a, b), f"row {i}: {mismatch_report(a, b)}"
+    # the prefix's KV itself is bit-identical across the two requests
+    for li in range(cfg.layers):
+        ka = pool.k[li, pages_a[:full]].view(torch.int16)
+        kc = pool.k[li, pages_c[:full]].view(torch.int16)
+        assert torch.equal(ka, kc)
+
+
 # ---------------------------------------------------------------------------
 # schedule fuzzing on the GPU engine
 # ---------------------------------------------------------------------------
