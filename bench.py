@@ -55,7 +55,8 @@ def parse():
     ap.add_argument("--sweep", default="1,7,32", help="extra batch sizes ('' for none)")
     ap.add_argument("--only", default="",
                     help="time one kernel of the step instead (decode_attn, gemm_qkv, ..., "
-                         "'log_softmax' for logprobs of the batch's logits, or 'copy' for a "
+                         "'log_softmax' / 'sample' for logprobs / seeded draws over the batch's "
+                         "logits, or 'copy' for a "
                          "plain 1 GiB device copy), e.g. under rocprofv3 --pmc")
     ap.add_argument("--twin", action="store_true", help="with --only: the twin's kernel")
     ap.add_argument("--launches", type=int, default=50)
@@ -410,6 +411,17 @@ def only_kernel(args, torch, dev):
         y = torch.empty_like(x)
         fn, alg = (lambda: _lib.bi_log_softmax(x, y)), 2 * 4 * args.batch * V
         label = f"log_softmax, batch {args.batch}"
+    elif args.only == "sample":
+        # seeded Gumbel-max draw per row over fp32 logits [batch, vocab]
+        from invariant_bi_rmsnorm_amd import _lib
+        V = model_config(args).vocab
+        x = torch.empty((args.batch, V), device=dev).normal_(std=3.0)
+        sd = torch.arange(args.batch, dtype=torch.int32, device=dev)
+        ps = torch.full((args.batch,), 1000, dtype=torch.int32, device=dev)
+        tp = torch.full((args.batch,), 0.8, dtype=torch.float32, device=dev)
+        out = torch.empty(args.batch, dtype=torch.int32, device=dev)
+        fn, alg = (lambda: _lib.bi_sample(x, sd, ps, tp, out)), 4 * args.batch * V
+        label = f"sample, batch {args.batch}"
     else:
         from invariant_bi_rmsnorm_amd.model import init_weights
         cfg = model_config(args)

@@ -302,6 +302,22 @@ bi_status bi_add(const void *a, const void *b, void *y, long n, int dtype, bi_st
  * a no-op), V >= 1; errors return BI_ERR_INVALID and launch nothing. */
 bi_status bi_log_softmax(const float *x, float *y, int M, int V, bi_stream stream);
 
+/* Seeded per-request sampling (Gumbel-max): out[i] = argmax_j of
+ * x[i][j] * (1 / T_i) + g_ij in binary64, g_ij = -log(-log(u_ij)),
+ * u_ij = (h_ij + 1/2) 2^-32, h_ij = MurmurHash3_x86_32 of the 8-byte key
+ * (pos[i], j) (two little-endian uint32) under seed[i]; lowest index on ties;
+ * T_i <= 0 gives the argmax of the row.  A request's draw depends only on its
+ * own logits, seed and position, never on the batch -- "Batch invariance and
+ * reproducible inference", "The weaker guarantees, which are usually enough"
+ * (per-request sampling determinism: noise from a 32-bit murmur hash of seed,
+ * position and column in float64).  log is the library's fixed binary64 log,
+ * so the oracle reproduces every draw.  x: device fp32 [M][V]; seed: device
+ * uint32 [M]; pos: device int32 [M] (the row's absolute position);
+ * temperature: device fp32 [M]; out: device int32 [M].  M >= 0 (0 is a no-op),
+ * V >= 1; errors return BI_ERR_INVALID and launch nothing. */
+bi_status bi_sample(const float *x, const uint32_t *seed, const int32_t *pos,
+                    const float *temperature, int32_t *out, int M, int V, bi_stream stream);
+
 /* SwiGLU: gu [M][2F] = [gate | up]; y[i][j] = round(g / (1 + exp(-g)) * u). */
 bi_status bi_silu_mul(const void *gu, void *y, int M, int F, int dtype, bi_stream stream);
 

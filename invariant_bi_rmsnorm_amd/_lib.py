@@ -46,6 +46,7 @@ SIGNATURES = {
     "bi_silu_mul": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _vp]),
     "bi_argmax": (_c_int, [_vp, _vp, _c_int, _c_int, _vp]),
     "bi_log_softmax": (_c_int, [_vp, _vp, _c_int, _c_int, _vp]),
+    "bi_sample": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _vp]),
     # batch-adaptive twins
     "bi_rmsnorm_free_workspace_bytes": (_c_size, [_c_int, _c_int]),
     "bi_rmsnorm_free": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_float, _c_int, _vp, _c_size,
@@ -248,6 +249,21 @@ def bi_log_softmax(x, y, stream=None):
                          f"{x.dtype} and {tuple(y.shape)} {y.dtype}")
     _check("bi_log_softmax", load().bi_log_softmax(_ptr(x), _ptr(y), M, V, _stream(stream)))
     return y
+
+
+def bi_sample(x, seed, pos, temperature, out, stream=None):
+    """Seeded Gumbel-max token per row.  seed: int32 tensor holding the uint32
+    seed bits; pos: int32; temperature: fp32 (<= 0: argmax); out: int32."""
+    M, V = x.shape
+    for t, dt, name in ((seed, torch.int32, "seed"), (pos, torch.int32, "pos"),
+                        (temperature, torch.float32, "temperature"), (out, torch.int32, "out")):
+        if t.dtype != dt or t.numel() != M:
+            raise ValueError(f"bi_sample: {name} must be {dt} with {M} entries")
+    if x.dtype != torch.float32:
+        raise ValueError("bi_sample: logits must be fp32")
+    _check("bi_sample", load().bi_sample(_ptr(x), _ptr(seed), _ptr(pos), _ptr(temperature),
+                                         _ptr(out), M, V, _stream(stream)))
+    return out
 
 
 def bi_argmax(x, idx, stream=None):

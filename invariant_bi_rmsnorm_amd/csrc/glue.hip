@@ -283,6 +283,113 @@ extern "C" bi_status bi_silu_mul(const void* gu, void* y, int M, int F, int dtyp
   return launched("bi_silu_mul");
 }
 
+// ---- seeded sampling ------------------------------------------------------
+// MurmurHash3_x86_32 (Appleby's public-domain definition) of the 8-byte key
+// (pos, col) as two little-endian 32-bit words, under a 32-bit seed.
+__device__ __forceinline__ uint32_t rotl32(uint32_t x, int r) { return (x << r) | (x >> (32 - r)); }
+__device__ __forceinline__ uint32_t murmur3_pos_col(uint32_t seed, uint32_t pos, uint32_t col) {
+  uint32_t h = seed;
+  uint32_t k = pos * 0xcc9e2d51u;
+  k = rotl32(k, 15) * 0x1b873593u;
+  h = rotl32(h ^ k, 13) * 5u + 0xe6546b64u;
+  k = col * 0xcc9e2d51u;
+  k = rotl32(k, 15) * 0x1b873593u;
+  h = rotl32(h ^ k, 13) * 5u + 0xe6546b64u;
+  h ^= 8u;
+  h ^= h >> 16;
+  h *= 0x85ebca6bu;
+  h ^= h >> 13;
+  h *= 0xc2b2ae35u;
+  h ^= h >> 16;
+  return h;
+}
+
+// Binary64 log fixed for the sampler, the binary32 log's method carried to
+// double: x = 2^e m, m in [sqrt(1/2), sqrt(2)], log m = 2 atanh(s) by its odd
+// series to s^23 (first omitted term below 2^-60 relative), then e ln 2 with
+// ln 2 split into a head whose last 21 mantissa bits are zero (e * head is
+// exact) and the binary64 tail.  Positive normal x only.
+__device__ __forceinline__ double log_fixed64(double x) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(x);
+  int e = (int)((b >> 52) & 0x7ffull) - 1023;
+  double m = __longlong_as_double((long long)((b & 0xfffffffffffffull) | 0x3ff0000000000000ull));
+  const bool big = m > 1.4142135623730951;
+  m = big ? 0.5 * m : m;
+  e = big ? e + 1 : e;
+  const double s = (m - 1.0) / (m + 1.0);
+  const double z = s * s;
+  double q = 1.0 / 23.0;
+  q = __builtin_fma(q, z, 1.0 / 21.0);
+  q = __builtin_fma(q, z, 1.0 / 19.0);
+  q = __builtin_fma(q, z, 1.0 / 17.0);
+  q = __builtin_fma(q, z, 1.0 / 15.0);
+  q = __builtin_fma(q, z, 1.0 / 13.0);
+  q = __builtin_fma(q, z, 1.0 / 11.0);
+  q = __builtin_fma(q, z, 1.0 / 9.0);
+  q = __builtin_fma(q, z, 1.0 / 7.0);
+  q = __builtin_fma(q, z, 1.0 / 5.0);
+  q = __builtin_fma(q, z, 1.0 / 3.0);
+  q = __builtin_fma(q, z, 1.0);
+  const double lm = (s + s) * q;
+  const double fe = (double)e;
+  return __builtin_fma(fe, 6.93147180369123816490e-01, __builtin_fma(fe, 1.90821492927058770002e-10, lm));
+}
+
+__device__ __forceinline__ void argbest64(double& v, int& i, double v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+}
+
+// Gumbel-max sampling per row: token = argmax_j (x_j * (1 / T) + g_j) in
+// binary64, g_j = -log(-log(u_j)), u_j = (h_j + 1/2) 2^-32 with h_j the hash
+// of (pos, j) under the row's seed; lowest index on ties; T <= 0: argmax of x.
+// A row's draw depends on its own logits, seed and position only.
+__global__ __launch_bounds__(1024) void k_sample_gumbel(const float* __restrict__ x,
+                                                        const uint32_t* __restrict__ seed,
+                                                        const int32_t* __restrict__ pos,
+                                                        const float* __restrict__ temp,
+                                                        int32_t* __restrict__ out, int V) {
+  const long row = blockIdx.x;
+  const float* xr = x + row * V;
+  const float T = temp[row];
+  const bool noise = T > 0.0f;
+  const double invT = noise ? 1.0 / (double)T : 1.0;
+  const uint32_t sd = seed[row], ps = (uint32_t)pos[row];
+  double bv = -__builtin_inf();
+  int bix = 0x7fffffff;
+  for (int j = threadIdx.x; j < V; j += 1024) {
+    double sc = (double)xr[j] * invT;
+    if (noise) {
+      const double u = ((double)murmur3_pos_col(sd, ps, (uint32_t)j) + 0.5) * 0x1p-32;
+      sc = sc + -log_fixed64(-log_fixed64(u));
+    }
+    argbest64(bv, bix, sc, j);
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    const double ov = __shfl_xor(bv, off);
+    const int oi = __shfl_xor(bix, off);
+    argbest64(bv, bix, ov, oi);
+  }
+  __shared__ double sv[16];
+  __shared__ int si[16];
+  if ((threadIdx.x & 63) == 0) { sv[threadIdx.x >> 6] = bv; si[threadIdx.x >> 6] = bix; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 16; ++w) argbest64(bv, bix, sv[w], si[w]);
+    out[row] = bix == 0x7fffffff ? 0 : bix;
+  }
+}
+
+extern "C" bi_status bi_sample(const float* x, const uint32_t* seed, const int32_t* pos,
+                               const float* temperature, int32_t* out, int M, int V,
+                               bi_stream stream) {
+  BI_REQUIRE(M >= 0 && V >= 1, BI_ERR_INVALID, "bi_sample: bad sizes M=%d V=%d", M, V);
+  if (M == 0) return BI_OK;
+  BI_REQUIRE(x && seed && pos && temperature && out, BI_ERR_INVALID, "bi_sample: null pointer");
+  hipLaunchKernelGGL(k_sample_gumbel, dim3(M), dim3(1024), 0, as_stream(stream), x, seed, pos,
+                     temperature, out, V);
+  return launched("bi_sample");
+}
+
 extern "C" bi_status bi_log_softmax(const float* x, float* y, int M, int V, bi_stream stream) {
   BI_REQUIRE(M >= 0 && V >= 1, BI_ERR_INVALID, "bi_log_softmax: bad sizes M=%d V=%d", M, V);
   if (M == 0) return BI_OK;

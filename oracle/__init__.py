@@ -56,6 +56,12 @@ def _load():
         "oracle_log": (ctypes.c_float, [ctypes.c_float]),
         "oracle_log_vec": (None, [_F, _F, ctypes.c_long]),
         "oracle_log_softmax": (None, [_F, _F, ctypes.c_int, ctypes.c_int]),
+        "oracle_murmur3_2w": (ctypes.c_uint32, [ctypes.c_uint32, ctypes.c_uint32,
+                                                ctypes.c_uint32]),
+        "oracle_log64_vec": (None, [ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_double), ctypes.c_long]),
+        "oracle_sample": (None, [_F, ctypes.POINTER(ctypes.c_uint32), _I, _F, _I,
+                                 ctypes.c_int, ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -244,3 +250,30 @@ def log_softmax(x) -> np.ndarray:
     y = np.empty_like(x)
     _load().oracle_log_softmax(_pf(x), _pf(y), M, V)
     return y
+
+
+def murmur3(seed: int, w0: int, w1: int) -> int:
+    """MurmurHash3_x86_32 of the key (w0, w1) as two little-endian uint32."""
+    return int(_load().oracle_murmur3_2w(seed & 0xffffffff, w0 & 0xffffffff, w1 & 0xffffffff))
+
+
+def log64(x) -> np.ndarray:
+    """The sampler's fixed binary64 log, elementwise."""
+    x = np.ascontiguousarray(np.atleast_1d(x), dtype=np.float64)
+    y = np.empty_like(x)
+    P = ctypes.POINTER(ctypes.c_double)
+    _load().oracle_log64_vec(x.ctypes.data_as(P), y.ctypes.data_as(P), x.size)
+    return y
+
+
+def sample(x, seed, pos, temperature) -> np.ndarray:
+    """Seeded Gumbel-max token per row (oracle.c: oracle_sample)."""
+    x = _f32(x)
+    M, V = x.shape
+    sd = np.ascontiguousarray(seed, dtype=np.uint32)
+    ps = _i32(pos)
+    tp = _f32(temperature)
+    out = np.empty(M, dtype=np.int32)
+    _load().oracle_sample(_pf(x), sd.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)), _pi(ps),
+                          _pf(tp), _pi(out), M, V)
+    return out

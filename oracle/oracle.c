@@ -588,3 +588,103 @@ void oracle_log_softmax(const float *x, float *y, int M, int V)
         for (int i = 0; i < V; ++i) yr[i] = none ? -INFINITY : (xr[i] - m) - ls;
     }
 }
+
+/* ------------------------------------------------------------------ */
+/* seeded sampling                                                     */
+/* ------------------------------------------------------------------ */
+
+/* MurmurHash3_x86_32 (Austin Appleby's public-domain definition) of the
+ * 8-byte key made of the two little-endian 32-bit words w0, w1. */
+static uint32_t rotl32(uint32_t x, int r) { return (x << r) | (x >> (32 - r)); }
+
+uint32_t oracle_murmur3_2w(uint32_t seed, uint32_t w0, uint32_t w1)
+{
+    const uint32_t c1 = 0xcc9e2d51u, c2 = 0x1b873593u;
+    uint32_t words[2] = {w0, w1};
+    uint32_t h = seed;
+    for (int i = 0; i < 2; ++i) {
+        uint32_t k = words[i];
+        k *= c1;
+        k = rotl32(k, 15);
+        k *= c2;
+        h ^= k;
+        h = rotl32(h, 13);
+        h = h * 5u + 0xe6546b64u;
+    }
+    h ^= 8u;                       /* key length in bytes */
+    h ^= h >> 16;
+    h *= 0x85ebca6bu;
+    h ^= h >> 13;
+    h *= 0xc2b2ae35u;
+    h ^= h >> 16;
+    return h;
+}
+
+/* Binary64 natural log for the sampler, fixed like the binary32 one: x =
+ * 2^e m, m in [sqrt(1/2), sqrt(2)], log m = 2 atanh(s), s = (m - 1)/(m + 1),
+ * by 2 s sum_{k=0..11} z^k / (2k + 1), z = s^2, Horner with fma (the first
+ * omitted term, z^12 / 25, is below 2^-60 relative); log x = fma(e, LN2H,
+ * fma(e, LN2L, log m)) with LN2H the binary64 value of ln 2 with its last 21
+ * mantissa bits cleared (e * LN2H exact) and LN2L = ln 2 - LN2H rounded.
+ * Positive normal x only. */
+double oracle_log64(double x)
+{
+    uint64_t b;
+    memcpy(&b, &x, 8);
+    int e = (int)((b >> 52) & 0x7ffu) - 1023;
+    uint64_t mb = (b & 0xfffffffffffffULL) | 0x3ff0000000000000ULL;
+    double m;
+    memcpy(&m, &mb, 8);
+    if (m > 1.4142135623730951) { m = 0.5 * m; e = e + 1; }
+    double s = (m - 1.0) / (m + 1.0);
+    double z = s * s;
+    double q = 1.0 / 23.0;
+    q = fma(q, z, 1.0 / 21.0);
+    q = fma(q, z, 1.0 / 19.0);
+    q = fma(q, z, 1.0 / 17.0);
+    q = fma(q, z, 1.0 / 15.0);
+    q = fma(q, z, 1.0 / 13.0);
+    q = fma(q, z, 1.0 / 11.0);
+    q = fma(q, z, 1.0 / 9.0);
+    q = fma(q, z, 1.0 / 7.0);
+    q = fma(q, z, 1.0 / 5.0);
+    q = fma(q, z, 1.0 / 3.0);
+    q = fma(q, z, 1.0);
+    double lm = (s + s) * q;
+    double fe = (double)e;
+    return fma(fe, 6.93147180369123816490e-01, fma(fe, 1.90821492927058770002e-10, lm));
+}
+
+void oracle_log64_vec(const double *x, double *y, long n)
+{
+    for (long i = 0; i < n; ++i) y[i] = oracle_log64(x[i]);
+}
+
+/* Gumbel-max draw per row ("Batch invariance and reproducible inference",
+ * "The weaker guarantees, which are usually enough": noise from a 32-bit
+ * murmur hash of (seed, position, column) in float64): score_j =
+ * x_j * (1 / T) + (-log(-log(u_j))), u_j = (hash(seed; pos, j) + 1/2) 2^-32,
+ * all in binary64; the token is the first j with the largest score.  T <= 0:
+ * the argmax of x. */
+void oracle_sample(const float *x, const uint32_t *seed, const int32_t *pos, const float *temp,
+                   int32_t *out, int M, int V)
+{
+#pragma omp parallel for schedule(dynamic)
+    for (int row = 0; row < M; ++row) {
+        const float *xr = x + (size_t)row * V;
+        int noise = temp[row] > 0.0f;
+        double invT = noise ? 1.0 / (double)temp[row] : 1.0;
+        double best = -INFINITY;
+        int bi = -1;
+        for (int j = 0; j < V; ++j) {
+            double sc = (double)xr[j] * invT;
+            if (noise) {
+                uint32_t h = oracle_murmur3_2w(seed[row], (uint32_t)pos[row], (uint32_t)j);
+                double u = ((double)h + 0.5) * 0x1p-32;
+                sc = sc + -oracle_log64(-oracle_log64(u));
+            }
+            if (bi < 0 || sc > best) { best = sc; bi = j; }
+        }
+        out[row] = bi < 0 ? 0 : bi;
+    }
+}

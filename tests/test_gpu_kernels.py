@@ -556,6 +556,32 @@ def test_log_softmax_masked_rows_and_overlap_check():
         L.bi_log_softmax(big[:2], big[1:])   # partial overlap is refused
 
 
+@pytest.mark.parametrize("M,V", [(1, 5), (8, 1000), (64, 128256)])
+def test_sample_equals_oracle_and_is_batch_invariant(M, V):
+    x = synth.normal((M, V), seed=M + V, std=2.0)
+    seed = torch.from_numpy(synth.uniform_lengths(M, 0, 2**31 - 1, seed=M).astype(np.int32))
+    seed[0] = -5                      # seed bits 0xfffffffb
+    pos = torch.from_numpy(synth.uniform_lengths(M, 0, 100000, seed=M + 1).astype(np.int32))
+    temp = torch.tensor([0.0 if r % 5 == 4 else 0.5 + 0.25 * (r % 4) for r in range(M)],
+                        dtype=torch.float32)
+    xd, sd, pd, td = x.to(dev()), seed.to(dev()), pos.to(dev()), temp.to(dev())
+    out = torch.empty(M, dtype=torch.int32, device=dev())
+    L.bi_sample(xd, sd, pd, td, out)
+    ref = oracle.sample(x.numpy(), seed.numpy().view(np.uint32), pos.numpy(), temp.numpy())
+    assert np.array_equal(out.cpu().numpy(), ref)
+    # a row alone draws the same token
+    for r in range(min(M, 6)):
+        o1 = torch.empty(1, dtype=torch.int32, device=dev())
+        L.bi_sample(xd[r:r + 1].contiguous(), sd[r:r + 1], pd[r:r + 1], td[r:r + 1], o1)
+        assert int(o1[0]) == int(out[r])
+    # temperature 0 is the argmax
+    am = torch.empty(M, dtype=torch.int32, device=dev())
+    L.bi_argmax(xd, am)
+    zero = torch.zeros(M, dtype=torch.float32, device=dev())
+    L.bi_sample(xd, sd, pd, zero, out)
+    assert torch.equal(out, am)
+
+
 # ---------------------------------------------------------------------------
 # fail-closed argument checks
 # ---------------------------------------------------------------------------

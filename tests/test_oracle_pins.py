@@ -577,3 +577,61 @@ def test_log_softmax_sums_in_the_stated_order():
     for v in e:
         ser = np.float32(ser + v)
     assert ser != s
+
+
+# --------------------------------------------------------------------------
+# seeded sampling
+# --------------------------------------------------------------------------
+
+def test_murmur3_matches_library_routine():
+    import struct as st
+    from sklearn.utils import murmurhash3_32
+    rng = np.random.default_rng(41)
+    for _ in range(2000):
+        seed, w0, w1 = (int(v) for v in rng.integers(0, 2**32, 3, dtype=np.uint64))
+        ref = murmurhash3_32(st.pack("<II", w0, w1), seed=seed, positive=True)
+        assert oracle.murmur3(seed, w0, w1) == ref
+    assert oracle.murmur3(0, 0, 0) == murmurhash3_32(b"\0" * 8, seed=0, positive=True)
+
+
+def test_log64_within_two_ulps_of_math_log():
+    rng = np.random.default_rng(42)
+    x = np.exp(rng.uniform(-700.0, 700.0, 100000))
+    x = np.concatenate([x, [1.0, 2.0, 0.5, 2.0 ** -32 * 0.5, 1.0 - 2.0 ** -33, 22.9]])
+    got = oracle.log64(x)
+    ref = np.array([math.log(v) for v in x])
+    far = np.abs(ref) > 1e-3
+    ulp = np.abs(got[far].view(np.int64) - ref[far].view(np.int64))
+    assert ulp.max() <= 2 and np.mean(ulp > 0) < 1e-3
+    assert np.abs(got[~far] - ref[~far]).max() < 1e-18
+    assert oracle.log64(np.array([1.0]))[0] == 0.0
+
+
+def test_sample_distribution_and_limits():
+    """Draws over many positions follow softmax(x / T) (a sign or temperature
+    slip fails the chi-square bound), T -> 0+ and T <= 0 give the argmax, and a
+    draw depends on (seed, position) only."""
+    logits = np.float32([[1.0, 0.0, -1.0, 2.0, 0.5]])
+    T = 0.7
+    n = 20000
+    x = np.repeat(logits, n, axis=0)
+    toks = oracle.sample(x, np.full(n, 1234, np.uint32), np.arange(n), np.full(n, T, np.float32))
+    p = np.exp(logits[0] / T)
+    p /= p.sum()
+    cnt = np.bincount(toks, minlength=5)
+    chi2 = float(((cnt - n * p) ** 2 / (n * p)).sum())
+    assert chi2 < 20.5           # 4 degrees of freedom, p ~ 4e-4
+    am = int(np.argmax(logits[0]))
+    assert np.all(oracle.sample(x[:50], np.arange(50), np.arange(50),
+                                np.full(50, 1e-6, np.float32)) == am)
+    assert np.all(oracle.sample(x[:5], np.arange(5), np.arange(5), np.zeros(5, np.float32)) == am)
+    # same seed and position, same token; other seeds scatter
+    a = oracle.sample(x[:1], [7], [9], [1.0])
+    assert np.all(oracle.sample(np.repeat(logits, 8, 0), np.full(8, 7), np.full(8, 9),
+                                np.ones(8, np.float32)) == a[0])
+    assert len(set(oracle.sample(np.repeat(logits, 64, 0), np.arange(64), np.full(64, 9),
+                                 np.ones(64, np.float32)).tolist())) > 1
+    # masked entries are never drawn
+    xm = np.repeat(np.float32([[0.0, -np.inf, 0.0]]), 500, 0)
+    assert not np.any(oracle.sample(xm, np.arange(500), np.arange(500),
+                                    np.ones(500, np.float32)) == 1)
