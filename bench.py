@@ -60,6 +60,12 @@ def parse():
                          "plain 1 GiB device copy), e.g. under rocprofv3 --pmc")
     ap.add_argument("--twin", action="store_true", help="with --only: the twin's kernel")
     ap.add_argument("--launches", type=int, default=50)
+    ap.add_argument("--dvr", action="store_true",
+                    help="decode-verify-rollback (twins decode, invariant kernels verify) "
+                         "against greedy decoding on each engine alone; eager steps")
+    ap.add_argument("--dvr-new", type=int, default=256, help="with --dvr: tokens per request")
+    ap.add_argument("--dvr-window", type=int, default=64)
+    ap.add_argument("--dvr-group", type=int, default=8)
     ap.add_argument("--traffic-summary", default="",
                     help="summarise rocprofv3 --pmc runs (FETCH_SIZE / WRITE_SIZE of --only "
                          "decode_attn and of --only copy) found under this directory")
@@ -459,6 +465,68 @@ def only_kernel(args, torch, dev):
     print(json.dumps(out), flush=True)
 
 
+def dvr_compare(args, torch, dev):
+    """Decode-verify-rollback ("LLM-42", "The Decode-Verify-Rollback
+    Protocol") with the twins as the fast path and the invariant kernels as
+    the verifier, against greedy decoding on the invariant kernels alone and
+    on the twins alone: the same prompts, eager steps for all three (host
+    launch time included alike), tokens per second over the generated tokens
+    after the prompts' prefill."""
+    import synth
+    from invariant_bi_rmsnorm_amd import harness as H
+    from invariant_bi_rmsnorm_amd.model import Engine, KVPool, init_weights
+    cfg = model_config(args)
+    B, new, win, grp = args.batch if args.batch != 64 else 8, args.dvr_new, args.dvr_window, \
+        args.dvr_group
+    w = init_weights(cfg, args.seed + 14, dev, source="device")
+    lens = synth.uniform_lengths(B, 256, 1024, seed=args.seed + 21)
+    prompts = [[int(t) for t in synth.token_ids(int(n), cfg.vocab, seed=args.seed + 100 + r)]
+               for r, n in enumerate(lens)]
+    per = (int(lens.max()) + new + win + cfg.page_size) // cfg.page_size + 1
+    pool = KVPool(cfg, B * per, dev)
+    pages = [list(range(r * per, (r + 1) * per)) for r in range(B)]
+    chunk = 512
+    rows = max(B * chunk, grp * win, B)
+    inv = Engine(cfg, w, pool, dev, max_rows=rows, max_pages_per_req=per)
+    fast = Engine(cfg, w, pool, dev, max_rows=rows, max_pages_per_req=per, free=True)
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        out = fn()
+        torch.cuda.synchronize()
+        return out, time.perf_counter() - t0
+
+    def prefill_time(engine):
+        return timed(lambda: H._prefill(engine, prompts, pages, chunk))[1]
+
+    # warm both engines (kernel attributes, workspaces) on a short run
+    H.greedy_decode(inv, prompts, pages, 4, chunk=chunk)
+    H.decode_verify_rollback(fast, inv, prompts, pages, 4, window=2, group=grp, chunk=chunk)
+    res = {}
+    ref, t = timed(lambda: H.greedy_decode(inv, prompts, pages, new, chunk=chunk))
+    res["invariant"] = t - prefill_time(inv)
+    fast_seq, t = timed(lambda: H.greedy_decode(fast, prompts, pages, new, chunk=chunk))
+    res["twins"] = t - prefill_time(fast)
+    (dvr_seq, st), t = timed(lambda: H.decode_verify_rollback(fast, inv, prompts, pages, new,
+                                                              window=win, group=grp,
+                                                              chunk=chunk))
+    res["dvr"] = t - prefill_time(inv)
+    toks = B * (new - 1)
+    line = {
+        "mode": "decode-verify-rollback", "batch": B, "prompt_lens": [int(v) for v in lens],
+        "new_tokens": new, "window": win, "verify_group": grp, "steps": "eager",
+        "tokens_per_s": {k: round(toks / v, 1) for k, v in res.items()},
+        "dvr_vs_invariant_pct": round(100.0 * (res["dvr"] / res["invariant"] - 1.0), 1),
+        "dvr_equals_invariant_greedy": dvr_seq == ref,
+        "twins_equal_invariant_greedy": fast_seq == ref,
+        "windows": st.windows, "mismatched_windows": st.mismatches,
+        "discarded_candidates": st.discarded, "fast_steps": st.fast_steps,
+        "verify_launches": st.verify_steps,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def _rounded(d):
     return {k: (round(v, 3) if isinstance(v, float) else v) for k, v in d.items()}
 
@@ -482,6 +550,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.only:
         only_kernel(args, torch, dev)
+        return
+    if args.dvr:
+        dvr_compare(args, torch, dev)
         return
     cfg = model_config(args)
     w = init_weights(cfg, args.seed + 14, dev, source="device")

@@ -342,3 +342,121 @@ class EngineBackend:
     def _idx(self, pages):
         import torch
         return torch.tensor(pages, dtype=torch.long, device=self.e.pool.k.device)
+
+
+# ---------------------------------------------------------------------------
+# decode-verify-rollback over the twins
+# ---------------------------------------------------------------------------
+# "LLM-42: ... verified speculation", "The Decode-Verify-Rollback Protocol":
+# decode a window of tokens on the fast, batch-adaptive path; replay the
+# window under the fixed reduction schedule in verify batches of a few
+# requests; commit the candidates up to the first one the replay disagrees
+# with, plus the replay's own token there, and resume decoding from it.  Here
+# the fast path is an engine on the twins and the verifier an engine on the
+# invariant kernels, over one shared KV pool: the replay is a prefill of the
+# window (every row's logits) that also rewrites the window's KV with the
+# invariant values, so every committed token equals greedy decoding on the
+# invariant kernels alone.
+
+@dataclass
+class DvrStats:
+    windows: int = 0          # windows verified (per request)
+    verify_steps: int = 0     # verifier launches (groups of requests)
+    fast_steps: int = 0       # decode steps on the fast path
+    committed: int = 0        # tokens committed after verification
+    mismatches: int = 0       # windows cut at a disagreeing token
+    discarded: int = 0        # fast candidates thrown away by rollbacks
+
+
+def _prefill(engine, prompts, pages, chunk):
+    """Prefill every prompt (chunks of at most `chunk` rows per request);
+    returns the argmax token after each prompt."""
+    firsts = [None] * len(prompts)
+    done = [0] * len(prompts)
+    while any(d < len(p) for d, p in zip(done, prompts)):
+        segs, who = [], []
+        for r, p in enumerate(prompts):
+            if done[r] < len(p):
+                n = min(chunk, len(p) - done[r])
+                segs.append(_seg(pages[r], done[r], p[done[r]:done[r] + n]))
+                who.append((r, done[r] + n == len(p)))
+                done[r] += n
+        out = engine.step(segs)
+        toks = out.tokens.cpu().numpy()
+        for k, si in enumerate(out.seg_index):
+            r, last = who[si]
+            if last:
+                firsts[r] = int(toks[k])
+    return firsts
+
+
+def _seg(pages, pos0, tokens, all_logits=False):
+    from .model import Segment
+    return Segment(pages=pages, pos0=pos0, tokens=list(tokens), want_logits=True,
+                   all_logits=all_logits)
+
+
+def greedy_decode(engine, prompts, pages, max_new, chunk=256):
+    """Greedy generation on one engine: all live requests decode together."""
+    seqs = [[t] for t in _prefill(engine, prompts, pages, chunk)]
+    while True:
+        live = [r for r in range(len(prompts)) if len(seqs[r]) < max_new]
+        if not live:
+            return seqs
+        segs = [_seg(pages[r], len(prompts[r]) + len(seqs[r]) - 1, [seqs[r][-1]]) for r in live]
+        out = engine.step(segs)
+        toks = out.tokens.cpu().numpy()
+        for k, si in enumerate(out.seg_index):
+            seqs[live[si]].append(int(toks[k]))
+
+
+def decode_verify_rollback(fast, verifier, prompts, pages, max_new, window=64, group=8,
+                           chunk=256):
+    """Generate max_new tokens per request by decode-verify-rollback.  `fast`
+    and `verifier` are engines over the same KV pool; `pages[r]` must hold
+    len(prompts[r]) + max_new + window positions.  Returns (tokens, DvrStats)."""
+    st = DvrStats()
+    seqs = [[t] for t in _prefill(verifier, prompts, pages, chunk)]
+    n = len(prompts)
+    while True:
+        live = [r for r in range(n) if len(seqs[r]) < max_new]
+        if not live:
+            return seqs, st
+        # decode: a window of candidates for every live request, batched
+        want = {r: min(window, max_new - len(seqs[r])) for r in live}
+        cand = {r: [] for r in live}
+        for step in range(max(want.values())):
+            act = [r for r in live if len(cand[r]) < want[r]]
+            segs = []
+            for r in act:
+                ctx = seqs[r] + cand[r]
+                segs.append(_seg(pages[r], len(prompts[r]) + len(ctx) - 1, [ctx[-1]]))
+            out = fast.step(segs)
+            st.fast_steps += 1
+            toks = out.tokens.cpu().numpy()
+            for k, si in enumerate(out.seg_index):
+                cand[act[si]].append(int(toks[k]))
+        # verify: replay each window (the last committed token, then all but
+        # the last candidate) in groups, every row's logits
+        for g0 in range(0, len(live), group):
+            grp = live[g0:g0 + group]
+            segs = [_seg(pages[r], len(prompts[r]) + len(seqs[r]) - 1,
+                         [seqs[r][-1]] + cand[r][:-1], all_logits=True) for r in grp]
+            out = verifier.step(segs)
+            st.verify_steps += 1
+            toks = out.tokens.cpu().numpy()
+            rows = {}
+            for k, si in enumerate(out.seg_index):
+                rows.setdefault(si, []).append(int(toks[k]))
+            for si, r in enumerate(grp):
+                ver = rows[si]
+                st.windows += 1
+                cut = next((i for i, (c, v) in enumerate(zip(cand[r], ver)) if c != v), None)
+                if cut is None:
+                    seqs[r].extend(cand[r])
+                    st.committed += len(cand[r])
+                else:
+                    seqs[r].extend(cand[r][:cut] + [ver[cut]])
+                    st.committed += cut + 1
+                    st.mismatches += 1
+                    st.discarded += len(cand[r]) - cut

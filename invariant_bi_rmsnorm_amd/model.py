@@ -143,13 +143,14 @@ class Segment:
     pos0: int
     tokens: list
     want_logits: bool = True   # logits of the segment's last row
+    all_logits: bool = False   # logits of every row (a verifier's replay)
 
 
 @dataclass
 class StepOutput:
-    logits: torch.Tensor       # [n_segments_with_logits, vocab] fp32 (device)
+    logits: torch.Tensor       # [wanted rows, vocab] fp32 (device), packed order
     tokens: torch.Tensor       # argmax of each logits row (device int32)
-    seg_index: list = field(default_factory=list)
+    seg_index: list = field(default_factory=list)   # the segment of each row
 
 
 class Engine:
@@ -217,12 +218,15 @@ class Engine:
                 [len(s.tokens) for s in pre])]).astype(np.int32) - len(dec),
             "pos0_pre": np.array([s.pos0 for s in pre], np.int32),
         }
-        # rows whose logits are wanted: last row of each segment (packed order)
+        # rows whose logits are wanted: the last row of each segment, or every
+        # row of a segment that asks for all (packed order)
         want, row = [], 0
         for k, s in enumerate(dec + pre):
+            if s.all_logits:
+                want.extend((order[k], row + j) for j in range(len(s.tokens)))
+            elif s.want_logits:
+                want.append((order[k], row + len(s.tokens) - 1))
             row += len(s.tokens)
-            if s.want_logits:
-                want.append((order[k], row - 1))
         meta["want"] = want
         return meta
 

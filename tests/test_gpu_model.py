@@ -283,6 +283,28 @@ def test_prefix_reuse_bitwise_equal_to_recompute(n_prefix):
         assert torch.equal(ka, kc)
 
 
+def test_decode_verify_rollback_on_twins_commits_invariant_greedy():
+    """Decode-verify-rollback with the twins as the fast path and the
+    invariant kernels as the verifier (one shared KV pool): the committed
+    tokens equal greedy decoding on the invariant kernels alone."""
+    cfg = SMALL
+    w = init_weights(cfg, 41, dev(), source="synth")
+    pool = KVPool(cfg, 512, dev())
+    inv = Engine(cfg, w, pool, dev(), max_rows=256, max_pages_per_req=64)
+    fast = Engine(cfg, w, pool, dev(), max_rows=256, max_pages_per_req=64, free=True)
+    rng = np.random.default_rng(42)
+    n, max_new, window = 6, 80, 16
+    prompts = [[int(t) for t in synth.token_ids(int(rng.integers(5, 150)), cfg.vocab,
+                                                seed=300 + r)] for r in range(n)]
+    pages = [list(range(r * 16, r * 16 + 16)) for r in range(n)]   # 256 positions each
+    ref = H.greedy_decode(inv, prompts, pages, max_new, chunk=40)
+    out, st = H.decode_verify_rollback(fast, inv, prompts, pages, max_new, window=window,
+                                       group=4, chunk=40)
+    assert out == ref
+    assert st.committed == n * (max_new - 1) and st.windows >= n * ((max_new - 1) // window)
+    print("dvr stats:", st)
+
+
 # ---------------------------------------------------------------------------
 # schedule fuzzing on the GPU engine
 # ---------------------------------------------------------------------------

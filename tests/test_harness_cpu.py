@@ -139,3 +139,70 @@ def test_report_write_is_atomic(tmp_path):
     with open(p) as f:
         assert json.load(f) == {"verdict": "RED", "n": 2}
     assert [x for x in os.listdir(os.path.dirname(p)) if x.endswith(".tmp")] == []
+
+
+# ---------------------------------------------------------------------------
+# decode-verify-rollback (protocol logic on mock engines)
+# ---------------------------------------------------------------------------
+
+class MockEngine:
+    """Engine-shaped mock over a shared token store: the value at position p
+    hashes the token at p with the value at p - 1, and a row's next token is
+    that value mod V.  noise > 0 makes it a 'fast path': with that
+    probability (drawn from the position, the batch size and a step counter)
+    a row's token is bumped by one -- a batch-dependent flip."""
+
+    V = 50
+
+    def __init__(self, store, noise=0.0):
+        self.store, self.noise, self.steps = store, noise, 0
+
+    def _h(self, *vals):
+        d = hashlib.blake2b(repr(vals).encode(), digest_size=8).digest()
+        return int.from_bytes(d, "little")
+
+    def step(self, segs):
+        import torch
+        from invariant_bi_rmsnorm_amd.model import StepOutput
+        self.steps += 1
+        order = [i for i, s in enumerate(segs) if len(s.tokens) == 1] + \
+                [i for i, s in enumerate(segs) if len(s.tokens) > 1]
+        toks, seg_index = [], []
+        for i in order:
+            s = segs[i]
+            key = tuple(s.pages)
+            for j, t in enumerate(s.tokens):
+                p = s.pos0 + j
+                prev = self.store.get((key, p - 1), 0)
+                self.store[(key, p)] = self._h(t, prev)
+                if s.all_logits or (s.want_logits and j == len(s.tokens) - 1):
+                    tok = self.store[(key, p)] % self.V
+                    if self.noise and (self._h(p, len(segs), self.steps) % 1000) < 1000 * self.noise:
+                        tok = (tok + 1) % self.V
+                    toks.append(tok)
+                    seg_index.append(i)
+        t = torch.tensor(toks, dtype=torch.int32)
+        return StepOutput(torch.zeros((len(toks), 1)), t, seg_index)
+
+
+@pytest.mark.parametrize("noise,window,group", [(0.0, 8, 2), (0.05, 8, 2), (0.3, 5, 3),
+                                                (0.05, 64, 8)])
+def test_decode_verify_rollback_commits_the_verifier_sequence(noise, window, group):
+    rng = np.random.default_rng(7)
+    prompts = [list(rng.integers(0, 50, int(rng.integers(1, 30)))) for _ in range(6)]
+    pages = [[1000 + r] for r in range(6)]          # one 'page' list per request
+    ref = H.greedy_decode(MockEngine({}), prompts, pages, max_new=70, chunk=7)
+    store = {}
+    out, st = H.decode_verify_rollback(MockEngine(store, noise), MockEngine(store), prompts,
+                                       pages, max_new=70, window=window, group=group, chunk=7)
+    assert [o[:70] for o in out] == [r[:70] for r in ref]
+    assert all(len(o) == 70 for o in out)
+    if noise == 0.0:
+        assert st.mismatches == 0 and st.discarded == 0
+    else:
+        assert st.mismatches > 0 and st.discarded > 0
+    assert st.committed == sum(len(o) - 1 for o in out)
+    # the fast path alone does drift from the verifier's sequence
+    if noise >= 0.05:
+        fast_only = H.greedy_decode(MockEngine({}, noise), prompts, pages, max_new=70, chunk=7)
+        assert fast_only != ref
