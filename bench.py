@@ -592,6 +592,10 @@ def main():
         "invariance_overhead_pct": round(res["invariance_overhead_pct"], 2),
         "twin_tokens_per_s": round(res["free"]["tokens_per_s"], 1),
         "graph": res["inv"]["graph"], "graph_matches_eager": res["inv"]["graph_matches_eager"],
+        "per_kernel_note": "HIP event pairs around each launch of 20 eager steps, a device "
+                           "spin ahead of each start event; each pair adds its own cost of a "
+                           "few us, so short kernels read high (profiles/ has their "
+                           "kernel-trace durations)",
         "per_kernel": {k: _rounded(v) for k, v in per.items()},
         "per_kernel_twin": {k: _rounded(v) for k, v in per_free.items()},
     }
