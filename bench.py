@@ -185,7 +185,7 @@ def per_kernel_times(eng, meta, steps, torch):
 
     def timer(name, fn):
         if spin is not None:
-            spin(200000)
+            spin(600000)   # ~250 us: the host is well ahead when the events land
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
