@@ -408,21 +408,22 @@ static void launch_small_k(const void* A, const void* W, void* C, int M, int N, 
 
 // Rows (8 MB) and 16-column strips (CT) per workgroup, chosen from M and N:
 // a workgroup moves its rows of A plus its strips of W, one workgroup per CU
-// at a time, so the time goes with rounds * (MB + 2 CT) (KiB per 32 k).  One
-// 8-row block (M <= 8) always takes single strips: A is then negligible, two
-// such workgroups share a CU, and HBM streams best when each CU sweeps few
-// rows of W at a time.
+// at a time, so the time goes with rounds * (MB + 2 CT) (KiB per 32 k).  At
+// M <= 8 it is always one 8-row block and one strip: A is then negligible,
+// two such workgroups share a CU, and HBM streams best when each CU sweeps
+// few rows of W at a time (measured faster than the model's pick there).
 struct SmallShape {
   int mb, ct;
 };
 static SmallShape small_shape(int M, int N) {
+  if (M <= 8) return SmallShape{1, 1};
   const long tiles = (N + 15) / 16;
   SmallShape best{8, 1};
   long best_cost = -1, best_wgs = 0;
   for (int mb : {1, 2, 4, 6, 8}) {
     const long rg = (M + 8 * mb - 1) / (8 * mb);
     for (int ct : {1, 2, 3, 4, 7, 8}) {
-      if (mb == 1 && ct != 1) continue;   // one 8-row block: 16-row strips, two per CU
+      if (mb == 1 && ct != 1) continue;   // 8-row blocks: 16-row strips, two per CU
       const long wgs = rg * ((tiles + ct - 1) / ct);
       const long cost = ((wgs + 255) / 256) * (mb + 2 * ct);
       if (best_cost < 0 || cost < best_cost || (cost == best_cost && wgs < best_wgs))
