@@ -433,22 +433,37 @@ __global__ __launch_bounds__(256) void k_merge(const float* __restrict__ part_ml
     for (int e = 0; e < DPL; ++e) Elem<OUT_DT>::st(out, o + e, 0.f);
     return;
   }
-  const long step = REV ? -(long)h : (long)h;
-  long row = (long)(REV ? c0 + n - 1 : c0) * h + hi;
+  // partial row of the c-th chunk in merge order
+  auto prow = [&](int c) { return (long)(REV ? c0 + n - 1 - c : c0 + c) * h + hi; };
+  long row = prow(0);
   float M = part_ml[2 * row], L = part_ml[2 * row + 1];
   float A[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) A[e] = part_acc[row * DH + DPL * lane + e];
-  for (int c = 1; c < n; ++c) {
-    row += step;
-    const float mc = part_ml[2 * row], lc = part_ml[2 * row + 1];
-    const float Mn = M > mc ? M : mc;
-    const float a = exp_fixed(M - Mn), b = exp_fixed(mc - Mn);
-    L = __builtin_fmaf(lc, b, L * a);
+  // the merge is serial, but its loads are not: G chunks are loaded at a time
+  // (indices clamped to the last chunk), then merged one by one in order
+  constexpr int G = 8;
+  for (int cg = 1; cg < n; cg += G) {
+    float mc[G], lc[G], ac[G][DPL];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e)
-      A[e] = __builtin_fmaf(part_acc[row * DH + DPL * lane + e], b, A[e] * a);
-    M = Mn;
+    for (int i = 0; i < G; ++i) {
+      const long rw = prow(min(cg + i, n - 1));
+      mc[i] = part_ml[2 * rw];
+      lc[i] = part_ml[2 * rw + 1];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) ac[i][e] = part_acc[rw * DH + DPL * lane + e];
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (cg + i < n) {
+        const float Mn = M > mc[i] ? M : mc[i];
+        const float a = exp_fixed(M - Mn), b = exp_fixed(mc[i] - Mn);
+        L = __builtin_fmaf(lc[i], b, L * a);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) A[e] = __builtin_fmaf(ac[i][e], b, A[e] * a);
+        M = Mn;
+      }
+    }
   }
 #pragma unroll
   for (int e = 0; e < DPL; ++e) Elem<OUT_DT>::st(out, o + e, A[e] / L);
