@@ -140,6 +140,23 @@ bi_status bi_gemm(const void *A, const void *W, void *C, int M, int N, int K, in
 bi_status bi_gemm_swiglu(const void *A, const void *W, void *act, int M, int I, int K,
                          bi_stream stream);
 
+/* QKV projection of a decode batch with RoPE and the KV append in its
+ * epilogue: the result is bit-identical to bi_gemm of A and W into a bf16
+ * [M][(h + 2 h_kv) d_h] buffer followed by bi_rope_kv_append of it (same
+ * arguments, dtype BI_BF16), without the intermediate.  Each output element is
+ * bi_gemm's K chain ("2 . Cross-block accumulation"); only which W rows share a
+ * 16-column MFMA tile changes (dims i and i + d_h/2 of a head), which does not
+ * touch any element's arithmetic.  A: device bf16 [M][K]; W: device bf16
+ * [(h + 2 h_kv) d_h][K], rows [q | k | v] as for bi_rope_kv_append; the other
+ * arguments as there (q_out device bf16 [M][h][d_h], pools bf16).  0 <= M <=
+ * 64 (larger M: bi_gemm then bi_rope_kv_append), K % 8 == 0, d_h % 16 == 0, A
+ * and W 16-byte aligned; anything else returns BI_ERR_INVALID and launches
+ * nothing.  Slots of different rows must differ (as for bi_rope_kv_append). */
+bi_status bi_gemm_qkv_rope(const void *A, const void *W, int M, int K, int h, int h_kv, int d_h,
+                           const int32_t *pos, const float *cos_t, const float *sin_t,
+                           const int32_t *slot_mapping, int page_size, void *q_out,
+                           void *k_pool, void *v_pool, bi_stream stream);
+
 /* Twin: picks its tiling from M and, when M x N offers too few tiles to fill
  * the device, splits K over workgroups that add fp32 partials with atomics
  * (order undefined) -- the split-K the pages describe.  Needs

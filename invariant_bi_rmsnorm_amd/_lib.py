@@ -34,6 +34,8 @@ SIGNATURES = {
     "bi_add_rmsnorm": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_float, _c_int, _vp]),
     "bi_gemm": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
     "bi_gemm_swiglu": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp]),
+    "bi_gemm_qkv_rope": (_c_int, [_vp, _vp] + [_c_int] * 5 + [_vp] * 4 + [_c_int]
+                         + [_vp] * 4),
     "bi_decode_attn": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp] + [_c_int] * 8
                        + [_c_float, _c_int, _vp, _vp, _vp]),
     "bi_merge_partials": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _c_int, _vp]),
@@ -181,6 +183,23 @@ def bi_gemm_swiglu(A, W, act, stream=None):
     _check("bi_gemm_swiglu", load().bi_gemm_swiglu(_ptr(A), _ptr(W), _ptr(act), M, I, K,
                                                    _stream(stream)))
     return act
+
+
+def bi_gemm_qkv_rope(A, W, h: int, h_kv: int, d_h: int, pos, cos_t, sin_t, slot_mapping,
+                     q_out, k_pool, v_pool, stream=None):
+    """bi_gemm of A and W (rows [q | k | v]) then bi_rope_kv_append, in one pass."""
+    M, K = A.shape
+    if tuple(W.shape) != ((h + 2 * h_kv) * d_h, K) or tuple(q_out.shape) != (M, h, d_h):
+        raise ValueError(f"shape mismatch A{tuple(A.shape)} W{tuple(W.shape)} "
+                         f"q_out{tuple(q_out.shape)}")
+    if any(t.dtype != torch.bfloat16 for t in (A, W, q_out, k_pool, v_pool)):
+        raise TypeError("bi_gemm_qkv_rope takes bf16 A, W, q_out and pools")
+    page_size = k_pool.shape[2]
+    _check("bi_gemm_qkv_rope", load().bi_gemm_qkv_rope(
+        _ptr(A), _ptr(W), M, K, h, h_kv, d_h, _i32(pos) if pos is not None else None,
+        _ptr(cos_t), _ptr(sin_t), _i32(slot_mapping), page_size, _ptr(q_out), _ptr(k_pool),
+        _ptr(v_pool), _stream(stream)))
+    return q_out
 
 
 def bi_decode_attn(q, k_pool, v_pool, block_table, kv_len, chunk_off, total_chunks: int,

@@ -74,6 +74,79 @@ __device__ __forceinline__ void store_swiglu(void* act, const f32x4_t& acc, int 
   }
 }
 
+// Where the QKV projection's epilogue puts its results: rotary tables (both
+// NULL for no rotation), positions, the token -> cache slot map and the
+// outputs, laid out as bi_rope_kv_append takes them.
+struct RopeArgs {
+  const int32_t* pos;
+  const float* cos_t;
+  const float* sin_t;
+  const int32_t* slots;
+  void* q_out;
+  void* k_pool;
+  void* v_pool;
+  int page_size, h, h_kv, d_h;
+};
+
+// RoPE + KV-append epilogue of a pair tile: MFMA columns 0..7 are dims i0 ..
+// i0 + 7 of head hh, columns 8..15 the dims d_h / 2 further on, the two
+// halves a rotation mixes.  Each is rounded to bf16 as the GEMM's own output
+// would be, then rotated and stored with the arithmetic of bi_rope_kv_append,
+// so the tile equals the GEMM followed by it.
+__device__ __forceinline__ void store_rope(const RopeArgs& ra, const f32x4_t& acc, int row0,
+                                           int tile, int M, int N, int lane) {
+  float other[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) other[j] = __shfl_xor(acc[j], 8);   // lane l ^ 8: the other half
+  if (tile >= N / 16) return;
+  const int per_head = ra.d_h / 16, half = ra.d_h / 2;
+  const int hh = tile / per_head, c = lane & 15, hi = c >> 3;
+  const int i = (tile - hh * per_head) * 8 + (c & 7);
+  const bool rotate = hh < ra.h + ra.h_kv && ra.cos_t != nullptr;
+  const int rbase = row0 + 4 * (lane >> 4);
+  // every load of the four rows goes out before the first store: positions
+  // and slots, then the table entries (rows past M read row M - 1, unused)
+  int32_t sl[4] = {0, 0, 0, 0};
+  float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
+  if (hh >= ra.h) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sl[j] = ra.slots[min(rbase + j, M - 1)];
+  }
+  if (rotate) {   // uniform over the wave: one tile, one head
+    int32_t pr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pr[j] = ra.pos[min(rbase + j, M - 1)];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const long t = (long)pr[j] * half + i;
+      cs[j] = ra.cos_t[t];
+      sn[j] = ra.sin_t[t];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = rbase + j;
+    if (row >= M) continue;
+    const float own = bf16_bits_to_f32((uint16_t)f32_to_bf16_bits(acc[j]));
+    const float oth = bf16_bits_to_f32((uint16_t)f32_to_bf16_bits(other[j]));
+    float y = own;
+    if (rotate)
+      y = hi ? __builtin_fmaf(own, cs[j], oth * sn[j]) : __builtin_fmaf(own, cs[j], -(oth * sn[j]));
+    long o;
+    void* dst;
+    if (hh < ra.h) {
+      dst = ra.q_out;
+      o = ((long)row * ra.h + hh) * ra.d_h;
+    } else {
+      const int g = hh < ra.h + ra.h_kv ? hh - ra.h : hh - ra.h - ra.h_kv;
+      const int page = sl[j] / ra.page_size, in_page = sl[j] - page * ra.page_size;
+      dst = hh < ra.h + ra.h_kv ? ra.k_pool : ra.v_pool;
+      o = (((long)page * ra.h_kv + g) * ra.page_size + in_page) * ra.d_h;
+    }
+    static_cast<uint16_t*>(dst)[o + i + hi * half] = (uint16_t)f32_to_bf16_bits(y);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // small-M kernel (M <= 64): one workgroup per CT 16-column strips of W and one
 // group of 8 MB rows of A (blockIdx.z; MB and CT are chosen from M and N so
@@ -135,10 +208,14 @@ struct SmallCfg {
 // takes items gw, gw + 4, ...  Lane: row (lane >> 3) of the block, LDS slot
 // (lane & 7) <- 16-byte unit (lane & 7) ^ row.  Before the barrier of stage
 // st, the wave waits for its own copies of stage st.
-template <int NB, int LPS, int RD, bool NT>
+// PAIR 0: block b holds rows row0 + 8 b ..; PAIR 1 (SwiGLU): block 2p holds
+// gate rows row0 + 8p .., block 2p + 1 the up rows `arg` further on; PAIR 2
+// (RoPE): blocks 2p, 2p + 1 hold the two rotation halves of 16-column pair
+// tile row0 / 16 + p, heads of `arg` rows (8 dims of each half per tile).
+template <int NB, int LPS, int RD, bool NT, int PAIR = 0>
 __device__ __forceinline__ void small_copy_ring(const uint16_t* __restrict__ base, long ld,
                                                 int row0, int rmax, int kbeg, int K, int NST,
-                                                char* ring, int gw, int lane, int half = 0) {
+                                                char* ring, int gw, int lane, int arg = 0) {
   constexpr int NIT = NB * LPS, QB = NIT / kSmallGroupWaves, XR = NIT % kSmallGroupWaves;
   constexpr int QMAX = QB + (XR > 0), KS = 2 * LPS;
   const bool extra = gw < XR;
@@ -147,10 +224,16 @@ __device__ __forceinline__ void small_copy_ring(const uint16_t* __restrict__ bas
 #pragma unroll
   for (int i = 0; i < QMAX; ++i) {
     const int j = min(gw + kSmallGroupWaves * i, NIT - 1), b = j % NB, line = j / NB;
-    // half > 0 (SwiGLU pairs): block 2p is gate rows row0 + 8p .., block 2p + 1
-    // the up rows `half` further on
-    const int row = half > 0 ? (b & 1) * half + min(row0 + (b >> 1) * 8 + crow, rmax)
-                             : min(row0 + b * 8 + crow, rmax);
+    int row;
+    if constexpr (PAIR == 1) {
+      row = (b & 1) * arg + min(row0 + (b >> 1) * 8 + crow, rmax);
+    } else if constexpr (PAIR == 2) {
+      const int per_head = arg / 16, tile = min(row0 / 16 + (b >> 1), rmax / 16);
+      const int hh = tile / per_head;
+      row = hh * arg + (b & 1) * (arg / 2) + (tile - hh * per_head) * 8 + crow;
+    } else {
+      row = min(row0 + b * 8 + crow, rmax);
+    }
     src[i] = base + (long)row * ld + kbeg + line * 64 + koff;
   }
   auto issue = [&](int st) {
@@ -181,7 +264,7 @@ __device__ __forceinline__ void small_copy_ring(const uint16_t* __restrict__ bas
 template <int MB, int CT, int OUTF32>
 __global__ __launch_bounds__(kSmallThreads) void k_gemm_small(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, void* C, int M, int N,
-    int Ktot, int kslice) {
+    int Ktot, int kslice, RopeArgs ra) {
   using G = SmallCfg<MB, CT>;
   constexpr int KS = G::KS, LPS = G::LPS, MT = G::MT;
   // K slice of this workgroup (all of K on the invariant path; the split-K
@@ -200,11 +283,19 @@ __global__ __launch_bounds__(kSmallThreads) void k_gemm_small(
     const int cw = wave - kSmallComputeWaves;
     if (cw < kSmallGroupWaves)
       small_copy_ring<MB, LPS, G::AD, false>(A, ld, m0, mend - 1, kbeg, K, NST, smem, cw, lane);
+    else if constexpr (OUTF32 == 3)
+      // SwiGLU: N = 2 I; strip x holds pair tiles CT x .. CT x + CT - 1
+      small_copy_ring<2 * CT, LPS, G::WD, true, 1>(W, ld, n0 / 2, N / 2 - 1, kbeg, K, NST,
+                                                   smem + G::A_RING, cw - kSmallGroupWaves,
+                                                   lane, N / 2);
+    else if constexpr (OUTF32 == 4)
+      // RoPE: strip x holds pair tiles CT x .. CT x + CT - 1 (N % 16 == 0)
+      small_copy_ring<2 * CT, LPS, G::WD, true, 2>(W, ld, n0, N - 1, kbeg, K, NST,
+                                                   smem + G::A_RING, cw - kSmallGroupWaves,
+                                                   lane, ra.d_h);
     else
-      // OUTF32 3 (SwiGLU): N = 2 I; strip x holds pair tiles CT x .. CT x + CT - 1
-      small_copy_ring<2 * CT, LPS, G::WD, true>(
-          W, ld, OUTF32 == 3 ? n0 / 2 : n0, (OUTF32 == 3 ? N / 2 : N) - 1, kbeg, K, NST,
-          smem + G::A_RING, cw - kSmallGroupWaves, lane, OUTF32 == 3 ? N / 2 : 0);
+      small_copy_ring<2 * CT, LPS, G::WD, true>(W, ld, n0, N - 1, kbeg, K, NST,
+                                                smem + G::A_RING, cw - kSmallGroupWaves, lane);
     return;
   }
 
@@ -280,6 +371,8 @@ __global__ __launch_bounds__(kSmallThreads) void k_gemm_small(
       const int m = wm + G::WM * i, c = wn + G::WN * j;
       if constexpr (OUTF32 == 3) {   // every lane joins the exchange
         if (m < MT) store_swiglu(C, acc[i][j], m0 + m * 16, n0 / 2 + c * 8, mend, N / 2, lane);
+      } else if constexpr (OUTF32 == 4) {
+        if (m < MT) store_rope(ra, acc[i][j], m0 + m * 16, n0 / 16 + c, mend, N, lane);
       } else if (m < MT) {
         store_tile<OUTF32>(C, acc[i][j], m0 + m * 16, n0 + c * 16, mend, N, lane);
       }
@@ -392,7 +485,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A,
 // ---------------------------------------------------------------------------
 template <int MB, int CT, int OUTF32>
 static void launch_small_k(const void* A, const void* W, void* C, int M, int N, int K,
-                           hipStream_t s, int splits, int kslice) {
+                           hipStream_t s, int splits, int kslice, const RopeArgs& ra) {
   constexpr int lds = SmallCfg<MB, CT>::LDS;
   static bool attr = false;
   if (!attr) {
@@ -403,7 +496,7 @@ static void launch_small_k(const void* A, const void* W, void* C, int M, int N, 
   hipLaunchKernelGGL((k_gemm_small<MB, CT, OUTF32>),
                      dim3((N + 16 * CT - 1) / (16 * CT), splits, (M + 8 * MB - 1) / (8 * MB)),
                      dim3(kSmallThreads), lds, s,
-                     (const uint16_t*)A, (const uint16_t*)W, C, M, N, K, kslice);
+                     (const uint16_t*)A, (const uint16_t*)W, C, M, N, K, kslice, ra);
 }
 
 // Rows (8 MB) and 16-column strips (CT) per workgroup, chosen from M and N:
@@ -435,12 +528,13 @@ static SmallShape small_shape(int M, int N) {
 
 template <int OUTF32>
 static void dispatch_small(const void* A, const void* W, void* C, int M, int N, int K,
-                           hipStream_t s, int splits = 1, int kslice = 0) {
+                           hipStream_t s, int splits = 1, int kslice = 0,
+                           const RopeArgs& ra = RopeArgs{}) {
   if (splits == 1) kslice = K;
   const SmallShape sh = small_shape(M, N);
 #define BI_SMALL(MB_, CT_)                                                      \
   if (sh.mb == MB_ && sh.ct == CT_) {                                           \
-    launch_small_k<MB_, CT_, OUTF32>(A, W, C, M, N, K, s, splits, kslice);      \
+    launch_small_k<MB_, CT_, OUTF32>(A, W, C, M, N, K, s, splits, kslice, ra);  \
     return;                                                                     \
   }
 #define BI_SMALL_M(MB_) \
@@ -649,4 +743,29 @@ extern "C" bi_status bi_gemm_swiglu(const void* A, const void* W, void* act, int
   BI_REQUIRE(2L * I * K < (1L << 40), BI_ERR_INVALID, "bi_gemm_swiglu: tensor too large");
   dispatch_small<3>(A, W, act, M, 2 * I, K, as_stream(stream));
   return launched("bi_gemm_swiglu");
+}
+
+extern "C" bi_status bi_gemm_qkv_rope(const void* A, const void* W, int M, int K, int h,
+                                      int h_kv, int d_h, const int32_t* pos, const float* cos_t,
+                                      const float* sin_t, const int32_t* slot_mapping,
+                                      int page_size, void* q_out, void* k_pool, void* v_pool,
+                                      bi_stream stream) {
+  using namespace bi;
+  BI_REQUIRE(M >= 0 && M <= 64 && K >= 8 && K % 8 == 0 && h >= 1 && h_kv >= 1 && d_h >= 16 &&
+                 d_h % 16 == 0 && page_size >= 1,
+             BI_ERR_INVALID, "bi_gemm_qkv_rope: need 0 <= M <= 64, K %% 8 == 0, d_h %% 16 == 0 "
+             "(M=%d K=%d d_h=%d)", M, K, d_h);
+  BI_REQUIRE((cos_t == nullptr) == (sin_t == nullptr), BI_ERR_INVALID,
+             "bi_gemm_qkv_rope: cos_t and sin_t must both be given or both be NULL");
+  if (M == 0) return BI_OK;
+  BI_REQUIRE(A && W && slot_mapping && q_out && k_pool && v_pool && (pos || !cos_t),
+             BI_ERR_INVALID, "bi_gemm_qkv_rope: null pointer");
+  BI_REQUIRE(aligned16(A) && aligned16(W), BI_ERR_INVALID,
+             "bi_gemm_qkv_rope: A and W must be 16-byte aligned");
+  const long N = (long)(h + 2 * h_kv) * d_h;
+  BI_REQUIRE(N * K < (1L << 40) && N < (1L << 30), BI_ERR_INVALID,
+             "bi_gemm_qkv_rope: tensor too large");
+  RopeArgs ra{pos, cos_t, sin_t, slot_mapping, q_out, k_pool, v_pool, page_size, h, h_kv, d_h};
+  dispatch_small<4>(A, W, nullptr, M, (int)N, K, as_stream(stream), 1, 0, ra);
+  return launched("bi_gemm_qkv_rope");
 }

@@ -150,6 +150,85 @@ def test_gemm_swiglu_rejects_bad_shapes():
         L.bi_gemm_swiglu(A[:1], W12, act12)  # I % 8 != 0
 
 
+# (M, h, h_kv, d_h, K): the Llama-3-8B projection at decode batch sizes, a
+# ragged row block, the largest M, the smallest head and an odd head mix
+QKV_ROPE_SHAPES = [(1, 32, 8, 128, 4096), (8, 32, 8, 128, 4096), (5, 32, 8, 128, 4096),
+                   (64, 32, 8, 128, 4096), (13, 4, 2, 64, 520), (3, 3, 1, 16, 40),
+                   (33, 6, 2, 32, 1000)]
+
+
+def _qkv_rope_case(M, h, h_kv, d_h, K, seed):
+    ps = 16
+    A = synth.normal((M, K), seed=seed).to(torch.bfloat16).to(dev())
+    W = synth.normal(((h + 2 * h_kv) * d_h, K), seed=seed + 1, std=0.05).to(torch.bfloat16)
+    rng = np.random.default_rng(seed)
+    pages = M + 3
+    slots = rng.choice(pages * ps, size=M, replace=False).astype(np.int32)
+    pos = rng.integers(0, 4096, size=M).astype(np.int32)
+    kp = synth.normal((pages, h_kv, ps, d_h), seed=seed + 2).to(torch.bfloat16).to(dev())
+    vp = synth.normal((pages, h_kv, ps, d_h), seed=seed + 3).to(torch.bfloat16).to(dev())
+    return A, W.to(dev()), torch.from_numpy(slots).to(dev()), torch.from_numpy(pos).to(dev()), kp, vp
+
+
+@pytest.mark.parametrize("M,h,h_kv,d_h,K", QKV_ROPE_SHAPES)
+@pytest.mark.parametrize("tables", [True, False])
+def test_gemm_qkv_rope_equals_gemm_then_rope_append(M, h, h_kv, d_h, K, tables):
+    A, W, slots, pos, kp, vp = _qkv_rope_case(M, h, h_kv, d_h, K, seed=M + K + d_h)
+    cos_t, sin_t = synth.rope_tables(4096, d_h)
+    cos_t, sin_t = (cos_t.to(dev()), sin_t.to(dev())) if tables else (None, None)
+    kp2, vp2 = kp.clone(), vp.clone()
+    q = torch.empty((M, h, d_h), dtype=torch.bfloat16, device=dev())
+    L.bi_gemm_qkv_rope(A, W, h, h_kv, d_h, pos, cos_t, sin_t, slots, q, kp, vp)
+    qkv = torch.empty((M, W.shape[0]), dtype=torch.bfloat16, device=dev())
+    L.bi_gemm(A, W, qkv)
+    q2 = torch.empty_like(q)
+    L.bi_rope_kv_append(qkv, h, h_kv, d_h, pos, cos_t, sin_t, slots, q2, kp2, vp2)
+    assert bits_equal(to_np(q), to_np(q2))
+    # whole pools: the appended slots match and nothing else was written
+    assert bits_equal(to_np(kp), to_np(kp2))
+    assert bits_equal(to_np(vp), to_np(vp2))
+
+
+def test_gemm_qkv_rope_integer_exact_vs_oracle():
+    # integer operands: the GEMM is exact in fp32, so q and the appended k, v
+    # are the oracle's GEMM then RoPE to the bit
+    M, h, h_kv, d_h, K, ps = 6, 4, 2, 64, 264, 16
+    A = synth.integers((M, K), -3, 3, seed=5).to(torch.bfloat16)
+    W = synth.integers(((h + 2 * h_kv) * d_h, K), -3, 3, seed=6).to(torch.bfloat16)
+    pos = np.array([0, 1, 9, 255, 256, 4095], np.int32)
+    slots = np.array([0, 17, 33, 50, 64 + 15, 95], np.int32)
+    cos_t, sin_t = synth.rope_tables(4096, d_h)
+    kp = torch.zeros((6, h_kv, ps, d_h), dtype=torch.bfloat16, device=dev())
+    vp = torch.zeros_like(kp)
+    q = torch.empty((M, h, d_h), dtype=torch.bfloat16, device=dev())
+    L.bi_gemm_qkv_rope(A.to(dev()), W.to(dev()), h, h_kv, d_h, torch.from_numpy(pos).to(dev()),
+                       cos_t.to(dev()), sin_t.to(dev()), torch.from_numpy(slots).to(dev()), q,
+                       kp, vp)
+    x = oracle.gemm(A, W, round_bf16=True).reshape(M, h + 2 * h_kv, d_h)
+    rq = oracle.rope(x[:, :h], pos, cos_t, sin_t, round_bf16=True)
+    rk = oracle.rope(x[:, h:h + h_kv], pos, cos_t, sin_t, round_bf16=True)
+    assert bits_equal(to_np(q), rq), mismatch_report(to_np(q), rq)
+    kpn, vpn = to_np(kp), to_np(vp)
+    for i, s in enumerate(slots):
+        assert bits_equal(kpn[s // ps, :, s % ps], rk[i])
+        assert bits_equal(vpn[s // ps, :, s % ps], x[i, h + h_kv:])
+
+
+def test_gemm_qkv_rope_rejects_bad_shapes():
+    A = torch.zeros((65, 64), dtype=torch.bfloat16, device=dev())
+    W = torch.zeros((4 * 16, 64), dtype=torch.bfloat16, device=dev())
+    kp = torch.zeros((70, 1, 1, 16), dtype=torch.bfloat16, device=dev())
+    slots = torch.arange(65, dtype=torch.int32, device=dev())
+    q = torch.empty((65, 2, 16), dtype=torch.bfloat16, device=dev())
+    with pytest.raises(L.BiError):   # M > 64
+        L.bi_gemm_qkv_rope(A, W, 2, 1, 16, None, None, None, slots, q, kp, kp.clone())
+    W8 = torch.zeros((4 * 8, 64), dtype=torch.bfloat16, device=dev())
+    kp8 = torch.zeros((2, 1, 1, 8), dtype=torch.bfloat16, device=dev())
+    q8 = torch.empty((1, 2, 8), dtype=torch.bfloat16, device=dev())
+    with pytest.raises(L.BiError):   # d_h % 16 != 0
+        L.bi_gemm_qkv_rope(A[:1], W8, 2, 1, 8, None, None, None, slots[:1], q8, kp8, kp8.clone())
+
+
 @pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 def test_gemm_bf16_integer_exact(M, N, K, out):
