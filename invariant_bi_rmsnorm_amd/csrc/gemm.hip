@@ -19,6 +19,8 @@
 // global->LDS instruction per fragment, read back by the same lane); the
 // small-M and large-tile kernels copy whole 128-byte row lines and read
 // fragments back through a swizzled line-major layout.
+#include <type_traits>
+
 #include "api.h"
 #include "common.h"
 
@@ -562,56 +564,90 @@ static void launch_tiled(const void* A, const void* W, void* C, int M, int N, in
 
 // ---------------------------------------------------------------------------
 // large tiles for large M (chunked prefill): 256 x 256 output tile per
-// workgroup, 8 waves as 2 (M) x 4 (N), each 128 x 64 (8 x 4 MFMA tiles).
-// Two K-tiles per stage, two stages of A and W rows in LDS by direct copies
-// of whole 128-byte lines.  Same MFMA chain per output element as every
-// other path.  Workgroups are mapped so that each XCD (blockIdx % 8) takes a
-// contiguous range of tiles in grouped order (4 row-blocks at a time), so
-// the tiles resident on one XCD share A rows and W columns in its L2.
+// workgroup, eight waves in two groups that take turns ("ping-pong").  Group
+// g = wave / 4 holds one wave on each SIMD and owns output rows 128 g ..
+// 128 g + 127; wave wn of a group owns columns 64 wn .. 64 wn + 63 (8 x 4
+// MFMA tiles).  Phases are separated by workgroup barriers: in every phase
+// one group reads its fragments of a K-tile from LDS and issues direct copies
+// while the other runs its 32 MFMAs on the K-tile it read in the phase before,
+// so each SIMD's matrix core has work while its other wave feeds LDS.  Group 0
+// takes K-tile s in phases 2s (memory) and 2s + 1 (MFMA), group 1 one phase
+// later.  Each output element is still one MFMA chain over the K-tiles in
+// ascending order, as on every other path.
+//
+// LDS holds two line stages of 64 KiB: 128-byte lines (two K-tiles) of 256 A
+// rows then 256 W rows, 8 rows per 1 KiB block, the 16-byte unit u of row r at
+// slot u ^ (r & 7); each direct copy moves 8 whole lines.  The copies of line
+// stage L + 1 are spread over the four memory phases of K-tiles 2L and 2L + 1
+// (four per wave): W rows 0-127 (group 0), W rows 128-255 (group 1), then the
+// A rows of group 0's half and of group 1's.  Group 0 waits for its copies at
+// the end of phase 4L + 3, before it reads the stage in phase 4L + 4; group 1
+// waits for its W copies then and for its A copies at the end of phase
+// 4L + 4, before its own read.  Workgroups are mapped so that each XCD
+// (blockIdx % 8) takes a contiguous range of tiles in grouped order (4
+// row-blocks at a time), so the tiles resident on one XCD share A rows and W
+// columns in its L2.
 // ---------------------------------------------------------------------------
+// a[i] = LDS[ba + 2048 i] (i < 8), b[j] = LDS[bb + 2048 j] (j < 4), not waited for
+__device__ __forceinline__ void lds_read_8_4_nowait(u32x4_t (&a)[8], u32x4_t (&b)[4],
+                                                    uint32_t ba, uint32_t bb) {
+  asm volatile(
+      "ds_read_b128 %0, %12\n\tds_read_b128 %1, %12 offset:2048\n\t"
+      "ds_read_b128 %2, %12 offset:4096\n\tds_read_b128 %3, %12 offset:6144\n\t"
+      "ds_read_b128 %4, %12 offset:8192\n\tds_read_b128 %5, %12 offset:10240\n\t"
+      "ds_read_b128 %6, %12 offset:12288\n\tds_read_b128 %7, %12 offset:14336\n\t"
+      "ds_read_b128 %8, %13\n\tds_read_b128 %9, %13 offset:2048\n\t"
+      "ds_read_b128 %10, %13 offset:4096\n\tds_read_b128 %11, %13 offset:6144"
+      : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]),
+        "=&v"(a[6]), "=&v"(a[7]), "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
+      : "v"(ba), "v"(bb)
+      : "memory");
+}
+
+// waits for the reads above; the operands tie every later use of a and b to it
+__device__ __forceinline__ void lds_wait_8_4(u32x4_t (&a)[8], u32x4_t (&b)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(a[4]), "+v"(a[5]),
+                 "+v"(a[6]), "+v"(a[7]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3])
+               :
+               : "memory");
+}
+
 template <int OUTF32>
 __global__ __launch_bounds__(512) void k_gemm_big(const uint16_t* __restrict__ A,
                                                   const uint16_t* __restrict__ W, void* C,
                                                   int M, int N, int K, int tiles_m, int tiles_n) {
-  // Stage = 2 K-tiles (64 columns of K = one 128-byte line per row).  LDS
-  // stage layout is line-major: A rows 0..255 then W rows 0..255, 8 rows
-  // (8 lines) per 1 KiB block; the 16-byte unit u of row r sits at slot
-  // u ^ (r & 7).  Each direct copy moves 8 whole lines (128-byte requests);
-  // a fragment (16 rows x 32 K) is read back with per-lane addresses.
-  constexpr int NS = 2, BLK = 64, PER_WAVE = BLK / 8;  // 1 KiB blocks per stage
-  constexpr int STAGE = BLK * 1024;
+  constexpr int NS = 2, STAGE = 64 * 1024;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int nt = tiles_m * tiles_n, b = blockIdx.x;
-  const int xcd = b % 8, idx = b / 8;
+  const int nt = tiles_m * tiles_n, bid = blockIdx.x;
+  const int xcd = bid % 8, idx = bid / 8;
   const int per = nt / 8, rem = nt % 8;
   const int t = xcd * per + (xcd < rem ? xcd : rem) + idx;
-  // grouped order inside that range: GM row-blocks at a time, row fastest,
-  // so the XCD's resident workgroups form a GM x (32 / GM) block of tiles
-  // sharing A rows and W columns in its L2
+  // grouped order inside that range: GM row-blocks at a time, row fastest
   constexpr int GM = 4;
   const int grp = t / (GM * tiles_n), first = grp * GM;
   const int gm = min(GM, tiles_m - first);
   const int tm = first + (t % (GM * tiles_n)) % gm, tn = (t % (GM * tiles_n)) / gm;
   const int m0 = tm * 256, n0 = tn * 256;
-  const int wm = wave >> 2, wn = wave & 3;
-  const int KT = (K + 31) >> 5;
-  const int NST = (KT + 1) >> 1;
+  const int g = wave >> 2, wn = wave & 3;   // group = row half; column quarter
+  const int KT = (K + 31) >> 5, NLS = (KT + 1) >> 1;
 
   // copy lane: row (lane >> 3) of its block, slot (lane & 7) holds unit
   // slot ^ (row & 7) of that row's 128-byte span
   const int crow = lane >> 3, cunit = (lane & 7) ^ crow;
-  auto issue = [&](int st) {
-    char* slot = smem + (st % NS) * STAGE;
-    int kk = st * 64 + cunit * 8;
+  // NB copies of line stage ls: row blocks base + wn + 4 i of X (rows from x0,
+  // clamped to xmax) into stage blocks sblk0 + ..
+  auto issue = [&](auto nb_c, int ls, const uint16_t* __restrict__ X, int x0, int xmax,
+                   int sblk0, int base) {
+    constexpr int NB = decltype(nb_c)::value;
+    char* slot = smem + (ls % NS) * STAGE;
+    int kk = ls * 64 + cunit * 8;
     kk = kk < K ? kk : 0;
 #pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const int blk = wave + 8 * i;  // 0..31 A row blocks, 32..63 W row blocks
-      const uint16_t* src = blk < 32
-          ? A + (long)min(m0 + blk * 8 + crow, M - 1) * K + kk
-          : W + (long)min(n0 + (blk - 32) * 8 + crow, N - 1) * K + kk;
-      dma16(src, slot + blk * 1024);
+    for (int i = 0; i < NB; ++i) {
+      const int blk = base + wn + 4 * i;
+      dma16(X + (long)min(x0 + blk * 8 + crow, xmax) * K + kk, slot + (sblk0 + blk) * 1024);
     }
   };
   // read lane: row (lane & 15) of a 16-row tile, unit 4 kt + (lane >> 4)
@@ -620,47 +656,60 @@ __global__ __launch_bounds__(512) void k_gemm_big(const uint16_t* __restrict__ A
     return (uint32_t)(((r >> 3) & 1) * 1024 + (r & 7) * 128 + 16 * (u ^ (r & 7)));
   };
   const uint32_t off0 = rd_off(0), off1 = rd_off(1);
+  const uint32_t lds0 = lds_addr(smem);
 
   f32x4_t acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  issue(0);
-  const uint32_t lds0 = lds_addr(smem);
-  for (int st = 0; st < NST; ++st) {
-    BI_WAIT_VMCNT(0);
-    __builtin_amdgcn_s_barrier();
-    if (st + 1 < NST) issue(st + 1);
-    const uint32_t sb = lds0 + (st % NS) * STAGE;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int ktg = 2 * st + kt;
-      if (ktg < KT) {
-        const uint32_t off = kt ? off1 : off0;
-        u32x4_t a[8], bw[4];
-        // A row tiles 8 wm .. 8 wm + 7 (tile t at blocks 2t, 2t + 1: stride
-        // 2 KiB), W column tiles 4 wn .. 4 wn + 3
-        lds_read_8_stride2k(a, sb + (8 * wm) * 2048 + off);
-        lds_read_4_stride2k(bw, sb + 32 * 1024 + (4 * wn) * 2048 + off);
-        if (ktg * 32 + 8 * (lane >> 4) >= K) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) a[i] = u32x4_t{0, 0, 0, 0};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) bw[j] = u32x4_t{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = mfma(a[i], bw[j], acc[i][j]);
-      }
+  u32x4_t a[8], bw[4];
+
+  // prologue: line stage 0, A rows by group 0 and W rows by group 1
+  if (g == 0) issue(std::integral_constant<int, 8>{}, 0, A, m0, M - 1, 0, 0);
+  else issue(std::integral_constant<int, 8>{}, 0, W, n0, N - 1, 32, 0);
+  BI_WAIT_VMCNT(0);
+  __builtin_amdgcn_s_barrier();
+  if (g == 1) __builtin_amdgcn_s_barrier();   // phase 0: group 0 alone
+  // one K-tile: its memory phase, then its MFMA phase.  `tail` (the last
+  // K-tile when K % 32 != 0): units past K enter both operands as zeros.
+  auto step = [&](int s, bool tail) {
+    // ---- memory phase of K-tile s
+    const uint32_t sb = lds0 + ((s >> 1) % NS) * STAGE + ((s & 1) ? off1 : off0);
+    lds_read_8_4_nowait(a, bw, sb + (8 * g) * 2048, sb + 32 * 1024 + (4 * wn) * 2048);
+    if ((s >> 1) + 1 < NLS) {
+      using I4 = std::integral_constant<int, 4>;
+      if (s & 1) issue(I4{}, (s >> 1) + 1, A, m0, M - 1, 0, 16 * g);
+      else issue(I4{}, (s >> 1) + 1, W, n0, N - 1, 32, 16 * g);
     }
-  }
+    lds_wait_8_4(a, bw);
+    if (tail && s * 32 + 8 * (lane >> 4) >= K) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a[i] = u32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bw[j] = u32x4_t{0, 0, 0, 0};
+    }
+    // end of phase 4L + 3 for group 1: its W copies (the older four) are in
+    if ((s & 1) && g == 1) BI_WAIT_VMCNT(4);
+    __builtin_amdgcn_s_barrier();
+    // ---- MFMA phase of K-tile s
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma(a[i], bw[j], acc[i][j]);
+    // end of phase 4L + 3 (group 0) / 4L + 4 (group 1): all its copies are in
+    if (s & 1) BI_WAIT_VMCNT(0);
+    // the last phase (group 1's last MFMAs) ends without a barrier: group 0
+    // goes on to its stores
+    if (g == 0 || s + 1 < KT) __builtin_amdgcn_s_barrier();
+  };
+  for (int s = 0; s < KT - 1; ++s) step(s, false);
+  step(KT - 1, (K & 31) != 0);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      store_tile<OUTF32>(C, acc[i][j], m0 + (8 * wm + i) * 16, n0 + (4 * wn + j) * 16, M, N,
+      store_tile<OUTF32>(C, acc[i][j], m0 + (8 * g + i) * 16, n0 + (4 * wn + j) * 16, M, N,
                          lane);
 }
 

@@ -686,11 +686,13 @@ def test_unsupported_configs_fail_closed():
     assert e.value.status == L.BI_ERR_UNSUPPORTED
 
 
-def test_gemm_large_tile_rows_equal_small_M_rows():
+@pytest.mark.parametrize("K", [4096, 4104, 4128, 40, 32])
+def test_gemm_large_tile_rows_equal_small_M_rows(K):
     # chunked-prefill GEMM (M = 2048 + 5 rows, 256 x 256 tiles, ragged in M
-    # and N) against the skinny and 128-tile paths, bit for bit per row; and
-    # the integer-exact case against the oracle
-    K, N = 4096, 2304 + 40
+    # and N; K with a partial last K-tile, an odd count of K-tiles, two and
+    # one K-tiles) against the skinny and 128-tile paths, bit for bit per row;
+    # and the integer-exact case against the oracle
+    N = 2304 + 40
     M = 2053
     A = synth.normal((M, K), seed=21).to(torch.bfloat16).to(dev())
     W = synth.normal((N, K), seed=22, std=0.02).to(torch.bfloat16).to(dev())
@@ -702,6 +704,8 @@ def test_gemm_large_tile_rows_equal_small_M_rows():
         c = torch.empty((m, N), dtype=torch.float32, device=dev())
         L.bi_gemm(A[rows].contiguous(), W, c)
         assert torch.equal(c.view(torch.int32), big[rows].view(torch.int32)), f"m={m}"
+    if K != 4096:
+        return
     Ai = synth.integers((M, 512), -8, 8, seed=23).to(torch.bfloat16)
     Wi = synth.integers((N, 512), -8, 8, seed=24).to(torch.bfloat16)
     ci = torch.empty((M, N), dtype=torch.float32, device=dev())
