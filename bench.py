@@ -71,6 +71,10 @@ def parse():
     ap.add_argument("--traffic-summary", default="",
                     help="summarise rocprofv3 --pmc runs (FETCH_SIZE / WRITE_SIZE of --only "
                          "decode_attn and of --only copy) found under this directory")
+    ap.add_argument("--mfma-summary", default="",
+                    help="summarise a rocprofv3 --pmc run of --only prefill_gemm "
+                         "(SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16, "
+                         "GRBM_GUI_ACTIVE) found under this directory")
     return ap.parse_args()
 
 
@@ -333,19 +337,25 @@ def prefill_gemm(torch, dev, M=8192, N=14336, K=4096, launches=20):
     us = 1e3 * a.elapsed_time(b) / launches
     tf = 2.0 * M * N * K / us / 1e6
     return {"kernel": "bi_gemm prefill", "M": M, "N": N, "K": K, "avg_us": round(us, 1),
-            "TFLOPs": round(tf, 1), "peak": BF16_PEAK / 1e12, "frac": round(tf * 1e12 / BF16_PEAK, 4)}
+            "TFLOPs": round(tf, 1), "peak": BF16_PEAK / 1e12, "frac": round(tf * 1e12 / BF16_PEAK, 4),
+            # rocprofv3 counters of the same launch (profiles/), null once the
+            # GEMM sources changed since they were taken
+            "counters": measured_mfma()}
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_attn_traffic_llama3_8b_b64.md")
+MFMA_PROFILE = os.path.join(ROOT, "profiles", "prefill_gemm_mfma_m8192_n14336_k4096.md")
+MFMA_SOURCES = ("invariant_bi_rmsnorm_amd/csrc/gemm.hip", "invariant_bi_rmsnorm_amd/csrc/common.h")
 TRAFFIC_SOURCES = ("invariant_bi_rmsnorm_amd/csrc/attention.hip",
                    "invariant_bi_rmsnorm_amd/csrc/common.h")
 
 
-def kernel_source_hash():
-    """sha256 over the sources the decode-attention kernel is built from."""
+def kernel_source_hash(sources=None):
+    """sha256 over the sources a kernel is built from (by default the
+    decode-attention kernel's)."""
     import hashlib
     h = hashlib.sha256()
-    for rel in TRAFFIC_SOURCES:
+    for rel in sources or TRAFFIC_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -397,6 +407,67 @@ def traffic_summary(d):
     print(f"| HBM bytes per decode-attention launch | {fetch + write:.4g} |")
     print()
     print("traffic-record: " + json.dumps(rec))
+
+
+def mfma_summary(d, M=8192, N=14336, K=4096, simds=1024, xcds=8):
+    """MFMA utilisation of the prefill GEMM (k_gemm_big) per dispatch from one
+    rocprofv3 --pmc run: busy = SQ_VALU_MFMA_BUSY_CYCLES summed over the
+    SIMDs, over GRBM_GUI_ACTIVE x SIMDs (GRBM_GUI_ACTIVE is reported summed
+    over the XCDs, so it is divided by their count); the MFMA work checked
+    against 2MNK (SQ_INSTS_VALU_MFMA_MOPS_BF16 counts units of 512 FLOPs);
+    and the clock the dispatch ran at (GUI-active cycles per XCD over its
+    duration)."""
+    import csv
+    import glob
+    import statistics
+    rows = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if "k_gemm_big" in r["Kernel_Name"]:
+                    key = (f, r["Dispatch_Id"])
+                    e = rows.setdefault(key, {"ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+                    e[r["Counter_Name"]] = float(r["Counter_Value"])
+    need = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "GRBM_GUI_ACTIVE")
+    rows = [e for e in rows.values() if all(k in e for k in need)]
+    if not rows:
+        raise SystemExit(f"no k_gemm_big counter rows under {d}")
+    util = [e["SQ_VALU_MFMA_BUSY_CYCLES"] / (e["GRBM_GUI_ACTIVE"] / xcds * simds) for e in rows]
+    flops = [e["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 for e in rows]
+    ghz = [e["GRBM_GUI_ACTIVE"] / xcds / e["ns"] for e in rows]
+    us = [e["ns"] / 1e3 for e in rows]
+    alg = 2.0 * M * N * K
+    med = statistics.median
+    print("| quantity (median over %d dispatches, M %d N %d K %d) | value |" % (len(rows), M, N, K))
+    print("|---|---|")
+    print(f"| MFMA busy / GUI-active cycles (all SIMDs) | {100 * med(util):.1f}% (range {100 * min(util):.1f}-{100 * max(util):.1f}%) |")
+    print(f"| MFMA FLOPs counted / 2MNK | {med(flops) / alg:.4f} |")
+    print(f"| clock while active (GHz) | {med(ghz):.2f} (range {min(ghz):.2f}-{max(ghz):.2f}) |")
+    print(f"| dispatch duration (us) | {med(us):.1f} (range {min(us):.1f}-{max(us):.1f}) |")
+    print(f"| achieved / bf16 dense peak at 2.4 GHz (2.5 PFLOP/s) | {100 * alg / (med(us) * 1e-6) / 2.5e15:.1f}% |")
+    rec = {"kernel": "k_gemm_big", "M": M, "N": N, "K": K, "dispatches": len(rows),
+           "mfma_busy": round(med(util), 4), "mfma_busy_range": [round(min(util), 4), round(max(util), 4)],
+           "clock_ghz": round(med(ghz), 3), "flops_counted_over_2mnk": round(med(flops) / alg, 4),
+           "source_sha256": kernel_source_hash(MFMA_SOURCES)}
+    print()
+    print("mfma-record: " + json.dumps(rec))
+
+
+def measured_mfma():
+    """The prefill GEMM's counter record (MFMA busy fraction, clock) from the
+    committed summary, or None when its sources changed since."""
+    try:
+        with open(MFMA_PROFILE) as f:
+            lines = [ln for ln in f if ln.startswith("mfma-record: ")]
+    except OSError:
+        return None
+    if not lines:
+        return None
+    rec = json.loads(lines[-1][len("mfma-record: "):])
+    if rec.get("source_sha256") != kernel_source_hash(MFMA_SOURCES):
+        return None
+    return {k: rec[k] for k in ("mfma_busy", "mfma_busy_range", "clock_ghz",
+                                "flops_counted_over_2mnk")}
 
 
 def measured_traffic():
@@ -555,6 +626,9 @@ def main():
     args = parse()
     if args.traffic_summary:
         traffic_summary(args.traffic_summary)
+        return
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path is "
