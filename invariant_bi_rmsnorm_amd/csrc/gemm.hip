@@ -568,25 +568,27 @@ static void launch_tiled(const void* A, const void* W, void* C, int M, int N, in
 // g = wave / 4 holds one wave on each SIMD and owns output rows 128 g ..
 // 128 g + 127; wave wn of a group owns columns 64 wn .. 64 wn + 63 (8 x 4
 // MFMA tiles).  Phases are separated by workgroup barriers: in every phase
-// one group reads its fragments of a K-tile from LDS and issues direct copies
-// while the other runs its 32 MFMAs on the K-tile it read in the phase before,
-// so each SIMD's matrix core has work while its other wave feeds LDS.  Group 0
-// takes K-tile s in phases 2s (memory) and 2s + 1 (MFMA), group 1 one phase
-// later.  Each output element is still one MFMA chain over the K-tiles in
-// ascending order, as on every other path.
+// one group reads its fragments of a line stage (two K-tiles) from LDS and
+// issues direct copies while the other runs its 64 MFMAs on the stage it read
+// in the phase before, so each SIMD's matrix core has work while its other
+// wave feeds LDS.  Group 0 takes stage L in phases 2L (memory) and 2L + 1
+// (MFMA), group 1 one phase later.  Each output element is still one MFMA
+// chain over the K-tiles in ascending order, as on every other path.
 //
 // LDS holds two line stages of 64 KiB: 128-byte lines (two K-tiles) of 256 A
 // rows then 256 W rows, 8 rows per 1 KiB block, the 16-byte unit u of row r at
-// slot u ^ (r & 7); each direct copy moves 8 whole lines.  The copies of line
-// stage L + 1 are spread over the four memory phases of K-tiles 2L and 2L + 1
-// (four per wave): W rows 0-127 (group 0), W rows 128-255 (group 1), then the
-// A rows of group 0's half and of group 1's.  Group 0 waits for its copies at
-// the end of phase 4L + 3, before it reads the stage in phase 4L + 4; group 1
-// waits for its W copies then and for its A copies at the end of phase
-// 4L + 4, before its own read.  Workgroups are mapped so that each XCD
-// (blockIdx % 8) takes a contiguous range of tiles in grouped order (4
-// row-blocks at a time), so the tiles resident on one XCD share A rows and W
-// columns in its L2.
+// slot u ^ (r & 7); each copy moves 8 whole lines.  Copies are buffer loads
+// to LDS: the tile's rows of A and of W are two buffers, so one lane offset
+// serves every copy (the block's row offset rides in the scalar offset) and
+// rows past M or N read as zeros (they feed only outputs that are not
+// stored).  Stage L + 1 goes to the slot that stage L - 1 used, which group 1
+// finished reading in phase 2L - 1: group 0 copies the W rows and its own A
+// rows in phase 2L (12 per wave), group 1 its A rows in phase 2L + 1 (4 per
+// wave), and each group waits for its copies at the end of its next MFMA
+// phase, before the first read that needs them.  Workgroups are mapped so
+// that each XCD (blockIdx % 8) takes a contiguous range of tiles in grouped
+// order (4 row-blocks at a time), so the tiles resident on one XCD share A
+// rows and W columns in its L2.
 // ---------------------------------------------------------------------------
 // a[i] = LDS[ba + 2048 i] (i < 8), b[j] = LDS[bb + 2048 j] (j < 4), not waited for
 __device__ __forceinline__ void lds_read_8_4_nowait(u32x4_t (&a)[8], u32x4_t (&b)[4],
@@ -615,8 +617,8 @@ __device__ __forceinline__ void lds_wait_8_4(u32x4_t (&a)[8], u32x4_t (&b)[4]) {
 
 template <int OUTF32>
 __global__ __launch_bounds__(512) void k_gemm_big(const uint16_t* __restrict__ A,
-                                                  const uint16_t* __restrict__ W, void* C,
-                                                  int M, int N, int K, int tiles_m, int tiles_n) {
+                                                   const uint16_t* __restrict__ W, void* C,
+                                                   int M, int N, int K, int tiles_m, int tiles_n) {
   constexpr int NS = 2, STAGE = 64 * 1024;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -624,33 +626,37 @@ __global__ __launch_bounds__(512) void k_gemm_big(const uint16_t* __restrict__ A
   const int xcd = bid % 8, idx = bid / 8;
   const int per = nt / 8, rem = nt % 8;
   const int t = xcd * per + (xcd < rem ? xcd : rem) + idx;
-  // grouped order inside that range: GM row-blocks at a time, row fastest
   constexpr int GM = 4;
   const int grp = t / (GM * tiles_n), first = grp * GM;
   const int gm = min(GM, tiles_m - first);
   const int tm = first + (t % (GM * tiles_n)) % gm, tn = (t % (GM * tiles_n)) / gm;
   const int m0 = tm * 256, n0 = tn * 256;
-  const int g = wave >> 2, wn = wave & 3;   // group = row half; column quarter
+  const int g = wave >> 2, wn = wave & 3;
   const int KT = (K + 31) >> 5, NLS = (KT + 1) >> 1;
-
-  // copy lane: row (lane >> 3) of its block, slot (lane & 7) holds unit
-  // slot ^ (row & 7) of that row's 128-byte span
+  // buffers over the tile's rows (word 3 = 0x20000: data format 32-bit, as a
+  // raw buffer needs); record counts in bytes, so reads past them give zeros
+  const uint32_t rowbytes = (uint32_t)K * 2;
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(A + (long)m0 * K), (short)0, (int)(min(256, M - m0) * rowbytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W + (long)n0 * K), (short)0, (int)(min(256, N - n0) * rowbytes), 0x00020000);
   const int crow = lane >> 3, cunit = (lane & 7) ^ crow;
-  // NB copies of line stage ls: row blocks base + wn + 4 i of X (rows from x0,
-  // clamped to xmax) into stage blocks sblk0 + ..
-  auto issue = [&](auto nb_c, int ls, const uint16_t* __restrict__ X, int x0, int xmax,
-                   int sblk0, int base) {
+  const uint32_t voff = crow * rowbytes + cunit * 16;
+  // NB copies of line stage ls: row blocks base + wn + 4 i of buffer r into
+  // stage blocks sblk0 + ..  (lane: row crow of the block, unit cunit of its
+  // 128-byte line, written to slot lane & 7)
+  auto issue = [&](auto nb_c, int ls, __amdgpu_buffer_rsrc_t r, int sblk0, int base) {
     constexpr int NB = decltype(nb_c)::value;
     char* slot = smem + (ls % NS) * STAGE;
-    int kk = ls * 64 + cunit * 8;
-    kk = kk < K ? kk : 0;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int blk = base + wn + 4 * i;
-      dma16(X + (long)min(x0 + blk * 8 + crow, xmax) * K + kk, slot + (sblk0 + blk) * 1024);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(slot + (sblk0 + blk) * 1024), 16,
+                                               voff, blk * 8 * rowbytes + ls * 128, 0, 0);
     }
   };
-  // read lane: row (lane & 15) of a 16-row tile, unit 4 kt + (lane >> 4)
+  using I4 = std::integral_constant<int, 4>;
+  using I8 = std::integral_constant<int, 8>;
   auto rd_off = [&](int kt) {
     const int r = lane & 15, u = 4 * kt + (lane >> 4);
     return (uint32_t)(((r >> 3) & 1) * 1024 + (r & 7) * 128 + 16 * (u ^ (r & 7)));
@@ -663,48 +669,60 @@ __global__ __launch_bounds__(512) void k_gemm_big(const uint16_t* __restrict__ A
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  u32x4_t a[8], bw[4];
+  u32x4_t a0[8], b0[4], a1[8], b1[4];
 
-  // prologue: line stage 0, A rows by group 0 and W rows by group 1
-  if (g == 0) issue(std::integral_constant<int, 8>{}, 0, A, m0, M - 1, 0, 0);
-  else issue(std::integral_constant<int, 8>{}, 0, W, n0, N - 1, 32, 0);
+  // prologue: stage 0, A rows by group 0 and W rows by group 1
+  if (g == 0) issue(I8{}, 0, rA, 0, 0);
+  else issue(I8{}, 0, rW, 32, 0);
   BI_WAIT_VMCNT(0);
   __builtin_amdgcn_s_barrier();
   if (g == 1) __builtin_amdgcn_s_barrier();   // phase 0: group 0 alone
-  // one K-tile: its memory phase, then its MFMA phase.  `tail` (the last
-  // K-tile when K % 32 != 0): units past K enter both operands as zeros.
-  auto step = [&](int s, bool tail) {
-    // ---- memory phase of K-tile s
-    const uint32_t sb = lds0 + ((s >> 1) % NS) * STAGE + ((s & 1) ? off1 : off0);
-    lds_read_8_4_nowait(a, bw, sb + (8 * g) * 2048, sb + 32 * 1024 + (4 * wn) * 2048);
-    if ((s >> 1) + 1 < NLS) {
-      using I4 = std::integral_constant<int, 4>;
-      if (s & 1) issue(I4{}, (s >> 1) + 1, A, m0, M - 1, 0, 16 * g);
-      else issue(I4{}, (s >> 1) + 1, W, n0, N - 1, 32, 16 * g);
+  // one line stage: its memory phase, then its MFMA phase.  `tail` (the last
+  // stage): units at k >= K enter both operands as zeros, and a stage with a
+  // single K-tile runs only its MFMAs.
+  auto step = [&](int L, bool tail) {
+    const uint32_t sb = lds0 + (L % NS) * STAGE + (8 * g) * 2048;
+    const uint32_t sw = lds0 + (L % NS) * STAGE + 32 * 1024 + (4 * wn) * 2048;
+    const bool two = 2 * L + 1 < KT;
+    lds_read_8_4_nowait(a0, b0, sb + off0, sw + off0);
+    if (two) lds_read_8_4_nowait(a1, b1, sb + off1, sw + off1);
+    if (L + 1 < NLS) {
+      if (g == 0) {
+        issue(I8{}, L + 1, rW, 32, 0);
+        issue(I4{}, L + 1, rA, 0, 0);
+      } else {
+        issue(I4{}, L + 1, rA, 0, 16);
+      }
     }
-    lds_wait_8_4(a, bw);
-    if (tail && s * 32 + 8 * (lane >> 4) >= K) {
+    lds_wait_8_4(a0, b0);
+    if (two) lds_wait_8_4(a1, b1);
+    if (tail) {
+      const u32x4_t zero = {0, 0, 0, 0};
+      const bool z0 = 2 * L * 32 + 8 * (lane >> 4) >= K;
+      const bool z1 = (2 * L + 1) * 32 + 8 * (lane >> 4) >= K;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) a[i] = u32x4_t{0, 0, 0, 0};
+      for (int i = 0; i < 8; ++i) a0[i] = z0 ? zero : a0[i], a1[i] = z1 ? zero : a1[i];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bw[j] = u32x4_t{0, 0, 0, 0};
+      for (int j = 0; j < 4; ++j) b0[j] = z0 ? zero : b0[j], b1[j] = z1 ? zero : b1[j];
     }
-    // end of phase 4L + 3 for group 1: its W copies (the older four) are in
-    if ((s & 1) && g == 1) BI_WAIT_VMCNT(4);
     __builtin_amdgcn_s_barrier();
-    // ---- MFMA phase of K-tile s
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma(a[i], bw[j], acc[i][j]);
-    // end of phase 4L + 3 (group 0) / 4L + 4 (group 1): all its copies are in
-    if (s & 1) BI_WAIT_VMCNT(0);
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma(a0[i], b0[j], acc[i][j]);
+    if (two) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma(a1[i], b1[j], acc[i][j]);
+    }
+    BI_WAIT_VMCNT(0);   // this group's copies of stage L + 1
     // the last phase (group 1's last MFMAs) ends without a barrier: group 0
     // goes on to its stores
-    if (g == 0 || s + 1 < KT) __builtin_amdgcn_s_barrier();
+    if (g == 0 || L + 1 < NLS) __builtin_amdgcn_s_barrier();
   };
-  for (int s = 0; s < KT - 1; ++s) step(s, false);
-  step(KT - 1, (K & 31) != 0);
+  for (int L = 0; L < NLS - 1; ++L) step(L, false);
+  step(NLS - 1, true);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -715,7 +733,7 @@ __global__ __launch_bounds__(512) void k_gemm_big(const uint16_t* __restrict__ A
 
 template <int OUTF32>
 static void launch_big(const void* A, const void* W, void* C, int M, int N, int K,
-                       hipStream_t s) {
+                        hipStream_t s) {
   constexpr size_t lds = 2 * 64 * 1024;
   static bool attr = false;
   if (!attr) {
@@ -741,7 +759,8 @@ void gemm_dispatch(const void* A, const void* W, void* C, int M, int N, int K, i
   if (M <= 64) {
     if (out_f32) dispatch_small<1>(A, W, C, M, N, K, s);
     else dispatch_small<0>(A, W, C, M, N, K, s);
-  } else if (M >= 1024 && N >= 2048) {
+  } else if (M >= 1024 && N >= 2048 && K < (1 << 22)) {
+    // (the large-tile kernel's buffers hold 256 rows of K: byte counts < 2^31)
     if (out_f32) launch_big<1>(A, W, C, M, N, K, s);
     else launch_big<0>(A, W, C, M, N, K, s);
   } else {
