@@ -509,20 +509,21 @@ static void launch_small_k(const void* A, const void* W, void* C, int M, int N, 
 // few rows of W at a time (measured faster than the model's pick there).
 struct SmallShape {
   int mb, ct;
+  long cost;   // rounds of 256 workgroups x (MB + 2 CT): KiB per CU per 32 k
 };
 static SmallShape small_shape(int M, int N) {
-  if (M <= 8) return SmallShape{1, 1};
   const long tiles = (N + 15) / 16;
-  SmallShape best{8, 1};
-  long best_cost = -1, best_wgs = 0;
+  if (M <= 8) return SmallShape{1, 1, ((tiles + 255) / 256) * 3};
+  SmallShape best{8, 1, -1};
+  long best_wgs = 0;
   for (int mb : {1, 2, 4, 6, 8}) {
     const long rg = (M + 8 * mb - 1) / (8 * mb);
     for (int ct : {1, 2, 3, 4, 7, 8}) {
       if (mb == 1 && ct != 1) continue;   // 8-row blocks: 16-row strips, two per CU
       const long wgs = rg * ((tiles + ct - 1) / ct);
       const long cost = ((wgs + 255) / 256) * (mb + 2 * ct);
-      if (best_cost < 0 || cost < best_cost || (cost == best_cost && wgs < best_wgs))
-        best = SmallShape{mb, ct}, best_cost = cost, best_wgs = wgs;
+      if (best.cost < 0 || cost < best.cost || (cost == best.cost && wgs < best_wgs))
+        best = SmallShape{mb, ct, cost}, best_wgs = wgs;
     }
   }
   return best;
@@ -754,13 +755,26 @@ void gemm_splitk_atomic(const void* A, const void* W, float* C32, int M, int N, 
   dispatch_small<2>(A, W, C32, M, N, K, s, splits, kslice);
 }
 
+// Which kernel runs never changes a bit (every path keeps the same chain per
+// element); the choice is speed alone.  Measured at N 4096-14336 and K
+// 4096-14336 for 64 < M <= 1000: the skinny kernel takes about 0.48 ns x its
+// cost x K and the large-tile kernel about 19 ns x its rounds of 256 tiles x
+// K, and the 128-tile kernel was never the faster of the three.  So beyond 64
+// rows the skinny kernel runs while its cost stays under 40 x the large-tile
+// rounds; the 128-tile kernel remains for N < 2048.
 void gemm_dispatch(const void* A, const void* W, void* C, int M, int N, int K, int out_f32,
                    hipStream_t s) {
-  if (M <= 64) {
+  // (the large-tile kernel's buffers hold 256 rows of K: byte counts < 2^31)
+  const bool big_ok = N >= 2048 && K < (1 << 22);
+  bool small = M <= 64;
+  if (!small && big_ok) {
+    const long rounds = (((long)(M + 255) / 256) * ((N + 255) / 256) + 255) / 256;
+    small = small_shape(M, N).cost < 40 * rounds;
+  }
+  if (small) {
     if (out_f32) dispatch_small<1>(A, W, C, M, N, K, s);
     else dispatch_small<0>(A, W, C, M, N, K, s);
-  } else if (M >= 1024 && N >= 2048 && K < (1 << 22)) {
-    // (the large-tile kernel's buffers hold 256 rows of K: byte counts < 2^31)
+  } else if (big_ok) {
     if (out_f32) launch_big<1>(A, W, C, M, N, K, s);
     else launch_big<0>(A, W, C, M, N, K, s);
   } else {

@@ -268,12 +268,30 @@ def test_gemm_rows_invariant_across_M_and_position():
         L.bi_gemm(a, W, c)
         return c
 
-    full = run(list(range(300)))            # tiled kernel
+    full = run(list(range(300)))            # 300 rows: the skinny kernel in row groups
     rng = np.random.default_rng(0)
     for M in [1, 2, 7, 16, 17, 33, 64, 65, 128, 200]:
         rows = list(rng.choice(300, size=M, replace=False))
         got = run(rows)
         assert torch.equal(got.view(torch.int32), full[rows].view(torch.int32)), f"M={M}"
+
+
+@pytest.mark.parametrize("M,N", [(160, 6144), (576, 14336), (1000, 4096)])
+def test_gemm_mid_M_rows_equal_alone(M, N):
+    # past 64 rows the kernel is chosen by cost (skinny kernel in row groups
+    # at 160 x 6144, 256 x 256 tiles at the others); every row still equals
+    # the same row computed alone, bit for bit
+    K = 4096
+    A = synth.normal((M, K), seed=M).to(torch.bfloat16).to(dev())
+    W = synth.normal((N, K), seed=N, std=0.02).to(torch.bfloat16).to(dev())
+    full = torch.empty((M, N), dtype=torch.bfloat16, device=dev())
+    L.bi_gemm(A, W, full)
+    rng = np.random.default_rng(M)
+    for m in (1, 37, 64):
+        rows = sorted(rng.choice(M, size=m, replace=False).tolist())
+        c = torch.empty((m, N), dtype=torch.bfloat16, device=dev())
+        L.bi_gemm(A[rows].contiguous(), W, c)
+        assert torch.equal(c.view(torch.int16), full[rows].view(torch.int16)), f"m={m}"
 
 
 @pytest.mark.parametrize("N", [16448, 14336])
