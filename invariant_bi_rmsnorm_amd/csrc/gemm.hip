@@ -150,9 +150,10 @@ __device__ __forceinline__ void store_rope(const RopeArgs& ra, const f32x4_t& ac
 }
 
 // ---------------------------------------------------------------------------
-// small-M kernel (M <= 64): one workgroup per CT 16-column strips of W and one
-// group of 8 MB rows of A (blockIdx.z; MB and CT are chosen from M and N so
-// that rows x columns per workgroup balance).  Per CU the bytes to move are
+// skinny kernel (every M <= 64, and larger M while it is the cheaper kernel):
+// one workgroup per CT 16-column strips of W and one group of 8 MB rows of A
+// (blockIdx.z; MB and CT are chosen from M and N so that rows x columns per
+// workgroup balance).  Per CU the bytes to move are
 // its rows of A plus its strips of W, so both ride the fastest path into a
 // CU: direct global->LDS copies of
 // whole 128-byte lines (8 rows x 128 bytes per instruction).  One wave
