@@ -120,6 +120,44 @@ def _i32(t: torch.Tensor):
     return _ptr(t)
 
 
+def _need(ok: bool, fn: str, msg: str) -> None:
+    """Host-side argument check of the binding: raise before any pointer is
+    taken or any kernel is launched."""
+    if not ok:
+        raise ValueError(f"{fn}: {msg}")
+
+
+def _check_gemm_args(fn: str, A, W, C) -> tuple:
+    M, K = A.shape
+    N = W.shape[0]
+    _need(W.dim() == 2 and W.shape[1] == K and tuple(C.shape) == (M, N), fn,
+          f"shape mismatch A{tuple(A.shape)} W{tuple(W.shape)} C{tuple(C.shape)}")
+    # the kernel reads W with A's element size: a mixed pair would read past W
+    _need(W.dtype == A.dtype, fn, f"W is {W.dtype} but A is {A.dtype}")
+    return M, N, K
+
+
+def _check_attn_args(fn: str, q, k_pool, v_pool, block_table, B: int) -> None:
+    _need(k_pool.dim() == 4 and tuple(v_pool.shape) == tuple(k_pool.shape), fn,
+          f"pools must be [pages][h_kv][page][d_h] of one shape, got {tuple(k_pool.shape)} "
+          f"and {tuple(v_pool.shape)}")
+    _need(k_pool.dtype == q.dtype and v_pool.dtype == q.dtype, fn,
+          f"q is {q.dtype} but the pools are {k_pool.dtype} / {v_pool.dtype}")
+    _need(k_pool.shape[3] == q.shape[2], fn, f"d_h of q ({q.shape[2]}) and pools "
+          f"({k_pool.shape[3]}) differ")
+    _need(block_table.dim() == 2 and block_table.shape[0] >= B, fn,
+          f"block_table {tuple(block_table.shape)} has fewer than {B} rows")
+
+
+def _check_partials(fn: str, part_ml, part_acc, rows: int, h: int, d_h: int) -> None:
+    _need(part_ml.dtype == torch.float32 and part_acc.dtype == torch.float32, fn,
+          "partials must be fp32")
+    _need(part_ml.numel() >= rows * h * 2, fn,
+          f"part_ml holds {part_ml.numel()} floats, needs {rows} x {h} x 2")
+    _need(part_acc.numel() >= rows * h * d_h, fn,
+          f"part_acc holds {part_acc.numel()} floats, needs {rows} x {h} x {d_h}")
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -165,10 +203,7 @@ def bi_add_rmsnorm(h, o, gamma, y, eps: float, stream=None):
 
 
 def bi_gemm(A, W, C, stream=None):
-    M, K = A.shape
-    N = W.shape[0]
-    if W.shape[1] != K or tuple(C.shape) != (M, N):
-        raise ValueError(f"shape mismatch A{tuple(A.shape)} W{tuple(W.shape)} C{tuple(C.shape)}")
+    M, N, K = _check_gemm_args("bi_gemm", A, W, C)
     _check("bi_gemm", load().bi_gemm(_ptr(A), _ptr(W), _ptr(C), M, N, K, _dt(A), _dt(C),
                                      _stream(stream)))
     return C
@@ -205,6 +240,11 @@ def bi_gemm_qkv_rope(A, W, h: int, h_kv: int, d_h: int, pos, cos_t, sin_t, slot_
 def bi_decode_attn(q, k_pool, v_pool, block_table, kv_len, chunk_off, total_chunks: int,
                    kv_chunk: int, scale: float, part_ml, part_acc, stream=None):
     B, h, d_h = q.shape
+    _check_attn_args("bi_decode_attn", q, k_pool, v_pool, block_table, B)
+    _need(kv_len.numel() == B, "bi_decode_attn", f"kv_len has {kv_len.numel()} entries, not {B}")
+    _need(chunk_off.numel() == B + 1, "bi_decode_attn",
+          f"chunk_off has {chunk_off.numel()} entries, not B + 1 = {B + 1}")
+    _check_partials("bi_decode_attn", part_ml, part_acc, total_chunks, h, d_h)
     _, h_kv, page_size, _ = k_pool.shape
     _check("bi_decode_attn", load().bi_decode_attn(
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _i32(block_table), _i32(kv_len), _i32(chunk_off),
@@ -214,6 +254,14 @@ def bi_decode_attn(q, k_pool, v_pool, block_table, kv_len, chunk_off, total_chun
 
 def bi_merge_partials(part_ml, part_acc, chunk_off, out, stream=None):
     B, h, d_h = out.shape
+    _need(chunk_off.numel() == B + 1, "bi_merge_partials",
+          f"chunk_off has {chunk_off.numel()} entries, not B + 1 = {B + 1}")
+    _need(part_acc.dim() == 3 and tuple(part_acc.shape[1:]) == (h, d_h)
+          and part_ml.dim() == 3 and tuple(part_ml.shape[1:]) == (h, 2)
+          and part_ml.shape[0] == part_acc.shape[0], "bi_merge_partials",
+          f"partials {tuple(part_ml.shape)} / {tuple(part_acc.shape)} do not match "
+          f"[rows][{h}][2] / [rows][{h}][{d_h}]")
+    _check_partials("bi_merge_partials", part_ml, part_acc, part_acc.shape[0], h, d_h)
     _check("bi_merge_partials", load().bi_merge_partials(
         _ptr(part_ml), _ptr(part_acc), _i32(chunk_off), B, h, d_h, _ptr(out), _dt(out),
         _stream(stream)))
@@ -223,8 +271,13 @@ def bi_merge_partials(part_ml, part_acc, chunk_off, out, stream=None):
 def bi_prefill_attn(q, q_start, q_pos0, k_pool, v_pool, block_table, kv_chunk: int,
                     scale: float, out, stream=None):
     T, h, d_h = q.shape
-    _, h_kv, page_size, _ = k_pool.shape
     R = q_pos0.numel()
+    _check_attn_args("bi_prefill_attn", q, k_pool, v_pool, block_table, R)
+    _need(q_start.numel() == R + 1, "bi_prefill_attn",
+          f"q_start has {q_start.numel()} entries, not R + 1 = {R + 1}")
+    _need(tuple(out.shape) == (T, h, d_h), "bi_prefill_attn",
+          f"out {tuple(out.shape)} is not {(T, h, d_h)}")
+    _, h_kv, page_size, _ = k_pool.shape
     _check("bi_prefill_attn", load().bi_prefill_attn(
         _ptr(q), _i32(q_start), _i32(q_pos0), R, T, _ptr(k_pool), _ptr(v_pool),
         _i32(block_table), h, h_kv, d_h, page_size, block_table.shape[1], kv_chunk, scale,
@@ -329,10 +382,7 @@ def bi_rmsnorm_free(x, gamma, y, eps: float, stream=None):
 
 
 def bi_gemm_free(A, W, C, stream=None):
-    M, K = A.shape
-    N = W.shape[0]
-    if W.shape[1] != K or tuple(C.shape) != (M, N):
-        raise ValueError(f"shape mismatch A{tuple(A.shape)} W{tuple(W.shape)} C{tuple(C.shape)}")
+    M, N, K = _check_gemm_args("bi_gemm_free", A, W, C)
     ws, n = _workspace(load().bi_gemm_free_workspace_bytes(M, N, K), A.device)
     _check("bi_gemm_free", load().bi_gemm_free(_ptr(A), _ptr(W), _ptr(C), M, N, K, _dt(A),
                                                _dt(C), ws, n, _stream(stream)))
@@ -344,6 +394,11 @@ def bi_decode_attn_free(q, k_pool, v_pool, block_table, kv_len, max_kv_len: int,
     """Decode attention with the occupancy-driven split policy; writes the
     merged output directly.  max_kv_len: the host's bound on kv_len."""
     B, h, d_h = q.shape
+    _check_attn_args("bi_decode_attn_free", q, k_pool, v_pool, block_table, B)
+    _need(kv_len.numel() == B, "bi_decode_attn_free",
+          f"kv_len has {kv_len.numel()} entries, not {B}")
+    _need(tuple(out.shape) == (B, h, d_h), "bi_decode_attn_free",
+          f"out {tuple(out.shape)} is not {(B, h, d_h)}")
     _, h_kv, page_size, _ = k_pool.shape
     ws, n = _workspace(load().bi_decode_attn_free_workspace_bytes(B, h, d_h, max_kv_len),
                        q.device)
@@ -356,6 +411,9 @@ def bi_decode_attn_free(q, k_pool, v_pool, block_table, kv_len, max_kv_len: int,
 
 def bi_merge_partials_free(part_ml, part_acc, chunk_off, out, stream=None):
     B, h, d_h = out.shape
+    _need(chunk_off.numel() == B + 1, "bi_merge_partials_free",
+          f"chunk_off has {chunk_off.numel()} entries, not B + 1 = {B + 1}")
+    _check_partials("bi_merge_partials_free", part_ml, part_acc, part_acc.shape[0], h, d_h)
     _check("bi_merge_partials_free", load().bi_merge_partials_free(
         _ptr(part_ml), _ptr(part_acc), _i32(chunk_off), B, h, d_h, _ptr(out), _dt(out),
         _stream(stream)))
@@ -365,8 +423,11 @@ def bi_merge_partials_free(part_ml, part_acc, chunk_off, out, stream=None):
 def bi_prefill_attn_free(q, q_start, q_pos0, k_pool, v_pool, block_table, scale: float, out,
                          stream=None):
     T, h, d_h = q.shape
-    _, h_kv, page_size, _ = k_pool.shape
     R = q_pos0.numel()
+    _check_attn_args("bi_prefill_attn_free", q, k_pool, v_pool, block_table, R)
+    _need(q_start.numel() == R + 1, "bi_prefill_attn_free",
+          f"q_start has {q_start.numel()} entries, not R + 1 = {R + 1}")
+    _, h_kv, page_size, _ = k_pool.shape
     _check("bi_prefill_attn_free", load().bi_prefill_attn_free(
         _ptr(q), _i32(q_start), _i32(q_pos0), R, T, _ptr(k_pool), _ptr(v_pool),
         _i32(block_table), h, h_kv, d_h, page_size, block_table.shape[1], scale, _dt(q),

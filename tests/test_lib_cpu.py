@@ -68,3 +68,50 @@ def test_binding_argument_counts_match_header():
         name, params = m.group(1), m.group(2).strip()
         n = 0 if params in ("", "void") else params.count(",") + 1
         assert len(L.SIGNATURES[name][1]) == n, name
+
+
+def test_binding_rejects_mismatched_buffers_before_launch():
+    """The binding's host checks raise before any pointer is taken: CPU
+    tensors reach them, so no GPU is needed.  Each case would otherwise let a
+    kernel read or write past a buffer (a bf16 W read with fp32 A's element
+    size; partials or offsets shorter than the chunk rows)."""
+    import torch
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    A = torch.zeros((4, 16), dtype=f32)
+    with pytest.raises(ValueError, match="W is"):
+        L.bi_gemm(A, torch.zeros((8, 16), dtype=bf), torch.zeros((4, 8), dtype=f32))
+    with pytest.raises(ValueError, match="W is"):
+        L.bi_gemm_free(A, torch.zeros((8, 16), dtype=bf), torch.zeros((4, 8), dtype=f32))
+    with pytest.raises(ValueError, match="shape mismatch"):
+        L.bi_gemm(A, torch.zeros((8, 12), dtype=f32), torch.zeros((4, 8), dtype=f32))
+
+    B, h, h_kv, d_h, tot = 2, 4, 2, 64, 5
+    q = torch.zeros((B, h, d_h), dtype=bf)
+    kp = torch.zeros((8, h_kv, 16, d_h), dtype=bf)
+    bt = torch.zeros((B, 4), dtype=i32)
+    kvl = torch.ones(B, dtype=i32)
+    off = torch.zeros(B + 1, dtype=i32)
+    ml = torch.zeros((tot, h, 2), dtype=f32)
+    acc = torch.zeros((tot, h, d_h), dtype=f32)
+    with pytest.raises(ValueError, match="part_acc"):
+        L.bi_decode_attn(q, kp, kp, bt, kvl, off, tot, 64, 0.1, ml, acc[:tot - 1])
+    with pytest.raises(ValueError, match="part_ml"):
+        L.bi_decode_attn(q, kp, kp, bt, kvl, off, tot, 64, 0.1, ml[:2], acc)
+    with pytest.raises(ValueError, match="chunk_off"):
+        L.bi_decode_attn(q, kp, kp, bt, kvl, off[:B], tot, 64, 0.1, ml, acc)
+    with pytest.raises(ValueError, match="kv_len"):
+        L.bi_decode_attn(q, kp, kp, bt, kvl[:1], off, tot, 64, 0.1, ml, acc)
+    with pytest.raises(ValueError, match="pools"):
+        L.bi_decode_attn(q, kp, kp.float(), bt, kvl, off, tot, 64, 0.1, ml, acc)
+    with pytest.raises(ValueError, match="block_table"):
+        L.bi_decode_attn(q, kp, kp, bt[:1], kvl, off, tot, 64, 0.1, ml, acc)
+    with pytest.raises(ValueError, match="fp32"):
+        L.bi_decode_attn(q, kp, kp, bt, kvl, off, tot, 64, 0.1, ml.to(bf), acc)
+    out = torch.zeros((B, h, d_h), dtype=bf)
+    with pytest.raises(ValueError, match="chunk_off"):
+        L.bi_merge_partials(ml, acc, off[:B], out)
+    with pytest.raises(ValueError, match="partials"):
+        L.bi_merge_partials(ml, acc[:, :, :32], off, out)
+    with pytest.raises(ValueError, match="q_start"):
+        L.bi_prefill_attn(q, torch.zeros(1, dtype=i32), torch.zeros(2, dtype=i32), kp, kp,
+                          bt, 64, 0.1, q.clone())
