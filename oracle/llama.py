@@ -7,7 +7,11 @@ a request cannot depend on one.  KV lives in the oracle's own paged pools
 (numpy), written at the same (page, slot) addresses.
 
 The model is bf16 throughout, so attention takes the bf16-weight form
-(p rounded to bf16 before the sums, as matrix cores consume it).
+(p rounded to bf16 before the sums, as matrix cores consume it).  With
+bf16=False every intermediate stays fp32 and attention keeps fp32 weights:
+the same wiring without the carried rounding, which is how the composition
+itself is checked against a float64 forward written from the layer
+definition (tests/test_oracle_model_pin.py).
 
 Layer (pre-norm, SwiGLU, RoPE on q and k):
   x = rmsnorm(h) ; qkv = x W_qkv^T ; q,k = rope(q,k) ; append k,v
@@ -33,12 +37,14 @@ class OracleModel:
     scale and rope (bool); weights: object with embed, layers (attn_norm,
     wqkv, wo, ffn_norm, wgu, wdown), final_norm, lm_head (torch or numpy);
     gemm: the GEMM primitive (the oracle's serial one unless a test swaps in
-    another valid order to measure how far two orders drift apart)."""
+    another valid order to measure how far two orders drift apart); bf16:
+    carry bf16 between operations (the model's precision) or fp32."""
 
     def __init__(self, cfg, weights, num_pages: int, cos_t=None, sin_t=None, layers=None,
-                 gemm=gemm):
+                 gemm=gemm, bf16: bool = True):
         self.cfg = cfg
         self.gemm = gemm
+        self.rb = bool(bf16)
         self.nl = layers if layers is not None else len(weights.layers)
         self.embed = _np(weights.embed)
         self.layers = []
@@ -53,41 +59,52 @@ class OracleModel:
         self.k = np.zeros(shape, np.float32)
         self.v = np.zeros(shape, np.float32)
 
+    def layer(self, li: int, h, pages, pos0: int):
+        """Decoder layer li on the residual rows h [n, d] of one request at
+        positions pos0 .. pos0 + n - 1: appends their K and V to the layer's
+        pool at the request's pages and returns the new residual rows."""
+        c, rb = self.cfg, self.rb
+        lw = self.layers[li]
+        n = h.shape[0]
+        pos = np.arange(pos0, pos0 + n, dtype=np.int32)
+        bt = np.asarray(pages, np.int32)[None, :]
+        hd = c.h * c.d_h
+        kvd = c.h_kv * c.d_h
+        x = rmsnorm(h, lw["attn_norm"], c.eps, rb)
+        qkv = self.gemm(x, lw["wqkv"], rb)
+        q = qkv[:, :hd].reshape(n, c.h, c.d_h)
+        k = qkv[:, hd:hd + kvd].reshape(n, c.h_kv, c.d_h)
+        v = qkv[:, hd + kvd:].reshape(n, c.h_kv, c.d_h)
+        if c.rope:
+            q = rope(q, pos, self.cos, self.sin, rb)
+            k = rope(k, pos, self.cos, self.sin, rb)
+        pg = bt[0, pos // c.page_size]
+        self.k[li, pg, :, pos % c.page_size] = k
+        self.v[li, pg, :, pos % c.page_size] = v
+        if n == 1:
+            a = decode_attn(q, self.k[li], self.v[li], bt, np.array([pos0 + 1], np.int32),
+                            c.h_kv, c.page_size, c.kv_chunk, c.scale, rb, p_bf16=rb)
+        else:
+            a = prefill_attn(q, np.array([0, n], np.int32), np.array([pos0], np.int32),
+                             self.k[li], self.v[li], bt, c.h_kv, c.page_size, c.kv_chunk,
+                             c.scale, rb, p_bf16=rb)
+        h = add(h, self.gemm(a.reshape(n, hd), lw["wo"], rb), rb)
+        x = rmsnorm(h, lw["ffn_norm"], c.eps, rb)
+        act = silu_mul(self.gemm(x, lw["wgu"], rb), rb)
+        return add(h, self.gemm(act, lw["wdown"], rb), rb)
+
+    def head(self, h):
+        """Final norm and LM head of residual rows h [n, d]: fp32 logits [n, V]."""
+        x = rmsnorm(h, self.final_norm, self.cfg.eps, self.rb)
+        return self.gemm(x, self.lm_head, False)
+
     def forward(self, pages, pos0: int, tokens, want_logits: bool = True):
         """Rows tokens[0..n) of one request at positions pos0.. ; returns the
         fp32 logits of the last row (or None) and its argmax."""
-        c = self.cfg
-        n = len(tokens)
-        pos = np.arange(pos0, pos0 + n, dtype=np.int32)
-        bt = np.asarray(pages, np.int32)[None, :]
         h = self.embed[np.asarray(tokens, np.int64)]
-        hd = c.h * c.d_h
-        kvd = c.h_kv * c.d_h
-        for li, lw in enumerate(self.layers):
-            x = rmsnorm(h, lw["attn_norm"], c.eps, True)
-            qkv = self.gemm(x, lw["wqkv"], True)
-            q = qkv[:, :hd].reshape(n, c.h, c.d_h)
-            k = qkv[:, hd:hd + kvd].reshape(n, c.h_kv, c.d_h)
-            v = qkv[:, hd + kvd:].reshape(n, c.h_kv, c.d_h)
-            if c.rope:
-                q = rope(q, pos, self.cos, self.sin, True)
-                k = rope(k, pos, self.cos, self.sin, True)
-            pg = bt[0, pos // c.page_size]
-            self.k[li, pg, :, pos % c.page_size] = k
-            self.v[li, pg, :, pos % c.page_size] = v
-            if n == 1:
-                a = decode_attn(q, self.k[li], self.v[li], bt, np.array([pos0 + 1], np.int32),
-                                c.h_kv, c.page_size, c.kv_chunk, c.scale, True, p_bf16=True)
-            else:
-                a = prefill_attn(q, np.array([0, n], np.int32), np.array([pos0], np.int32),
-                                 self.k[li], self.v[li], bt, c.h_kv, c.page_size, c.kv_chunk,
-                                 c.scale, True, p_bf16=True)
-            h = add(h, self.gemm(a.reshape(n, hd), lw["wo"], True), True)
-            x = rmsnorm(h, lw["ffn_norm"], c.eps, True)
-            act = silu_mul(self.gemm(x, lw["wgu"], True), True)
-            h = add(h, self.gemm(act, lw["wdown"], True), True)
+        for li in range(self.nl):
+            h = self.layer(li, h, pages, pos0)
         if not want_logits:
             return None, None
-        x = rmsnorm(h[-1:], self.final_norm, c.eps, True)
-        logits = self.gemm(x, self.lm_head, False)
+        logits = self.head(h[-1:])
         return logits[0], int(argmax(logits)[0])
