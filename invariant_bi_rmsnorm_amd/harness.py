@@ -152,6 +152,8 @@ class FuzzConfig:
     p_swap: float = 0.5          # readmission by swap (else recompute)
     prefill_whole: bool = False  # baseline: prompt in one segment
     alone: bool = False          # baseline: one request at a time
+    p_full: float = 0.0          # per step, chance to take every runnable request
+    arrival_steps: int | None = None   # arrivals spread over this many steps
 
 
 class Runner:
@@ -169,6 +171,10 @@ class Runner:
         self.pool = PagePool(backend.num_pages, self.rng)
         self.reqs = [Request(r.rid, list(r.prompt), r.max_new) for r in reqs]
         self.steps = 0
+        self.max_segments = 0     # most requests in one step
+        self.max_rows = 0         # most rows in one step
+        self.swaps = 0            # preemptions readmitted by swap
+        self.recomputes = 0       # preemptions readmitted by recompute
 
     def _ensure_pages(self, r: Request, upto: int):
         need = -(-upto // self.b.page_size) - len(r.pages)
@@ -178,9 +184,11 @@ class Runner:
     def _preempt(self, r: Request):
         if self.rng.random() < self.fz.p_swap and r.computed > 0:
             r.saved_kv = (self.b.swap_out(r.pages), r.computed)
+            self.swaps += 1
         else:
             r.saved_kv = None
             r.computed = 0
+            self.recomputes += 1
         self.pool.give(r.pages)
         r.pages = []
         r.state = "preempted"
@@ -207,7 +215,8 @@ class Runner:
         order = list(range(len(self.reqs)))
         if not fz.alone:
             rng.shuffle(order)
-        arrivals = {rid: (0 if fz.alone else int(rng.integers(0, 4 + len(order) // 2)))
+        spread = fz.arrival_steps if fz.arrival_steps is not None else 4 + len(order) // 2
+        arrivals = {rid: (0 if fz.alone else int(rng.integers(0, max(1, spread))))
                     for rid in order}
         pending = list(order)
         while any(not r.done() for r in self.reqs):
@@ -233,8 +242,14 @@ class Runner:
             runnable = [r for r in self.reqs if r.state == "running" and not r.done()]
             if not runnable:
                 continue
+            share = None
             if fz.alone:
                 chosen = runnable[:1]
+            elif fz.p_full > 0 and rng.random() < fz.p_full:
+                # every runnable request, each with an equal share of the rows
+                perm = rng.permutation(len(runnable))[:fz.max_reqs]
+                chosen = [runnable[int(i)] for i in perm]
+                share = max(1, fz.max_rows // len(chosen))
             else:
                 k = int(rng.integers(1, min(len(runnable), fz.max_reqs) + 1))
                 chosen = list(rng.choice(runnable, size=k, replace=False))
@@ -242,7 +257,7 @@ class Runner:
             for r in chosen:
                 if budget <= 0:
                     break
-                n = self._segment_len(r, budget)
+                n = self._segment_len(r, budget if share is None else min(share, budget))
                 budget -= n
                 upto = r.computed + n
                 try:
@@ -256,6 +271,8 @@ class Runner:
                 owners.append((r, upto, want))
             if not segs:
                 continue
+            self.max_segments = max(self.max_segments, len(segs))
+            self.max_rows = max(self.max_rows, sum(len(sg.tokens) for sg in segs))
             rows, toks = self.b.step(segs)
             it = iter(zip(rows, toks))
             for r, upto, want in owners:
@@ -278,19 +295,30 @@ class Runner:
         return {r.rid: dict(r.records) for r in self.reqs}
 
 
-def verify(backend_factory, reqs: list, n_schedules: int, fuzz: FuzzConfig,
+def verify(backend_factory, reqs: list, n_schedules: int, fuzz,
            report_path: str | None = None) -> dict:
-    """Baseline (each request alone, prompt in one prefill) against
-    n_schedules fuzzed schedules; returns (and optionally writes) the
-    verdict report."""
-    base = Runner(backend_factory(), reqs, FuzzConfig(seed=fuzz.seed, alone=True,
+    """Baseline (each request alone, prompt in one prefill) against fuzzed
+    schedules; returns (and optionally writes) the verdict report.  fuzz: a
+    FuzzConfig, run under n_schedules seeds derived from its seed, or a list
+    of FuzzConfigs, one schedule each (n_schedules is then ignored)."""
+    first = fuzz[0] if isinstance(fuzz, (list, tuple)) else fuzz
+    base = Runner(backend_factory(), reqs, FuzzConfig(seed=first.seed, alone=True,
                                                       prefill_whole=True)).run()
     runs, cob, comp, remis = [], {r.rid: 0 for r in reqs}, {r.rid: True for r in reqs}, 0
-    seeds = list(np.random.Generator(np.random.PCG64(fuzz.seed + 1)).integers(1, 2**31, n_schedules))
-    for s in seeds:
-        fz = FuzzConfig(**{**fuzz.__dict__, "seed": int(s)})
+    if isinstance(fuzz, (list, tuple)):
+        configs = list(fuzz)
+    else:
+        seeds = np.random.Generator(np.random.PCG64(fuzz.seed + 1)).integers(1, 2**31,
+                                                                             n_schedules)
+        configs = [FuzzConfig(**{**fuzz.__dict__, "seed": int(s)}) for s in seeds]
+    max_segments = max_rows = swaps = recomputes = 0
+    for fz in configs:
         runner = Runner(backend_factory(), reqs, fz)
         runs.append(runner.run())
+        max_segments = max(max_segments, runner.max_segments)
+        max_rows = max(max_rows, runner.max_rows)
+        swaps += runner.swaps
+        recomputes += runner.recomputes
         for r in runner.reqs:
             cob[r.rid] += r.cobatched_steps
             comp[r.rid] = comp[r.rid] and r.done()
@@ -300,8 +328,11 @@ def verify(backend_factory, reqs: list, n_schedules: int, fuzz: FuzzConfig,
     out["rerecord_mismatch"] = remis
     if remis:
         out["verdict"] = RED
-    out["schedules"] = n_schedules
-    out["schedule_seeds"] = [int(s) for s in seeds]
+    out["schedules"] = len(configs)
+    out["max_requests_per_step"] = max_segments
+    out["max_rows_per_step"] = max_rows
+    out["preemptions"] = {"swap": swaps, "recompute": recomputes}
+    out["schedule_seeds"] = [int(fz.seed) for fz in configs]
     out["divergent"] = {str(k): v for k, v in rep["divergent"].items()}
     if report_path:
         write_report(report_path, out)

@@ -251,12 +251,18 @@ class Engine:
         return m
 
     # -- the forward pass ------------------------------------------------------
-    def forward(self, m, layers=None, timer=None) -> StepOutput:
+    def forward(self, m, layers=None, timer=None, tap=None) -> StepOutput:
         """One forward pass over the packed rows of `m` (from upload()).
         `timer`, if given, is called as timer(name, fn) around the kernels it
-        brackets ("decode_attn", "gemm_gate_up", ...)."""
+        brackets ("decode_attn", "gemm_gate_up", ...).  `tap`, if given, is
+        called as tap(name, layer, tensor) with the device buffer a kernel
+        has just written (packed rows; the buffers are reused by the next
+        layer, so a tap copies what it keeps): per layer "h_in", "x_attn",
+        "q" (after RoPE), "att", "o", "h_mid", "x_ffn", "gu" (when the gate/up
+        product is not fused), "act", "down", "h_out"; then "x_final"."""
         c, w, T = self.cfg, self.w, m["T"]
         run = timer if timer is not None else (lambda name, fn: fn())
+        see = tap if tap is not None else (lambda name, li, t: None)
         if T > self.cap:
             self._alloc(T)
         h, x, qkv, q, att = self.h[:T], self.x[:T], self.qkv[:T], self.q[:T], self.att[:T]
@@ -275,8 +281,10 @@ class Engine:
         for li, lw in enumerate(lws):
             kp, vp = self.pool.k[li], self.pool.v[li]
             nxt = lws[li + 1].attn_norm if li + 1 < len(lws) else w.final_norm
+            see("h_in", li, h)
             if not fuse:
                 run("rmsnorm", lambda: rms(h, lw.attn_norm, x, c.eps))
+            see("x_attn", li, x)
             if fuse and T <= 64 and c.dtype == torch.bfloat16 and c.d_h % 16 == 0:
                 # the same bits in one pass (RoPE + KV append in the GEMM's
                 # epilogue); the step measured 2.5% faster at batch 1, 0.5-1.2%
@@ -289,6 +297,7 @@ class Engine:
                 run("rope_kv_append", lambda: L.bi_rope_kv_append(
                     qkv, c.h, c.h_kv, c.d_h, m["pos"] if c.rope else None, self.cos, self.sin,
                     m["slots"], q, kp, vp))
+            see("q", li, q)
             if nd and fr:
                 run("decode_attn", lambda: L.bi_decode_attn_free(
                     q[:nd], kp, vp, m["bt_dec"], m["kv_len"], m["max_kv_len"], c.scale,
@@ -306,12 +315,16 @@ class Engine:
                 run("prefill_attn", lambda: L.bi_prefill_attn(
                     q[nd:], m["q_start"], m["pos0"], kp, vp, m["bt_pre"], c.kv_chunk, c.scale,
                     att[nd:]))
+            see("att", li, att)
             run("gemm_o", lambda: gemm(att.view(T, c.h * c.d_h), lw.wo, o))
+            see("o", li, o)
             if fuse:
                 run("add_rmsnorm", lambda: L.bi_add_rmsnorm(h, o, lw.ffn_norm, x, c.eps))
             else:
                 run("add", lambda: L.bi_add(h, o, h))
                 run("rmsnorm", lambda: rms(h, lw.ffn_norm, x, c.eps))
+            see("h_mid", li, h)
+            see("x_ffn", li, x)
             if fuse and T <= 8 and c.dtype == torch.bfloat16:
                 # the same bits in one pass (GEMM epilogue); at up to 8 rows
                 # (one-block strips) the step measured 3.7% faster at batch 1
@@ -319,14 +332,19 @@ class Engine:
                 run("gemm_gate_up", lambda: L.bi_gemm_swiglu(x, lw.wgu, act))
             else:
                 run("gemm_gate_up", lambda: gemm(x, lw.wgu, gu))
+                see("gu", li, gu)
                 run("silu_mul", lambda: L.bi_silu_mul(gu, act))
+            see("act", li, act)
             run("gemm_down", lambda: gemm(act, lw.wdown, o))
+            see("down", li, o)
             if fuse:
                 run("add_rmsnorm", lambda: L.bi_add_rmsnorm(h, o, nxt, x, c.eps))
             else:
                 run("add", lambda: L.bi_add(h, o, h))
+            see("h_out", li, h)
         if not fuse:
             rms(h, w.final_norm, x, c.eps)
+        see("x_final", len(lws), x)
         nw = len(m["want"])
         if nw == 0:
             return StepOutput(torch.empty((0, c.vocab), device=self.dev),

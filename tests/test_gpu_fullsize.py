@@ -10,10 +10,12 @@ on sampled outputs the oracle can compute one by one.
   sampled rows against the oracle within the GEMM bound, and each equal bit
   for bit to the same row computed alone (the small-M kernel).
 - The full 32-layer Llama-3-8B-shaped decode step of the bench (batch 64, KV
-  lengths 32..4096, random-init bf16 weights): three sampled requests against
-  the oracle model -- the LM head within 2e-3 of the oracle's on the engine's
-  own final row with the same argmax, and the end-to-end logits within twice
-  the drift between two valid summation orders of the oracle itself.
+  lengths 32..4096, random-init bf16 weights): three sampled requests, every
+  kernel of every layer against the oracle on the engine's own inputs, every
+  layer as a whole against the oracle model's layer, the LM head within 2e-3
+  of the oracle's on the engine's own final row with the same argmax, and
+  the end-to-end logits within twice the drift between two valid summation
+  orders of the oracle itself.
 """
 import numpy as np
 import pytest
@@ -109,9 +111,24 @@ def test_prefill_gemm_full_size_sampled_rows():
         assert bits_equal(to_np(one)[0], got[i]), f"row {r} alone"
 
 
-@pytest.mark.timeout(900)
-def test_llama8b_decode_step_sampled_requests_vs_oracle_model():
+@pytest.mark.timeout(1200)
+def test_llama8b_decode_step_every_layer_teacher_forced_vs_oracle():
+    """The bench's batch-64 step of the 32-layer Llama-3-8B shape, three
+    sampled requests (shortest, longest, median KV):
+    - every kernel of every layer against the oracle on the engine's own
+      input to that kernel (tests/layer_check.py): bitwise where the order
+      is mirrored, within the derived bound for the GEMMs and attention;
+    - every layer as a whole: the oracle model's layer from the engine's
+      input row, the output row's relative gap reported and held within two
+      bf16 ulps of the row's largest element (2^-6 relative: the kernels'
+      bounded differences can flip a rounding of the residual row);
+    - the LM head on the engine's final row within 2e-3 with the same argmax;
+    - end to end, the drift from the oracle model within twice the drift
+      between two valid summation orders of the oracle itself, with the
+      argmax equal wherever the oracle's top-2 gap exceeds twice the error
+      (the near-tie count is reported)."""
     import oracle.llama as OL
+    from layer_check import check_layer, layer_taps, tap_rows, whole_layer_gap
     from invariant_bi_rmsnorm_amd.model import LLAMA3_8B, Engine, KVPool, Segment, init_weights
     cfg = LLAMA3_8B
     B = 64
@@ -131,17 +148,49 @@ def test_llama8b_decode_step_sampled_requests_vs_oracle_model():
         segs.append(Segment(pages=[int(p) for p in place.block_table[r, :npg]],
                             pos0=int(lens[r]) - 1, tokens=[int(toks[r])]))
     pick = [int(np.argmin(lens)), int(np.argmax(lens)), int(np.argsort(lens)[B // 2])]
-    # the sampled requests' KV as it is before the step (the step appends the
-    # current token's K and V; the oracle appends its own)
+    # the sampled requests' KV as it is before the step (the end-to-end
+    # oracle appends its own current token)
     saved = {r: (pool.k[:, torch.tensor(segs[r].pages, device=dev())].float().cpu().numpy(),
                  pool.v[:, torch.tensor(segs[r].pages, device=dev())].float().cpu().numpy())
              for r in pick}
-    out = eng.step(segs)
+    m = eng.upload(eng.pack(segs))
+    packed = [m["order"].index(r) for r in pick]        # all rows are decode rows
+    tap, store = tap_rows(packed)
+    out = eng.forward(m, tap=tap)
+    torch.cuda.synchronize()
     logits = out.logits.cpu().numpy()
-    xfin = eng.x[:B].float().cpu().numpy()
-    lm = w.lm_head.float().cpu().numpy()
     om = OL.OracleModel(cfg, w, num_pages=max(len(segs[r].pages) for r in pick),
                         cos_t=eng.cos.cpu(), sin_t=eng.sin.cpu())
+    cos_t, sin_t = om.cos, om.sin
+    pos = [int(lens[r]) - 1 for r in pick]
+    worst, gaps = {}, []
+    for li in range(cfg.layers):
+        idx = {r: torch.tensor(segs[r].pages, device=dev()) for r in pick}
+        kps = [pool.k[li, idx[r]].float().cpu().numpy() for r in pick]
+        vps = [pool.v[li, idx[r]].float().cpu().numpy() for r in pick]
+        t = layer_taps(store, li)
+        rep = check_layer(cfg, om.layers[li], t, li, pos, kps, vps, cos_t, sin_t)
+        for k_, v_ in rep.items():
+            worst[k_] = max(worst.get(k_, 0.0), v_)
+        for i in range(len(pick)):
+            gap = whole_layer_gap(om, li, t["h_in"][i:i + 1], pos[i], kps[i], vps[i],
+                                  t["h_out"][i:i + 1])
+            gaps.append(gap)
+            assert gap <= 2.0 ** -6, f"layer {li}, request {pick[i]}: whole-layer gap {gap}"
+    print("per-kernel max error / bound over 32 layers:",
+          {k_: round(v_, 3) for k_, v_ in worst.items()})
+    print(f"whole-layer gap: max {max(gaps):.2e}, median {float(np.median(gaps)):.2e}")
+    # LM head gate on the engine's own final rows
+    xfin = store[("x_final", cfg.layers)]
+    lm = om.lm_head
+    lo_all = oracle.gemm(xfin, lm, False)
+    for i, r in enumerate(pick):
+        row = out.seg_index.index(r)
+        gl, lo = logits[row], lo_all[i]
+        e_head = float(np.max(np.abs(gl - lo)) / np.max(np.abs(lo)))
+        assert e_head <= 2e-3, f"request {r}: LM head rel err {e_head}"
+        assert int(np.argmax(gl)) == int(np.argmax(lo)), f"request {r}: argmax"
+    # end to end, against the drift between two valid orders of the oracle
     serial = om.gemm
 
     def gemm64(A_, W_, round_bf16):
@@ -150,15 +199,9 @@ def test_llama8b_decode_step_sampled_requests_vs_oracle_model():
             res = torch.from_numpy(res).to(torch.bfloat16).float().numpy()
         return res
 
+    agree, near_tie = 0, 0
     for r in pick:
-        row = out.seg_index.index(r)
-        gl = logits[row]
-        # the LM head gate on the engine's own final normalised row
-        lo = oracle.gemm(xfin[row:row + 1], lm, False)[0]
-        e_head = float(np.max(np.abs(gl - lo)) / np.max(np.abs(lo)))
-        assert e_head <= 2e-3, f"request {r}: LM head rel err {e_head}"
-        assert int(np.argmax(gl)) == int(np.argmax(lo)), f"request {r}: argmax"
-        # end to end, against the drift between two valid orders of the oracle
+        gl = logits[out.seg_index.index(r)]
         npg = len(segs[r].pages)
         res = []
         for gm in (serial, gemm64):
@@ -166,11 +209,16 @@ def test_llama8b_decode_step_sampled_requests_vs_oracle_model():
             om.k[:, :npg], om.v[:, :npg] = saved[r]
             o, _ = om.forward(list(range(npg)), int(lens[r]) - 1, [int(toks[r])])
             res.append(o)
+        om.gemm = serial
         e2e = float(np.max(np.abs(gl - res[0])) / np.max(np.abs(res[0])))
         spread = float(np.max(np.abs(res[0] - res[1])) / np.max(np.abs(res[0])))
-        print(f"request {r} (kv {lens[r]}): head {e_head:.1e}, end-to-end {e2e:.1e}, "
+        print(f"request {r} (kv {lens[r]}): end-to-end {e2e:.1e}, "
               f"oracle order spread {spread:.1e}")
         assert e2e <= max(2e-3, 2.0 * spread), f"request {r}: {e2e} vs spread {spread}"
         top2 = np.sort(res[0])[-2:]
         if top2[1] - top2[0] > 2 * np.max(np.abs(gl - res[0])):
             assert int(np.argmax(gl)) == int(np.argmax(res[0])), f"request {r}: e2e argmax"
+            agree += 1
+        else:
+            near_tie += 1
+    print(f"end-to-end argmax: {agree} decided and equal, {near_tie} near ties")

@@ -294,6 +294,30 @@ def test_gemm_mid_M_rows_equal_alone(M, N):
         assert torch.equal(c.view(torch.int16), full[rows].view(torch.int16)), f"m={m}"
 
 
+@pytest.mark.parametrize("K", [4096, 4104, 96])
+def test_gemm_128_tile_rows_equal_rows_alone(K):
+    """Past 64 rows with N < 2048 the 128 x 128-tile kernel runs.  On random
+    inputs (where a different per-element order would show) each of its rows
+    equals the same row computed alone by the small-M kernel, bit for bit,
+    and so do subsets of 37 and 64 rows (ragged M: 300 = 2 x 128 + 44;
+    ragged N: 1000 = 7 x 128 + 104; K with a partial last K-tile)."""
+    M, N = 300, 1000
+    A = synth.normal((M, K), seed=K + 5).to(torch.bfloat16).to(dev())
+    W = synth.normal((N, K), seed=K + 6, std=0.02).to(torch.bfloat16).to(dev())
+    full = torch.empty((M, N), dtype=torch.float32, device=dev())
+    L.bi_gemm(A, W, full)
+    one = torch.empty((1, N), dtype=torch.float32, device=dev())
+    for r in range(M):
+        L.bi_gemm(A[r:r + 1].contiguous(), W, one)
+        assert torch.equal(one.view(torch.int32), full[r:r + 1].view(torch.int32)), f"row {r}"
+    rng = np.random.default_rng(K)
+    for m in (37, 64):
+        rows = sorted(rng.choice(M, size=m, replace=False).tolist())
+        c = torch.empty((m, N), dtype=torch.float32, device=dev())
+        L.bi_gemm(A[rows].contiguous(), W, c)
+        assert torch.equal(c.view(torch.int32), full[rows].view(torch.int32)), f"m={m}"
+
+
 @pytest.mark.parametrize("N", [16448, 14336])
 def test_gemm_wide_rows_invariant_across_M(N):
     K = 4096
@@ -305,7 +329,7 @@ def test_gemm_wide_rows_invariant_across_M(N):
         L.bi_gemm(A[rows].contiguous(), W, c)
         return c
 
-    full = run(list(range(96)))             # tiled kernel
+    full = run(list(range(96)))             # 96 rows: the skinny kernel in row groups
     rng = np.random.default_rng(1)
     for M in [1, 5, 16, 31, 48, 64]:
         rows = list(rng.choice(96, size=M, replace=False))
@@ -708,8 +732,9 @@ def test_unsupported_configs_fail_closed():
 def test_gemm_large_tile_rows_equal_small_M_rows(K):
     # chunked-prefill GEMM (M = 2048 + 5 rows, 256 x 256 tiles, ragged in M
     # and N; K with a partial last K-tile, an odd count of K-tiles, two and
-    # one K-tiles) against the skinny and 128-tile paths, bit for bit per row;
-    # and the integer-exact case against the oracle
+    # one K-tiles) against the skinny kernel (1..64 rows in one launch, 300
+    # rows in row groups), bit for bit per row; and the integer-exact case
+    # against the oracle
     N = 2304 + 40
     M = 2053
     A = synth.normal((M, K), seed=21).to(torch.bfloat16).to(dev())

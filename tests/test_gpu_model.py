@@ -131,7 +131,7 @@ def _engine(cfg, seed, num_pages=512, max_rows=256):
     return Engine(cfg, w, pool, dev(), max_rows=max_rows, max_pages_per_req=64), w
 
 
-def _order_spread(cfg, w, cos_t, sin_t, pages, steps):
+def _order_spread(cfg, w, cos_t, sin_t, pages, steps, num_pages=512):
     """Logit drift between the oracle and the same oracle with its GEMMs
     summed exactly (fp64, one rounding): two valid fixed orders.  Rare bf16
     rounding flips in one GEMM feed every output of the next, so the flips
@@ -144,8 +144,8 @@ def _order_spread(cfg, w, cos_t, sin_t, pages, steps):
         if round_bf16:
             r = torch.from_numpy(r).to(torch.bfloat16).float().numpy()
         return r
-    a = OL.OracleModel(cfg, w, num_pages=512, cos_t=cos_t, sin_t=sin_t)
-    b = OL.OracleModel(cfg, w, num_pages=512, cos_t=cos_t, sin_t=sin_t, gemm=gemm64)
+    a = OL.OracleModel(cfg, w, num_pages=num_pages, cos_t=cos_t, sin_t=sin_t)
+    b = OL.OracleModel(cfg, w, num_pages=num_pages, cos_t=cos_t, sin_t=sin_t, gemm=gemm64)
     out = []
     for p0, toks in steps:
         la, _ = a.forward(pages, p0, toks)
@@ -278,11 +278,43 @@ def test_prefix_reuse_bitwise_equal_to_recompute(n_prefix):
     assert len(shared) == len(alone) == 5
     for i, (a, b) in enumerate(zip(shared, alone)):
         assert bits_equal(a, b), f"row {i}: {mismatch_report(a, b)}"
+    # and the values are the oracle model's: B's sequence teacher-forced
+    # through the oracle (the prompt in one prefill, then the engine's greedy
+    # tokens one decode at a time), each logits row within the end-to-end
+    # gate of test_engine_logits_match_oracle_model
+    toks = [int(np.argmax(r)) for r in shared[:-1]]
+    steps = [(0, prefix + suf_b)] + [(n_prefix + 40 + j, [t]) for j, t in enumerate(toks)]
+    _assert_oracle_gate(cfg, w, eng, npg, steps, shared)
     # the prefix's KV itself is bit-identical across the two requests
     for li in range(cfg.layers):
         ka = pool.k[li, pages_a[:full]].view(torch.int16)
         kc = pool.k[li, pages_c[:full]].view(torch.int16)
         assert torch.equal(ka, kc)
+
+
+def _assert_oracle_gate(cfg, w, eng, npg, steps, rows):
+    """rows[i] (engine logits) against the oracle model run over `steps`
+    ((pos0, tokens) per call, one request): end-to-end relative error within
+    max(2e-3, twice the drift between two valid summation orders of the
+    oracle); the argmax equal wherever the oracle's top-2 gap exceeds twice
+    the error.  Returns (decided, near ties)."""
+    import oracle.llama as OL
+    om = OL.OracleModel(cfg, w, num_pages=npg + 1, cos_t=eng.cos.cpu(), sin_t=eng.sin.cpu())
+    pages = list(range(npg + 1))
+    ref = [om.forward(pages, p0, toks)[0] for p0, toks in steps]
+    spread = _order_spread(cfg, w, eng.cos.cpu(), eng.sin.cpu(), pages, steps,
+                           num_pages=npg + 1)
+    decided = ties = 0
+    for i, (g, o, sp) in enumerate(zip(rows, ref, spread)):
+        err = float(np.max(np.abs(g - o)) / np.max(np.abs(o)))
+        assert err <= max(2e-3, 2.0 * sp), f"row {i}: rel err {err} vs order spread {sp}"
+        top2 = np.sort(o)[-2:]
+        if top2[1] - top2[0] > 2 * np.max(np.abs(g - o)):
+            assert int(np.argmax(g)) == int(np.argmax(o)), f"row {i}: argmax"
+            decided += 1
+        else:
+            ties += 1
+    return decided, ties
 
 
 def test_decode_verify_rollback_on_twins_commits_invariant_greedy():
@@ -305,6 +337,24 @@ def test_decode_verify_rollback_on_twins_commits_invariant_greedy():
     assert out == ref
     assert st.committed == n * (max_new - 1) and st.windows >= n * ((max_new - 1) // window)
     print("dvr stats:", st)
+    # the committed tokens against the oracle model, teacher-forced on the
+    # committed sequence: the engine's logits of every generated position
+    # (one prefill replay with every row's logits; bit-equal to the decode
+    # steps by invariance) within the end-to-end gate, and each committed
+    # token the oracle's argmax wherever its top-2 gap exceeds twice the error
+    decided = ties = 0
+    for r in (0, 3):
+        seq = prompts[r] + out[r]
+        res = inv.step([Segment(pages=pages[r], pos0=0, tokens=seq[:-1], want_logits=True,
+                                all_logits=True)])
+        lg = res.logits.cpu().numpy()[len(prompts[r]) - 1:]
+        assert [int(np.argmax(x)) for x in lg] == out[r]
+        steps = [(0, prompts[r])] + [(len(prompts[r]) + j, [t])
+                                     for j, t in enumerate(out[r][:-1])]
+        d_, t_ = _assert_oracle_gate(cfg, w, inv, len(pages[r]), steps, list(lg))
+        decided, ties = decided + d_, ties + t_
+    print(f"dvr vs oracle: {decided} tokens decided and equal, {ties} near ties")
+    assert decided > 0
 
 
 # ---------------------------------------------------------------------------

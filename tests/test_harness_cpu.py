@@ -206,3 +206,25 @@ def test_decode_verify_rollback_commits_the_verifier_sequence(noise, window, gro
     if noise >= 0.05:
         fast_only = H.greedy_decode(MockEngine({}, noise), prompts, pages, max_new=70, chunk=7)
         assert fast_only != ref
+
+
+def test_full_batch_schedules_and_config_list():
+    """p_full = 1 with all arrivals at once puts every request in one step
+    (batch 1 in the baseline vs all of them here), the rows shared out so
+    that no segment is dropped; a list of configs runs one schedule each;
+    preemptions by swap and by recompute are both counted."""
+    reqs = make_reqs(12, seed=4)
+    for r in reqs:
+        r.max_new = max(r.max_new, 4)
+    full = H.FuzzConfig(seed=5, max_rows=64, max_reqs=64, p_preempt=0.0, p_full=1.0,
+                        arrival_steps=1)
+    mixed = H.FuzzConfig(seed=6, max_rows=64, max_reqs=64, p_preempt=0.6, p_swap=0.5,
+                         p_full=0.3)
+    out = H.verify(lambda: MockBackend(), reqs, n_schedules=0, fuzz=[full, mixed])
+    assert out["verdict"] == H.GREEN, out
+    assert out["schedules"] == 2 and out["schedule_seeds"] == [5, 6]
+    assert out["max_requests_per_step"] == len(reqs)
+    assert out["max_rows_per_step"] <= 64
+    assert out["preemptions"]["swap"] > 0 and out["preemptions"]["recompute"] > 0
+    out = H.verify(lambda: MockBackend(divergence=True), reqs, n_schedules=0, fuzz=[full])
+    assert out["verdict"] == H.RED
