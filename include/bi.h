@@ -232,6 +232,31 @@ bi_status bi_merge_partials(const float *part_ml, const float *part_acc,
                             int out_dtype, bi_stream stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): decode
+ * attention straight to its output, bi_decode_attn followed by
+ * bi_merge_partials with the same arguments, bit for bit, but with the fp32
+ * partials held in a static device buffer of BI_NOALLOC_SCRATCH_BYTES inside
+ * the library instead of caller workspace.  Nothing is allocated: the buffer
+ * exists on each GPU from the library's load to the end of the process (its
+ * address is looked up once per device, on the first call there).  The
+ * partials (total_chunks * h * (d_h + 2) * 4 bytes, plus alignment) must fit,
+ * else BI_ERR_WORKSPACE and nothing is launched; at h = 32, d_h = 128 that is
+ * up to 2016 chunk rows (e.g. 64 requests of 7936 tokens at kv_chunk 256).
+ * Every call on one GPU uses the same buffer, and the merge reads only rows
+ * the same call has written, so nothing needs clearing between calls; calls
+ * that overlap on one GPU (concurrent streams) race on it and must be
+ * serialised by the caller.  out: device [B][h][d_h] of out_dtype; the other
+ * arguments, limits and errors as for bi_decode_attn. */
+#define BI_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
+bi_status bi_decode_attn_noalloc(const void *q, const void *k_pool, const void *v_pool,
+                                 const int32_t *block_table, const int32_t *kv_len,
+                                 const int32_t *chunk_off, int B, int total_chunks, int h,
+                                 int h_kv, int d_h, int page_size, int max_pages, int kv_chunk,
+                                 float scale, int dtype, void *out, int out_dtype,
+                                 bi_stream stream);
+
+/*
  * Causal prefill over packed query rows.  q: device [T][h][d_h]; request r
  * owns rows q_start[r] .. q_start[r+1]-1 (device int32 [R+1], T ==
  * q_start[R]); row t sits at absolute position q_pos0[r] + t - q_start[r]

@@ -38,6 +38,8 @@ SIGNATURES = {
                          + [_vp] * 4),
     "bi_decode_attn": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp] + [_c_int] * 8
                        + [_c_float, _c_int, _vp, _vp, _vp]),
+    "bi_decode_attn_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp] + [_c_int] * 8
+                               + [_c_float, _c_int, _vp, _c_int, _vp]),
     "bi_merge_partials": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _c_int, _vp]),
     "bi_prefill_attn": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp] + [_c_int] * 6
                         + [_c_float, _c_int, _vp, _vp]),
@@ -250,6 +252,29 @@ def bi_decode_attn(q, k_pool, v_pool, block_table, kv_len, chunk_off, total_chun
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _i32(block_table), _i32(kv_len), _i32(chunk_off),
         B, total_chunks, h, h_kv, d_h, page_size, block_table.shape[1], kv_chunk, scale, _dt(q),
         _ptr(part_ml), _ptr(part_acc), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024      # BI_NOALLOC_SCRATCH_BYTES
+
+
+def bi_decode_attn_noalloc(q, k_pool, v_pool, block_table, kv_len, chunk_off,
+                           total_chunks: int, kv_chunk: int, scale: float, out, stream=None):
+    """bi_decode_attn + bi_merge_partials into out, with the partials in the
+    library's static device buffer (no allocation by the library or here)."""
+    B, h, d_h = q.shape
+    _check_attn_args("bi_decode_attn_noalloc", q, k_pool, v_pool, block_table, B)
+    _need(kv_len.numel() == B, "bi_decode_attn_noalloc",
+          f"kv_len has {kv_len.numel()} entries, not {B}")
+    _need(chunk_off.numel() == B + 1, "bi_decode_attn_noalloc",
+          f"chunk_off has {chunk_off.numel()} entries, not B + 1 = {B + 1}")
+    _need(tuple(out.shape) == (B, h, d_h), "bi_decode_attn_noalloc",
+          f"out {tuple(out.shape)} is not {(B, h, d_h)}")
+    _, h_kv, page_size, _ = k_pool.shape
+    _check("bi_decode_attn_noalloc", load().bi_decode_attn_noalloc(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _i32(block_table), _i32(kv_len), _i32(chunk_off),
+        B, total_chunks, h, h_kv, d_h, page_size, block_table.shape[1], kv_chunk, scale, _dt(q),
+        _ptr(out), _dt(out), _stream(stream)))
+    return out
 
 
 def bi_merge_partials(part_ml, part_acc, chunk_off, out, stream=None):

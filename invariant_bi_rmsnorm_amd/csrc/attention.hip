@@ -23,6 +23,7 @@
 // the fly with the merge kernel's formula, so prefill row t equals a decode
 // of kv_len = t + 1 bit for bit.
 #include <cmath>
+#include <mutex>
 
 #include "api.h"
 #include "common.h"
@@ -1397,6 +1398,84 @@ extern "C" bi_status bi_merge_partials(const float* part_ml, const float* part_a
     else hipLaunchKernelGGL((k_merge<64, 0>), grid, dim3(256), 0, s, part_ml, part_acc, chunk_off, B, h, out);
   }
   return launched("bi_merge_partials");
+}
+
+// ---------------------------------------------------------------------------
+// decode attention that allocates nothing: partials in a static device buffer
+// ---------------------------------------------------------------------------
+
+namespace bi {
+namespace {
+
+// Scratch of bi_decode_attn_noalloc: the fp32 partials (m, l) then acc.  One
+// copy per GPU, held from the library's load on that GPU to the end of the
+// process; every call on a GPU reuses it.  In host code `scratch` is only a
+// stand-in for the device symbol: its device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[BI_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up on first use there).
+bi_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(BI_ERR_HIP, "bi_decode_attn_noalloc: hipGetDevice: %s",
+                                   hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(BI_ERR_UNSUPPORTED, "bi_decode_attn_noalloc: device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(BI_ERR_HIP, "bi_decode_attn_noalloc: hipGetSymbolAddress: %s",
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BI_OK;
+}
+
+}  // namespace
+}  // namespace bi
+
+extern "C" bi_status bi_decode_attn_noalloc(const void* q, const void* k_pool,
+                                            const void* v_pool, const int32_t* block_table,
+                                            const int32_t* kv_len, const int32_t* chunk_off,
+                                            int B, int total_chunks, int h, int h_kv, int d_h,
+                                            int page_size, int max_pages, int kv_chunk,
+                                            float scale, int dtype, void* out, int out_dtype,
+                                            bi_stream stream) {
+  using namespace bi;
+  bi_status st = AttnArgsCheck::common("bi_decode_attn_noalloc", h, h_kv, d_h, page_size,
+                                       kv_chunk, dtype);
+  if (st != BI_OK) return st;
+  BI_REQUIRE(out_dtype == BI_F32 || out_dtype == BI_BF16, BI_ERR_UNSUPPORTED,
+             "bi_decode_attn_noalloc: out dtype %d", out_dtype);
+  BI_REQUIRE(B >= 0 && total_chunks >= 0, BI_ERR_INVALID,
+             "bi_decode_attn_noalloc: bad sizes B=%d total_chunks=%d", B, total_chunks);
+  if (B == 0 || total_chunks == 0) return BI_OK;
+  const size_t ml_bytes = (size_t)total_chunks * h * 2 * sizeof(float);
+  const size_t acc_off = (ml_bytes + 255) & ~(size_t)255;
+  const size_t need = acc_off + (size_t)total_chunks * h * d_h * sizeof(float);
+  BI_REQUIRE(need <= (size_t)BI_NOALLOC_SCRATCH_BYTES, BI_ERR_WORKSPACE,
+             "bi_decode_attn_noalloc: %zu bytes of partials exceed the %d-byte static buffer "
+             "(total_chunks=%d h=%d d_h=%d)", need, (int)BI_NOALLOC_SCRATCH_BYTES,
+             total_chunks, h, d_h);
+  BI_REQUIRE(out != nullptr, BI_ERR_INVALID, "bi_decode_attn_noalloc: null pointer");
+  void* base = nullptr;
+  st = scratch_on_current_device(&base);
+  if (st != BI_OK) return st;
+  float* part_ml = static_cast<float*>(base);
+  float* part_acc = reinterpret_cast<float*>(static_cast<unsigned char*>(base) + acc_off);
+  st = bi_decode_attn(q, k_pool, v_pool, block_table, kv_len, chunk_off, B, total_chunks, h,
+                      h_kv, d_h, page_size, max_pages, kv_chunk, scale, dtype, part_ml,
+                      part_acc, stream);
+  if (st != BI_OK) return st;
+  return bi_merge_partials(part_ml, part_acc, chunk_off, B, h, d_h, out, out_dtype, stream);
 }
 
 // ---------------------------------------------------------------------------
