@@ -308,6 +308,13 @@ bi_status bi_prefill_attn_free(const void *q, const int32_t *q_start, const int3
 /* ---------------------------------------------------------------------- */
 /* elementwise glue of a Llama-shaped layer (no reductions)               */
 /* ---------------------------------------------------------------------- */
+/* No passage of the pages defines these steps.  They are the decoder layer's
+ * own arithmetic around the reductions (embedding gather, rotate-half RoPE
+ * with the KV append, residual add, the SiLU-gated product, argmax), each a
+ * function of its own row's inputs with no sum across rows, so none of them
+ * can depend on the batch; the readings they follow (RoPE with theta =
+ * 500000, SiLU through the library's exp, lowest index on argmax ties) are
+ * stated with each function. */
 
 /* out[i][:] = table[ids[i]][:]; table device [V][d], ids device int32 [M]. */
 bi_status bi_embed(const void *table, const int32_t *ids, void *out, int M, int d, int dtype,
