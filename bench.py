@@ -56,9 +56,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", default="1,7,32", help="extra batch sizes ('' for none)")
     ap.add_argument("--only", default="",
-                    help="time one kernel of the step instead (decode_attn, gemm_qkv, ..., "
-                         "'log_softmax' / 'sample' for logprobs / seeded draws over the batch's "
-                         "logits, or 'copy' for a "
+                    help="time one kernel of the step instead (decode_attn, merge, ...; a "
+                         "comma list of gemm_qkv, gemm_o, gemm_gate_up, gemm_down for the "
+                         "projection GEMMs over the weights of all layers in turn; "
+                         "'decode_attn_long' for paged decode attention at KV lengths "
+                         "log-uniform 128..32768; 'prefill_gemm'; 'log_softmax' / 'sample' for "
+                         "logprobs / seeded draws over the batch's logits; or 'copy' for a "
                          "plain 1 GiB device copy), e.g. under rocprofv3 --pmc")
     ap.add_argument("--twin", action="store_true", help="with --only: the twin's kernel")
     ap.add_argument("--launches", type=int, default=50)
@@ -71,6 +74,10 @@ def parse():
     ap.add_argument("--traffic-summary", default="",
                     help="summarise rocprofv3 --pmc runs (FETCH_SIZE / WRITE_SIZE of --only "
                          "decode_attn and of --only copy) found under this directory")
+    ap.add_argument("--gemm-counters-summary", default="",
+                    help="summarise rocprofv3 --pmc passes of --only gemm_qkv,gemm_o,"
+                         "gemm_gate_up,gemm_down (one subdirectory per pass) found under this "
+                         "directory")
     ap.add_argument("--mfma-summary", default="",
                     help="summarise a rocprofv3 --pmc run of --only prefill_gemm "
                          "(SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16, "
@@ -453,6 +460,139 @@ def mfma_summary(d, M=8192, N=14336, K=4096, simds=1024, xcds=8):
     print("mfma-record: " + json.dumps(rec))
 
 
+GEMM_NAMES = ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down")
+GEMM_PROFILE = os.path.join(ROOT, "profiles", "decode_gemms_counters_llama3_8b_b64.md")
+GEMM_PASSES = {
+    "fetch": ("FETCH_SIZE",),
+    "write": ("WRITE_SIZE",),
+    "tcp": ("TCP_TCC_READ_REQ_sum", "TCP_TCC_READ_REQ_LATENCY_sum", "TCP_PENDING_STALL_CYCLES_sum",
+            "TCP_TCR_TCP_STALL_CYCLES_sum", "GRBM_GUI_ACTIVE"),
+    "tcc": ("TCC_HIT_sum", "TCC_MISS_sum", "TCC_TAG_STALL_sum", "TCC_REQ_sum", "TA_BUSY_avr",
+            "TA_ADDR_STALLED_BY_TC_CYCLES_sum", "GRBM_GUI_ACTIVE"),
+    "sq": ("SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_ANY",
+           "SQ_BUSY_CYCLES", "SQ_INSTS_VMEM_RD", "SQ_INST_LEVEL_VMEM", "SQ_WAVE_CYCLES",
+           "GRBM_GUI_ACTIVE"),
+    "tlb": ("TCP_UTCL1_TRANSLATION_MISS_sum", "TCP_UTCL1_TRANSLATION_HIT_sum",
+            "TCP_READ_TAGCONFLICT_STALL_CYCLES_sum", "TCP_TOTAL_CACHE_ACCESSES_sum"),
+}
+
+
+def _dispatch_rows(d, match):
+    """{dispatch id: {counter: value, 'ns': duration}} of the kernels whose
+    name contains `match`, from the rocprofv3 csv output under d."""
+    import csv
+    import glob
+    rows = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if match in r["Kernel_Name"]:
+                    e = rows.setdefault(int(r["Dispatch_Id"]), {
+                        "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+                    e[r["Counter_Name"]] = float(r["Counter_Value"])
+    return rows
+
+
+def gemm_counters_summary(d, names=GEMM_NAMES, launches=32, warm=3, cus=256, xcds=8):
+    """Counters of the decode projection GEMMs at batch 64 from one
+    rocprofv3 --pmc pass per subdirectory of d (GEMM_PASSES; each a run of
+    `bench.py --only gemm_qkv,gemm_o,gemm_gate_up,gemm_down --launches N`),
+    plus copy_fetch / copy_write (the 1 GiB copy that scales FETCH_SIZE and
+    WRITE_SIZE) under d or beside it.  The k_gemm_small dispatches of a run come in the order of
+    `names`, warm + launches each; the warm-ups are dropped and each counter
+    is the median over the timed launches.  Prints a markdown summary whose
+    `gemm-counters-record:` line bench.py reads back."""
+    import statistics
+    med = statistics.median
+    per = {n: {} for n in names}
+    for pas, counters in GEMM_PASSES.items():
+        rows = _dispatch_rows(os.path.join(d, pas), "k_gemm_small")
+        ids = sorted(rows)
+        if len(ids) != len(names) * (warm + launches):
+            raise SystemExit(f"pass {pas}: {len(ids)} k_gemm_small dispatches, expected "
+                             f"{len(names) * (warm + launches)}")
+        for i, n in enumerate(names):
+            block = [rows[k] for k in ids[i * (warm + launches) + warm:(i + 1) * (warm + launches)]]
+            for c in counters + ("ns",):
+                vals = [e[c] for e in block if c in e]
+                if vals:
+                    per[n][f"{pas}:{c}"] = med(vals)
+    gib = float(1 << 30)
+    cd = d if os.path.isdir(os.path.join(d, "copy_fetch")) else os.path.dirname(d.rstrip("/"))
+    cf = _counter_rows(os.path.join(cd, "copy_fetch"), "FETCH_SIZE", "copy")
+    cw = _counter_rows(os.path.join(cd, "copy_write"), "WRITE_SIZE", "copy")
+    f_scale, w_scale = gib / (max(cf) * 1024.0), gib / (max(cw) * 1024.0)
+    cfg_b = 64
+    shapes = {"gemm_qkv": (6144, 4096), "gemm_o": (4096, 4096), "gemm_gate_up": (28672, 4096),
+              "gemm_down": (4096, 14336)}
+    recs = {}
+    print("| quantity (median over %d launches, batch %d, weights of 32 layers in rotation) | "
+          % (launches, cfg_b) + " | ".join(names) + " |")
+    print("|---|" + "---|" * len(names))
+    table = []
+    for n in names:
+        e = per[n]
+        N, K = shapes[n]
+        alg = 2 * N * K + 2 * cfg_b * K + 2 * cfg_b * N
+        us = e["tcp:ns"] / 1e3
+        hbm = e["fetch:FETCH_SIZE"] * 1024 * f_scale + e["write:WRITE_SIZE"] * 1024 * w_scale
+        req = e["tcp:TCP_TCC_READ_REQ_sum"]
+        lat = e["tcp:TCP_TCC_READ_REQ_LATENCY_sum"] / max(req, 1.0)
+        clk = e["tcp:GRBM_GUI_ACTIVE"] / xcds / e["tcp:ns"]            # GHz
+        cyc = e["tcp:GRBM_GUI_ACTIVE"] / xcds
+        l2_bytes = req * 128.0                                      # whole 128-byte lines
+        per_cu = l2_bytes / cus / (us * 1e-6) / 1e9                 # GB/s into one CU
+        inflight = per_cu * 1e9 * (lat / (clk * 1e9)) / 1024.0      # KiB, Little's law
+        hit = e["tcc:TCC_HIT_sum"] / max(e["tcc:TCC_HIT_sum"] + e["tcc:TCC_MISS_sum"], 1.0)
+        rec = {"us": round(us, 2), "alg_bytes": alg, "hbm_bytes": round(hbm),
+               "hbm_over_alg": round(hbm / alg, 3), "hbm_TBps": round(hbm / us / 1e6, 2),
+               "l2_to_cu_bytes": round(l2_bytes), "l2_to_cu_over_alg": round(l2_bytes / alg, 2),
+               "per_cu_GBps": round(per_cu, 1), "tcp_tcc_read_latency_cycles": round(lat),
+               "inflight_KiB_per_cu": round(inflight, 1), "l2_hit": round(hit, 3),
+               "clock_ghz": round(clk, 2),
+               "tcp_pending_stall_frac": round(e["tcp:TCP_PENDING_STALL_CYCLES_sum"] / cus / cyc, 3),
+               "ta_busy_frac": round(e["tcc:TA_BUSY_avr"] / cyc, 3),
+               "lds_bank_conflict_per_lds_inst": round(
+                   e["sq:SQ_LDS_BANK_CONFLICT"] / max(e["sq:SQ_INSTS_LDS"], 1.0), 3),
+               "utcl1_miss": round(e["tlb:TCP_UTCL1_TRANSLATION_MISS_sum"]),
+               "utcl1_hit": round(e["tlb:TCP_UTCL1_TRANSLATION_HIT_sum"])}
+        recs[n] = rec
+    rows_out = [
+        ("duration (us)", "us"), ("HBM bytes (FETCH x %.3f + WRITE x %.3f)" % (f_scale, w_scale), "hbm_bytes"),
+        ("HBM bytes / algorithmic", "hbm_over_alg"), ("HBM TB/s", "hbm_TBps"),
+        ("L2 -> CU bytes (TCP_TCC_READ_REQ x 128)", "l2_to_cu_bytes"),
+        ("L2 -> CU bytes / algorithmic", "l2_to_cu_over_alg"), ("intake per CU (GB/s)", "per_cu_GBps"),
+        ("mean TCP -> TCC read latency (cycles)", "tcp_tcc_read_latency_cycles"),
+        ("bytes in flight per CU, Little's law (KiB)", "inflight_KiB_per_cu"),
+        ("L2 hit rate", "l2_hit"), ("clock while active (GHz)", "clock_ghz"),
+        ("TCP pending-stall cycles / CU cycles", "tcp_pending_stall_frac"),
+        ("TA busy / cycles", "ta_busy_frac"),
+        ("LDS bank conflicts per LDS instruction", "lds_bank_conflict_per_lds_inst"),
+        ("UTCL1 translation misses", "utcl1_miss"), ("UTCL1 translation hits", "utcl1_hit")]
+    for label, key in rows_out:
+        print(f"| {label} | " + " | ".join(str(recs[n][key]) for n in names) + " |")
+    out = {"kernels": recs, "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "source_sha256": kernel_source_hash(MFMA_SOURCES)}
+    print()
+    print("gemm-counters-record: " + json.dumps(out))
+
+
+def measured_gemm_counters():
+    """The decode GEMMs' counter record from the committed summary, or None
+    when the GEMM sources changed since it was taken."""
+    try:
+        with open(GEMM_PROFILE) as f:
+            lines = [ln for ln in f if ln.startswith("gemm-counters-record: ")]
+    except OSError:
+        return None
+    if not lines:
+        return None
+    rec = json.loads(lines[-1][len("gemm-counters-record: "):])
+    if rec.get("source_sha256") != kernel_source_hash(MFMA_SOURCES):
+        return None
+    return rec["kernels"]
+
+
 def measured_mfma():
     """The prefill GEMM's counter record (MFMA busy fraction, clock) from the
     committed summary, or None when its sources changed since."""
@@ -486,11 +626,105 @@ def measured_traffic():
     return rec
 
 
+GEMM_NAMES = ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down")
+
+
+def decode_attn_long(args, torch, dev):
+    """The paged decode-attention workload on its own: --batch requests with
+    KV lengths log-uniform in 128..32768 (seeded), h 32 / h_kv 8 / d_h 128,
+    bf16 K and V N(0, 1) in 16-token pages scattered over a pool 1.25x the
+    live pages, 256-key chunks.  Two such pools are used in turn, so every
+    call reads K and V that are cold in L2 and in the 256 MB last-level
+    cache.  Returns (launch, algorithmic bytes, label)."""
+    import synth
+    from invariant_bi_rmsnorm_amd import _lib as L
+    B, h, h_kv, d_h, C, ps = args.batch, 32, 8, 128, 256, 16
+    kv_len = synth.log_uniform_lengths(B, 128, 32768, seed=args.seed + 31)
+    place = synth.scatter_pages(kv_len, ps, seed=args.seed + 32)
+    g = torch.Generator(device=dev).manual_seed(args.seed + 33)
+    shape = (place.num_pages, h_kv, ps, d_h)
+    pools = [tuple(torch.empty(shape, dtype=torch.bfloat16, device=dev).normal_(generator=g)
+                   for _ in range(2)) for _ in range(2)]
+    q = torch.empty((B, h, d_h), dtype=torch.bfloat16, device=dev).normal_(generator=g)
+    off = L.bi_chunk_offsets(kv_len, C)
+    tot = int(off[-1])
+    ml = torch.empty((tot, h, 2), device=dev)
+    acc = torch.empty((tot, h, d_h), device=dev)
+    bt = torch.from_numpy(place.block_table.copy()).to(dev)
+    kvl, offd = torch.from_numpy(kv_len).to(dev), off.to(dev)
+    scale = float(1.0 / math.sqrt(d_h))
+    turn = [0]
+
+    def fn():
+        kp, vp = pools[turn[0] % 2]
+        turn[0] += 1
+        L.bi_decode_attn(q, kp, vp, bt, kvl, offd, tot, C, scale, ml, acc)
+
+    alg = int(kv_len.sum()) * h_kv * d_h * 2 * 2 + B * h * d_h * 2 + tot * h * (d_h + 2) * 4
+    label = (f"decode_attn, batch {B}, KV lengths log-uniform 128..32768 ({int(kv_len.sum())} "
+             f"tokens, {tot} chunk rows), two pools in turn")
+    return fn, alg, label
+
+
+def only_gemms(args, torch, dev, names):
+    """The decode step's projection GEMMs at the bench's batch, each launched
+    --launches times back to back, cycling through the weights of all the
+    model's layers as the step does (each launch reads weights that are cold
+    in L2 and in the 256 MB last-level cache), in the order given.  The
+    activations are N(0, 1); the QKV product runs with its RoPE + KV-append
+    epilogue, as in the step.  Prints one JSON line per GEMM."""
+    from invariant_bi_rmsnorm_amd import _lib as L
+    from invariant_bi_rmsnorm_amd.model import init_weights
+    cfg = model_config(args)
+    w = init_weights(cfg, args.seed + 14, dev, source="device")
+    _, eng, _, meta, kv_len, _ = build_workload(args, args.batch, torch, dev, w)
+    T = meta["T"]
+    c = cfg
+    for buf in (eng.x, eng.att, eng.act):
+        buf.normal_()
+    nl = len(w.layers)
+
+    def fn_for(name, i):
+        lw = w.layers[i % nl]
+        if name == "gemm_qkv":
+            return lambda: L.bi_gemm_qkv_rope(
+                eng.x[:T], lw.wqkv, c.h, c.h_kv, c.d_h, meta["pos"], eng.cos, eng.sin,
+                meta["slots"], eng.q[:T], eng.pool.k[i % nl], eng.pool.v[i % nl])
+        if name == "gemm_o":
+            return lambda: L.bi_gemm(eng.att[:T].view(T, c.h * c.d_h), lw.wo, eng.o[:T])
+        if name == "gemm_gate_up":
+            return lambda: L.bi_gemm(eng.x[:T], lw.wgu, eng.gu[:T])
+        return lambda: L.bi_gemm(eng.act[:T], lw.wdown, eng.o[:T])
+
+    for name in names:
+        fns = [fn_for(name, i) for i in range(nl)]
+        for f in fns[:3]:
+            f()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(args.launches):
+            fns[i % nl]()
+        b.record()
+        torch.cuda.synchronize()
+        us = 1e3 * a.elapsed_time(b) / args.launches
+        alg = algorithmic_bytes(name, cfg, args.batch, kv_len, meta)
+        print(json.dumps({"kernel": f"{name}, batch {args.batch}", "launches": args.launches,
+                          "warmup_launches": 3, "weights": f"{nl} layers in rotation",
+                          "avg_us": round(us, 2), "alg_bytes": alg,
+                          "GBps": round(alg / us / 1e3, 1),
+                          "hbm_frac": round(alg / us / 1e3 / (HBM_PEAK / 1e9), 4)}), flush=True)
+
+
 def only_kernel(args, torch, dev):
     """Launch one kernel of the step (the last layer's instance) --launches
     times back to back and report its average duration from HIP events on
     its stream.  'copy' copies 1 GiB device to device (the yardstick that
     calibrates HBM byte counters)."""
+    names = [n for n in args.only.split(",") if n]
+    if names and all(n in GEMM_NAMES for n in names):
+        only_gemms(args, torch, dev, names)
+        return
     if args.only == "copy":
         n = 1 << 28
         src = torch.empty(n, device=dev).normal_()
@@ -499,6 +733,8 @@ def only_kernel(args, torch, dev):
     elif args.only == "prefill_gemm":
         print(json.dumps(prefill_gemm(torch, dev, launches=args.launches)), flush=True)
         return
+    elif args.only == "decode_attn_long":
+        fn, alg, label = decode_attn_long(args, torch, dev)
     elif args.only == "log_softmax":
         # logprobs of a decode batch: fp32 logits [batch, vocab], read once and
         # written once (the second and third passes over a row hit L2)
@@ -630,6 +866,9 @@ def main():
     if args.mfma_summary:
         mfma_summary(args.mfma_summary)
         return
+    if args.gemm_counters_summary:
+        gemm_counters_summary(args.gemm_counters_summary, launches=args.launches)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path is "
               "data-parallel across GPUs and nothing here uses a second device", file=sys.stderr)
@@ -697,6 +936,15 @@ def main():
         "per_kernel": {k: _rounded(v) for k, v in per.items()},
         "per_kernel_twin": {k: _rounded(v) for k, v in per_free.items()},
     }
+    gc = measured_gemm_counters()
+    if gc is not None:
+        # counter record of the projection GEMMs (profiles/), while their
+        # sources match it: HBM and L2 -> CU bytes over the algorithmic ones,
+        # the intake per CU and the bytes it keeps in flight
+        out["gemm_counters"] = {k: {f: v[f] for f in ("hbm_over_alg", "l2_to_cu_over_alg",
+                                                      "per_cu_GBps", "inflight_KiB_per_cu",
+                                                      "tcp_pending_stall_frac")}
+                                for k, v in gc.items()}
     sweep = [int(x) for x in args.sweep.split(",") if x.strip()]
     if sweep:
         keep = detail
