@@ -14,11 +14,15 @@ the token it decodes), so every step does the same work.
 
 Prints one JSON line.  `value` = decode tokens/s of the whole step (the
 step is captured in a HIP graph and replayed; the graph's logits are
-checked bitwise against an eager step first).  The same step on the
-batch-adaptive twins (bi_*_free) is timed the same way over the same KV
-pool and weights: `invariance_overhead_pct` = invariant step time / twin
-step time - 1.  `sweep` repeats both at other batch sizes (1, 7, 32 by
-default).  `roofline` is for the
+checked bitwise against an eager step first).  The same step on the tuned
+batch-adaptive twin (the engine's "tuned" mode: at every call site the
+fastest of the invariant configuration and the batch-adaptive ones --
+split-K GEMMs, 64-key KV chunks, occupancy-driven KV splits, norms split
+over workgroups -- measured per shape on first use) is timed the same way,
+graph-replayed, over the same KV pool and weights:
+`invariance_overhead_pct` = invariant step time / twin step time - 1,
+with the twin's choices and per-kernel deltas.  `sweep` repeats both at
+other batch sizes (1, 7, 32 by default).  `roofline` is for the
 kernel with the largest share of step time in a second timed region of eager
 steps (HIP event pairs on the launch stream around every kernel); its
 duration is then taken from back-to-back launches of the step's last-layer
@@ -64,6 +68,9 @@ def parse():
                          "logprobs / seeded draws over the batch's logits; or 'copy' for a "
                          "plain 1 GiB device copy), e.g. under rocprofv3 --pmc")
     ap.add_argument("--twin", action="store_true", help="with --only: the twin's kernel")
+    ap.add_argument("--twin-mode", default="tuned", choices=("tuned", "free"),
+                    help="with --only --twin: the tuned twin (fastest configuration per "
+                         "site) or the all-adaptive one")
     ap.add_argument("--launches", type=int, default=50)
     ap.add_argument("--dvr", action="store_true",
                     help="decode-verify-rollback (twins decode, invariant kernels verify) "
@@ -95,9 +102,11 @@ def model_config(args):
     return replace(LLAMA3_8B, layers=args.layers)
 
 
-def build_workload(args, B, torch, dev, w, free=False):
+def build_workload(args, B, torch, dev, w, free=False, twin_mode="tuned"):
     """KV pool, engine(s) and the packed decode step for batch B; free=True
-    also builds an engine on the batch-adaptive twins over the same pool."""
+    also builds a twin engine (mode twin_mode: "tuned", the fair
+    batch-adaptive baseline, or "free", every kernel on its twin) over the
+    same pool."""
     import synth
     from invariant_bi_rmsnorm_amd.model import Engine, KVPool, Segment
     cfg = model_config(args)
@@ -110,7 +119,7 @@ def build_workload(args, B, torch, dev, w, free=False):
         pool.v[li].normal_(generator=g)
     eng = Engine(cfg, w, pool, dev, max_rows=B, max_pages_per_req=max(place.max_pages, 257))
     twin = Engine(cfg, w, pool, dev, max_rows=B, max_pages_per_req=max(place.max_pages, 257),
-                  free=True) if free else None
+                  mode=twin_mode) if free else None
     toks = synth.token_ids(B, cfg.vocab, seed=args.seed + 15)
     segs = []
     for r in range(B):
@@ -118,7 +127,8 @@ def build_workload(args, B, torch, dev, w, free=False):
         segs.append(Segment(pages=[int(p) for p in place.block_table[r, :npg]],
                             pos0=int(kv_len[r]) - 1, tokens=[int(toks[r])]))
     meta = eng.upload(eng.pack(segs))
-    return cfg, eng, twin, meta, kv_len, place
+    tmeta = twin.upload(twin.pack(segs)) if free else None
+    return cfg, eng, twin, meta, kv_len, place, tmeta
 
 
 def algorithmic_bytes(name, cfg, B, kv_len, meta):
@@ -155,10 +165,12 @@ def time_steps(eng, meta, steps, torch, graph):
     return (time.perf_counter() - t0) / steps
 
 
-def capture(eng, meta, torch, warmup):
+def capture(eng, meta, torch, warmup, exact=True):
     """Eager warmup, then the step captured in a HIP graph; the graph's
-    logits must equal an eager step's bit for bit over several replays with
-    eager work in between, else the eager step is timed."""
+    logits must equal an eager step's over several replays with eager work
+    in between -- bit for bit (exact), or, for a twin whose kernels need not
+    repeat their bits, within 1e-3 of the largest logit -- else the eager
+    step is timed.  Returns (graph or None, check result)."""
     for _ in range(max(warmup, 1)):
         ref = eng.forward(meta)
     torch.cuda.synchronize()
@@ -175,7 +187,12 @@ def capture(eng, meta, torch, warmup):
         for _ in range(3):
             graph.replay()
             torch.cuda.synchronize()
-            same &= bool(torch.equal(out.logits.view(torch.int32), ref_logits.view(torch.int32)))
+            if exact:
+                same &= bool(torch.equal(out.logits.view(torch.int32),
+                                         ref_logits.view(torch.int32)))
+            else:
+                err = (out.logits - ref_logits).abs().max() / ref_logits.abs().max()
+                same &= bool(err <= 1e-3)
             eng.forward(meta)          # eager work between replays
             torch.cuda.synchronize()
         if not same:
@@ -236,32 +253,57 @@ def back_to_back_us(fn, torch, launches=20):
 
 
 def run_batch(args, B, torch, dev, w, want_detail):
-    cfg, eng, twin, meta, kv_len, place = build_workload(args, B, torch, dev, w, free=True)
+    cfg, eng, twin, meta, kv_len, place, tmeta = build_workload(args, B, torch, dev, w, free=True)
     log(f"B={B}: {int(sum(kv_len))} KV tokens, {meta['total_chunks']} chunks")
     res = {"B": B}
-    for tag, e in (("inv", eng), ("free", twin)):
-        graph, ok = (None, None) if args.no_graph else capture(e, meta, torch, args.warmup)
-        sec = time_steps(e, meta, args.steps, torch, graph)
+    for tag, e, mm in (("inv", eng, meta), ("free", twin, tmeta)):
+        graph, ok = (None, None) if args.no_graph else capture(e, mm, torch, args.warmup,
+                                                              exact=(tag == "inv"))
+        sec = time_steps(e, mm, args.steps, torch, graph)
         res[tag] = {"ms_per_step": sec * 1e3, "tokens_per_s": B / sec,
                     "graph": graph is not None, "graph_matches_eager": ok}
         del graph
     res["invariance_overhead_pct"] = 100.0 * (res["inv"]["ms_per_step"] /
                                               res["free"]["ms_per_step"] - 1.0)
+    res["twin_choices"] = twin_choices(twin)
     step_bytes = (cfg.weight_bytes() - 2 * cfg.vocab * cfg.d
                   + int(sum(kv_len)) * cfg.kv_bytes_per_token())
     res["step_bytes"] = step_bytes
     res["hbm_frac_of_step_bound"] = (step_bytes / (res["inv"]["ms_per_step"] * 1e-3)) / HBM_PEAK
-    log(f"B={B}: invariant {res['inv']['ms_per_step']:.3f} ms/step, twins "
+    log(f"B={B}: invariant {res['inv']['ms_per_step']:.3f} ms/step, tuned twin "
         f"{res['free']['ms_per_step']:.3f} ms/step")
     if not want_detail:
         return res, None
     # second timed region: eager steps, HIP events around every kernel
     per, grab = per_kernel_times(eng, meta, args.steps, torch)
-    per_free, _ = per_kernel_times(twin, meta, args.steps, torch)
+    per_free, _ = per_kernel_times(twin, tmeta, args.steps, torch)
     detail = {"per_kernel": per, "per_kernel_free": per_free, "grab": grab, "cfg": cfg,
               "kv_len": kv_len,
               "meta": meta, "eng": eng, "weights": w, "place": place}
     return res, detail
+
+
+def twin_choices(twin):
+    """Which configuration the tuned twin runs at each call site ("inv" =
+    the invariant kernel), with the candidates' measured us."""
+    labels = {"norm": ("inv", "split rows"), "qkv": ("inv", "split-K"),
+              "decode_attn": ("inv C=256", "inv C=64", "occupancy splits"),
+              "prefill_attn": ("inv", "cut-relative chunks"), "gemm_o": ("inv", "split-K"),
+              "add_norm": ("inv fused", "add + split rows"),
+              "gemm_gate_up": ("inv", "inv unfused", "split-K"),
+              "gemm_down": ("inv", "split-K"), "gemm_lm_head": ("inv", "split-K")}
+    out = {}
+    for key, k in twin.tuner.best.items():
+        site = key[0]
+        lab = labels.get(site, ())
+        times = twin.tuner.times.get(key)
+        if site == "gemm_gate_up" and times is not None and len(times) == 2:
+            lab = ("inv", "split-K")
+        if site == "decode_attn" and times is not None and len(times) == 2:
+            lab = ("inv C=256", "occupancy splits")
+        out[site] = {"picked": lab[k] if k < len(lab) else k,
+                     "candidates_us": dict(zip(lab, times)) if times else None}
+    return out
 
 
 def cpu_baseline(args, detail, B, budget_s=10.0):
@@ -677,7 +719,7 @@ def only_gemms(args, torch, dev, names):
     from invariant_bi_rmsnorm_amd.model import init_weights
     cfg = model_config(args)
     w = init_weights(cfg, args.seed + 14, dev, source="device")
-    _, eng, _, meta, kv_len, _ = build_workload(args, args.batch, torch, dev, w)
+    _, eng, _, meta, kv_len, _, _ = build_workload(args, args.batch, torch, dev, w)
     T = meta["T"]
     c = cfg
     for buf in (eng.x, eng.att, eng.act):
@@ -759,9 +801,10 @@ def only_kernel(args, torch, dev):
         from invariant_bi_rmsnorm_amd.model import init_weights
         cfg = model_config(args)
         w = init_weights(cfg, args.seed + 14, dev, source="device")
-        _, eng, twin, meta, kv_len, _ = build_workload(args, args.batch, torch, dev, w,
-                                                       free=args.twin)
-        e = twin if args.twin else eng
+        _, eng, twin, meta, kv_len, _, tmeta = build_workload(
+            args, args.batch, torch, dev, w, free=args.twin,
+            twin_mode=args.twin_mode)
+        e, meta = (twin, tmeta) if args.twin else (eng, meta)
         grab = {}
 
         def keep(name, f):
@@ -928,6 +971,13 @@ def main():
         "step_hbm_frac": round(res["hbm_frac_of_step_bound"], 4),
         "invariance_overhead_pct": round(res["invariance_overhead_pct"], 2),
         "twin_tokens_per_s": round(res["free"]["tokens_per_s"], 1),
+        "twin": {"mode": "tuned: per call site, the fastest of the invariant configuration "
+                         "and the batch-adaptive ones, measured on first use",
+                 "timing": "graph replay" if res["free"]["graph"] else "eager steps",
+                 "graph_matches_eager": res["free"]["graph_matches_eager"],
+                 "graph_check": "within 1e-3 of the largest logit (its kernels need not "
+                                "repeat their bits)",
+                 "choices": res["twin_choices"]},
         "graph": res["inv"]["graph"], "graph_matches_eager": res["inv"]["graph_matches_eager"],
         "per_kernel_note": "HIP event pairs around each launch of 20 eager steps, a device "
                            "spin ahead of each start event; each pair adds its own cost of a "
@@ -935,6 +985,8 @@ def main():
                            "kernel-trace durations)",
         "per_kernel": {k: _rounded(v) for k, v in per.items()},
         "per_kernel_twin": {k: _rounded(v) for k, v in per_free.items()},
+        "per_kernel_delta_us": {k: round(per[k]["avg_us"] - per_free[k]["avg_us"], 2)
+                                for k in per if k in per_free},
     }
     gc = measured_gemm_counters()
     if gc is not None:
@@ -956,7 +1008,9 @@ def main():
                 "tokens_per_s": round(r2["inv"]["tokens_per_s"], 1),
                 "ms_per_step": round(r2["inv"]["ms_per_step"], 3),
                 "twin_tokens_per_s": round(r2["free"]["tokens_per_s"], 1),
+                "twin_timing": "graph replay" if r2["free"]["graph"] else "eager steps",
                 "invariance_overhead_pct": round(r2["invariance_overhead_pct"], 2),
+                "twin_choices": {k: v["picked"] for k, v in r2["twin_choices"].items()},
                 "step_hbm_frac": round(r2["hbm_frac_of_step_bound"], 4)}
             torch.cuda.empty_cache()
         detail = keep

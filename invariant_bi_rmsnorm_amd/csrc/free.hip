@@ -2,16 +2,17 @@
 // mathematics as bi_rmsnorm / bi_gemm but choose their split points from the
 // batch and the device's 256 compute units, as ordinary serving kernels do
 // ("Batch invariance and reproducible inference", "From batch size to
-// reduction tree" and "2 . Cross-block accumulation": split-K merged by
-// atomics leaves the order to whichever workgroup lands first).  They exist
-// to price invariance and as the harness's negative control.
+// reduction tree" and "2 . Cross-block accumulation": split-K whose split
+// count follows the batch, and a norm whose partial sums meet through atomics
+// in whatever order the workgroups land).  They exist to price invariance and
+// as the harness's negative control.
 #include "api.h"
 #include "common.h"
 
 namespace bi {
 
-void gemm_splitk_atomic(const void* A, const void* W, float* C32, int M, int N, int K,
-                        int splits, int kslice, hipStream_t s);
+bool gemm_splitk_slices(const void* A, const void* W, float* C32, int M, int N, int K, int mb,
+                        int ct, int splits, int kslice, hipStream_t s);
 void gemm_dispatch(const void* A, const void* W, void* C, int M, int N, int K, int out_f32,
                    hipStream_t s);
 
@@ -21,10 +22,16 @@ __global__ void k_fill(float* __restrict__ p, long n) {
   for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) p[i] = 0.f;
 }
 
+// out[i] = sum over the split-K slices j = 0 .. splits-1 of part[j n + i]
+// (slices in order), converted to the output type.
 template <int OUT_DT>
-__global__ void k_convert(const float* __restrict__ src, void* __restrict__ dst, long n) {
-  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256)
-    Elem<OUT_DT>::st(dst, i, src[i]);
+__global__ void k_splitk_reduce(const float* __restrict__ part, void* __restrict__ out, long n,
+                                int splits) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+    float a = part[i];
+    for (int j = 1; j < splits; ++j) a += part[(long)j * n + i];
+    Elem<OUT_DT>::st(out, i, a);
+  }
 }
 
 // ---- RMSNorm twin ---------------------------------------------------------
@@ -121,42 +128,73 @@ extern "C" bi_status bi_rmsnorm_free(const void* x, const void* gamma, void* y, 
   return launched("bi_rmsnorm_free");
 }
 
+// The twin's split-K configuration for M <= 256: the tile (mb 8-row blocks by
+// ct 16-column strips) and split count s that move the fewest bytes into the
+// busiest CU -- rounds of 256 workgroups x (8 mb + 16 ct) rows x K / s -- plus
+// the partial sums written and read back; s = 1 means no split.  The row
+// count sets how many row groups share the device, so the split count (and
+// with it each output's sum tree) follows the batch: at N = K = 4096, eight
+// slices up to 64 rows, four at 128.
+namespace bi {
+struct SplitPick {
+  int mb, ct, s, kslice;
+};
+static SplitPick split_pick(int M, int N, int K) {
+  SplitPick best{0, 0, 1, K};
+  double best_cost = -1;
+  for (int mb : {1, 2, 4, 8}) {
+    const long rg = (M + 8 * mb - 1) / (8 * mb);
+    if (mb > 1 && 8 * (mb / 2) >= M) continue;   // a smaller block already holds every row
+    for (int ct : {2, 4, 8}) {
+      for (int s : {1, 2, 4, 8}) {
+        const int kslice = ((K + s - 1) / s + 63) / 64 * 64;
+        const int se = (K + kslice - 1) / kslice;
+        const long wgs = rg * ((N + 16 * ct - 1) / (16 * ct)) * se;
+        const double rounds = (double)((wgs + kCUs - 1) / kCUs);
+        double cost = rounds * (8.0 * mb + 16.0 * ct) * kslice * 2.0;
+        if (se > 1) cost += 2.0 * se * (double)M * N * 4.0 / kCUs;
+        if (best_cost < 0 || cost < best_cost) {
+          best_cost = cost;
+          best = SplitPick{mb, ct, se, kslice};
+        }
+      }
+    }
+  }
+  return best;
+}
+}  // namespace bi
+
+constexpr int kSplitMaxRows = 256;
+
 extern "C" size_t bi_gemm_free_workspace_bytes(int M, int N, int K) {
-  (void)K;
-  return (M > 0 && N > 0) ? (size_t)M * N * sizeof(float) : 0;
+  if (M <= 0 || N <= 0 || K <= 0 || M > kSplitMaxRows) return 0;
+  const SplitPick sp = split_pick(M, N, K);
+  return sp.s > 1 ? (size_t)sp.s * M * N * sizeof(float) : 0;
 }
 
 extern "C" bi_status bi_gemm_free(const void* A, const void* W, void* C, int M, int N, int K,
                                   int in_dtype, int out_dtype, void* workspace,
                                   size_t workspace_bytes, bi_stream stream) {
   BI_REQUIRE(M >= 0 && N >= 1 && K >= 1, BI_ERR_INVALID, "bi_gemm_free: bad shape");
-  if (in_dtype != BI_BF16 || M == 0 || M > 64 || K % 32 != 0)
+  if (in_dtype != BI_BF16 || M == 0 || M > kSplitMaxRows || K % 8 != 0)
     return bi_gemm(A, W, C, M, N, K, in_dtype, out_dtype, stream);
   BI_REQUIRE(out_dtype == BI_BF16 || out_dtype == BI_F32, BI_ERR_UNSUPPORTED,
              "bi_gemm_free: out dtype %d", out_dtype);
   BI_REQUIRE(A && W && C, BI_ERR_INVALID, "bi_gemm_free: null pointer");
-  // Workgroups the small-M kernels would launch along N; split K until the
-  // device holds a target that grows as the batch shrinks (fewer rows leave
-  // each workgroup less work to hide its latency behind).
-  const long tiles = (N + 15) / 16;
-  const long target = (M <= 16 ? 4L : 2L) * kCUs;
-  if (tiles >= target || K < 1024)
-    return bi_gemm(A, W, C, M, N, K, in_dtype, out_dtype, stream);
-  BI_REQUIRE(workspace && workspace_bytes >= bi_gemm_free_workspace_bytes(M, N, K),
+  const SplitPick sp = split_pick(M, N, K);
+  if (sp.s == 1) return bi_gemm(A, W, C, M, N, K, in_dtype, out_dtype, stream);
+  BI_REQUIRE(workspace && workspace_bytes >= (size_t)sp.s * M * N * sizeof(float),
              BI_ERR_WORKSPACE, "bi_gemm_free: workspace too small");
-  int splits = (int)((target + tiles - 1) / tiles);
-  splits = splits < 8 ? splits : 8;
-  int kslice = (K + splits - 1) / splits;
-  kslice = (kslice + 255) & ~255;               // whole pipeline stages
-  splits = (K + kslice - 1) / kslice;
   hipStream_t s = as_stream(stream);
-  float* c32 = static_cast<float*>(workspace);
+  float* part = static_cast<float*>(workspace);
+  if (!gemm_splitk_slices(A, W, part, M, N, K, sp.mb, sp.ct, sp.s, sp.kslice, s))
+    return fail(BI_ERR_UNSUPPORTED, "bi_gemm_free: no split kernel for mb %d ct %d", sp.mb,
+                sp.ct);
   const long n = (long)M * N;
-  hipLaunchKernelGGL(k_fill, dim3((unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096)),
-                     dim3(256), 0, s, c32, n);
-  gemm_splitk_atomic(A, W, c32, M, N, K, splits, kslice, s);
-  const unsigned g = (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
-  if (out_dtype == BI_BF16) hipLaunchKernelGGL(k_convert<1>, dim3(g), dim3(256), 0, s, c32, C, n);
-  else hipLaunchKernelGGL(k_convert<0>, dim3(g), dim3(256), 0, s, c32, C, n);
+  const unsigned g = (unsigned)((n + 255) / 256 < 2048 ? (n + 255) / 256 : 2048);
+  if (out_dtype == BI_BF16)
+    hipLaunchKernelGGL(k_splitk_reduce<1>, dim3(g), dim3(256), 0, s, part, C, n, sp.s);
+  else
+    hipLaunchKernelGGL(k_splitk_reduce<0>, dim3(g), dim3(256), 0, s, part, C, n, sp.s);
   return launched("bi_gemm_free");
 }

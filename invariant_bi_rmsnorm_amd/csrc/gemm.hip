@@ -32,7 +32,8 @@ __device__ __forceinline__ f32x4_t mfma(const u32x4_t& a, const u32x4_t& b, cons
   return mfma16(a, b, c);
 }
 
-// OUTF32: 0 = bf16 store, 1 = fp32 store, 2 = fp32 atomic add (split-K twin)
+// OUTF32: 0 = bf16 store, 1 = fp32 store (2 in the skinny kernel: fp32
+// store into the split-K twin's slice blockIdx.y)
 template <int OUTF32>
 __device__ __forceinline__ void store_tile(void* C, const f32x4_t& acc, int row0, int col0, int M,
                                            int N, int lane) {
@@ -43,9 +44,7 @@ __device__ __forceinline__ void store_tile(void* C, const f32x4_t& acc, int row0
     const int row = row0 + 4 * (lane >> 4) + j;
     if (row < M) {
       const long idx = (long)row * N + col;
-      if (OUTF32 == 2)
-        atomicAdd(static_cast<float*>(C) + idx, acc[j]);
-      else if (OUTF32 == 1)
+      if (OUTF32 == 1)
         static_cast<float*>(C)[idx] = acc[j];
       else
         static_cast<uint16_t*>(C)[idx] = (uint16_t)f32_to_bf16_bits(acc[j]);
@@ -376,6 +375,10 @@ __global__ __launch_bounds__(kSmallThreads) void k_gemm_small(
         if (m < MT) store_swiglu(C, acc[i][j], m0 + m * 16, n0 / 2 + c * 8, mend, N / 2, lane);
       } else if constexpr (OUTF32 == 4) {
         if (m < MT) store_rope(ra, acc[i][j], m0 + m * 16, n0 / 16 + c, mend, N, lane);
+      } else if constexpr (OUTF32 == 2) {   // split-K twin: this slice's partial sums
+        if (m < MT)
+          store_tile<1>(static_cast<float*>(C) + (long)blockIdx.y * M * N, acc[i][j],
+                        m0 + m * 16, n0 + c * 16, mend, N, lane);
       } else if (m < MT) {
         store_tile<OUTF32>(C, acc[i][j], m0 + m * 16, n0 + c * 16, mend, N, lane);
       }
@@ -748,12 +751,23 @@ static void launch_big(const void* A, const void* W, void* C, int M, int N, int 
                      (const uint16_t*)A, (const uint16_t*)W, C, M, N, K, tiles_m, tiles_n);
 }
 
-// Split-K over `splits` workgroup slices of kslice (multiple of 32) columns of
-// K, fp32 partial sums added atomically into C32 (which the caller zeroed).
-// Used only by the batch-adaptive twin.
-void gemm_splitk_atomic(const void* A, const void* W, float* C32, int M, int N, int K,
-                        int splits, int kslice, hipStream_t s) {
-  dispatch_small<2>(A, W, C32, M, N, K, s, splits, kslice);
+// Split-K for the batch-adaptive twin only: `splits` workgroup slices of
+// kslice columns of K (a multiple of 64), with the tile shape the twin picks
+// (mb 8-row blocks, ct 16-column strips); slice j writes its fp32 partial
+// sums to C32 + j M N.  Returns false for a shape it was not built for.
+bool gemm_splitk_slices(const void* A, const void* W, float* C32, int M, int N, int K, int mb,
+                        int ct, int splits, int kslice, hipStream_t s) {
+  const RopeArgs ra{};
+#define BI_SK(MB_, CT_)                                                              \
+  if (mb == MB_ && ct == CT_) {                                                      \
+    launch_small_k<MB_, CT_, 2>(A, W, C32, M, N, K, s, splits, kslice, ra);          \
+    return true;                                                                     \
+  }
+#define BI_SK_M(MB_) BI_SK(MB_, 2) BI_SK(MB_, 4) BI_SK(MB_, 8)
+  BI_SK_M(1) BI_SK_M(2) BI_SK_M(4) BI_SK_M(8)
+#undef BI_SK_M
+#undef BI_SK
+  return false;
 }
 
 // Which kernel runs never changes a bit (every path keeps the same chain per

@@ -153,18 +153,97 @@ class StepOutput:
     seg_index: list = field(default_factory=list)   # the segment of each row
 
 
+class Tuner:
+    """The tuned twin's choice, per call site and shape, of the fastest of
+    its candidate configurations, timed once on first use the way a step
+    runs: each candidate is captured in a HIP graph of `reps` launches
+    cycling through the layers' weights and KV (cold data, as in a step),
+    the graph is replayed a few times between HIP events and the median
+    replay time is taken; later calls reuse the choice.  The first candidate
+    (the invariant configuration) is kept unless another is faster by more
+    than `margin`, so measurement noise cannot make the twin slower than the
+    invariant path.  Nothing is timed under graph capture (a shape first met
+    there is an error: warm the engine up eagerly first)."""
+
+    def __init__(self, reps: int = 8, replays: int = 5, margin: float = 0.02):
+        self.reps, self.replays, self.margin = reps, replays, margin
+        self.best = {}
+        self.times = {}
+
+    def _time(self, fn, n_layers: int) -> float:
+        for j in range(2):
+            fn(j % n_layers)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                for t in range(self.reps):
+                    fn(t % n_layers)
+        torch.cuda.current_stream().wait_stream(side)
+        graph.replay()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(self.replays):
+            a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            graph.replay()
+            e.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(e))
+        del graph
+        return 1e3 * sorted(ms)[len(ms) // 2] / self.reps
+
+    def pick(self, key, cands, n_layers: int) -> int:
+        b = self.best.get(key)
+        if b is not None:
+            return b
+        if len(cands) == 1:
+            self.best[key] = 0
+            return 0
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError(f"tuned twin: {key} first met under graph capture")
+        us = [self._time(fn, n_layers) for fn in cands]
+        k = int(np.argmin(us))
+        if us[k] > us[0] * (1.0 - self.margin):
+            k = 0
+        self.best[key] = k
+        self.times[key] = [round(u, 2) for u in us]
+        return k
+
+
 class Engine:
     """Runs forward steps over packed rows through libbi.so.
 
-    free=True swaps every reduction kernel for its batch-adaptive twin
-    (bi_*_free): the same mathematics with split points chosen from the
-    batch, which prices invariance and serves as the negative control of the
-    schedule fuzzer."""
+    mode (or free=True for "free"):
+    - "invariant": the batch-invariant kernels, with each residual add fused
+      into the RMSNorm after it, the QKV projection fused with RoPE and the
+      KV append, and the gate/up projection fused with SiLU-mul at a few rows
+      (each fusion bit-equal to its unfused pair).
+    - "free": every reduction on its batch-adaptive twin (bi_*_free), the
+      same mathematics with split points chosen from the batch and no fusion:
+      the negative control of the schedule fuzzer.
+    - "tuned": the invariant engine's structure, but at every call site the
+      fastest of the invariant configuration and the batch-adaptive ones
+      (split-K GEMMs, KV chunks of 64, occupancy-driven KV splits, norms
+      split over workgroups), measured per shape on first use in graph
+      replays (Tuner): the fair batch-adaptive baseline that prices
+      invariance.  Where no adaptive configuration is faster it runs the
+      invariant kernel, so its step is no slower than the invariant one by
+      construction (up to the timing noise of separate runs)."""
+
+    MODES = ("invariant", "free", "tuned")
 
     def __init__(self, cfg: ModelConfig, weights: Weights, pool: KVPool, device,
-                 max_rows: int = 64, max_pages_per_req: int = 512, free: bool = False):
+                 max_rows: int = 64, max_pages_per_req: int = 512, free: bool = False,
+                 mode: str | None = None):
         self.cfg, self.w, self.pool, self.dev = cfg, weights, pool, device
-        self.free = free
+        self.mode = mode if mode is not None else ("free" if free else "invariant")
+        if self.mode not in self.MODES:
+            raise ValueError(f"mode {self.mode!r} not in {self.MODES}")
+        self.free = self.mode == "free"
+        self.tuner = Tuner() if self.mode == "tuned" else None
         self.max_pages = max_pages_per_req
         c = cfg
         if c.rope:
@@ -244,6 +323,13 @@ class Engine:
             nb = m["total_chunks"]
             m["ml"] = torch.empty((nb, self.cfg.h, 2), device=d)
             m["pacc"] = torch.empty((nb, self.cfg.h, self.cfg.d_h), device=d)
+            if self.mode == "tuned" and self.cfg.kv_chunk == 256:
+                # the twin may split the KV into 64-key chunks instead
+                off64 = L.bi_chunk_offsets(meta["kv_len_dec"], 64)
+                m["chunk_off64"] = off64.to(d)
+                m["total_chunks64"] = n64 = int(off64[-1])
+                m["ml64"] = torch.empty((n64, self.cfg.h, 2), device=d)
+                m["pacc64"] = torch.empty((n64, self.cfg.h, self.cfg.d_h), device=d)
         if meta["n_pre"]:
             m["q_start"] = torch.from_numpy(meta["q_start_pre"]).to(d)
             m["pos0"] = torch.from_numpy(meta["pos0_pre"]).to(d)
@@ -268,83 +354,148 @@ class Engine:
         h, x, qkv, q, att = self.h[:T], self.x[:T], self.qkv[:T], self.q[:T], self.att[:T]
         o, gu, act = self.o[:T], self.gu[:T], self.act[:T]
         nd = m["n_dec"]
-        fr = self.free
-        rms = L.bi_rmsnorm_free if fr else L.bi_rmsnorm
-        gemm = L.bi_gemm_free if fr else L.bi_gemm
-        L.bi_embed(w.embed, m["tokens"], h)
+        mode = self.mode
+        fr = mode == "free"
         lws = w.layers[:layers] if layers else w.layers
-        # invariant path: each residual add runs fused with the RMSNorm after
-        # it (the next sublayer's, or the final norm); the twins keep them apart
-        fuse = not fr
-        if fuse:
-            run("rmsnorm", lambda: rms(h, lws[0].attn_norm, x, c.eps))
-        for li, lw in enumerate(lws):
-            kp, vp = self.pool.k[li], self.pool.v[li]
-            nxt = lws[li + 1].attn_norm if li + 1 < len(lws) else w.final_norm
-            see("h_in", li, h)
-            if not fuse:
-                run("rmsnorm", lambda: rms(h, lw.attn_norm, x, c.eps))
-            see("x_attn", li, x)
-            if fuse and T <= 64 and c.dtype == torch.bfloat16 and c.d_h % 16 == 0:
+        nl = len(lws)
+        bf = c.dtype == torch.bfloat16
+        pos = m["pos"] if c.rope else None
+
+        def choose(site, key, cands):
+            """cands: functions of a layer index; invariant mode takes the
+            first, free mode the last, tuned mode the fastest."""
+            if mode == "invariant":
+                return cands[0]
+            if mode == "free":
+                return cands[-1]
+            return cands[self.tuner.pick((site,) + key, cands, nl)]
+
+        # each site: candidate launchers as functions of a layer index j
+        def qkv_cands():
+            def rope_append(j):
+                L.bi_rope_kv_append(qkv, c.h, c.h_kv, c.d_h, pos, self.cos, self.sin, m["slots"],
+                                    q, self.pool.k[j], self.pool.v[j])
+            if T <= 64 and bf and c.d_h % 16 == 0 and not fr:
                 # the same bits in one pass (RoPE + KV append in the GEMM's
                 # epilogue); the step measured 2.5% faster at batch 1, 0.5-1.2%
                 # at 4-32, even at 16 and 64
-                run("gemm_qkv", lambda: L.bi_gemm_qkv_rope(
-                    x, lw.wqkv, c.h, c.h_kv, c.d_h, m["pos"] if c.rope else None, self.cos,
-                    self.sin, m["slots"], q, kp, vp))
+                inv = lambda j: L.bi_gemm_qkv_rope(  # noqa: E731
+                    x, lws[j].wqkv, c.h, c.h_kv, c.d_h, pos, self.cos, self.sin, m["slots"], q,
+                    self.pool.k[j], self.pool.v[j])
             else:
-                run("gemm_qkv", lambda: gemm(x, lw.wqkv, qkv))
-                run("rope_kv_append", lambda: L.bi_rope_kv_append(
-                    qkv, c.h, c.h_kv, c.d_h, m["pos"] if c.rope else None, self.cos, self.sin,
-                    m["slots"], q, kp, vp))
-            see("q", li, q)
-            if nd and fr:
-                run("decode_attn", lambda: L.bi_decode_attn_free(
-                    q[:nd], kp, vp, m["bt_dec"], m["kv_len"], m["max_kv_len"], c.scale,
-                    att[:nd]))
-            elif nd:
-                run("decode_attn", lambda: L.bi_decode_attn(
-                    q[:nd], kp, vp, m["bt_dec"], m["kv_len"], m["chunk_off"], m["total_chunks"],
-                    c.kv_chunk, c.scale, m["ml"], m["pacc"]))
-                run("merge", lambda: L.bi_merge_partials(m["ml"], m["pacc"], m["chunk_off"],
-                                                         att[:nd]))
-            if m["n_pre"] and fr:
-                run("prefill_attn", lambda: L.bi_prefill_attn_free(
-                    q[nd:], m["q_start"], m["pos0"], kp, vp, m["bt_pre"], c.scale, att[nd:]))
-            elif m["n_pre"]:
-                run("prefill_attn", lambda: L.bi_prefill_attn(
-                    q[nd:], m["q_start"], m["pos0"], kp, vp, m["bt_pre"], c.kv_chunk, c.scale,
-                    att[nd:]))
-            see("att", li, att)
-            run("gemm_o", lambda: gemm(att.view(T, c.h * c.d_h), lw.wo, o))
-            see("o", li, o)
-            if fuse:
-                run("add_rmsnorm", lambda: L.bi_add_rmsnorm(h, o, lw.ffn_norm, x, c.eps))
+                inv = lambda j: (L.bi_gemm(x, lws[j].wqkv, qkv), rope_append(j))  # noqa: E731
+            return [inv, lambda j: (L.bi_gemm_free(x, lws[j].wqkv, qkv), rope_append(j))]
+
+        def gemm_cands(a_buf, wname, out):
+            return [lambda j: L.bi_gemm(a_buf, getattr(lws[j], wname), out),
+                    lambda j: L.bi_gemm_free(a_buf, getattr(lws[j], wname), out)]
+
+        def decode_cands():
+            cands = [lambda j: (
+                L.bi_decode_attn(q[:nd], self.pool.k[j], self.pool.v[j], m["bt_dec"], m["kv_len"],
+                                 m["chunk_off"], m["total_chunks"], c.kv_chunk, c.scale, m["ml"],
+                                 m["pacc"]),
+                L.bi_merge_partials(m["ml"], m["pacc"], m["chunk_off"], att[:nd]))]
+            if "chunk_off64" in m:
+                cands.append(lambda j: (
+                    L.bi_decode_attn(q[:nd], self.pool.k[j], self.pool.v[j], m["bt_dec"],
+                                     m["kv_len"], m["chunk_off64"], m["total_chunks64"], 64,
+                                     c.scale, m["ml64"], m["pacc64"]),
+                    L.bi_merge_partials(m["ml64"], m["pacc64"], m["chunk_off64"], att[:nd])))
+            cands.append(lambda j: L.bi_decode_attn_free(
+                q[:nd], self.pool.k[j], self.pool.v[j], m["bt_dec"], m["kv_len"],
+                m["max_kv_len"], c.scale, att[:nd]))
+            return cands
+
+        def prefill_cands():
+            return [lambda j: L.bi_prefill_attn(q[nd:], m["q_start"], m["pos0"], self.pool.k[j],
+                                                self.pool.v[j], m["bt_pre"], c.kv_chunk, c.scale,
+                                                att[nd:]),
+                    lambda j: L.bi_prefill_attn_free(q[nd:], m["q_start"], m["pos0"],
+                                                     self.pool.k[j], self.pool.v[j], m["bt_pre"],
+                                                     c.scale, att[nd:])]
+
+        def norm_cands(gamma, hh):
+            return [lambda j: L.bi_rmsnorm(hh, gamma, x, c.eps),
+                    lambda j: L.bi_rmsnorm_free(hh, gamma, x, c.eps)]
+
+        def add_norm(gamma):
+            """h += o, then x = RMSNorm(h): fused (invariant) or add + the
+            twin norm.  Tuned-mode timing runs on a copy of h (the add
+            updates h in place)."""
+            if mode == "tuned" and ("add_norm", T) not in self.tuner.best:
+                hs = h.clone()
+                self.tuner.pick(("add_norm", T), [
+                    lambda j: L.bi_add_rmsnorm(hs, o, gamma, x, c.eps),
+                    lambda j: (L.bi_add(hs, o, hs), L.bi_rmsnorm_free(hs, gamma, x, c.eps))], nl)
+            k = 0 if mode == "invariant" else (1 if fr else self.tuner.best[("add_norm", T)])
+            if k == 0:
+                run("add_rmsnorm", lambda: L.bi_add_rmsnorm(h, o, gamma, x, c.eps))
             else:
                 run("add", lambda: L.bi_add(h, o, h))
-                run("rmsnorm", lambda: rms(h, lw.ffn_norm, x, c.eps))
-            see("h_mid", li, h)
-            see("x_ffn", li, x)
-            if fuse and T <= 8 and c.dtype == torch.bfloat16:
+                run("rmsnorm", lambda: L.bi_rmsnorm_free(h, gamma, x, c.eps))
+
+        def swiglu_cands():
+            cands = []
+            if T <= 8 and bf and not fr:
                 # the same bits in one pass (GEMM epilogue); at up to 8 rows
                 # (one-block strips) the step measured 3.7% faster at batch 1
                 # and 0.5% at 7, at 64 rows 0.7% slower
-                run("gemm_gate_up", lambda: L.bi_gemm_swiglu(x, lw.wgu, act))
+                cands.append(lambda j: L.bi_gemm_swiglu(x, lws[j].wgu, act))
+            cands.append(lambda j: (L.bi_gemm(x, lws[j].wgu, gu), L.bi_silu_mul(gu, act)))
+            cands.append(lambda j: (L.bi_gemm_free(x, lws[j].wgu, gu), L.bi_silu_mul(gu, act)))
+            return cands
+
+        L.bi_embed(w.embed, m["tokens"], h)
+        # the invariant and tuned engines fuse each residual add into the
+        # RMSNorm after it (the next sublayer's, or the final norm)
+        fuse = not fr
+        if fuse:
+            f = choose("norm", (T,), norm_cands(lws[0].attn_norm, h))
+            run("rmsnorm", lambda f=f: f(0))
+        for li, lw in enumerate(lws):
+            nxt = lws[li + 1].attn_norm if li + 1 < nl else w.final_norm
+            see("h_in", li, h)
+            if not fuse:
+                run("rmsnorm", lambda: L.bi_rmsnorm_free(h, lw.attn_norm, x, c.eps))
+            see("x_attn", li, x)
+            f = choose("qkv", (T,), qkv_cands())
+            run("gemm_qkv", lambda f=f, li=li: f(li))
+            see("q", li, q)
+            if nd:
+                f = choose("decode_attn", (nd, m["total_chunks"]), decode_cands())
+                run("decode_attn", lambda f=f, li=li: f(li))
+            if m["n_pre"]:
+                f = choose("prefill_attn", (T - nd, m["n_pre"]), prefill_cands())
+                run("prefill_attn", lambda f=f, li=li: f(li))
+            see("att", li, att)
+            f = choose("gemm_o", (T,), gemm_cands(att.view(T, c.h * c.d_h), "wo", o))
+            run("gemm_o", lambda f=f, li=li: f(li))
+            see("o", li, o)
+            if fuse:
+                add_norm(lw.ffn_norm)
             else:
-                run("gemm_gate_up", lambda: gemm(x, lw.wgu, gu))
+                run("add", lambda: L.bi_add(h, o, h))
+                run("rmsnorm", lambda: L.bi_rmsnorm_free(h, lw.ffn_norm, x, c.eps))
+            see("h_mid", li, h)
+            see("x_ffn", li, x)
+            sw = swiglu_cands()
+            f = choose("gemm_gate_up", (T,), sw)
+            run("gemm_gate_up", lambda f=f, li=li: f(li))
+            if not (T <= 8 and bf and not fr and f is sw[0]):   # the product went to gu
                 see("gu", li, gu)
-                run("silu_mul", lambda: L.bi_silu_mul(gu, act))
             see("act", li, act)
-            run("gemm_down", lambda: gemm(act, lw.wdown, o))
+            f = choose("gemm_down", (T,), gemm_cands(act, "wdown", o))
+            run("gemm_down", lambda f=f, li=li: f(li))
             see("down", li, o)
             if fuse:
-                run("add_rmsnorm", lambda: L.bi_add_rmsnorm(h, o, nxt, x, c.eps))
+                add_norm(nxt)
             else:
                 run("add", lambda: L.bi_add(h, o, h))
             see("h_out", li, h)
         if not fuse:
-            rms(h, w.final_norm, x, c.eps)
-        see("x_final", len(lws), x)
+            L.bi_rmsnorm_free(h, w.final_norm, x, c.eps)
+        see("x_final", nl, x)
         nw = len(m["want"])
         if nw == 0:
             return StepOutput(torch.empty((0, c.vocab), device=self.dev),
@@ -355,7 +506,9 @@ class Engine:
             hs = torch.empty((nw, c.d), dtype=c.dtype, device=self.dev)
             L.bi_embed(x, m["want_rows"], hs)      # row gather
         logits = torch.empty((nw, c.vocab), dtype=torch.float32, device=self.dev)
-        run("gemm_lm_head", lambda: gemm(hs, w.lm_head, logits))
+        f = choose("gemm_lm_head", (nw,), [lambda j: L.bi_gemm(hs, w.lm_head, logits),
+                                            lambda j: L.bi_gemm_free(hs, w.lm_head, logits)])
+        run("gemm_lm_head", lambda f=f: f(0))
         toks = torch.empty(nw, dtype=torch.int32, device=self.dev)
         L.bi_argmax(logits, toks)
         return StepOutput(logits, toks, [i for i, _ in m["want"]])

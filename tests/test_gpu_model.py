@@ -357,6 +357,43 @@ def test_decode_verify_rollback_on_twins_commits_invariant_greedy():
     assert decided > 0
 
 
+def test_tuned_twin_close_to_invariant_and_picks_every_site():
+    """The tuned twin (per call site, the fastest of the invariant and the
+    batch-adaptive configurations) computes the same mathematics: on a
+    prefill and decode steps its logits stay within the drift of two valid
+    summation orders of the invariant engine's, its argmax agrees wherever
+    the top-2 gap is clear, and it has recorded a choice, with candidate
+    times, for every call site it met."""
+    cfg = replace(SMALL, kv_chunk=256)
+    w = init_weights(cfg, 43, dev(), source="synth")
+    pool_a, pool_b = KVPool(cfg, 256, dev()), KVPool(cfg, 256, dev())
+    inv = Engine(cfg, w, pool_a, dev(), max_rows=256, max_pages_per_req=64)
+    tun = Engine(cfg, w, pool_b, dev(), max_rows=256, max_pages_per_req=64, mode="tuned")
+    prompts = [[int(t) for t in synth.token_ids(n, cfg.vocab, seed=500 + n)] for n in (90, 300, 17)]
+    pages = [list(range(r * 40, r * 40 + 40)) for r in range(3)]
+    for eng in (inv, tun):
+        eng.step([Segment(pages=pages[r], pos0=0, tokens=p) for r, p in enumerate(prompts)])
+    worst = 0.0
+    for t in range(4):
+        segs = [Segment(pages=pages[r], pos0=len(p) + t, tokens=[int(p[t % len(p)])])
+                for r, p in enumerate(prompts)]
+        a = inv.step(segs).logits.cpu().numpy()
+        b = tun.step(segs).logits.cpu().numpy()
+        for i in range(3):
+            e = float(np.max(np.abs(a[i] - b[i])) / np.max(np.abs(a[i])))
+            worst = max(worst, e)
+            top2 = np.sort(a[i])[-2:]
+            if top2[1] - top2[0] > 2 * np.max(np.abs(a[i] - b[i])):
+                assert int(np.argmax(a[i])) == int(np.argmax(b[i]))
+    assert worst <= 3e-2, worst
+    sites = {k[0] for k in tun.tuner.best}
+    assert {"norm", "qkv", "decode_attn", "prefill_attn", "gemm_o", "add_norm", "gemm_gate_up",
+            "gemm_down", "gemm_lm_head"} <= sites, sites
+    assert all(len(v) >= 2 for v in tun.tuner.times.values())
+    print("tuned twin choices:", {k: tun.tuner.best[k] for k in sorted(tun.tuner.best)},
+          f"worst logit gap {worst:.1e}")
+
+
 # ---------------------------------------------------------------------------
 # schedule fuzzing on the GPU engine
 # ---------------------------------------------------------------------------

@@ -87,13 +87,14 @@ def test_rmsnorm_free_moves_with_batch():
 # ---------------------------------------------------------------------------
 
 GEMM_FREE = [(1, 4096, 4096), (7, 6144, 4096), (33, 4096, 4096), (64, 28672, 4096),
-             (16, 4096, 14336), (3, 1000, 1024)]
+             (16, 4096, 14336), (3, 1000, 1024), (128, 4096, 4096), (200, 6144, 4104)]
 
 
 @pytest.mark.parametrize("M,N,K", GEMM_FREE)
 def test_gemm_free_integer_exact(M, N, K):
     # integers in [-8, 8]: every partial sum is exact in fp32, so any split
-    # and any atomic order must give the oracle's value bit for bit
+    # and any order of adding the slices must give the oracle's value bit
+    # for bit
     A = synth.integers((M, K), -8, 8, seed=M + 1).to(torch.bfloat16)
     W = synth.integers((N, K), -8, 8, seed=N + 2).to(torch.bfloat16)
     C = torch.empty((M, N), dtype=torch.float32, device=dev())
@@ -118,7 +119,9 @@ def test_gemm_free_tolerance(M, N, K):
 
 
 def test_gemm_free_moves_with_batch():
-    M, N, K = 64, 4096, 4096
+    # the twin's split count follows the rows (eight K slices for one row,
+    # four for 128 at N = K = 4096), so a row's bits move with the batch
+    M, N, K = 128, 4096, 4096
     A = synth.normal((M, K), seed=31).to(torch.bfloat16).to(dev())
     W = synth.normal((N, K), seed=32, std=0.02).to(torch.bfloat16).to(dev())
     big = torch.empty((M, N), dtype=torch.float32, device=dev())
