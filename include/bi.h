@@ -169,9 +169,16 @@ bi_status bi_gemm_free(const void *A, const void *W, void *C, int M, int N, int 
 /* split-KV attention over a paged KV cache                               */
 /* ---------------------------------------------------------------------- */
 /*
- * KV cache layout (both pools): [num_pages][h_kv][page_size][d_h] of
- * `dtype`; token j of a request lives in page block_table[r][j / page_size]
- * at slot j % page_size.  block_table: device int32 [B][max_pages].
+ * KV cache layout: each pool is num_pages pages of h_kv blocks of page_size
+ * tokens x d_h elements of `dtype` (page p, kv head g: the block at element
+ * offset (p * h_kv + g) * page_size * d_h); token j of a request lives in
+ * page block_table[r][j / page_size] at slot j % page_size.  Within a block,
+ * V is token-major rows ([slot][d_h]), and K is stored by 16-byte units:
+ * unit u (elements 16/esize * u ..) of slot t at byte (u * page_size + t) *
+ * 16, so that one matrix-core operand of K (16 tokens x 32 dims) is a
+ * contiguous KiB.  bi_rope_kv_append and bi_gemm_qkv_rope write this layout;
+ * a cache held as token-major rows converts by that permutation of 16-byte
+ * units alone.  block_table: device int32 [B][max_pages].
  * Query head i reads kv head i / (h / h_kv).
  *
  * Chunking ("Lockstep", "The fix": attention split points come from the

@@ -166,6 +166,24 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def k_pool_from_rows(k: torch.Tensor) -> torch.Tensor:
+    """A K cache given as token-major rows, [..., page_size, d_h] per (page,
+    kv head) block, rearranged into the library's K page layout (bi.h, "KV
+    cache layout": 16-byte units stored unit-major within each block).  Same
+    shape, dtype and device; only the order of the bytes changes.  V keeps
+    token-major rows and needs no conversion."""
+    *lead, S, D = k.shape
+    e = 16 // k.element_size()
+    return k.reshape(*lead, S, D // e, e).transpose(-3, -2).contiguous().reshape(k.shape)
+
+
+def k_pool_to_rows(k: torch.Tensor) -> torch.Tensor:
+    """The inverse of k_pool_from_rows: token-major rows of a K cache."""
+    *lead, S, D = k.shape
+    e = 16 // k.element_size()
+    return k.reshape(*lead, D // e, S, e).transpose(-3, -2).contiguous().reshape(k.shape)
+
+
 # ---------------------------------------------------------------------------
 
 def bi_abi_version() -> int:

@@ -306,14 +306,15 @@ __device__ __forceinline__ void stage_chunk(char* lds, const void* k_pool, const
   int page[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) page[p] = (p * kPage < nk) ? bt[(j0 + wk0) / kPage + p] : pfall;
-  // K: one 1 KiB copy covers KPI consecutive keys of one page
+  // K: one 1 KiB copy covers KPI consecutive keys of one page (unit c of
+  // token `slot` sits at (c * kPage + slot) * 16 in the unit-major block)
 #pragma unroll
   for (int inst = 0; inst < 64 / S::KPI; ++inst) {
     const int k0 = inst * S::KPI;
     const int kk = k0 + lane / S::SLOTS;         // key of this lane within the wave
     const int slot = (k0 < nk) ? (kk % kPage) : 0;
     const int c = (lane % S::SLOTS) ^ ((wk0 + kk) & (S::SW - 1));
-    dma16(kp + page[k0 / kPage] * pstride + slot * S::RB + 16 * c, lds + (wk0 + k0) * S::RB);
+    dma16(kp + page[k0 / kPage] * pstride + (c * kPage + slot) * 16, lds + (wk0 + k0) * S::RB);
   }
   // V: lane-per-dim, one row per key of this wave, kept packed
   const long lane_off = (long)lane * S::DPL * S::ES;
@@ -677,14 +678,17 @@ __device__ __forceinline__ void mfma_stage_v(char* lds, const char* vbase, long 
 template <int DH>
 __device__ __forceinline__ void mfma_load_k(u32x4_t (&kf)[4][DH / 32], const char* kbase,
                                             long pstride, const int (&pg)[4]) {
-  constexpr int RB = DH * 2;
   const int lane = threadIdx.x & 63;
+  // lane l takes token l % 16, dims 32 s + 8 (l / 16) .. + 7: unit 4 s + l / 16
+  // of the unit-major block, at (unit * kPage + token) * 16 = 1024 s + 16 l --
+  // each operand is one contiguous KiB
+  static_assert(kPage == 16, "one 16-token page per operand");
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const char* row = kbase + pg[t] * pstride + (lane & 15) * RB + 16 * (lane >> 4);
+    const char* blk = kbase + pg[t] * pstride + 16 * lane;
 #pragma unroll
     for (int s = 0; s < DH / 32; ++s)   // read once: non-temporal
-      kf[t][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + 64 * s));
+      kf[t][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(blk + 1024 * s));
   }
 }
 

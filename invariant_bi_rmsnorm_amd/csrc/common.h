@@ -84,6 +84,18 @@ template <> __device__ __forceinline__ void store8<0>(void* p, long i, const flo
   q[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
+// K cache page layout.  A (page, kv head) block of K holds page_size tokens
+// of d_h elements as 16-byte units stored unit-major: unit u (elements
+// 16/es * u .. 16/es * u + 16/es - 1) of token t sits at byte
+// (u * page_size + t) * 16 of the block.  One matrix-core operand of K (16
+// tokens x 32 bf16 dims: units 4s .. 4s + 3 of each token) is then 1 KiB of
+// contiguous memory, read in whole 128-byte lines.  V keeps token-major rows.
+// Element offset, within its block, of element e of token t:
+__device__ __forceinline__ long k_block_elem(int t, int e, int page_size, int es) {
+  const int per = 16 / es;
+  return ((long)(e / per) * page_size + t) * per + e % per;
+}
+
 // ---- the library's exp ----------------------------------------------------
 // One fixed binary32 exp for softmax and SiLU, so a result never depends on
 // which hardware approximation a compiler picks: Cody & Waite range

@@ -133,18 +133,25 @@ __device__ __forceinline__ void store_rope(const RopeArgs& ra, const f32x4_t& ac
     float y = own;
     if (rotate)
       y = hi ? __builtin_fmaf(own, cs[j], oth * sn[j]) : __builtin_fmaf(own, cs[j], -(oth * sn[j]));
+    const int e = i + hi * half;   // element of the head row
     long o;
     void* dst;
     if (hh < ra.h) {
       dst = ra.q_out;
-      o = ((long)row * ra.h + hh) * ra.d_h;
+      o = ((long)row * ra.h + hh) * ra.d_h + e;
     } else {
       const int g = hh < ra.h + ra.h_kv ? hh - ra.h : hh - ra.h - ra.h_kv;
       const int page = sl[j] / ra.page_size, in_page = sl[j] - page * ra.page_size;
-      dst = hh < ra.h + ra.h_kv ? ra.k_pool : ra.v_pool;
-      o = (((long)page * ra.h_kv + g) * ra.page_size + in_page) * ra.d_h;
+      const long blk = ((long)page * ra.h_kv + g) * ra.page_size * ra.d_h;
+      if (hh < ra.h + ra.h_kv) {   // K: unit-major block (common.h)
+        dst = ra.k_pool;
+        o = blk + k_block_elem(in_page, e, ra.page_size, 2);
+      } else {
+        dst = ra.v_pool;
+        o = blk + (long)in_page * ra.d_h + e;
+      }
     }
-    static_cast<uint16_t*>(dst)[o + i + hi * half] = (uint16_t)f32_to_bf16_bits(y);
+    static_cast<uint16_t*>(dst)[o] = (uint16_t)f32_to_bf16_bits(y);
   }
 }
 

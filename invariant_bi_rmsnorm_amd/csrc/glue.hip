@@ -45,19 +45,23 @@ __global__ __launch_bounds__(256) void k_rope_kv_append(
     ya = __builtin_fmaf(a, c, -(b * s));
     yb = __builtin_fmaf(b, c, a * s);
   }
-  long o;
-  void* dst;
   if (hh < h) {
-    dst = q_out;
-    o = (row * h + hh) * (long)d_h;
-  } else {
-    const int g = hh < h + h_kv ? hh - h : hh - h - h_kv;
-    const long slot = slot_mapping[row];
-    dst = hh < h + h_kv ? k_pool : v_pool;
-    o = (((slot / page_size) * h_kv + g) * page_size + slot % page_size) * (long)d_h;
+    const long o = (row * h + hh) * (long)d_h;
+    Elem<DT>::st(q_out, o + i, ya);
+    Elem<DT>::st(q_out, o + i + half, yb);
+    return;
   }
-  Elem<DT>::st(dst, o + i, ya);
-  Elem<DT>::st(dst, o + i + half, yb);
+  const int g = hh < h + h_kv ? hh - h : hh - h - h_kv;
+  const long slot = slot_mapping[row];
+  const int t = (int)(slot % page_size);
+  const long blk = ((slot / page_size) * h_kv + g) * page_size * (long)d_h;   // (page, head) block
+  if (hh < h + h_kv) {   // K: unit-major block (common.h)
+    Elem<DT>::st(k_pool, blk + k_block_elem(t, i, page_size, Elem<DT>::bytes), ya);
+    Elem<DT>::st(k_pool, blk + k_block_elem(t, i + half, page_size, Elem<DT>::bytes), yb);
+  } else {               // V: token-major rows
+    Elem<DT>::st(v_pool, blk + (long)t * d_h + i, ya);
+    Elem<DT>::st(v_pool, blk + (long)t * d_h + i + half, yb);
+  }
 }
 
 template <int DT>

@@ -31,8 +31,10 @@ def mismatch_report(a, b, n=5) -> str:
 
 
 class PagedKV:
-    """Paged K/V pools [pages][h_kv][page_size][d_h] with random scattered
-    placement of each request's pages, filled from synth normals."""
+    """Paged K/V pools [pages][h_kv][page_size][d_h] (token-major rows, the
+    oracle's layout) with random scattered placement of each request's
+    pages, filled from synth normals; to() gives the device copies, K in the
+    library's K page layout."""
 
     def __init__(self, kv_len, h_kv, d_h, page_size, seed, dtype, capacity=None, slack=1.25):
         cap = np.asarray(capacity if capacity is not None else kv_len)
@@ -44,7 +46,9 @@ class PagedKV:
         self.page_size = page_size
 
     def to(self, device):
-        return self.k.to(device), self.v.to(device), self.bt.to(device)
+        """K (in the library's K page layout), V and the block table on device."""
+        from invariant_bi_rmsnorm_amd._lib import k_pool_from_rows
+        return k_pool_from_rows(self.k).to(device), self.v.to(device), self.bt.to(device)
 
 
 def gemm_bf16_tol(A: np.ndarray, W: np.ndarray, ref: np.ndarray) -> np.ndarray:

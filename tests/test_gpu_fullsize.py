@@ -48,7 +48,8 @@ def _compact_pool(kp, vp, bt_rows, lens, page_size):
     bt = np.zeros((len(rows), width), np.int32)
     for i, r in enumerate(rows):
         bt[i, :len(r)] = r
-    return kp[idx].float().cpu().numpy(), vp[idx].float().cpu().numpy(), bt
+    return (L.k_pool_to_rows(kp[idx]).float().cpu().numpy(), vp[idx].float().cpu().numpy(),
+            bt)
 
 
 @pytest.mark.timeout(600)
@@ -150,7 +151,8 @@ def test_llama8b_decode_step_every_layer_teacher_forced_vs_oracle():
     pick = [int(np.argmin(lens)), int(np.argmax(lens)), int(np.argsort(lens)[B // 2])]
     # the sampled requests' KV as it is before the step (the end-to-end
     # oracle appends its own current token)
-    saved = {r: (pool.k[:, torch.tensor(segs[r].pages, device=dev())].float().cpu().numpy(),
+    saved = {r: (L.k_pool_to_rows(pool.k[:, torch.tensor(segs[r].pages, device=dev())])
+                 .float().cpu().numpy(),
                  pool.v[:, torch.tensor(segs[r].pages, device=dev())].float().cpu().numpy())
              for r in pick}
     m = eng.upload(eng.pack(segs))
@@ -166,7 +168,7 @@ def test_llama8b_decode_step_every_layer_teacher_forced_vs_oracle():
     worst, gaps = {}, []
     for li in range(cfg.layers):
         idx = {r: torch.tensor(segs[r].pages, device=dev()) for r in pick}
-        kps = [pool.k[li, idx[r]].float().cpu().numpy() for r in pick]
+        kps = [L.k_pool_to_rows(pool.k[li, idx[r]]).float().cpu().numpy() for r in pick]
         vps = [pool.v[li, idx[r]].float().cpu().numpy() for r in pick]
         t = layer_taps(store, li)
         rep = check_layer(cfg, om.layers[li], t, li, pos, kps, vps, cos_t, sin_t)

@@ -208,7 +208,7 @@ def test_gemm_qkv_rope_integer_exact_vs_oracle():
     rq = oracle.rope(x[:, :h], pos, cos_t, sin_t, round_bf16=True)
     rk = oracle.rope(x[:, h:h + h_kv], pos, cos_t, sin_t, round_bf16=True)
     assert bits_equal(to_np(q), rq), mismatch_report(to_np(q), rq)
-    kpn, vpn = to_np(kp), to_np(vp)
+    kpn, vpn = to_np(L.k_pool_to_rows(kp)), to_np(vp)   # K back to token-major rows
     for i, s in enumerate(slots):
         assert bits_equal(kpn[s // ps, :, s % ps], rk[i])
         assert bits_equal(vpn[s // ps, :, s % ps], x[i, h + h_kv:])
@@ -599,7 +599,7 @@ def test_rope_kv_append_bitwise():
     rq = oracle.rope(x[:, :h], pos, cos_t, sin_t, round_bf16=True)
     rk = oracle.rope(x[:, h:h + h_kv], pos, cos_t, sin_t, round_bf16=True)
     assert bits_equal(to_np(qo), rq)
-    kpn, vpn = to_np(kp), to_np(vp)
+    kpn, vpn = to_np(L.k_pool_to_rows(kp)), to_np(vp)   # K back to token-major rows
     for i, s in enumerate(slots):
         assert bits_equal(kpn[s // ps, :, s % ps], rk[i])
         assert bits_equal(vpn[s // ps, :, s % ps], x[i, h + h_kv:])

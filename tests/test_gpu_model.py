@@ -68,7 +68,7 @@ class ToyLayer:
         L.bi_rmsnorm(x, self.g.to(d), y, 1e-5)
         qkv = torch.empty((len(idx), 512), device=d)
         L.bi_gemm(y, self.w.to(d), qkv)
-        kp, vp = self.k0.clone().to(d), self.v0.clone().to(d)
+        kp, vp = L.k_pool_from_rows(self.k0).to(d), self.v0.clone().to(d)
         q = torch.empty((len(idx), self.h, self.d_h), device=d)
         L.bi_rope_kv_append(qkv, self.h, self.h_kv, self.d_h, None, None, None,
                             torch.from_numpy(self.slots[idx]).to(d), q, kp, vp)

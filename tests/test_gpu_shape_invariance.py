@@ -103,7 +103,7 @@ def test_single_full_layer_batches_1_7_32_64_bitwise_and_oracle():
     kps, vps, pos = [], [], []
     for si in pick:
         idx = torch.tensor(segs[si].pages, device=dev())
-        kps.append(pool.k[0, idx].float().cpu().numpy())
+        kps.append(L.k_pool_to_rows(pool.k[0, idx]).float().cpu().numpy())
         vps.append(pool.v[0, idx].float().cpu().numpy())
         pos.append(segs[si].pos0)
     rep = check_layer(cfg, om.layers[0], layer_taps(store, 0), 0, pos, kps, vps, om.cos, om.sin)

@@ -115,3 +115,25 @@ def test_binding_rejects_mismatched_buffers_before_launch():
     with pytest.raises(ValueError, match="q_start"):
         L.bi_prefill_attn(q, torch.zeros(1, dtype=i32), torch.zeros(2, dtype=i32), kp, kp,
                           bt, 64, 0.1, q.clone())
+
+
+def test_k_page_layout_helpers():
+    """k_pool_from_rows puts unit u of token t of a (page, head) block at byte
+    (u * page_size + t) * 16 of the block (the layout bi.h states), and
+    k_pool_to_rows undoes it; V needs no conversion."""
+    import torch
+    for dt, it, per in ((torch.bfloat16, torch.int16, 8), (torch.float32, torch.int32, 4)):
+        P, H, S, D = 3, 2, 16, 64
+        # every element a distinct bit pattern
+        k = torch.arange(P * H * S * D, dtype=it).reshape(P, H, S, D).view(dt)
+        dev = L.k_pool_from_rows(k)
+        assert dev.shape == k.shape and dev.dtype == dt
+        flat = dev.view(it).reshape(-1)
+        kb = k.view(it)
+        for p in range(P):
+            for g in range(H):
+                for t in range(S):
+                    for e in range(D):
+                        off = (p * H + g) * S * D + ((e // per) * S + t) * per + e % per
+                        assert flat[off] == kb[p, g, t, e]
+        assert torch.equal(L.k_pool_to_rows(dev).view(it), kb)
