@@ -40,6 +40,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -72,6 +74,7 @@ def parse():
                     help="with --only --twin: the tuned twin (fastest configuration per "
                          "site) or the all-adaptive one")
     ap.add_argument("--launches", type=int, default=50)
+    ap.add_argument("--prompt", type=int, default=2048, help="with --only prefill_attn")
     ap.add_argument("--dvr", action="store_true",
                     help="decode-verify-rollback (twins decode, invariant kernels verify) "
                          "against greedy decoding on each engine alone; eager steps")
@@ -708,6 +711,37 @@ def decode_attn_long(args, torch, dev):
     return fn, alg, label
 
 
+def prefill_attn_bench(args, torch, dev):
+    """Causal prefill attention of one prompt of --prompt tokens (default
+    2048) at h 32 / h_kv 8 / d_h 128, 256-key chunks at absolute positions,
+    bf16 K and V N(0, 1) already in 16-token pages scattered over a pool (as
+    after the prompt's KV append), q N(0, 1).  Algorithmic work: 4 d_h h
+    (t + 1) FLOPs for the row at position t (q K^T and P V over its visible
+    keys), summed over the prompt; bound: bf16 matrix cores.  Returns
+    (launch, FLOPs, label)."""
+    import synth
+    from invariant_bi_rmsnorm_amd import _lib as L
+    T, h, h_kv, d_h, C, ps = args.prompt, 32, 8, 128, 256, 16
+    lens = np.array([T], np.int32)
+    place = synth.scatter_pages(lens, ps, seed=args.seed + 41)
+    g = torch.Generator(device=dev).manual_seed(args.seed + 42)
+    shape = (place.num_pages, h_kv, ps, d_h)
+    kp = torch.empty(shape, dtype=torch.bfloat16, device=dev).normal_(generator=g)
+    vp = torch.empty(shape, dtype=torch.bfloat16, device=dev).normal_(generator=g)
+    q = torch.empty((T, h, d_h), dtype=torch.bfloat16, device=dev).normal_(generator=g)
+    out = torch.empty_like(q)
+    qs = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    p0 = torch.tensor([0], dtype=torch.int32, device=dev)
+    bt = torch.from_numpy(place.block_table.copy()).to(dev)
+    scale = float(1.0 / math.sqrt(d_h))
+
+    def fn():
+        L.bi_prefill_attn(q, qs, p0, kp, vp, bt, C, scale, out)
+
+    flops = 4 * d_h * h * (T * (T + 1) // 2)
+    return fn, flops, f"prefill_attn, one prompt of {T} tokens, h 32 / h_kv 8 / d_h 128, chunk {C}"
+
+
 def only_gemms(args, torch, dev, names):
     """The decode step's projection GEMMs at the bench's batch, each launched
     --launches times back to back, cycling through the weights of all the
@@ -777,6 +811,24 @@ def only_kernel(args, torch, dev):
         return
     elif args.only == "decode_attn_long":
         fn, alg, label = decode_attn_long(args, torch, dev)
+    elif args.only == "prefill_attn":
+        fn, flops, label = prefill_attn_bench(args, torch, dev)
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.launches):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        us = 1e3 * a.elapsed_time(b) / args.launches
+        tf = flops / us / 1e6
+        print(json.dumps({"kernel": label, "launches": args.launches, "avg_us": round(us, 2),
+                          "flops": flops, "TFLOPs": round(tf, 1), "bound": "mfma",
+                          "peak_TFLOPs": BF16_PEAK / 1e12,
+                          "frac": round(tf * 1e12 / BF16_PEAK, 4)}), flush=True)
+        return
     elif args.only == "log_softmax":
         # logprobs of a decode batch: fp32 logits [batch, vocab], read once and
         # written once (the second and third passes over a row hit L2)

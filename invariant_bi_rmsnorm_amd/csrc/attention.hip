@@ -30,6 +30,39 @@
 
 namespace bi {
 
+// Softmax weight on the matrix-core paths: p = exp(x) with x = s - m <= 0,
+// or -inf for a masked key.  For every such x the value is exp_fixed's (NaN
+// stays NaN): the overflow case cannot arise, and exp_fixed's two exact-power
+// steps 2^(n/2) 2^(n - n/2) are one ldexp -- the exact product p 2^n is
+// rounded once either way (the first step is exact, its result being at
+// least 2^-76).
+__device__ __forceinline__ float exp_p(float x) {
+  const float xc = __builtin_fmaxf(x, -104.0f);
+  const float n = __builtin_rintf(xc * 1.44269502162933349609375f);
+  float r = __builtin_fmaf(-n, 0.693145751953125f, xc);
+  r = __builtin_fmaf(-n, 1.428606765330187045037746429443359375e-06f, r);
+  float p = 1.0f / 5040.0f;
+  p = __builtin_fmaf(p, r, 1.0f / 720.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 120.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 24.0f);
+  p = __builtin_fmaf(p, r, 1.0f / 6.0f);
+  p = __builtin_fmaf(p, r, 0.5f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_amdgcn_ldexpf(p, (int)n);
+  p = x < -104.0f ? 0.0f : p;
+  return x != x ? x : p;
+}
+
+// Two softmax weights as packed bf16 (lo in bits 0..15): the hardware
+// conversion, round to nearest even (the rule of f32_to_bf16_bits for every
+// finite value).
+__device__ __forceinline__ uint32_t p_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+  typedef float f32x2_v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_v{lo, hi}, bf16x2_v));
+}
+
 template <int DT, int DH>
 struct AttnShape {
   static constexpr int ES = Elem<DT>::bytes;
@@ -812,11 +845,12 @@ __device__ __forceinline__ void mfma_chunk(char* lds, const u32x4_t (&qf)[MT][DH
       for (int j = 0; j < RJ; ++j) {
         const int row = 4 * g4 + j;
         const float mm = m_out[mt][j];
-        const float p = (sv[mt][t][j] == -__builtin_inff()) ? 0.0f : exp_fixed(sv[mt][t][j] - mm);
+        // a masked key: exp(-inf) = 0 (a row with no visible key subtracts 0)
+        const float p = exp_p(sv[mt][t][j] - (mm == -__builtin_inff() ? 0.0f : mm));
         const int prow = PR == 16 ? row : row >> 2;   // row 4 g4 when PR = 4
         const uint32_t off = (uint32_t)((mt * PR + prow) * C * 2 +
                                         16 * ((key >> 3) ^ (row & L::PM)) + 2 * (key & 7));
-        *reinterpret_cast<uint16_t*>(pl + off) = (uint16_t)f32_to_bf16_bits(p);
+        *reinterpret_cast<uint16_t*>(pl + off) = (uint16_t)p_bf16x2(p, 0.0f);
       }
     }
   }
@@ -1012,14 +1046,15 @@ __global__ __launch_bounds__(C) void k_prefill_mfma(
     const int32_t* __restrict__ q_pos0, int Rq, const void* __restrict__ k_pool,
     const void* __restrict__ v_pool, const int32_t* __restrict__ block_table, int h, int h_kv,
     int max_pages, float scale, void* __restrict__ out) {
-  typedef MfmaLds<DH, C, MT> L;
+  typedef MfmaLds<DH, C, MT, 2> L;   // V through LDS in two halves
   constexpr int KS = DH / 32, DPW = DH / 16 / L::NW, QB = MT * 16 / R;
   static_assert((MT * 16) % R == 0, "row tiles hold whole query rows");
   extern __shared__ __attribute__((aligned(1024))) char lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, g4 = lane >> 4;
-  const int blk = blockIdx.x, g = blockIdx.y;
+  // the last row blocks see the most chunks: launch them first
+  const int blk = gridDim.x - 1 - blockIdx.x, g = blockIdx.y;
   int r = -1, firstb = 0;  // request of this block: blocks of QB rows, request by request
   for (int i = 0; i < Rq; ++i) {
     const int nb = (q_start[i + 1] - q_start[i] + QB - 1) / QB;
@@ -1070,19 +1105,26 @@ __global__ __launch_bounds__(C) void k_prefill_mfma(
   for (int c = 0; c < nch; ++c) {
     const int j0 = jstart(c);
     const int n = min(jstart(c + 1), pos_last + 1) - j0;
-    int pg[4];
+    int pg[4], vpg[2][2];   // K pages of this wave's 64 keys; V pages of its 32 keys per half
     const int first = bt[j0 / kPage];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int k0 = 64 * wave + kPage * p;
       pg[p] = k0 < n ? bt[(j0 + k0) / kPage] : first;
     }
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int k0 = C / 2 * hf + 32 * wave + kPage * p;
+        vpg[hf][p] = k0 < n ? bt[(j0 + k0) / kPage] : first;
+      }
     if (c > 0) __syncthreads();  // the previous chunk's V and P are no longer read
     u32x4_t kf[4][KS];
     mfma_load_k<DH>(kf, kbase, pstride, pg);
-    mfma_stage_v<DH>(lds, vbase, pstride, pg, wave);
+    mfma_stage_v_half<DH, C>(lds, vbase, pstride, vpg[0], wave);
     BI_WAIT_VMCNT(0);
-    if (n < C) mfma_zero_v_tail<DH>(lds, n, wave);
+    if (n < C / 2) mfma_zero_v_half_tail<DH, C>(lds, n, 0, wave);
     int lastpos[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -1090,7 +1132,17 @@ __global__ __launch_bounds__(C) void k_prefill_mfma(
       for (int j = 0; j < 4; ++j) lastpos[mt][j] = min(rowpos[mt][j], j0 + n - 1);
     float m[MT][4], l[MT][4];
     f32x4_t acc[MT][DPW];
-    mfma_chunk<DH, C, MT>(lds, qf, kf, j0, lastpos, scale, m, l, acc);
+    // between the halves of P V: every wave is done with the first half of
+    // V; copy the second (keys past n only zeroed) and wait for all of it
+    auto v_second_half = [&]() {
+      __syncthreads();
+      if (n > C / 2) mfma_stage_v_half<DH, C>(lds, vbase, pstride, vpg[1], wave);
+      BI_WAIT_VMCNT(0);
+      if (n < C) mfma_zero_v_half_tail<DH, C>(lds, n, 1, wave);
+      __syncthreads();
+    };
+    mfma_chunk<DH, C, MT, 4, 2>(lds, qf, kf, j0, lastpos, scale, m, l, acc, NoHook(),
+                                v_second_half);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -1123,6 +1175,316 @@ __global__ __launch_bounds__(C) void k_prefill_mfma(
 #pragma unroll
         for (int d = 0; d < DPW; ++d)
           Elem<1>::st(out, o + 16 * (wave * DPW + d) + col, A[mt][d][j] / Lr[mt][j]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 KV, 256-key chunks at absolute positions: prefill with each chunk
+// staged once per workgroup for 128 TPW (row, head) pairs.
+//
+// Eight waves; wave w owns TPW tiles of 16 pairs: pair p = 16 (TPW w + tt) +
+// i is query row p / R of the block at query head p % R of the kv head.  Per
+// chunk, K of all 256 keys (page blocks as in the pool, unit-major) and V
+// (rows of d_h, 16-byte pieces XOR-swizzled by the key) are copied to LDS
+// once; each wave then takes its own rows through the whole chunk:
+//   pass 1: S = q K^T key tile by key tile; the row maxima, m = max + 0;
+//   pass 2: per 32 keys, S again (the same MFMA chains: the same bits),
+//           p = bf16(exp(s - m)) into the wave's LDS scratch as P^T
+//           [key][row], read back as A operands by transposing reads;
+//           l = P . 1 and acc = P V, one MFMA chain each over the chunk's
+//           keys in steps of 32.
+// Every per-element chain -- a score's chain over d_h, the key chains of l
+// and acc, the mask, the exp and the rounding of p -- is the decode chunk's,
+// with the same operand layouts, so each row's chunk partial is the decode
+// partial bit for bit.  Steps past the wave's last visible key are skipped:
+// their P is zero in every row of the wave, and a step of zero products
+// leaves each accumulator (never a negative zero) as it is.  Each row merges
+// its chunk partials in chunk order with the decode merge rule.
+// ---------------------------------------------------------------------------
+template <int DH, int TPW>
+struct RowsLds {
+  static constexpr int C = 256, NWV = 8, RB = DH * 2;
+  static constexpr int K_OFF = 0;                 // bf16 K page blocks [C / 16][unit][16]
+  static constexpr int V_OFF = C * RB;            // bf16 V [C][DH], swizzled pieces
+  static constexpr int P_OFF = 2 * C * RB;        // per wave: bf16 P^T [TPW][32][16]
+  static constexpr int PW = TPW * 16 * 64;
+  static constexpr int BYTES = P_OFF + NWV * PW;
+};
+
+// One chunk for one wave's TPW row tiles: the maxima (pass 1), then P, l and
+// acc 32 keys at a time (pass 2).  K and V are staged in LDS; pscr is the
+// wave's P scratch, bf16 P^T [32 keys][16 rows] per tile, read back as A
+// operands by transposing reads.  MASK = false: every row sees all nkt * 16
+// keys.  A masked score gives p = exp(-inf) = 0; a row that sees no key of
+// the chunk (m = -inf) subtracts 0 instead of m, so that p is 0, not NaN.
+template <int DH, int TPW, bool MASK>
+__device__ __forceinline__ void rows_chunk(char* lds, char* pscr,
+                                           const u32x4_t (&qf)[TPW][DH / 32],
+                                           const int (&rowpos)[TPW][4], int j0, int nkt, int nks,
+                                           float scale, float (&m)[TPW][4],
+                                           f32x4_t (&lacc)[TPW], f32x4_t (&acc)[TPW][DH / 16]) {
+  typedef RowsLds<DH, TPW> L;
+  constexpr int KS = DH / 32, DT = DH / 16, RB = L::RB;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15, g4 = lane >> 4;
+  const int e = col >> 2, c4 = col & 3;  // this lane as a transposing-read source
+  const char* kl = lds + L::K_OFF + 16 * lane;
+  // ---- pass 1: row maxima
+  float mx[TPW][4];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mx[tt][j] = -__builtin_inff();
+  // two key tiles per step, their chains interleaved (a tile at or past nkt
+  // lies past every row's last key: masked)
+#pragma unroll 2
+  for (int kt = 0; kt < nkt; kt += 2) {
+    u32x4_t kf[2][KS];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        kf[h2][s] = *reinterpret_cast<const u32x4_t*>(kl + (kt + h2) * kPage * RB + 1024 * s);
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      f32x4_t cc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) cc[h2] = mfma16(qf[tt][s], kf[h2][s], cc[h2]);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int key = j0 + 16 * (kt + h2) + col;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          mx[tt][j] = fmaxf(mx[tt][j], (!MASK || key <= rowpos[tt][j]) ? cc[h2][j] * scale
+                                                                     : -__builtin_inff());
+      }
+    }
+  }
+  float msub[TPW][4];  // subtracted before the exp
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m[tt][j] = row16_max(mx[tt][j]) + 0.0f;
+      msub[tt][j] = (MASK && m[tt][j] == -__builtin_inff()) ? 0.0f : m[tt][j];
+    }
+  // ---- pass 2
+  const u32x4_t ones = u32x4_t{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    lacc[tt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int d = 0; d < DT; ++d) acc[tt][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int ks = 0; ks < nks; ++ks) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the last step's P reads are done
+    u32x4_t kf[2][KS];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        kf[h2][s] = *reinterpret_cast<const u32x4_t*>(kl + (2 * ks + h2) * kPage * RB + 1024 * s);
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      f32x4_t cc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) cc[h2] = mfma16(qf[tt][s], kf[h2][s], cc[h2]);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int key = j0 + 16 * (2 * ks + h2) + col;
+        float pv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float sv =
+              (!MASK || key <= rowpos[tt][j]) ? cc[h2][j] * scale : -__builtin_inff();
+          pv[j] = exp_p(sv - msub[tt][j]);
+        }
+        // rows 4 g4 .. 4 g4 + 3 of key 16 h2 + col: 8 bytes of P^T
+        *reinterpret_cast<uint2*>(pscr + tt * 1024 + (16 * h2 + col) * 32 + 8 * g4) =
+            make_uint2(p_bf16x2(pv[0], pv[1]), p_bf16x2(pv[2], pv[3]));
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // P written
+    u32x4_t a[TPW];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+      // A row col, keys 8 g4 .. 8 g4 + 7 of the 32
+      const uint2 lo = lds_read_tr16(pscr, tt * 1024 + (8 * g4 + e) * 32 + 8 * c4);
+      const uint2 hi = lds_read_tr16(pscr, tt * 1024 + (8 * g4 + 4 + e) * 32 + 8 * c4);
+      a[tt] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+      lacc[tt] = mfma16(a[tt], ones, lacc[tt]);
+    }
+#pragma unroll
+    for (int d = 0; d < DT; ++d) {
+      const int piece = 2 * d + (c4 >> 1);
+      const int k0 = 32 * ks + 8 * g4 + e;
+      const uint2 lo = lds_read_tr16(lds + L::V_OFF, vswz<DH>(k0, piece) + 8 * (c4 & 1));
+      const uint2 hi = lds_read_tr16(lds + L::V_OFF, vswz<DH>(k0 + 4, piece) + 8 * (c4 & 1));
+      const u32x4_t b = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt) acc[tt][d] = mfma16(a[tt], b, acc[tt][d]);
+    }
+  }
+}
+
+template <int DH, int R, int TPW>
+__global__ __launch_bounds__(512) void k_prefill_rows(
+    const void* __restrict__ q, const int32_t* __restrict__ q_start,
+    const int32_t* __restrict__ q_pos0, int Rq, const void* __restrict__ k_pool,
+    const void* __restrict__ v_pool, const int32_t* __restrict__ block_table, int h, int h_kv,
+    int max_pages, float scale, void* __restrict__ out) {
+  typedef RowsLds<DH, TPW> L;
+  constexpr int C = L::C, KS = DH / 32, DT = DH / 16, RB = L::RB;
+  constexpr int PAIRS = 16 * TPW * L::NWV, QB = PAIRS / R;
+  constexpr int KI = kPage * RB / 1024;                  // 1 KiB copies per K page block
+  constexpr int SLOTS = RB / 16, KPI = 1024 / RB;        // V: pieces per row, rows per copy
+  static_assert(PAIRS % R == 0, "a block holds whole query rows");
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, g4 = lane >> 4;
+  // one-dimensional grid, kv head fastest: the row blocks that see the most
+  // chunks start first on every head, and (with the workgroups dealt to the
+  // XCDs in turn) the blocks of one kv head share one XCD's L2 when h_kv is
+  // a multiple of the XCD count
+  const int g = blockIdx.x % h_kv, blk = gridDim.x / h_kv - 1 - blockIdx.x / h_kv;
+  int r = -1, firstb = 0;  // request of this block: blocks of QB rows, request by request
+  for (int i = 0; i < Rq; ++i) {
+    const int nb = (q_start[i + 1] - q_start[i] + QB - 1) / QB;
+    if (blk < firstb + nb) { r = i; break; }
+    firstb += nb;
+  }
+  if (r < 0) return;
+  const int t0 = q_start[r] + (blk - firstb) * QB;
+  const int t1 = min(t0 + QB, q_start[r + 1]);
+  if (t0 >= t1) return;
+  const int nrows = t1 - t0;
+  const int pos0 = q_pos0[r] + (t0 - q_start[r]);
+  const int pos_last = pos0 + nrows - 1;
+  const int32_t* bt = block_table + (long)r * max_pages;
+  const long hstride = (long)kPage * DH * 2, pstride = hstride * h_kv;
+  const char* kbase = static_cast<const char*>(k_pool) + g * hstride;
+  const char* vbase = static_cast<const char*>(v_pool) + g * hstride;
+
+  // q fragments: A row i of tile tt is pair 16 (TPW wave + tt) + i
+  u32x4_t qf[TPW][KS];
+  int rowpos[TPW][4];  // this lane's result rows: absolute position, or -1
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int rr = 16 * (TPW * wave + tt) + col, rho = rr / R, hd = rr % R;
+    const bool real = rho < nrows;
+    const uint16_t* qrow =
+        static_cast<const uint16_t*>(q) + ((long)(t0 + (real ? rho : 0)) * h + g * R + hd) * DH;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(qrow + 8 * g4 + 32 * s);
+      qf[tt][s] = real ? v : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rj = (16 * (TPW * wave + tt) + 4 * g4 + j) / R;
+      rowpos[tt][j] = rj < nrows ? pos0 + rj : -1;
+    }
+  }
+  // last position among the wave's rows (-1: the wave has none)
+  const int rho_first = 16 * TPW * wave / R;
+  const int wlast = rho_first < nrows ? pos0 + min((16 * TPW * (wave + 1) - 1) / R, nrows - 1)
+                                      : -1;
+  char* pscr = lds + L::P_OFF + wave * L::PW;
+  float M[TPW][4], Lr[TPW][4];
+  f32x4_t A[TPW][DT];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) M[tt][j] = Lr[tt][j] = 0.0f;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) A[tt][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const int nch = pos_last / C + 1;
+  for (int c = 0; c < nch; ++c) {
+    const int j0 = c * C;
+    const int n = min(C, pos_last + 1 - j0);
+    // this wave copies pages 2 w, 2 w + 1 of the chunk (keys 32 w .. + 31);
+    // pages past the chunk's end read its first page and their V is zeroed
+    const int first = bt[j0 / kPage];
+    int pid[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int k0 = 32 * wave + kPage * p;
+      pid[p] = k0 < n ? bt[(j0 + k0) / kPage] : first;
+    }
+    if (c > 0) __syncthreads();  // every wave is done with the previous chunk
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int kb = 32 * wave + kPage * p;  // first key of the page in the chunk
+      const char* ksrc = kbase + pid[p] * pstride + 16 * lane;
+#pragma unroll
+      for (int i = 0; i < KI; ++i) dma16_nt(ksrc + 1024 * i, lds + L::K_OFF + kb * RB + 1024 * i);
+      const char* vsrc = vbase + pid[p] * pstride;
+#pragma unroll
+      for (int inst = 0; inst < kPage / KPI; ++inst) {
+        const int k = inst * KPI + lane / SLOTS, slot = lane % SLOTS;
+        dma16_nt(vsrc + k * RB + 16 * (slot ^ ((kb + k) & 7)),
+                 lds + L::V_OFF + (kb + inst * KPI) * RB);
+      }
+    }
+    BI_WAIT_VMCNT(0);
+    if (n < 32 * wave + 32) {  // zero V rows of this wave's keys at or past n
+      const int k0 = max(n, 32 * wave);
+      for (int i = lane; i < (32 * wave + 32 - k0) * SLOTS; i += 64)
+        *reinterpret_cast<uint4*>(lds + L::V_OFF + (k0 + i / SLOTS) * RB + 16 * (i % SLOTS)) =
+            make_uint4(0u, 0u, 0u, 0u);
+    }
+    __syncthreads();
+    if (wlast < j0) continue;  // no row of this wave sees a key of the chunk
+    const int vis = min(n, wlast + 1 - j0);  // keys the wave's rows may see
+    const int nkt = (vis + 15) / 16, nks = (vis + 31) / 32;
+
+    float m[TPW][4];
+    f32x4_t lacc[TPW], acc[TPW][DT];
+    // every row of the wave sees every key of the chunk: no mask
+    if (n == C && pos0 + rho_first >= j0 + C - 1)
+      rows_chunk<DH, TPW, false>(lds, pscr, qf, rowpos, j0, C / 16, C / 32, scale, m, lacc, acc);
+    else
+      rows_chunk<DH, TPW, true>(lds, pscr, qf, rowpos, j0, nkt, nks, scale, m, lacc, acc);
+    // ---- merge the chunk partial into each row's running result
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (c == 0) {
+          M[tt][j] = m[tt][j];
+          Lr[tt][j] = lacc[tt][j];
+#pragma unroll
+          for (int d = 0; d < DT; ++d) A[tt][d][j] = acc[tt][d][j];
+        } else if (m[tt][j] != -__builtin_inff()) {  // the row sees keys of this chunk
+          const float Mo = M[tt][j], mc = m[tt][j];
+          const float Mn = Mo > mc ? Mo : mc;
+          const float ea = exp_fixed(Mo - Mn), eb = exp_fixed(mc - Mn);
+          Lr[tt][j] = __builtin_fmaf(lacc[tt][j], eb, Lr[tt][j] * ea);
+#pragma unroll
+          for (int d = 0; d < DT; ++d)
+            A[tt][d][j] = __builtin_fmaf(acc[tt][d][j], eb, A[tt][d][j] * ea);
+          M[tt][j] = Mn;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rr = 16 * (TPW * wave + tt) + 4 * g4 + j, rho = rr / R, hd = rr % R;
+      if (rho < nrows) {
+        const long o = ((long)(t0 + rho) * h + g * R + hd) * DH;
+#pragma unroll
+        for (int d = 0; d < DT; ++d) Elem<1>::st(out, o + 16 * d + col, A[tt][d][j] / Lr[tt][j]);
       }
     }
   }
@@ -1184,20 +1546,28 @@ static void launch_decode_mfma(dim3 grid, const void* q, const void* kp, const v
                      off, B, h, h_kv, mp, scale, ml, acc, chunk2, stride);
 }
 
+// Row tiles per workgroup of k_prefill_mfma (the twin's kernel, and the
+// invariant path's at 64-key chunks): two at 256-key chunks (a 2048-token
+// prompt measured 260 us against 300 with one and 414 with four, where the
+// registers leave one workgroup per CU), one at 64 (more would spill).
+template <int C>
+constexpr int prefill_tiles() { return C == 256 ? 2 : 1; }
+
 template <int DH, int R, int C, bool REL>
 static void launch_prefill_mfma(const void* q, const int32_t* qs, const int32_t* qp, int Rq,
                                 int T, const void* kp, const void* vp, const int32_t* bt, int h,
                                 int h_kv, int mp, float scale, void* out, hipStream_t s) {
-  constexpr int lds = MfmaLds<DH, C, 1>::BYTES, QB = 16 / R;
+  constexpr int MT = prefill_tiles<C>();
+  constexpr int lds = MfmaLds<DH, C, MT, 2>::BYTES, QB = 16 * MT / R;
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute((const void*)k_prefill_mfma<DH, R, C, 1, REL>,
+    (void)hipFuncSetAttribute((const void*)k_prefill_mfma<DH, R, C, MT, REL>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     attr = true;
   }
   const int blocks = (T + QB - 1) / QB + Rq;
-  hipLaunchKernelGGL((k_prefill_mfma<DH, R, C, 1, REL>), dim3(blocks, h_kv), dim3(C), lds, s, q,
-                     qs, qp, Rq, kp, vp, bt, h, h_kv, mp, scale, out);
+  hipLaunchKernelGGL((k_prefill_mfma<DH, R, C, MT, REL>), dim3(blocks, h_kv), dim3(C), lds, s,
+                     q, qs, qp, Rq, kp, vp, bt, h, h_kv, mp, scale, out);
 }
 
 template <int DT, int DH, int R>
@@ -1241,12 +1611,29 @@ static void launch_prefill(const void* q, const int32_t* qs, const int32_t* qp, 
                      dim3(64 * NW), lds, s, q, qs, qp, Rq, kp, vp, bt, h, h_kv, ps, mp, scale, out);
 }
 
+template <int DH, int R, int TPW = 1>
+static void launch_prefill_rows(const void* q, const int32_t* qs, const int32_t* qp, int Rq,
+                                int T, const void* kp, const void* vp, const int32_t* bt, int h,
+                                int h_kv, int mp, float scale, void* out, hipStream_t s) {
+  constexpr int lds = RowsLds<DH, TPW>::BYTES, QR = 128 * TPW / R;
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)k_prefill_rows<DH, R, TPW>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    attr = true;
+  }
+  const int blocks = (T + QR - 1) / QR + Rq;
+  hipLaunchKernelGGL((k_prefill_rows<DH, R, TPW>), dim3(blocks * h_kv), dim3(512), lds, s, q, qs,
+                     qp, Rq, kp, vp, bt, h, h_kv, mp, scale, out);
+}
+
 template <int DT, int DH, int R, bool REL = false>
 static void prefill_nw(int nw, const void* q, const int32_t* qs, const int32_t* qp, int Rq, int T,
                        const void* kp, const void* vp, const int32_t* bt, int h, int h_kv, int ps,
                        int mp, float scale, void* out, hipStream_t s) {
   if constexpr (DT == 1) {
     if (nw == 1) launch_prefill_mfma<DH, R, 64, REL>(q, qs, qp, Rq, T, kp, vp, bt, h, h_kv, mp, scale, out, s);
+    else if (!REL) launch_prefill_rows<DH, R>(q, qs, qp, Rq, T, kp, vp, bt, h, h_kv, mp, scale, out, s);
     else launch_prefill_mfma<DH, R, 256, REL>(q, qs, qp, Rq, T, kp, vp, bt, h, h_kv, mp, scale, out, s);
   } else {
     if (nw == 1) launch_prefill<DT, DH, R, 1, REL>(q, qs, qp, Rq, T, kp, vp, bt, h, h_kv, ps, mp, scale, out, s);

@@ -534,7 +534,11 @@ def test_prefill_bitwise_and_equal_to_decode(dt, h, h_kv, d_h, chunk):
     _check_equal_to_decode(q, q_start, pos0, lens, kv, chunk, scale, out, dt)
 
 
-@pytest.mark.parametrize("dt,h,h_kv,d_h,chunk", BF16_CFGS)
+# 256-key chunks run the row-block kernel: both query-group sizes, both head dims
+PREFILL_BF16_CFGS = BF16_CFGS + [("bf16", 8, 4, 128, 256), ("bf16", 16, 4, 64, 256)]
+
+
+@pytest.mark.parametrize("dt,h,h_kv,d_h,chunk", PREFILL_BF16_CFGS)
 def test_prefill_bf16_equal_to_decode_and_oracle(dt, h, h_kv, d_h, chunk):
     from oracle.bounds import attn_bound
     scale = scale_for(d_h)
@@ -575,6 +579,36 @@ def test_prefill_invariant_to_chunk_cuts():
     whole = run([0, Lq])
     for cuts in ([0, 1, 256, 257, Lq], [0, 333, 334, 600, Lq], [0, 100, 200, 300, 400, 500, Lq]):
         assert torch.equal(run(cuts).view(torch.int16), whole.view(torch.int16)), cuts
+
+
+def test_prefill_2048_token_prompt_equal_to_decode_and_oracle():
+    """A 2048-token prompt at h 32 / h_kv 8 / d_h 128 (256-key chunks: eight
+    chunks for the last rows) plus a 600-token continuation at position 3000
+    in one call: every row bit for bit the decode of kv_len = pos + 1, and
+    sampled rows within the oracle's bound."""
+    from oracle.bounds import attn_bound
+    h, h_kv, d_h = 32, 8, 128
+    lens, pos0 = [2048, 600], [0, 3000]
+    cap = np.array([p + n for p, n in zip(pos0, lens)], np.int32)
+    kv = PagedKV(cap, h_kv, d_h, 16, seed=520, dtype=torch.bfloat16)
+    T = sum(lens)
+    q = synth.normal((T, h, d_h), seed=521).to(torch.bfloat16)
+    q_start = np.array([0, lens[0], T], np.int32)
+    scale = scale_for(d_h)
+    out = _gpu_prefill(q, q_start, pos0, kv, 256, scale, "bf16")
+    _check_equal_to_decode(q, q_start, pos0, lens, kv, 256, scale, out, "bf16")
+    got = to_np(out)
+    for t in (0, 1, 15, 63, 64, 255, 256, 511, 1000, 1791, 1792, 2047, 2048, 2100, 2647):
+        r = 0 if t < lens[0] else 1
+        pos = pos0[r] + t - q_start[r]
+        qi = q[t:t + 1]
+        bt = kv.bt[r:r + 1]
+        kvl = np.array([pos + 1], np.int32)
+        ref = oracle.decode_attn(qi, kv.k, kv.v, bt, kvl, h_kv, 16, 256, scale, round_bf16=True,
+                                 p_bf16=True)
+        bnd = attn_bound(qi, kv.k, kv.v, bt, kvl, h_kv, 16, 256, scale, out_bf16=True)
+        err = np.abs(got[t:t + 1] - ref)
+        assert np.all(err <= bnd), f"row {t}: {np.max(err / (bnd + 1e-30)):.3g}x of the bound"
 
 
 # ---------------------------------------------------------------------------
