@@ -32,10 +32,12 @@ namespace bi {
 
 // Softmax weight on the matrix-core paths: p = exp(x) with x = s - m <= 0,
 // or -inf for a masked key.  For every such x the value is exp_fixed's (NaN
-// stays NaN): the overflow case cannot arise, and exp_fixed's two exact-power
+// stays NaN): the overflow case cannot arise; exp_fixed's two exact-power
 // steps 2^(n/2) 2^(n - n/2) are one ldexp -- the exact product p 2^n is
 // rounded once either way (the first step is exact, its result being at
-// least 2^-76).
+// least 2^-76); and below -104 no select is needed, since at the clamp
+// (n = -150, p(r) = 0.97...) the product is under half the least subnormal
+// and rounds to +0.
 __device__ __forceinline__ float exp_p(float x) {
   const float xc = __builtin_fmaxf(x, -104.0f);
   const float n = __builtin_rintf(xc * 1.44269502162933349609375f);
@@ -50,7 +52,6 @@ __device__ __forceinline__ float exp_p(float x) {
   p = __builtin_fmaf(p, r, 1.0f);
   p = __builtin_fmaf(p, r, 1.0f);
   p = __builtin_amdgcn_ldexpf(p, (int)n);
-  p = x < -104.0f ? 0.0f : p;
   return x != x ? x : p;
 }
 
@@ -684,9 +685,19 @@ struct MfmaLds {
   static constexpr int PM = (C / 8 < 16 ? C / 8 : 16) - 1;  // P block swizzle mask
 };
 
+// V rows in LDS: the 16-byte pieces of row `key` are XOR-swizzled by an even
+// mask, so pairs of pieces (the 32 bytes one transposing read takes from a
+// row) stay together, and the four rows of a 16-lane group and the rows of
+// two neighbouring groups (keys 8 apart) fall on distinct banks.
+template <int DH>
+__device__ __forceinline__ int vswz_mask(int key) {
+  constexpr int PAIRS = DH * 2 / 32;
+  return 2 * (((key & 3) | (((key >> 3) & 1) << 2)) & (PAIRS - 1));
+}
+
 template <int DH>
 __device__ __forceinline__ uint32_t vswz(int key, int piece) {
-  return (uint32_t)(key * DH * 2 + 16 * (piece ^ (key & 7)));
+  return (uint32_t)(key * DH * 2 + 16 * (piece ^ vswz_mask<DH>(key)));
 }
 
 // Copies V rows of this wave's 64 keys (absolute keys j0 + 64w + k) into the
@@ -702,7 +713,7 @@ __device__ __forceinline__ void mfma_stage_v(char* lds, const char* vbase, long 
     const int slot = lane % SLOTS;
     const int key = 64 * wave + k;                 // key within the chunk
     const int page = pg[k / kPage];
-    const char* src = vbase + page * pstride + (k % kPage) * RB + 16 * (slot ^ (key & 7));
+    const char* src = vbase + page * pstride + (k % kPage) * RB + 16 * (slot ^ vswz_mask<DH>(key));
     dma16_nt(src, lds + (64 * wave + inst * KPI) * RB);
   }
 }
@@ -751,7 +762,7 @@ __device__ __forceinline__ void mfma_stage_v_half(char* lds, const char* vbase, 
     const int slot = lane % SLOTS;
     const int row = KW * wave + k;                 // row of the half buffer
     const char* src = vbase + vpg[k / kPage] * pstride + (k % kPage) * RB +
-                      16 * (slot ^ (row & 7));
+                      16 * (slot ^ vswz_mask<DH>(row));
     dma16_nt(src, lds + (KW * wave + inst * KPI) * RB);
   }
 }
@@ -1280,14 +1291,26 @@ __device__ __forceinline__ void rows_chunk(char* lds, char* pscr,
 #pragma unroll
     for (int d = 0; d < DT; ++d) acc[tt][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+  // per-lane LDS addresses of step 0; step ks adds ks 32 rows of V and
+  // ks 2 pages of K (the V swizzle mask of a key depends on key % 4 and
+  // key / 8 % 2 only, the same at every step, and the high half of a
+  // transposing read lies 4 rows on)
+  uint32_t vofs[DT];  // from lds
+#pragma unroll
+  for (int d = 0; d < DT; ++d)
+    vofs[d] = L::V_OFF + vswz<DH>(8 * g4 + e, 2 * d + (c4 >> 1)) + 8 * (c4 & 1);
+  const uint32_t pw0 = (uint32_t)(col * 32 + 8 * (g4 ^ (col >> 3)));  // key col of half 0
+  const uint32_t pw1 = (uint32_t)((16 + col) * 32 + 8 * (g4 ^ (2 + (col >> 3))));
+  const uint32_t pr = (uint32_t)((8 * g4 + e) * 32 + 8 * (c4 ^ g4));
   for (int ks = 0; ks < nks; ++ks) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the last step's P reads are done
     u32x4_t kf[2][KS];
+    const char* kstep = kl + ks * 2 * kPage * RB;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
       for (int s = 0; s < KS; ++s)
-        kf[h2][s] = *reinterpret_cast<const u32x4_t*>(kl + (2 * ks + h2) * kPage * RB + 1024 * s);
+        kf[h2][s] = *reinterpret_cast<const u32x4_t*>(kstep + h2 * kPage * RB + 1024 * s);
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
       f32x4_t cc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
@@ -1305,8 +1328,10 @@ __device__ __forceinline__ void rows_chunk(char* lds, char* pscr,
               (!MASK || key <= rowpos[tt][j]) ? cc[h2][j] * scale : -__builtin_inff();
           pv[j] = exp_p(sv - msub[tt][j]);
         }
-        // rows 4 g4 .. 4 g4 + 3 of key 16 h2 + col: 8 bytes of P^T
-        *reinterpret_cast<uint2*>(pscr + tt * 1024 + (16 * h2 + col) * 32 + 8 * g4) =
+        // rows 4 g4 .. 4 g4 + 3 of key 16 h2 + col: 8 bytes of P^T, in slot
+        // g4 ^ (key / 8) of the key's 32 (lanes col and col + 8 on
+        // different banks)
+        *reinterpret_cast<uint2*>(pscr + tt * 1024 + (h2 ? pw1 : pw0)) =
             make_uint2(p_bf16x2(pv[0], pv[1]), p_bf16x2(pv[2], pv[3]));
       }
     }
@@ -1314,18 +1339,17 @@ __device__ __forceinline__ void rows_chunk(char* lds, char* pscr,
     u32x4_t a[TPW];
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
-      // A row col, keys 8 g4 .. 8 g4 + 7 of the 32
-      const uint2 lo = lds_read_tr16(pscr, tt * 1024 + (8 * g4 + e) * 32 + 8 * c4);
-      const uint2 hi = lds_read_tr16(pscr, tt * 1024 + (8 * g4 + 4 + e) * 32 + 8 * c4);
+      // A row col, keys 8 g4 .. 8 g4 + 7 of the 32 (key / 8 = g4)
+      const uint2 lo = lds_read_tr16(pscr, tt * 1024 + pr);
+      const uint2 hi = lds_read_tr16(pscr, tt * 1024 + pr + 4 * 32);
       a[tt] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
       lacc[tt] = mfma16(a[tt], ones, lacc[tt]);
     }
 #pragma unroll
     for (int d = 0; d < DT; ++d) {
-      const int piece = 2 * d + (c4 >> 1);
-      const int k0 = 32 * ks + 8 * g4 + e;
-      const uint2 lo = lds_read_tr16(lds + L::V_OFF, vswz<DH>(k0, piece) + 8 * (c4 & 1));
-      const uint2 hi = lds_read_tr16(lds + L::V_OFF, vswz<DH>(k0 + 4, piece) + 8 * (c4 & 1));
+      const uint32_t o = vofs[d] + ks * 32 * RB;
+      const uint2 lo = lds_read_tr16(lds, o);
+      const uint2 hi = lds_read_tr16(lds, o + 4 * RB);
       const u32x4_t b = u32x4_t{lo.x, lo.y, hi.x, hi.y};
 #pragma unroll
       for (int tt = 0; tt < TPW; ++tt) acc[tt][d] = mfma16(a[tt], b, acc[tt][d]);
@@ -1430,7 +1454,7 @@ __global__ __launch_bounds__(512) void k_prefill_rows(
 #pragma unroll
       for (int inst = 0; inst < kPage / KPI; ++inst) {
         const int k = inst * KPI + lane / SLOTS, slot = lane % SLOTS;
-        dma16_nt(vsrc + k * RB + 16 * (slot ^ ((kb + k) & 7)),
+        dma16_nt(vsrc + k * RB + 16 * (slot ^ vswz_mask<DH>(kb + k)),
                  lds + L::V_OFF + (kb + inst * KPI) * RB);
       }
     }
@@ -1464,9 +1488,13 @@ __global__ __launch_bounds__(512) void k_prefill_rows(
 #pragma unroll
           for (int d = 0; d < DT; ++d) A[tt][d][j] = acc[tt][d][j];
         } else if (m[tt][j] != -__builtin_inff()) {  // the row sees keys of this chunk
+          // the decode merge's weights exp(Mo - Mn) and exp(mc - Mn): one of
+          // them is exp(0) = 1
           const float Mo = M[tt][j], mc = m[tt][j];
-          const float Mn = Mo > mc ? Mo : mc;
-          const float ea = exp_fixed(Mo - Mn), eb = exp_fixed(mc - Mn);
+          const bool old_max = Mo > mc;
+          const float Mn = old_max ? Mo : mc;
+          const float ex = exp_p(old_max ? mc - Mo : Mo - mc);
+          const float ea = old_max ? 1.0f : ex, eb = old_max ? ex : 1.0f;
           Lr[tt][j] = __builtin_fmaf(lacc[tt][j], eb, Lr[tt][j] * ea);
 #pragma unroll
           for (int d = 0; d < DT; ++d)
