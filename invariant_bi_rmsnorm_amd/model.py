@@ -337,6 +337,18 @@ class Engine:
         return m
 
     # -- the forward pass ------------------------------------------------------
+    def decode_partials_launch(self, m, li: int):
+        """A function that launches bi_decode_attn alone (no merge) for the
+        decode rows of `m` at layer li, with the invariant configuration, on
+        the buffers forward() uses: for timing the partial kernel by itself."""
+        c, nd = self.cfg, m["n_dec"]
+        if nd == 0:
+            raise ValueError("no decode rows")
+        q = self.q[:m["T"]]
+        return lambda: L.bi_decode_attn(q[:nd], self.pool.k[li], self.pool.v[li], m["bt_dec"],
+                                        m["kv_len"], m["chunk_off"], m["total_chunks"],
+                                        c.kv_chunk, c.scale, m["ml"], m["pacc"])
+
     def forward(self, m, layers=None, timer=None, tap=None) -> StepOutput:
         """One forward pass over the packed rows of `m` (from upload()).
         `timer`, if given, is called as timer(name, fn) around the kernels it
