@@ -75,6 +75,10 @@ def parse():
                          "site) or the all-adaptive one")
     ap.add_argument("--launches", type=int, default=50)
     ap.add_argument("--prompt", type=int, default=2048, help="with --only prefill_attn")
+    ap.add_argument("--oracle-table", action="store_true",
+                    help="time the CPU oracle beside the GPU kernels on the decode-attention "
+                         "(batch 1 and 64, long contexts), M=513 GEMM and prefill-attention "
+                         "workloads")
     ap.add_argument("--dvr", action="store_true",
                     help="decode-verify-rollback (twins decode, invariant kernels verify) "
                          "against greedy decoding on each engine alone; eager steps")
@@ -674,16 +678,17 @@ def measured_traffic():
 GEMM_NAMES = ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down")
 
 
-def decode_attn_long(args, torch, dev):
+def decode_attn_long(args, torch, dev, batch=None, parts=None):
     """The paged decode-attention workload on its own: --batch requests with
     KV lengths log-uniform in 128..32768 (seeded), h 32 / h_kv 8 / d_h 128,
     bf16 K and V N(0, 1) in 16-token pages scattered over a pool 1.25x the
     live pages, 256-key chunks.  Two such pools are used in turn, so every
     call reads K and V that are cold in L2 and in the 256 MB last-level
-    cache.  Returns (launch, algorithmic bytes, label)."""
+    cache.  Returns (launch, algorithmic bytes, label); with `parts` (a
+    dict) it also leaves the first pool's tensors there."""
     import synth
     from invariant_bi_rmsnorm_amd import _lib as L
-    B, h, h_kv, d_h, C, ps = args.batch, 32, 8, 128, 256, 16
+    B, h, h_kv, d_h, C, ps = batch or args.batch, 32, 8, 128, 256, 16
     kv_len = synth.log_uniform_lengths(B, 128, 32768, seed=args.seed + 31)
     place = synth.scatter_pages(kv_len, ps, seed=args.seed + 32)
     g = torch.Generator(device=dev).manual_seed(args.seed + 33)
@@ -708,6 +713,9 @@ def decode_attn_long(args, torch, dev):
     alg = int(kv_len.sum()) * h_kv * d_h * 2 * 2 + B * h * d_h * 2 + tot * h * (d_h + 2) * 4
     label = (f"decode_attn, batch {B}, KV lengths log-uniform 128..32768 ({int(kv_len.sum())} "
              f"tokens, {tot} chunk rows), two pools in turn")
+    if parts is not None:
+        parts.update(q=q, k=pools[0][0], v=pools[0][1], block_table=place.block_table,
+                     kv_len=kv_len, h_kv=h_kv, chunk=C, scale=scale)
     return fn, alg, label
 
 
@@ -738,8 +746,77 @@ def prefill_attn_bench(args, torch, dev):
     def fn():
         L.bi_prefill_attn(q, qs, p0, kp, vp, bt, C, scale, out)
 
+    fn.parts = {"q": q, "k": kp, "v": vp, "block_table": place.block_table, "scale": scale}
     flops = 4 * d_h * h * (T * (T + 1) // 2)
     return fn, flops, f"prefill_attn, one prompt of {T} tokens, h 32 / h_kv 8 / d_h 128, chunk {C}"
+
+
+def _b2b_us(fn, torch, launches=20):
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(launches):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return 1e3 * a.elapsed_time(b) / launches
+
+
+def oracle_table(args, torch, dev):
+    """The CPU oracle timed beside the GPU kernels on the workloads the
+    scope table names: decode attention with KV lengths log-uniform
+    128..32768 at batch 1 and 64, the mixed-batch GEMM at M = 513 (N 14336,
+    K 4096), and causal prefill attention of a 2048-token prompt.  Each
+    oracle call runs once, on the same inputs as the GPU kernel (K converted
+    to the oracle's token-major pages).  Prints one JSON line per
+    workload."""
+    import oracle
+    from invariant_bi_rmsnorm_amd import _lib as L
+    threads = oracle.num_threads()
+
+    def line(name, gpu_us, oracle_s, sample):
+        print(json.dumps({"oracle_table": name, "gpu_us": round(gpu_us, 2),
+                          "oracle_s": round(oracle_s, 3), "oracle_threads": threads,
+                          "oracle_over_gpu": round(oracle_s * 1e6 / gpu_us, 1),
+                          "sample": sample}), flush=True)
+
+    for B in (1, 64):
+        parts = {}
+        fn, _, label = decode_attn_long(args, torch, dev, batch=B, parts=parts)
+        us = _b2b_us(fn, torch)
+        q = parts["q"].float().cpu().numpy()
+        kp = L.k_pool_to_rows(parts["k"]).float().cpu().numpy()
+        vp = parts["v"].float().cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.decode_attn(q, kp, vp, parts["block_table"], parts["kv_len"], parts["h_kv"], 16,
+                           parts["chunk"], parts["scale"], round_bf16=True, p_bf16=True)
+        line(label, us, time.perf_counter() - t0, "the whole call")
+        del parts, kp, vp
+    M, N, K = 513, 14336, 4096
+    g = torch.Generator(device=dev).manual_seed(args.seed + 51)
+    A = torch.empty((M, K), dtype=torch.bfloat16, device=dev).normal_(generator=g)
+    W = torch.empty((N, K), dtype=torch.bfloat16, device=dev).normal_(0, 0.02, generator=g)
+    Cm = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    us = _b2b_us(lambda: L.bi_gemm(A, W, Cm), torch)
+    Ac, Wc = A.float().cpu().numpy(), W.float().cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.gemm(Ac, Wc, True)
+    line(f"bi_gemm M {M} N {N} K {K} (bf16 in and out)", us, time.perf_counter() - t0,
+         "the whole product")
+    del A, W, Cm, Ac, Wc
+    fn, _, label = prefill_attn_bench(args, torch, dev)
+    us = _b2b_us(fn, torch)
+    T, parts = args.prompt, fn.parts
+    q = parts["q"].float().cpu().numpy()
+    kp = L.k_pool_to_rows(parts["k"]).float().cpu().numpy()
+    vp = parts["v"].float().cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.prefill_attn(q, np.array([0, T], np.int32), np.array([0], np.int32), kp, vp,
+                        parts["block_table"], 8, 16, 256, parts["scale"], round_bf16=True,
+                        p_bf16=True)
+    line(label, us, time.perf_counter() - t0, "the whole prompt")
 
 
 def only_gemms(args, torch, dev, names):
@@ -978,6 +1055,9 @@ def main():
         sys.exit(1)
     _lib.load()
     dev = torch.device("cuda:0")
+    if args.oracle_table:
+        oracle_table(args, torch, dev)
+        return
     if args.only:
         only_kernel(args, torch, dev)
         return
