@@ -239,6 +239,21 @@ bi_status bi_merge_partials(const float *part_ml, const float *part_acc,
                             int out_dtype, bi_stream stream);
 
 /*
+ * The softmax weight of the bf16 (matrix-core) attention paths, on its own:
+ * p[i] = exp(x[i]) evaluated as decode and prefill attention evaluate
+ * exp(s - m) -- the library's fixed exp (Cody & Waite reduction, degree-7
+ * Taylor polynomial, scaling by 2^n) -- and p_bf16[i] its bf16 bits (round
+ * to nearest even).  No passage defines this call: it exposes that one
+ * evaluation so that it can be checked against the oracle's exp over any
+ * set of arguments.  x: device fp32 [n], each x <= 0 or -inf (the arguments
+ * the kernels use; larger values give unspecified results, NaN gives NaN);
+ * p: device fp32 [n]; p_bf16: device uint16 [n], or NULL.  n >= 0 (0 is a
+ * no-op); errors return BI_ERR_INVALID and launch nothing.
+ */
+bi_status bi_softmax_weights(const float *x, float *p, uint16_t *p_bf16, int n,
+                             bi_stream stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): decode
  * attention straight to its output, bi_decode_attn followed by

@@ -41,6 +41,7 @@ SIGNATURES = {
     "bi_decode_attn_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp] + [_c_int] * 8
                                + [_c_float, _c_int, _vp, _c_int, _vp]),
     "bi_merge_partials": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _c_int, _vp]),
+    "bi_softmax_weights": (_c_int, [_vp, _vp, _vp, _c_int, _vp]),
     "bi_prefill_attn": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _vp, _vp, _vp] + [_c_int] * 6
                         + [_c_float, _c_int, _vp, _vp]),
     "bi_embed": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp]),
@@ -354,6 +355,19 @@ def bi_silu_mul(gu, y, stream=None):
     M, F = y.shape
     _check("bi_silu_mul", load().bi_silu_mul(_ptr(gu), _ptr(y), M, F, _dt(gu), _stream(stream)))
     return y
+
+
+def bi_softmax_weights(x, p, p_bf16=None, stream=None):
+    """p = the attention kernels' softmax weight exp(x) for x <= 0 (fp32),
+    p_bf16 = its bf16 bits (int16 tensor, optional)."""
+    n = x.numel()
+    if x.dtype != torch.float32 or p.dtype != torch.float32 or p.numel() != n:
+        raise ValueError("bi_softmax_weights: need fp32 x and p of one size")
+    if p_bf16 is not None and (p_bf16.dtype != torch.int16 or p_bf16.numel() != n):
+        raise ValueError("bi_softmax_weights: p_bf16 must be int16 with x's size")
+    _check("bi_softmax_weights", load().bi_softmax_weights(
+        _ptr(x), _ptr(p), _ptr(p_bf16) if p_bf16 is not None else None, n, _stream(stream)))
+    return p
 
 
 def bi_log_softmax(x, y, stream=None):

@@ -1726,7 +1726,29 @@ static void launch_decode_free(const void* q, const void* kp, const void* vp, co
   }
 }
 
+// The softmax weights alone: p[i] = exp_p(x[i]) and its bf16 bits.
+__global__ __launch_bounds__(256) void k_softmax_weights(const float* __restrict__ x,
+                                                         float* __restrict__ p,
+                                                         uint16_t* __restrict__ pb, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const float v = exp_p(x[i]);
+  p[i] = v;
+  if (pb != nullptr) pb[i] = (uint16_t)(p_bf16x2(v, 0.0f) & 0xffffu);
+}
+
 }  // namespace bi
+
+extern "C" bi_status bi_softmax_weights(const float* x, float* p, uint16_t* p_bf16, int n,
+                                        bi_stream stream) {
+  using namespace bi;
+  BI_REQUIRE(n >= 0, BI_ERR_INVALID, "bi_softmax_weights: bad size n=%d", n);
+  if (n == 0) return BI_OK;
+  BI_REQUIRE(x && p, BI_ERR_INVALID, "bi_softmax_weights: null pointer");
+  hipLaunchKernelGGL(k_softmax_weights, dim3((n + 255) / 256), dim3(256), 0, as_stream(stream),
+                     x, p, p_bf16, n);
+  return launched("bi_softmax_weights");
+}
 
 extern "C" bi_status bi_prefill_attn(const void* q, const int32_t* q_start,
                                      const int32_t* q_pos0, int R, int T, const void* k_pool,

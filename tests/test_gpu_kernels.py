@@ -611,6 +611,36 @@ def test_prefill_2048_token_prompt_equal_to_decode_and_oracle():
         assert np.all(err <= bnd), f"row {t}: {np.max(err / (bnd + 1e-30)):.3g}x of the bound"
 
 
+def test_softmax_weight_equals_the_oracle_exp_for_every_nonpositive_argument():
+    """The attention kernels' softmax weight (bi_softmax_weights) against the
+    oracle's exp: bit for bit on a dense grid of [-110, 0] (the polynomial,
+    the scaling down to subnormal results at x < -87.3, the underflow to +0
+    below -103.97), on random arguments, and on -inf, -0 and NaN; its bf16
+    rounding against round-to-nearest-even of the same fp32 value."""
+    rng = np.random.default_rng(77)
+    grid = np.linspace(-110.0, 0.0, 2_200_001, dtype=np.float64).astype(np.float32)
+    rand = -rng.exponential(8.0, 1_000_000).astype(np.float32)
+    edge = np.array([-np.inf, -0.0, 0.0, -104.0, np.nextafter(np.float32(-104), np.float32(0)),
+                     -103.972, -87.3365, -87.33655, -1e-30, -1e-45, -0.5, -1.0],
+                    np.float32)
+    x = np.concatenate([grid, rand, edge])
+    xd = torch.from_numpy(x).to(dev())
+    p = torch.empty_like(xd)
+    pb = torch.empty(x.shape, dtype=torch.int16, device=dev())
+    L.bi_softmax_weights(xd, p, pb)
+    got = p.cpu().numpy()
+    ref = oracle.exp_array(x)
+    assert bits_equal(got, ref), mismatch_report(got, ref)
+    assert np.any((got > 0) & (got < np.float32(1.1754944e-38))), "no subnormal result covered"
+    u = ref.view(np.uint32).astype(np.uint64)
+    rne = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    assert np.array_equal(pb.cpu().numpy().view(np.uint16), rne)
+    nan = torch.tensor([float("nan")], device=dev())
+    out = torch.empty_like(nan)
+    L.bi_softmax_weights(nan, out)
+    assert torch.isnan(out).all()
+
+
 # ---------------------------------------------------------------------------
 # glue
 # ---------------------------------------------------------------------------
