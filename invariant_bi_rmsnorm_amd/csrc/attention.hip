@@ -19,9 +19,12 @@
 //       its wave's 64 keys in registers; within the wave (= a block of 64
 //       keys) l and acc are serial sums over keys ascending (acc by fma).
 //   blocks are added in wave order: ((B0 + B1) + B2) + B3.
-// Prefill runs the same device code per query row and merges the chunks on
-// the fly with the merge kernel's formula, so prefill row t equals a decode
-// of kv_len = t + 1 bit for bit.
+// That is the fp32 (VALU) path.  bf16 KV runs on matrix cores (see
+// "bf16 KV: the chunk on matrix cores" below), with the same structure:
+// fixed chunks at absolute positions, one partial per chunk, a serial merge.
+// Prefill evaluates each query row with the decode chunk's per-element
+// arithmetic and merges the chunks on the fly with the merge kernel's
+// formula, so prefill row t equals a decode of kv_len = t + 1 bit for bit.
 #include <cmath>
 #include <mutex>
 

@@ -611,6 +611,24 @@ def test_prefill_2048_token_prompt_equal_to_decode_and_oracle():
         assert np.all(err <= bnd), f"row {t}: {np.max(err / (bnd + 1e-30)):.3g}x of the bound"
 
 
+@pytest.mark.parametrize("h,h_kv,d_h", [(32, 8, 128), (16, 8, 64)])
+def test_prefill_many_short_requests_equal_to_decode(h, h_kv, d_h):
+    """64 requests of 1..100 prompt rows at random absolute starts 0..600 in
+    one call: the row blocks straddle requests, chunk boundaries and the
+    ragged ends; every row equals the decode of its position bit for bit."""
+    rng = np.random.default_rng(530 + d_h)
+    lens = [int(v) for v in rng.integers(1, 101, 64)]
+    pos0 = [int(v) for v in rng.integers(0, 601, 64)]
+    cap = np.array([p + n for p, n in zip(pos0, lens)], np.int32)
+    kv = PagedKV(cap, h_kv, d_h, 16, seed=531, dtype=torch.bfloat16)
+    T = sum(lens)
+    q = synth.normal((T, h, d_h), seed=532).to(torch.bfloat16)
+    q_start = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    scale = scale_for(d_h)
+    out = _gpu_prefill(q, q_start, pos0, kv, 256, scale, "bf16")
+    _check_equal_to_decode(q, q_start, pos0, lens, kv, 256, scale, out, "bf16")
+
+
 def test_softmax_weight_equals_the_oracle_exp_for_every_nonpositive_argument():
     """The attention kernels' softmax weight (bi_softmax_weights) against the
     oracle's exp: bit for bit on a dense grid of [-110, 0] (the polynomial,
