@@ -94,8 +94,47 @@ struct RopeArgs {
 // halves a rotation mixes.  Each is rounded to bf16 as the GEMM's own output
 // would be, then rotated and stored with the arithmetic of bi_rope_kv_append,
 // so the tile equals the GEMM followed by it.
-__device__ __forceinline__ void store_rope(const RopeArgs& ra, const f32x4_t& acc, int row0,
-                                           int tile, int M, int N, int lane) {
+// The loads the epilogue of pair tile `tile` needs for this lane's four rows
+// (cache slots, and the rotary table entries at the rows' positions; rows
+// past M read row M - 1, unused).  They depend on no product, so the kernel
+// issues them before its K loop and they arrive while the chain runs.
+struct RopePre {
+  int32_t sl[4];
+  float cs[4], sn[4];
+};
+
+__device__ __forceinline__ RopePre rope_prefetch(const RopeArgs& ra, int row0, int tile, int M,
+                                                 int N, int lane) {
+  RopePre p;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) p.sl[j] = 0, p.cs[j] = 1.f, p.sn[j] = 0.f;
+  if (tile >= N / 16) return p;
+  const int per_head = ra.d_h / 16, half = ra.d_h / 2;
+  const int hh = tile / per_head, c = lane & 15;
+  const int i = (tile - hh * per_head) * 8 + (c & 7);
+  const bool rotate = hh < ra.h + ra.h_kv && ra.cos_t != nullptr;
+  const int rbase = row0 + 4 * (lane >> 4);
+  if (hh >= ra.h) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p.sl[j] = ra.slots[min(rbase + j, M - 1)];
+  }
+  if (rotate) {   // uniform over the wave: one tile, one head
+    int32_t pr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pr[j] = ra.pos[min(rbase + j, M - 1)];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const long t = (long)pr[j] * half + i;
+      p.cs[j] = ra.cos_t[t];
+      p.sn[j] = ra.sin_t[t];
+    }
+  }
+  return p;
+}
+
+__device__ __forceinline__ void store_rope(const RopeArgs& ra, const f32x4_t& acc,
+                                           const RopePre& pre, int row0, int tile, int M, int N,
+                                           int lane) {
   float other[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) other[j] = __shfl_xor(acc[j], 8);   // lane l ^ 8: the other half
@@ -105,25 +144,6 @@ __device__ __forceinline__ void store_rope(const RopeArgs& ra, const f32x4_t& ac
   const int i = (tile - hh * per_head) * 8 + (c & 7);
   const bool rotate = hh < ra.h + ra.h_kv && ra.cos_t != nullptr;
   const int rbase = row0 + 4 * (lane >> 4);
-  // every load of the four rows goes out before the first store: positions
-  // and slots, then the table entries (rows past M read row M - 1, unused)
-  int32_t sl[4] = {0, 0, 0, 0};
-  float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
-  if (hh >= ra.h) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sl[j] = ra.slots[min(rbase + j, M - 1)];
-  }
-  if (rotate) {   // uniform over the wave: one tile, one head
-    int32_t pr[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) pr[j] = ra.pos[min(rbase + j, M - 1)];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const long t = (long)pr[j] * half + i;
-      cs[j] = ra.cos_t[t];
-      sn[j] = ra.sin_t[t];
-    }
-  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = rbase + j;
@@ -132,7 +152,8 @@ __device__ __forceinline__ void store_rope(const RopeArgs& ra, const f32x4_t& ac
     const float oth = bf16_bits_to_f32((uint16_t)f32_to_bf16_bits(other[j]));
     float y = own;
     if (rotate)
-      y = hi ? __builtin_fmaf(own, cs[j], oth * sn[j]) : __builtin_fmaf(own, cs[j], -(oth * sn[j]));
+      y = hi ? __builtin_fmaf(own, pre.cs[j], oth * pre.sn[j])
+             : __builtin_fmaf(own, pre.cs[j], -(oth * pre.sn[j]));
     const int e = i + hi * half;   // element of the head row
     long o;
     void* dst;
@@ -141,7 +162,7 @@ __device__ __forceinline__ void store_rope(const RopeArgs& ra, const f32x4_t& ac
       o = ((long)row * ra.h + hh) * ra.d_h + e;
     } else {
       const int g = hh < ra.h + ra.h_kv ? hh - ra.h : hh - ra.h - ra.h_kv;
-      const int page = sl[j] / ra.page_size, in_page = sl[j] - page * ra.page_size;
+      const int page = pre.sl[j] / ra.page_size, in_page = pre.sl[j] - page * ra.page_size;
       const long blk = ((long)page * ra.h_kv + g) * ra.page_size * ra.d_h;
       if (hh < ra.h + ra.h_kv) {   // K: unit-major block (common.h)
         dst = ra.k_pool;
@@ -326,6 +347,17 @@ __global__ __launch_bounds__(kSmallThreads) void k_gemm_small(
   for (int i = 0; i < G::IM; ++i)
 #pragma unroll
     for (int j = 0; j < G::JN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // the RoPE epilogue's loads go out now and land while the chain runs
+  RopePre rpre[OUTF32 == 4 ? G::IM : 1][OUTF32 == 4 ? G::JN : 1];
+  if constexpr (OUTF32 == 4) {
+#pragma unroll
+    for (int i = 0; i < G::IM; ++i)
+#pragma unroll
+      for (int j = 0; j < G::JN; ++j) {
+        const int m = min(wm + G::WM * i, MT - 1), c = wn + G::WN * j;
+        rpre[i][j] = rope_prefetch(ra, m0 + m * 16, n0 / 16 + c, mend, N, lane);
+      }
+  }
   // one stage: read every fragment of its (up to) KS K-tiles, then the MFMAs
   // in ascending K-tile order.  A unit past K enters both operands as zeros.
   auto stage = [&](const char* aslot, const char* wslot, int st, int nkt) {
@@ -381,7 +413,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_gemm_small(
       if constexpr (OUTF32 == 3) {   // every lane joins the exchange
         if (m < MT) store_swiglu(C, acc[i][j], m0 + m * 16, n0 / 2 + c * 8, mend, N / 2, lane);
       } else if constexpr (OUTF32 == 4) {
-        if (m < MT) store_rope(ra, acc[i][j], m0 + m * 16, n0 / 16 + c, mend, N, lane);
+        if (m < MT) store_rope(ra, acc[i][j], rpre[i][j], m0 + m * 16, n0 / 16 + c, mend, N, lane);
       } else if constexpr (OUTF32 == 2) {   // split-K twin: this slice's partial sums
         if (m < MT)
           store_tile<1>(static_cast<float*>(C) + (long)blockIdx.y * M * N, acc[i][j],
