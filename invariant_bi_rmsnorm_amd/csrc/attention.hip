@@ -721,10 +721,11 @@ __device__ __forceinline__ void mfma_stage_v(char* lds, const char* vbase, long 
   }
 }
 
-// K fragments (B operand of QK) of this wave's four key tiles.
+// K fragments (B operand of QK) of this wave's four key tiles; tiles at or
+// past `ntiles` (wholly past the chunk's end, masked) are not read.
 template <int DH>
 __device__ __forceinline__ void mfma_load_k(u32x4_t (&kf)[4][DH / 32], const char* kbase,
-                                            long pstride, const int (&pg)[4]) {
+                                            long pstride, const int (&pg)[4], int ntiles) {
   const int lane = threadIdx.x & 63;
   // lane l takes token l % 16, dims 32 s + 8 (l / 16) .. + 7: unit 4 s + l / 16
   // of the unit-major block, at (unit * kPage + token) * 16 = 1024 s + 16 l --
@@ -735,8 +736,15 @@ __device__ __forceinline__ void mfma_load_k(u32x4_t (&kf)[4][DH / 32], const cha
     const char* blk = kbase + pg[t] * pstride + 16 * lane;
 #pragma unroll
     for (int s = 0; s < DH / 32; ++s)   // read once: non-temporal
-      kf[t][s] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(blk + 1024 * s));
+      kf[t][s] = t < ntiles
+                     ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(blk + 1024 * s))
+                     : u32x4_t{0u, 0u, 0u, 0u};
   }
+}
+
+// Key tiles of wave `wave` (keys 64 wave + 16 t ..) that hold a key below n.
+__device__ __forceinline__ int live_tiles(int n, int wave) {
+  return min(4, max(0, (n - 64 * wave + 15) / 16));
 }
 
 // Zero V rows n .. of this wave's keys (keys past the chunk's end).
@@ -1004,7 +1012,7 @@ __global__ __launch_bounds__(C) void k_decode_mfma(
   const char* kbase = static_cast<const char*>(k_pool) + g * hstride;
   const char* vbase = static_cast<const char*>(v_pool) + g * hstride;
   u32x4_t kf[4][KS];
-  mfma_load_k<DH>(kf, kbase, pstride, pg);
+  mfma_load_k<DH>(kf, kbase, pstride, pg, live_tiles(n, wave));
   mfma_stage_v_half<DH, C>(lds, vbase, pstride, vpg[0], wave);
   // query head hd sits on A row 4 hd, so each row group of the score tile
   // (lanes 16 G .. 16 G + 15, j = 0) holds one head: every lane has a real
@@ -1135,7 +1143,7 @@ __global__ __launch_bounds__(C) void k_prefill_mfma(
       }
     if (c > 0) __syncthreads();  // the previous chunk's V and P are no longer read
     u32x4_t kf[4][KS];
-    mfma_load_k<DH>(kf, kbase, pstride, pg);
+    mfma_load_k<DH>(kf, kbase, pstride, pg, live_tiles(n, wave));
     mfma_stage_v_half<DH, C>(lds, vbase, pstride, vpg[0], wave);
     BI_WAIT_VMCNT(0);
     if (n < C / 2) mfma_zero_v_half_tail<DH, C>(lds, n, 0, wave);
@@ -1772,8 +1780,11 @@ extern "C" bi_status bi_prefill_attn(const void* q, const int32_t* q_start,
              "bi_prefill_attn: null pointer");
   BI_REQUIRE(aligned16(q) && aligned16(k_pool) && aligned16(v_pool) && aligned16(out),
              BI_ERR_INVALID, "bi_prefill_attn: pointers must be 16-byte aligned");
-  BI_REQUIRE((long)T / kPrefillQB + R < 0x7fffffffL && h_kv <= 65535, BI_ERR_INVALID,
-             "bi_prefill_attn: grid too large");
+  // grids: (T / 8 + R, h_kv) for fp32; (T / 32 + R) x h_kv in one dimension
+  // for the bf16 row-block kernel (32 or more rows per block)
+  BI_REQUIRE((long)T / kPrefillQB + R < 0x7fffffffL && h_kv <= 65535 &&
+                 ((long)T / 32 + R + 1) * h_kv < 0x7fffffffL,
+             BI_ERR_INVALID, "bi_prefill_attn: grid too large");
   const int Rg = h / h_kv, nw = kv_chunk / 64;
   hipStream_t s = as_stream(stream);
   if (dtype == BI_BF16) {
