@@ -949,6 +949,8 @@ def only_kernel(args, torch, dev):
             fn = e.decode_partials_launch(meta, cfg.layers - 1)
         alg = algorithmic_bytes(args.only, cfg, args.batch, kv_len, meta)
         label = f"{args.only}{' (twin)' if args.twin else ''}, batch {args.batch}"
+        if args.only == "decode_attn" and not args.twin:
+            label += " (bi_decode_attn alone, without the merge)"
     for _ in range(3):
         fn()
     torch.cuda.synchronize()
