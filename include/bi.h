@@ -157,6 +157,38 @@ bi_status bi_gemm_qkv_rope(const void *A, const void *W, int M, int K, int h, in
                            const int32_t *slot_mapping, int page_size, void *q_out,
                            void *k_pool, void *v_pool, bi_stream stream);
 
+/* The three products above with the residual add and the RMSNorm that
+ * precede them in a transformer layer done in their prologue, for batches
+ * of a few rows: first h_out = round(h + o) and x = RMSNorm(h_out) * gamma,
+ * exactly as bi_add_rmsnorm computes them (with o == NULL: x =
+ * RMSNorm(h) * gamma as bi_rmsnorm, and h_out must be NULL), then the
+ * product of x with W as bi_gemm / bi_gemm_swiglu / bi_gemm_qkv_rope compute
+ * it.  Every output is bit-identical to the two launches' ("Batch invariance
+ * and reproducible inference": rms_norm reduces each row inside one block;
+ * "2 . Cross-block accumulation": one K chain per output); this is one
+ * launch instead of two, which matters when a launch's fixed cost exceeds
+ * the work.  No passage defines the fusion itself.
+ *   h : device bf16 [M][K] (the residual stream), read only;
+ *   o : device bf16 [M][K] or NULL;  gamma : device bf16 [K];
+ *   h_out : device bf16 [M][K], written, must not alias h or o (NULL iff o is);
+ *   x_out : device bf16 [M][K] or NULL: the normalised rows, if wanted;
+ *   the rest as for the plain call (bf16 W and outputs; C of bi_norm_gemm
+ *   bf16 or fp32 by out_dtype).
+ * 0 <= M <= 4 and K <= 4096 (BI_ERR_UNSUPPORTED beyond: use the two calls),
+ * K % 8 == 0, pointers 16-byte aligned; other violations return
+ * BI_ERR_INVALID.  Nothing is launched on an error. */
+bi_status bi_norm_gemm(const void *h, const void *o, const void *gamma, float eps, void *h_out,
+                       void *x_out, const void *W, void *C, int M, int N, int K, int out_dtype,
+                       bi_stream stream);
+bi_status bi_norm_gemm_swiglu(const void *h, const void *o, const void *gamma, float eps,
+                              void *h_out, void *x_out, const void *W, void *act, int M, int I,
+                              int K, bi_stream stream);
+bi_status bi_norm_gemm_qkv_rope(const void *h, const void *o, const void *gamma, float eps,
+                                void *h_out, void *x_out, const void *W, int M, int K, int h_q,
+                                int h_kv, int d_h, const int32_t *pos, const float *cos_t,
+                                const float *sin_t, const int32_t *slot_mapping, int page_size,
+                                void *q_out, void *k_pool, void *v_pool, bi_stream stream);
+
 /* Twin: picks its tiling from M and, when M x N offers too few tiles to fill
  * the device, splits K over workgroups that add fp32 partials with atomics
  * (order undefined) -- the split-K the pages describe.  Needs

@@ -36,6 +36,12 @@ SIGNATURES = {
     "bi_gemm_swiglu": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp]),
     "bi_gemm_qkv_rope": (_c_int, [_vp, _vp] + [_c_int] * 5 + [_vp] * 4 + [_c_int]
                          + [_vp] * 4),
+    "bi_norm_gemm": (_c_int, [_vp, _vp, _vp, _c_float, _vp, _vp, _vp, _vp] + [_c_int] * 4
+                     + [_vp]),
+    "bi_norm_gemm_swiglu": (_c_int, [_vp, _vp, _vp, _c_float, _vp, _vp, _vp, _vp]
+                            + [_c_int] * 3 + [_vp]),
+    "bi_norm_gemm_qkv_rope": (_c_int, [_vp, _vp, _vp, _c_float, _vp, _vp, _vp] + [_c_int] * 5
+                              + [_vp] * 4 + [_c_int] + [_vp] * 4),
     "bi_decode_attn": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp] + [_c_int] * 8
                        + [_c_float, _c_int, _vp, _vp, _vp]),
     "bi_decode_attn_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp] + [_c_int] * 8
@@ -255,6 +261,64 @@ def bi_gemm_qkv_rope(A, W, h: int, h_kv: int, d_h: int, pos, cos_t, sin_t, slot_
         _ptr(A), _ptr(W), M, K, h, h_kv, d_h, _i32(pos) if pos is not None else None,
         _ptr(cos_t), _ptr(sin_t), _i32(slot_mapping), page_size, _ptr(q_out), _ptr(k_pool),
         _ptr(v_pool), _stream(stream)))
+    return q_out
+
+
+def _check_norm_args(fn: str, h, o, gamma, h_out, x_out, W, K: int) -> int:
+    """Host checks of the norm-prologue products; returns M."""
+    _need(h.dim() == 2 and h.shape[1] == K, fn, f"h{tuple(h.shape)} is not [M][{K}]")
+    _need(gamma.numel() == K, fn, f"gamma has {gamma.numel()} entries, not {K}")
+    for name, t in (("o", o), ("h_out", h_out), ("x_out", x_out)):
+        _need(t is None or tuple(t.shape) == tuple(h.shape), fn,
+              f"{name}{tuple(t.shape) if t is not None else ()} is not h's shape {tuple(h.shape)}")
+    _need((o is None) == (h_out is None), fn, "o and h_out must both be given or both be None")
+    _need(all(t is None or t.dtype == torch.bfloat16 for t in (h, o, gamma, h_out, x_out, W)),
+          fn, "h, o, gamma, h_out, x_out and W must be bf16")
+    return h.shape[0]
+
+
+def bi_norm_gemm(h, o, gamma, eps: float, h_out, x_out, W, C, stream=None):
+    """h_out = round(h + o) (o may be None: no add), x = RMSNorm(.) * gamma
+    (stored to x_out unless None), then C = x W^T: bi_add_rmsnorm (or
+    bi_rmsnorm) followed by bi_gemm, in one launch (at most 4 rows)."""
+    N, K = W.shape
+    M = _check_norm_args("bi_norm_gemm", h, o, gamma, h_out, x_out, W, K)
+    _need(tuple(C.shape) == (M, N), "bi_norm_gemm", f"C{tuple(C.shape)} is not [{M}][{N}]")
+    _check("bi_norm_gemm", load().bi_norm_gemm(
+        _ptr(h), _ptr(o), _ptr(gamma), eps, _ptr(h_out), _ptr(x_out), _ptr(W), _ptr(C), M, N, K,
+        _dt(C), _stream(stream)))
+    return C
+
+
+def bi_norm_gemm_swiglu(h, o, gamma, eps: float, h_out, x_out, W, act, stream=None):
+    """The norm prologue of bi_norm_gemm, then bi_gemm_swiglu's product."""
+    K = W.shape[1]
+    I = act.shape[1]
+    M = _check_norm_args("bi_norm_gemm_swiglu", h, o, gamma, h_out, x_out, W, K)
+    _need(tuple(W.shape) == (2 * I, K) and act.shape[0] == M and act.dtype == torch.bfloat16,
+          "bi_norm_gemm_swiglu", f"shape mismatch W{tuple(W.shape)} act{tuple(act.shape)}")
+    _check("bi_norm_gemm_swiglu", load().bi_norm_gemm_swiglu(
+        _ptr(h), _ptr(o), _ptr(gamma), eps, _ptr(h_out), _ptr(x_out), _ptr(W), _ptr(act), M, I,
+        K, _stream(stream)))
+    return act
+
+
+def bi_norm_gemm_qkv_rope(h, o, gamma, eps: float, h_out, x_out, W, h_q: int, h_kv: int,
+                          d_h: int, pos, cos_t, sin_t, slot_mapping, q_out, k_pool, v_pool,
+                          stream=None):
+    """The norm prologue of bi_norm_gemm, then bi_gemm_qkv_rope's product."""
+    K = W.shape[1]
+    M = _check_norm_args("bi_norm_gemm_qkv_rope", h, o, gamma, h_out, x_out, W, K)
+    _need(tuple(W.shape) == ((h_q + 2 * h_kv) * d_h, K) and tuple(q_out.shape) == (M, h_q, d_h),
+          "bi_norm_gemm_qkv_rope", f"shape mismatch W{tuple(W.shape)} q_out{tuple(q_out.shape)}")
+    _need(all(t.dtype == torch.bfloat16 for t in (q_out, k_pool, v_pool)),
+          "bi_norm_gemm_qkv_rope", "q_out and the pools must be bf16")
+    page_size = k_pool.shape[2]
+    _check("bi_norm_gemm_qkv_rope", load().bi_norm_gemm_qkv_rope(
+        _ptr(h), _ptr(o), _ptr(gamma), eps, _ptr(h_out), _ptr(x_out), _ptr(W), M, K, h_q, h_kv,
+        d_h, _i32(pos) if pos is not None else None, _ptr(cos_t), _ptr(sin_t),
+        _i32(slot_mapping), page_size, _ptr(q_out), _ptr(k_pool), _ptr(v_pool),
+        _stream(stream)))
     return q_out
 
 

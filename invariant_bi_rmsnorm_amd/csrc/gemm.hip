@@ -23,6 +23,7 @@
 
 #include "api.h"
 #include "common.h"
+#include "rownorm.h"
 
 namespace bi {
 
@@ -242,10 +243,13 @@ struct SmallCfg {
 // gate rows row0 + 8p .., block 2p + 1 the up rows `arg` further on; PAIR 2
 // (RoPE): blocks 2p, 2p + 1 hold the two rotation halves of 16-column pair
 // tile row0 / 16 + p, heads of `arg` rows (8 dims of each half per tile).
+// `pre` extra barriers, matching the compute waves' own before their first
+// stage, follow the first RD - 1 stages' copies.
 template <int NB, int LPS, int RD, bool NT, int PAIR = 0>
 __device__ __forceinline__ void small_copy_ring(const uint16_t* __restrict__ base, long ld,
                                                 int row0, int rmax, int kbeg, int K, int NST,
-                                                char* ring, int gw, int lane, int arg = 0) {
+                                                char* ring, int gw, int lane, int arg = 0,
+                                                int pre = 0) {
   constexpr int NIT = NB * LPS, QB = NIT / kSmallGroupWaves, XR = NIT % kSmallGroupWaves;
   constexpr int QMAX = QB + (XR > 0), KS = 2 * LPS;
   const bool extra = gw < XR;
@@ -282,6 +286,7 @@ __device__ __forceinline__ void small_copy_ring(const uint16_t* __restrict__ bas
 #pragma unroll
   for (int s = 0; s < RD - 1; ++s)
     if (s < NST) issue(s);
+  for (int i = 0; i < pre; ++i) __builtin_amdgcn_s_barrier();
   for (int st = 0; st < NST; ++st) {
     if (st + RD - 1 > NST) BI_WAIT_VMCNT(0);
     else if (extra) BI_WAIT_VMCNT((RD - 2) * QMAX);
@@ -422,6 +427,180 @@ __global__ __launch_bounds__(kSmallThreads) void k_gemm_small(
         store_tile<OUTF32>(C, acc[i][j], m0 + m * 16, n0 + c * 16, mend, N, lane);
       }
     }
+}
+
+// ---------------------------------------------------------------------------
+// Small batch with the RMSNorm in the prologue (at most kNormRows rows, K <=
+// 4096): x = RMSNorm(h [+ o]) * gamma is computed by every workgroup for
+// itself, into LDS, while its W ring fills, and then feeds the one-strip
+// skinny GEMM in place of A.  At a few rows a separate norm launch costs
+// several microseconds of fixed time for a few KiB of work; here it costs
+// one barrier.  The arithmetic is the norm kernels' (same lanes, same
+// vectors, the helpers of rownorm.h: bit for bit bi_add_rmsnorm /
+// bi_rmsnorm) followed by the skinny kernel's chain (ascending K-tiles, the
+// same fragment of each operand), so every output equals the two launches'.
+// Workgroup 0 alone stores the new residual h_out = round(h + o) and x, so
+// h_out must not alias h or o (other workgroups still read them).
+// LDS: [W ring: kNormWD stages][x: M rows of ceil(K/64) lines of 128 bytes,
+// unit u of a line of row m at slot u ^ (m & 7)][4 x 4 wave sums].
+// ---------------------------------------------------------------------------
+constexpr int kNormRows = 4, kNormWD = 5, kNormMaxK = 4096;
+constexpr int kNormThreads = (kSmallComputeWaves + kSmallGroupWaves) * 64;
+constexpr int kNormRing = kNormWD * SmallCfg<1, 1>::W_ITEMS * 1024;
+constexpr int kNormLdsMax = kNormRing + kNormRows * (kNormMaxK / 64) * 128 + 64;
+
+struct NormArgs {
+  const uint16_t* h;
+  const uint16_t* o;   // NULL: no residual add
+  const uint16_t* gamma;
+  uint16_t* h_out;     // with o: round(h + o), stored by workgroup 0
+  uint16_t* x_out;     // NULL or the normalised rows, stored by workgroup 0
+  float eps;
+};
+
+template <bool ADD, int OUTF32>
+__global__ __launch_bounds__(kNormThreads) void k_gemm_norm(NormArgs na,
+                                                            const uint16_t* __restrict__ W,
+                                                            void* C, int M, int N, int K,
+                                                            RopeArgs ra) {
+  using G = SmallCfg<1, 1>;
+  constexpr int KS = G::KS, LPS = G::LPS;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int rowb = ((K + 63) >> 6) * 128;   // LDS bytes per x row
+  char* xr = smem + kNormRing;
+  float* ws = reinterpret_cast<float*>(xr + M * rowb);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n0 = blockIdx.x * 16;
+  const int KT = (K + 31) >> 5;
+  const int NST = (KT + KS - 1) / KS;
+
+  if (wave >= kSmallComputeWaves) {   // W copies, after the one prologue barrier
+    const int cw = wave - kSmallComputeWaves;
+    if constexpr (OUTF32 == 3)
+      small_copy_ring<2, LPS, kNormWD, true, 1>(W, K, n0 / 2, N / 2 - 1, 0, K, NST, smem, cw,
+                                                lane, N / 2, 1);
+    else if constexpr (OUTF32 == 4)
+      small_copy_ring<2, LPS, kNormWD, true, 2>(W, K, n0, N - 1, 0, K, NST, smem, cw, lane,
+                                                ra.d_h, 1);
+    else
+      small_copy_ring<2, LPS, kNormWD, true>(W, K, n0, N - 1, 0, K, NST, smem, cw, lane, 0, 1);
+    return;
+  }
+
+  // ---- the norm, by the four compute waves (lane t of the row's 256) ----
+  const int t = threadIdx.x, nv = K >> 3;
+  const bool writer = blockIdx.x == 0;
+  u32x4_t gv[2], xv[kNormRows][2];   // gamma and the rounded rows, as bf16 bits
+  float a[kNormRows];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    if (t + 256 * j < nv) gv[j] = *reinterpret_cast<const u32x4_t*>(na.gamma + 8 * (t + 256 * j));
+#pragma unroll
+  for (int m = 0; m < kNormRows; ++m) {
+    a[m] = 0.0f;
+    if (m < M) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int v = t + 256 * j;
+        if (v < nv) {
+          const long i0 = (long)m * K + 8 * v;
+          float hs[8], xs[8];
+          load8<1>(na.h, i0, hs);
+          if constexpr (ADD) {
+            float os[8];
+            load8<1>(na.o, i0, os);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) hs[e] = hs[e] + os[e];
+          }
+          xv[m][j] = u32x4_t{pack_bf16x2(hs[0], hs[1]), pack_bf16x2(hs[2], hs[3]),
+                             pack_bf16x2(hs[4], hs[5]), pack_bf16x2(hs[6], hs[7])};
+          if (ADD && writer) *reinterpret_cast<u32x4_t*>(na.h_out + i0) = xv[m][j];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            xs[e] = bf16_bits_to_f32((uint16_t)(xv[m][j][e >> 1] >> (16 * (e & 1))));
+          a[m] = rn_fold8(xs, a[m]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < kNormRows; ++m) {
+    const float sum = rn_wave_sum(a[m]);
+    if (m < M && lane == 0) ws[4 * m + wave] = sum;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+  for (int m = 0; m < kNormRows; ++m) {
+    if (m < M) {
+      const float r = rn_inv_rms(ws + 4 * m, K, na.eps);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int v = t + 256 * j;
+        if (v < nv) {
+          float xs[8], gs[8], ys[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            xs[e] = bf16_bits_to_f32((uint16_t)(xv[m][j][e >> 1] >> (16 * (e & 1))));
+            gs[e] = bf16_bits_to_f32((uint16_t)(gv[j][e >> 1] >> (16 * (e & 1))));
+          }
+          rn_scale8(xs, gs, r, ys);
+          const u32x4_t y = {pack_bf16x2(ys[0], ys[1]), pack_bf16x2(ys[2], ys[3]),
+                             pack_bf16x2(ys[4], ys[5]), pack_bf16x2(ys[6], ys[7])};
+          *reinterpret_cast<u32x4_t*>(xr + m * rowb + (v >> 3) * 128 + (((v & 7) ^ (m & 7)) << 4)) =
+              y;
+          if (writer && na.x_out) *reinterpret_cast<u32x4_t*>(na.x_out + (long)m * K + 8 * v) = y;
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+
+  // ---- the skinny kernel's chain: wave 0 holds the one 16 x 16 tile ----
+  const int r = lane & 15, g = lane >> 4, rr = min(r, M - 1);
+  const uint32_t woff0 = ((r >> 3) << 10) + ((r & 7) << 7) + ((g ^ (r & 7)) << 4);
+  const uint32_t woff1 = ((r >> 3) << 10) + ((r & 7) << 7) + (((4 + g) ^ (r & 7)) << 4);
+  const char* xrow = xr + rr * rowb;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  RopePre rpre;
+  if constexpr (OUTF32 == 4)
+    if (wave == 0) rpre = rope_prefetch(ra, 0, n0 / 16, M, N, lane);
+  for (int st = 0; st < NST; ++st) {
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    const char* wslot = smem + (st % kNormWD) * (G::W_ITEMS * 1024);
+    const int nkt = min(KS, KT - st * KS);
+    if (wave == 0) {
+      u32x4_t av[KS], bv[KS];
+#pragma unroll
+      for (int kt = 0; kt < KS; ++kt) {
+        if (kt < nkt) {
+          const int ktg = st * KS + kt;
+          av[kt] = *reinterpret_cast<const u32x4_t*>(
+              xrow + (ktg >> 1) * 128 + (((((ktg & 1) << 2) | g) ^ (rr & 7)) << 4));
+          bv[kt] = *reinterpret_cast<const u32x4_t*>(wslot + (kt >> 1) * 2048 +
+                                                     ((kt & 1) ? woff1 : woff0));
+        }
+      }
+#pragma unroll
+      for (int kt = 0; kt < KS; ++kt) {
+        if (kt < nkt) {
+          const bool tail = (st * KS + kt) * 32 + 8 * g >= K;
+          acc = mfma(tail ? u32x4_t{0, 0, 0, 0} : av[kt], tail ? u32x4_t{0, 0, 0, 0} : bv[kt],
+                     acc);
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  }
+  if (wave != 0) return;
+  if constexpr (OUTF32 == 3)
+    store_swiglu(C, acc, 0, n0 / 2, M, N / 2, lane);
+  else if constexpr (OUTF32 == 4)
+    store_rope(ra, acc, rpre, 0, n0 / 16, M, N, lane);
+  else
+    store_tile<OUTF32>(C, acc, 0, n0, M, N, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -904,4 +1083,120 @@ extern "C" bi_status bi_gemm_qkv_rope(const void* A, const void* W, int M, int K
   RopeArgs ra{pos, cos_t, sin_t, slot_mapping, q_out, k_pool, v_pool, page_size, h, h_kv, d_h};
   dispatch_small<4>(A, W, nullptr, M, (int)N, K, as_stream(stream), 1, 0, ra);
   return launched("bi_gemm_qkv_rope");
+}
+
+// ---------------------------------------------------------------------------
+// The same three products with the residual add and RMSNorm in the prologue
+// (k_gemm_norm): a few rows only.
+// ---------------------------------------------------------------------------
+namespace bi {
+
+template <bool ADD, int OUTF32>
+static void launch_norm(const NormArgs& na, const void* W, void* C, int M, int N, int K,
+                        hipStream_t s, const RopeArgs& ra) {
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)k_gemm_norm<ADD, OUTF32>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, kNormLdsMax);
+    attr = true;
+  }
+  const int lds = kNormRing + M * (((K + 63) / 64) * 128) + 64;
+  hipLaunchKernelGGL((k_gemm_norm<ADD, OUTF32>), dim3((N + 15) / 16), dim3(kNormThreads), lds, s,
+                     na, (const uint16_t*)W, C, M, N, K, ra);
+}
+
+template <int OUTF32>
+static void dispatch_norm(const NormArgs& na, const void* W, void* C, int M, int N, int K,
+                          hipStream_t s, const RopeArgs& ra = RopeArgs{}) {
+  if (na.o) launch_norm<true, OUTF32>(na, W, C, M, N, K, s, ra);
+  else launch_norm<false, OUTF32>(na, W, C, M, N, K, s, ra);
+}
+
+// Checks shared by the three entry points; returns BI_OK or the status set.
+static bi_status check_norm(const char* fn, const void* h, const void* o, const void* gamma,
+                            float eps, const void* h_out, const void* x_out, const void* W,
+                            int M, int K) {
+  BI_REQUIRE(M >= 0 && K >= 8 && K % 8 == 0, BI_ERR_INVALID,
+             "%s: need M >= 0, K >= 8, K %% 8 == 0 (M=%d K=%d)", fn, M, K);
+  BI_REQUIRE(M <= kNormRows && K <= kNormMaxK, BI_ERR_UNSUPPORTED,
+             "%s: at most %d rows and K <= %d (M=%d K=%d); larger: the norm, then the product",
+             fn, kNormRows, kNormMaxK, M, K);
+  BI_REQUIRE((o == nullptr) == (h_out == nullptr), BI_ERR_INVALID,
+             "%s: o and h_out must both be given or both be NULL", fn);
+  BI_REQUIRE(eps >= 0.0f, BI_ERR_INVALID, "%s: eps must be >= 0", fn);
+  if (M == 0) return BI_OK;
+  BI_REQUIRE(h && gamma && W, BI_ERR_INVALID, "%s: null pointer", fn);
+  BI_REQUIRE(aligned16(h) && aligned16(gamma) && aligned16(W) && aligned16(o) &&
+                 aligned16(h_out) && aligned16(x_out),
+             BI_ERR_INVALID, "%s: pointers must be 16-byte aligned", fn);
+  BI_REQUIRE(!h_out || (h_out != h && h_out != o), BI_ERR_INVALID,
+             "%s: h_out must not alias h or o", fn);
+  BI_REQUIRE(!x_out || (x_out != h && x_out != o && x_out != h_out), BI_ERR_INVALID,
+             "%s: x_out must not alias h, o or h_out", fn);
+  return BI_OK;
+}
+
+}  // namespace bi
+
+extern "C" bi_status bi_norm_gemm(const void* h, const void* o, const void* gamma, float eps,
+                                  void* h_out, void* x_out, const void* W, void* C, int M,
+                                  int N, int K, int out_dtype, bi_stream stream) {
+  using namespace bi;
+  const bi_status st = check_norm("bi_norm_gemm", h, o, gamma, eps, h_out, x_out, W, M, K);
+  if (st != BI_OK || M == 0) return st;
+  BI_REQUIRE(N >= 1 && C, BI_ERR_INVALID, "bi_norm_gemm: N >= 1 and C needed (N=%d)", N);
+  BI_REQUIRE(aligned16(C), BI_ERR_INVALID, "bi_norm_gemm: C must be 16-byte aligned");
+  BI_REQUIRE(out_dtype == BI_BF16 || out_dtype == BI_F32, BI_ERR_UNSUPPORTED,
+             "bi_norm_gemm: out_dtype %d not supported", out_dtype);
+  BI_REQUIRE((long)N * K < (1L << 40), BI_ERR_INVALID, "bi_norm_gemm: tensor too large");
+  const NormArgs na{(const uint16_t*)h, (const uint16_t*)o, (const uint16_t*)gamma,
+                    (uint16_t*)h_out, (uint16_t*)x_out, eps};
+  if (out_dtype == BI_F32) dispatch_norm<1>(na, W, C, M, N, K, as_stream(stream));
+  else dispatch_norm<0>(na, W, C, M, N, K, as_stream(stream));
+  return launched("bi_norm_gemm");
+}
+
+extern "C" bi_status bi_norm_gemm_swiglu(const void* h, const void* o, const void* gamma,
+                                         float eps, void* h_out, void* x_out, const void* W,
+                                         void* act, int M, int I, int K, bi_stream stream) {
+  using namespace bi;
+  const bi_status st =
+      check_norm("bi_norm_gemm_swiglu", h, o, gamma, eps, h_out, x_out, W, M, K);
+  if (st != BI_OK || M == 0) return st;
+  BI_REQUIRE(I >= 8 && I % 8 == 0 && act, BI_ERR_INVALID,
+             "bi_norm_gemm_swiglu: need I %% 8 == 0 and act (I=%d)", I);
+  BI_REQUIRE(aligned16(act), BI_ERR_INVALID, "bi_norm_gemm_swiglu: act must be 16-byte aligned");
+  BI_REQUIRE(2L * I * K < (1L << 40), BI_ERR_INVALID, "bi_norm_gemm_swiglu: tensor too large");
+  const NormArgs na{(const uint16_t*)h, (const uint16_t*)o, (const uint16_t*)gamma,
+                    (uint16_t*)h_out, (uint16_t*)x_out, eps};
+  dispatch_norm<3>(na, W, act, M, 2 * I, K, as_stream(stream));
+  return launched("bi_norm_gemm_swiglu");
+}
+
+extern "C" bi_status bi_norm_gemm_qkv_rope(const void* h, const void* o, const void* gamma,
+                                           float eps, void* h_out, void* x_out, const void* W,
+                                           int M, int K, int nh, int h_kv, int d_h,
+                                           const int32_t* pos, const float* cos_t,
+                                           const float* sin_t, const int32_t* slot_mapping,
+                                           int page_size, void* q_out, void* k_pool,
+                                           void* v_pool, bi_stream stream) {
+  using namespace bi;
+  const bi_status st =
+      check_norm("bi_norm_gemm_qkv_rope", h, o, gamma, eps, h_out, x_out, W, M, K);
+  if (st != BI_OK) return st;
+  BI_REQUIRE(nh >= 1 && h_kv >= 1 && d_h >= 16 && d_h % 16 == 0 && page_size >= 1,
+             BI_ERR_INVALID, "bi_norm_gemm_qkv_rope: need d_h %% 16 == 0 (d_h=%d)", d_h);
+  BI_REQUIRE((cos_t == nullptr) == (sin_t == nullptr), BI_ERR_INVALID,
+             "bi_norm_gemm_qkv_rope: cos_t and sin_t must both be given or both be NULL");
+  if (M == 0) return BI_OK;
+  BI_REQUIRE(slot_mapping && q_out && k_pool && v_pool && (pos || !cos_t), BI_ERR_INVALID,
+             "bi_norm_gemm_qkv_rope: null pointer");
+  const long N = (long)(nh + 2 * h_kv) * d_h;
+  BI_REQUIRE(N * K < (1L << 40) && N < (1L << 30), BI_ERR_INVALID,
+             "bi_norm_gemm_qkv_rope: tensor too large");
+  const NormArgs na{(const uint16_t*)h, (const uint16_t*)o, (const uint16_t*)gamma,
+                    (uint16_t*)h_out, (uint16_t*)x_out, eps};
+  RopeArgs ra{pos, cos_t, sin_t, slot_mapping, q_out, k_pool, v_pool, page_size, nh, h_kv, d_h};
+  dispatch_norm<4>(na, W, nullptr, M, (int)N, K, as_stream(stream), ra);
+  return launched("bi_norm_gemm_qkv_rope");
 }

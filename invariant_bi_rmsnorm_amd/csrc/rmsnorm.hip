@@ -7,6 +7,7 @@
 // xor butterfly per wave, waves added in order) depends on d only.
 #include "api.h"
 #include "common.h"
+#include "rownorm.h"
 
 namespace bi {
 
@@ -25,8 +26,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const void* x, const void* __re
     const int i0 = v << 3;
     if (vec) {
       load8<DT>(x, base + i0, xs);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) a = __builtin_fmaf(xs[e], xs[e], a);
+      a = rn_fold8(xs, a);
     } else {
       const int n = min(8, d - i0);
       for (int e = 0; e < n; ++e) {
@@ -35,19 +35,11 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const void* x, const void* __re
       }
     }
   }
-  // xor butterfly inside the wave: masks 32, 16, 8, 4, 2, 1
-  a = a + __shfl_xor(a, 32);
-  a = a + __shfl_xor(a, 16);
-  a = a + __shfl_xor(a, 8);
-  a = a + __shfl_xor(a, 4);
-  a = a + __shfl_xor(a, 2);
-  a = a + __shfl_xor(a, 1);
+  a = rn_wave_sum(a);
   __shared__ float ws[4];
   if ((t & 63) == 0) ws[t >> 6] = a;
   __syncthreads();
-  const float ss = ((ws[0] + ws[1]) + ws[2]) + ws[3];
-  const float mean = ss / (float)d;
-  const float r = 1.0f / sqrtf(mean + eps);
+  const float r = rn_inv_rms(ws, d, eps);
 
   for (int v = t; v < nv; v += 256) {
     const int i0 = v << 3;
@@ -55,8 +47,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const void* x, const void* __re
       float xs[8], gs[8], ys[8];
       load8<DT>(x, base + i0, xs);
       load8<DT>(gamma, i0, gs);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ys[e] = (xs[e] * r) * gs[e];
+      rn_scale8(xs, gs, r, ys);
       store8<DT>(y, base + i0, ys);
     } else {
       const int n = min(8, d - i0);
@@ -92,12 +83,11 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm(void* h, const void* __rest
 #pragma unroll
       for (int e = 0; e < 8; ++e) rs[e] = hs[e] + os[e];
       store8<DT>(h, base + i0, rs);
+      float xs[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float xv = Elem<DT>::bytes == 2 ? bf16_bits_to_f32((uint16_t)f32_to_bf16_bits(rs[e]))
-                                              : rs[e];
-        a = __builtin_fmaf(xv, xv, a);
-      }
+      for (int e = 0; e < 8; ++e)
+        xs[e] = Elem<DT>::bytes == 2 ? bf16_bits_to_f32((uint16_t)f32_to_bf16_bits(rs[e])) : rs[e];
+      a = rn_fold8(xs, a);
     } else {
       const int n = min(8, d - i0);
       for (int e = 0; e < n; ++e) {
@@ -107,18 +97,11 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm(void* h, const void* __rest
       }
     }
   }
-  a = a + __shfl_xor(a, 32);
-  a = a + __shfl_xor(a, 16);
-  a = a + __shfl_xor(a, 8);
-  a = a + __shfl_xor(a, 4);
-  a = a + __shfl_xor(a, 2);
-  a = a + __shfl_xor(a, 1);
+  a = rn_wave_sum(a);
   __shared__ float ws[4];
   if ((t & 63) == 0) ws[t >> 6] = a;
   __syncthreads();
-  const float ss = ((ws[0] + ws[1]) + ws[2]) + ws[3];
-  const float mean = ss / (float)d;
-  const float r = 1.0f / sqrtf(mean + eps);
+  const float r = rn_inv_rms(ws, d, eps);
 
   for (int v = t; v < nv; v += 256) {
     const int i0 = v << 3;
@@ -126,8 +109,7 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm(void* h, const void* __rest
       float xs[8], gs[8], ys[8];
       load8<DT>(h, base + i0, xs);
       load8<DT>(gamma, i0, gs);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ys[e] = (xs[e] * r) * gs[e];
+      rn_scale8(xs, gs, r, ys);
       store8<DT>(y, base + i0, ys);
     } else {
       const int n = min(8, d - i0);

@@ -258,6 +258,7 @@ class Engine:
         c, d, dt = self.cfg, self.dev, self.cfg.dtype
         self.cap = rows
         self.h = torch.empty((rows, c.d), dtype=dt, device=d)
+        self.h2 = torch.empty((rows, c.d), dtype=dt, device=d)   # the other residual buffer
         self.x = torch.empty((rows, c.d), dtype=dt, device=d)
         self.qkv = torch.empty((rows, c.qkv_out), dtype=dt, device=d)
         self.q = torch.empty((rows, c.h, c.d_h), dtype=dt, device=d)
@@ -364,6 +365,7 @@ class Engine:
         if T > self.cap:
             self._alloc(T)
         h, x, qkv, q, att = self.h[:T], self.x[:T], self.qkv[:T], self.q[:T], self.att[:T]
+        alt = self.h2[:T]
         o, gu, act = self.o[:T], self.gu[:T], self.act[:T]
         nd = m["n_dec"]
         mode = self.mode
@@ -372,6 +374,13 @@ class Engine:
         nl = len(lws)
         bf = c.dtype == torch.bfloat16
         pos = m["pos"] if c.rope else None
+        # at up to 4 rows the residual add + RMSNorm before attention runs in
+        # the QKV projection's prologue (bi_norm_gemm_qkv_rope: the same bits
+        # in one launch instead of two; at one row 26.7 -> 18.8 us, graph-
+        # timed).  The new residual goes to the other buffer (alt), not over
+        # the old one.  (The wide products gain nothing from it: each of
+        # their many one-strip workgroups would redo the norm.)
+        nf = not fr and bf and T <= 4 and c.d <= 4096 and c.d % 8 == 0
 
         def choose(site, key, cands):
             """cands: functions of a layer index; invariant mode takes the
@@ -383,10 +392,26 @@ class Engine:
             return cands[self.tuner.pick((site,) + key, cands, nl)]
 
         # each site: candidate launchers as functions of a layer index j
+        def rope_append(j):
+            L.bi_rope_kv_append(qkv, c.h, c.h_kv, c.d_h, pos, self.cos, self.sin, m["slots"],
+                                q, self.pool.k[j], self.pool.v[j])
+
+        def twin_add_norm(hin, o_, hout, gamma):
+            # the twin's residual add (into hout) and norm, for the fused sites
+            if o_ is not None:
+                L.bi_add(hin, o_, hout)
+            L.bi_rmsnorm_free(hout if o_ is not None else hin, gamma, x, c.eps)
+
+        def norm_qkv_cands(hin, o_, hout, gamma):
+            def twin(j):
+                twin_add_norm(hin, o_, hout, gamma)
+                L.bi_gemm_free(x, lws[j].wqkv, qkv)
+                rope_append(j)
+            return [lambda j: L.bi_norm_gemm_qkv_rope(
+                hin, o_, gamma, c.eps, hout, x, lws[j].wqkv, c.h, c.h_kv, c.d_h, pos, self.cos,
+                self.sin, m["slots"], q, self.pool.k[j], self.pool.v[j]), twin]
+
         def qkv_cands():
-            def rope_append(j):
-                L.bi_rope_kv_append(qkv, c.h, c.h_kv, c.d_h, pos, self.cos, self.sin, m["slots"],
-                                    q, self.pool.k[j], self.pool.v[j])
             if T <= 64 and bf and c.d_h % 16 == 0 and not fr:
                 # the same bits in one pass (RoPE + KV append in the GEMM's
                 # epilogue); the step measured 2.5% faster at batch 1, 0.5-1.2%
@@ -431,7 +456,7 @@ class Engine:
             return [lambda j: L.bi_rmsnorm(hh, gamma, x, c.eps),
                     lambda j: L.bi_rmsnorm_free(hh, gamma, x, c.eps)]
 
-        def add_norm(gamma):
+        def add_norm(gamma, h):
             """h += o, then x = RMSNorm(h): fused (invariant) or add + the
             twin norm.  Tuned-mode timing runs on a copy of h (the add
             updates h in place)."""
@@ -462,17 +487,30 @@ class Engine:
         # the invariant and tuned engines fuse each residual add into the
         # RMSNorm after it (the next sublayer's, or the final norm)
         fuse = not fr
-        if fuse:
+        if fuse and not nf:
             f = choose("norm", (T,), norm_cands(lws[0].attn_norm, h))
             run("rmsnorm", lambda f=f: f(0))
+        cur = h   # with nf: the buffer holding the residual stream
         for li, lw in enumerate(lws):
             nxt = lws[li + 1].attn_norm if li + 1 < nl else w.final_norm
-            see("h_in", li, h)
-            if not fuse:
-                run("rmsnorm", lambda: L.bi_rmsnorm_free(h, lw.attn_norm, x, c.eps))
-            see("x_attn", li, x)
-            f = choose("qkv", (T,), qkv_cands())
-            run("gemm_qkv", lambda f=f, li=li: f(li))
+            if nf:   # the previous layer's last residual add happens here
+                pend, hout = (o, alt) if li > 0 else (None, None)
+                # (tuned mode times the site on its first use, at layer 0,
+                # before any layer's KV of this step is final)
+                f = choose("norm_qkv", (T,), norm_qkv_cands(cur, pend, hout, lw.attn_norm))
+                run("gemm_qkv", lambda f=f, li=li: f(li))
+                if li > 0:
+                    cur, alt = alt, cur
+                    see("h_out", li - 1, cur)
+                see("h_in", li, cur)
+                see("x_attn", li, x)
+            else:
+                see("h_in", li, h)
+                if not fuse:
+                    run("rmsnorm", lambda: L.bi_rmsnorm_free(h, lw.attn_norm, x, c.eps))
+                see("x_attn", li, x)
+                f = choose("qkv", (T,), qkv_cands())
+                run("gemm_qkv", lambda f=f, li=li: f(li))
             see("q", li, q)
             if nd:
                 f = choose("decode_attn", (nd, m["total_chunks"]), decode_cands())
@@ -485,11 +523,11 @@ class Engine:
             run("gemm_o", lambda f=f, li=li: f(li))
             see("o", li, o)
             if fuse:
-                add_norm(lw.ffn_norm)
+                add_norm(lw.ffn_norm, cur)
             else:
                 run("add", lambda: L.bi_add(h, o, h))
                 run("rmsnorm", lambda: L.bi_rmsnorm_free(h, lw.ffn_norm, x, c.eps))
-            see("h_mid", li, h)
+            see("h_mid", li, cur)
             see("x_ffn", li, x)
             sw = swiglu_cands()
             f = choose("gemm_gate_up", (T,), sw)
@@ -500,15 +538,20 @@ class Engine:
             f = choose("gemm_down", (T,), gemm_cands(act, "wdown", o))
             run("gemm_down", lambda f=f, li=li: f(li))
             see("down", li, o)
+            if nf:   # its residual add happens in the next QKV prologue
+                continue
             if fuse:
-                add_norm(nxt)
+                add_norm(nxt, h)
             else:
                 run("add", lambda: L.bi_add(h, o, h))
             see("h_out", li, h)
+        if nf:
+            add_norm(w.final_norm, cur)
+            see("h_out", nl - 1, cur)
+        nw = len(m["want"])
         if not fuse:
             L.bi_rmsnorm_free(h, w.final_norm, x, c.eps)
         see("x_final", nl, x)
-        nw = len(m["want"])
         if nw == 0:
             return StepOutput(torch.empty((0, c.vocab), device=self.dev),
                               torch.empty(0, dtype=torch.int32, device=self.dev), [])

@@ -59,6 +59,20 @@ def test_invalid_arguments_rejected_before_launch():
     st = lib.bi_gemm(None, None, None, 4, 4, 4, 0, 1, None)   # f32 in, bf16 out
     assert st == L.BI_ERR_UNSUPPORTED
     assert lib.bi_rmsnorm(None, None, None, 0, 16, ctypes.c_float(1e-5), 1, None) == L.BI_OK
+    # the norm-prologue products: more than 4 rows or K past 4096 are not
+    # covered (the caller runs the two calls); o without h_out is invalid
+    eps = ctypes.c_float(1e-5)
+    st = lib.bi_norm_gemm(None, None, None, eps, None, None, None, None, 5, 64, 4096, 1, None)
+    assert st == L.BI_ERR_UNSUPPORTED and b"at most 4 rows" in lib.bi_last_error()
+    st = lib.bi_norm_gemm_swiglu(None, None, None, eps, None, None, None, None, 1, 64, 4104,
+                                 None)
+    assert st == L.BI_ERR_UNSUPPORTED
+    fake = ctypes.c_void_p(256)
+    st = lib.bi_norm_gemm(fake, fake, fake, eps, None, None, fake, fake, 1, 64, 4096, 1, None)
+    assert st == L.BI_ERR_INVALID and b"h_out" in lib.bi_last_error()
+    st = lib.bi_norm_gemm_qkv_rope(None, None, None, eps, None, None, None, 1, 4096, 32, 8, 120,
+                                   None, None, None, None, 16, None, None, None, None)
+    assert st == L.BI_ERR_INVALID                      # d_h % 16 != 0
 
 
 def test_binding_argument_counts_match_header():
@@ -112,6 +126,15 @@ def test_binding_rejects_mismatched_buffers_before_launch():
         L.bi_merge_partials(ml, acc, off[:B], out)
     with pytest.raises(ValueError, match="partials"):
         L.bi_merge_partials(ml, acc[:, :, :32], off, out)
+    with pytest.raises(ValueError, match="o and h_out"):
+        L.bi_norm_gemm(A.to(bf), A.to(bf), torch.zeros(16, dtype=bf), 1e-5, None, None,
+                       torch.zeros((8, 16), dtype=bf), torch.zeros((4, 8), dtype=bf))
+    with pytest.raises(ValueError, match="gamma"):
+        L.bi_norm_gemm(A.to(bf), None, torch.zeros(12, dtype=bf), 1e-5, None, None,
+                       torch.zeros((8, 16), dtype=bf), torch.zeros((4, 8), dtype=bf))
+    with pytest.raises(ValueError, match="bf16"):
+        L.bi_norm_gemm(A, None, torch.zeros(16, dtype=bf), 1e-5, None, None,
+                       torch.zeros((8, 16), dtype=bf), torch.zeros((4, 8), dtype=bf))
     with pytest.raises(ValueError, match="q_start"):
         L.bi_prefill_attn(q, torch.zeros(1, dtype=i32), torch.zeros(2, dtype=i32), kp, kp,
                           bt, 64, 0.1, q.clone())
