@@ -19,6 +19,7 @@
 // global->LDS instruction per fragment, read back by the same lane); the
 // small-M and large-tile kernels copy whole 128-byte row lines and read
 // fragments back through a swizzled line-major layout.
+#include <algorithm>
 #include <type_traits>
 
 #include "api.h"
@@ -441,13 +442,18 @@ __global__ __launch_bounds__(kSmallThreads) void k_gemm_small(
 // same fragment of each operand), so every output equals the two launches'.
 // Workgroup 0 alone stores the new residual h_out = round(h + o) and x, so
 // h_out must not alias h or o (other workgroups still read them).
-// LDS: [W ring: kNormWD stages][x: M rows of ceil(K/64) lines of 128 bytes,
+// LDS: [W ring: WD stages][x: M rows of ceil(K/64) lines of 128 bytes,
 // unit u of a line of row m at slot u ^ (m & 7)][4 x 4 wave sums].
 // ---------------------------------------------------------------------------
-constexpr int kNormRows = 4, kNormWD = 5, kNormMaxK = 4096;
+// W ring stages: 7 for up to 2 rows, 5 for 3 and 4 (x takes the rest of
+// the 80 KiB that lets two workgroups share a CU)
+constexpr int kNormRows = 4, kNormMaxK = 4096;
 constexpr int kNormThreads = (kSmallComputeWaves + kSmallGroupWaves) * 64;
-constexpr int kNormRing = kNormWD * SmallCfg<1, 1>::W_ITEMS * 1024;
-constexpr int kNormLdsMax = kNormRing + kNormRows * (kNormMaxK / 64) * 128 + 64;
+constexpr int norm_ring_bytes(int wd) { return wd * SmallCfg<1, 1>::W_ITEMS * 1024; }
+constexpr int kNormLdsMax = 80 * 1024;
+static_assert(norm_ring_bytes(7) + 2 * (kNormMaxK / 64) * 128 + 64 <= kNormLdsMax &&
+                  norm_ring_bytes(5) + 4 * (kNormMaxK / 64) * 128 + 64 <= kNormLdsMax,
+              "two workgroups per CU");
 
 struct NormArgs {
   const uint16_t* h;
@@ -458,32 +464,71 @@ struct NormArgs {
   float eps;
 };
 
-template <bool ADD, int OUTF32>
-__global__ __launch_bounds__(kNormThreads) void k_gemm_norm(NormArgs na,
-                                                            const uint16_t* __restrict__ W,
-                                                            void* C, int M, int N, int K,
-                                                            RopeArgs ra) {
+// Row of W that lane row `crow` of 8-row block b copies for strip s: PAIR 0
+// the strip's 16 rows, 1 (SwiGLU) 8 gate rows then the matching 8 up rows
+// `arg` further on, 2 (RoPE) the two rotation halves of a head of `arg` rows
+// -- the skinny kernel's copy layouts for one strip.
+template <int PAIR>
+__device__ __forceinline__ int norm_strip_row(int s, int b, int crow, int N, int arg) {
+  if constexpr (PAIR == 1) {
+    return b * arg + min(s * 8 + crow, arg - 1);
+  } else if constexpr (PAIR == 2) {
+    const int per_head = arg / 16, hh = s / per_head;
+    return hh * arg + b * (arg / 2) + (s - hh * per_head) * 8 + crow;
+  } else {
+    return min(s * 16 + b * 8 + crow, N - 1);
+  }
+}
+
+// Workgroup b takes strips b, b + gridDim.x, ... of the product (the grid is
+// at most two workgroups per CU), so the norm runs once per workgroup and
+// its W ring streams on across strips: stage g of the ring is stage g % NST
+// of its strip g / NST.
+template <bool ADD, int OUTF32, int WD>
+__global__ __launch_bounds__(kNormThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_gemm_norm(
+    NormArgs na, const uint16_t* __restrict__ W, void* C, int M, int N, int K, RopeArgs ra) {
+  constexpr int RING = norm_ring_bytes(WD);
   using G = SmallCfg<1, 1>;
-  constexpr int KS = G::KS, LPS = G::LPS;
+  constexpr int KS = G::KS, NIT = G::W_ITEMS, QB = NIT / kSmallGroupWaves;
+  constexpr int PAIR = OUTF32 == 3 ? 1 : OUTF32 == 4 ? 2 : 0;
+  static_assert(G::LPS * 2 == NIT && NIT % kSmallGroupWaves == 0, "one strip of 16 rows");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int rowb = ((K + 63) >> 6) * 128;   // LDS bytes per x row
-  char* xr = smem + kNormRing;
+  char* xr = smem + RING;
   float* ws = reinterpret_cast<float*>(xr + M * rowb);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int n0 = blockIdx.x * 16;
   const int KT = (K + 31) >> 5;
   const int NST = (KT + KS - 1) / KS;
+  const int nstrips = (N + 15) >> 4;
+  const int mine = (nstrips - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int total = mine * NST;   // ring stages of this workgroup
 
-  if (wave >= kSmallComputeWaves) {   // W copies, after the one prologue barrier
+  if (wave >= kSmallComputeWaves) {   // W copies; one extra barrier: the prologue's
     const int cw = wave - kSmallComputeWaves;
-    if constexpr (OUTF32 == 3)
-      small_copy_ring<2, LPS, kNormWD, true, 1>(W, K, n0 / 2, N / 2 - 1, 0, K, NST, smem, cw,
-                                                lane, N / 2, 1);
-    else if constexpr (OUTF32 == 4)
-      small_copy_ring<2, LPS, kNormWD, true, 2>(W, K, n0, N - 1, 0, K, NST, smem, cw, lane,
-                                                ra.d_h, 1);
-    else
-      small_copy_ring<2, LPS, kNormWD, true>(W, K, n0, N - 1, 0, K, NST, smem, cw, lane, 0, 1);
+    const int crow = lane >> 3, koff = ((lane & 7) ^ crow) * 8;
+    const int arg = PAIR == 1 ? N / 2 : PAIR == 2 ? ra.d_h : 0;
+    auto issue = [&](int gs) {
+      const int i = gs / NST, st = gs - i * NST;
+      const int strip = blockIdx.x + i * gridDim.x;
+      char* slot = smem + (gs % WD) * (NIT * 1024);
+#pragma unroll
+      for (int q = 0; q < QB; ++q) {
+        const int j = cw + kSmallGroupWaves * q, line = j >> 1;
+        const int row = norm_strip_row<PAIR>(strip, j & 1, crow, N, arg);
+        const int k = st * (32 * KS) + line * 64 + koff;   // this lane's first k
+        dma16_nt(W + (long)row * K + (k < K ? k : 0), slot + j * 1024);
+      }
+    };
+#pragma unroll
+    for (int g = 0; g < WD - 1; ++g)
+      if (g < total) issue(g);
+    __builtin_amdgcn_s_barrier();
+    for (int g = 0; g < total; ++g) {
+      if (g + WD - 1 > total) BI_WAIT_VMCNT(0);
+      else BI_WAIT_VMCNT((WD - 2) * QB);
+      __builtin_amdgcn_s_barrier();
+      if (g + WD - 1 < total) issue(g + WD - 1);
+    }
     return;
   }
 
@@ -557,50 +602,58 @@ __global__ __launch_bounds__(kNormThreads) void k_gemm_norm(NormArgs na,
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
 
-  // ---- the skinny kernel's chain: wave 0 holds the one 16 x 16 tile ----
+  // ---- the skinny kernel's chain per strip: wave 0 holds the 16 x 16 tile ----
   const int r = lane & 15, g = lane >> 4, rr = min(r, M - 1);
   const uint32_t woff0 = ((r >> 3) << 10) + ((r & 7) << 7) + ((g ^ (r & 7)) << 4);
   const uint32_t woff1 = ((r >> 3) << 10) + ((r & 7) << 7) + (((4 + g) ^ (r & 7)) << 4);
   const char* xrow = xr + rr * rowb;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  RopePre rpre;
-  if constexpr (OUTF32 == 4)
-    if (wave == 0) rpre = rope_prefetch(ra, 0, n0 / 16, M, N, lane);
-  for (int st = 0; st < NST; ++st) {
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    const char* wslot = smem + (st % kNormWD) * (G::W_ITEMS * 1024);
-    const int nkt = min(KS, KT - st * KS);
-    if (wave == 0) {
-      u32x4_t av[KS], bv[KS];
+  for (int i = 0; i < mine; ++i) {
+    const int strip = blockIdx.x + i * gridDim.x;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    RopePre rpre;
+    if constexpr (OUTF32 == 4)
+      if (wave == 0) rpre = rope_prefetch(ra, 0, strip, M, N, lane);
+    for (int st = 0; st < NST; ++st) {
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      const char* wslot = smem + ((i * NST + st) % WD) * (NIT * 1024);
+      const int nkt = min(KS, KT - st * KS);
+      if (wave == 0) {   // half a stage's fragments at a time (registers)
 #pragma unroll
-      for (int kt = 0; kt < KS; ++kt) {
-        if (kt < nkt) {
-          const int ktg = st * KS + kt;
-          av[kt] = *reinterpret_cast<const u32x4_t*>(
-              xrow + (ktg >> 1) * 128 + (((((ktg & 1) << 2) | g) ^ (rr & 7)) << 4));
-          bv[kt] = *reinterpret_cast<const u32x4_t*>(wslot + (kt >> 1) * 2048 +
-                                                     ((kt & 1) ? woff1 : woff0));
+        for (int hf = 0; hf < KS; hf += KS / 2) {
+          u32x4_t av[KS / 2], bv[KS / 2];
+#pragma unroll
+          for (int u = 0; u < KS / 2; ++u) {
+            const int kt = hf + u, ktg = st * KS + kt;
+            if (kt < nkt) {
+              av[u] = *reinterpret_cast<const u32x4_t*>(
+                  xrow + (ktg >> 1) * 128 + (((((ktg & 1) << 2) | g) ^ (rr & 7)) << 4));
+              bv[u] = *reinterpret_cast<const u32x4_t*>(wslot + (kt >> 1) * 2048 +
+                                                        ((kt & 1) ? woff1 : woff0));
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < KS / 2; ++u) {
+            const int kt = hf + u;
+            if (kt < nkt) {
+              const bool tail = (st * KS + kt) * 32 + 8 * g >= K;
+              acc = mfma(tail ? u32x4_t{0, 0, 0, 0} : av[u],
+                         tail ? u32x4_t{0, 0, 0, 0} : bv[u], acc);
+            }
+          }
         }
       }
-#pragma unroll
-      for (int kt = 0; kt < KS; ++kt) {
-        if (kt < nkt) {
-          const bool tail = (st * KS + kt) * 32 + 8 * g >= K;
-          acc = mfma(tail ? u32x4_t{0, 0, 0, 0} : av[kt], tail ? u32x4_t{0, 0, 0, 0} : bv[kt],
-                     acc);
-        }
-      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    if (wave == 0) {
+      if constexpr (OUTF32 == 3)
+        store_swiglu(C, acc, 0, strip * 8, M, N / 2, lane);
+      else if constexpr (OUTF32 == 4)
+        store_rope(ra, acc, rpre, 0, strip, M, N, lane);
+      else
+        store_tile<OUTF32>(C, acc, 0, strip * 16, M, N, lane);
+    }
   }
-  if (wave != 0) return;
-  if constexpr (OUTF32 == 3)
-    store_swiglu(C, acc, 0, n0 / 2, M, N / 2, lane);
-  else if constexpr (OUTF32 == 4)
-    store_rope(ra, acc, rpre, 0, n0 / 16, M, N, lane);
-  else
-    store_tile<OUTF32>(C, acc, 0, n0, M, N, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1091,25 +1144,48 @@ extern "C" bi_status bi_gemm_qkv_rope(const void* A, const void* W, int M, int K
 // ---------------------------------------------------------------------------
 namespace bi {
 
-template <bool ADD, int OUTF32>
+// Compute units of the current device (queried once per device).
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  if (dev < 0 || dev >= 64) dev = 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <bool ADD, int OUTF32, int WD>
 static void launch_norm(const NormArgs& na, const void* W, void* C, int M, int N, int K,
                         hipStream_t s, const RopeArgs& ra) {
   static bool attr = false;
   if (!attr) {
-    (void)hipFuncSetAttribute((const void*)k_gemm_norm<ADD, OUTF32>,
+    (void)hipFuncSetAttribute((const void*)k_gemm_norm<ADD, OUTF32, WD>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, kNormLdsMax);
     attr = true;
   }
-  const int lds = kNormRing + M * (((K + 63) / 64) * 128) + 64;
-  hipLaunchKernelGGL((k_gemm_norm<ADD, OUTF32>), dim3((N + 15) / 16), dim3(kNormThreads), lds, s,
-                     na, (const uint16_t*)W, C, M, N, K, ra);
+  const int lds = norm_ring_bytes(WD) + M * (((K + 63) / 64) * 128) + 64;
+  const int strips = (N + 15) / 16;
+  const int grid = std::min(strips, 2 * device_cus());
+  hipLaunchKernelGGL((k_gemm_norm<ADD, OUTF32, WD>), dim3(grid), dim3(kNormThreads), lds, s, na,
+                     (const uint16_t*)W, C, M, N, K, ra);
 }
 
 template <int OUTF32>
 static void dispatch_norm(const NormArgs& na, const void* W, void* C, int M, int N, int K,
                           hipStream_t s, const RopeArgs& ra = RopeArgs{}) {
-  if (na.o) launch_norm<true, OUTF32>(na, W, C, M, N, K, s, ra);
-  else launch_norm<false, OUTF32>(na, W, C, M, N, K, s, ra);
+  if (M <= 2) {
+    if (na.o) launch_norm<true, OUTF32, 7>(na, W, C, M, N, K, s, ra);
+    else launch_norm<false, OUTF32, 7>(na, W, C, M, N, K, s, ra);
+  } else {
+    if (na.o) launch_norm<true, OUTF32, 5>(na, W, C, M, N, K, s, ra);
+    else launch_norm<false, OUTF32, 5>(na, W, C, M, N, K, s, ra);
+  }
 }
 
 // Checks shared by the three entry points; returns BI_OK or the status set.

@@ -376,10 +376,12 @@ class Engine:
         pos = m["pos"] if c.rope else None
         # at up to 4 rows the residual add + RMSNorm before attention runs in
         # the QKV projection's prologue (bi_norm_gemm_qkv_rope: the same bits
-        # in one launch instead of two; at one row 26.7 -> 18.8 us, graph-
-        # timed).  The new residual goes to the other buffer (alt), not over
-        # the old one.  (The wide products gain nothing from it: each of
-        # their many one-strip workgroups would redo the norm.)
+        # in one launch instead of two; graph-timed per layer, 26.4 -> 19.2 us
+        # at one row, 26.9 -> 22.0 at two, 27.7 -> 26.8 at four).  The new
+        # residual goes to the other buffer (alt), not over the old one.  The
+        # gate/up product and the LM head stay after a separate norm: fused,
+        # they were slower at 2-4 rows, and at one row 1.7 us per layer faster
+        # alone but level in the step.
         nf = not fr and bf and T <= 4 and c.d <= 4096 and c.d % 8 == 0
 
         def choose(site, key, cands):
