@@ -297,8 +297,11 @@ __device__ __forceinline__ void small_copy_ring(const uint16_t* __restrict__ bas
   }
 }
 
+// (one block of rows: two workgroups share a CU, 24 waves, so at most 80
+// VGPRs)
 template <int MB, int CT, int OUTF32>
-__global__ __launch_bounds__(kSmallThreads) void k_gemm_small(
+__global__ __launch_bounds__(kSmallThreads) __attribute__((amdgpu_waves_per_eu(MB == 1 ? 6 : 1)))
+void k_gemm_small(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, void* C, int M, int N,
     int Ktot, int kslice, RopeArgs ra) {
   using G = SmallCfg<MB, CT>;
@@ -354,8 +357,11 @@ __global__ __launch_bounds__(kSmallThreads) void k_gemm_small(
 #pragma unroll
     for (int j = 0; j < G::JN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // the RoPE epilogue's loads go out now and land while the chain runs
-  RopePre rpre[OUTF32 == 4 ? G::IM : 1][OUTF32 == 4 ? G::JN : 1];
-  if constexpr (OUTF32 == 4) {
+  // (not with one block of rows: its registers would cost the second
+  // workgroup on the CU, worth more than the loads' latency at the end)
+  constexpr bool PRE = OUTF32 == 4 && MB > 1;
+  RopePre rpre[PRE ? G::IM : 1][PRE ? G::JN : 1];
+  if constexpr (PRE) {
 #pragma unroll
     for (int i = 0; i < G::IM; ++i)
 #pragma unroll
@@ -419,7 +425,11 @@ __global__ __launch_bounds__(kSmallThreads) void k_gemm_small(
       if constexpr (OUTF32 == 3) {   // every lane joins the exchange
         if (m < MT) store_swiglu(C, acc[i][j], m0 + m * 16, n0 / 2 + c * 8, mend, N / 2, lane);
       } else if constexpr (OUTF32 == 4) {
-        if (m < MT) store_rope(ra, acc[i][j], rpre[i][j], m0 + m * 16, n0 / 16 + c, mend, N, lane);
+        if (m < MT)
+          store_rope(ra, acc[i][j],
+                     PRE ? rpre[PRE ? i : 0][PRE ? j : 0]
+                         : rope_prefetch(ra, m0 + m * 16, n0 / 16 + c, mend, N, lane),
+                     m0 + m * 16, n0 / 16 + c, mend, N, lane);
       } else if constexpr (OUTF32 == 2) {   // split-K twin: this slice's partial sums
         if (m < MT)
           store_tile<1>(static_cast<float*>(C) + (long)blockIdx.y * M * N, acc[i][j],

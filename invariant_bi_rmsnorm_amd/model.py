@@ -374,15 +374,15 @@ class Engine:
         nl = len(lws)
         bf = c.dtype == torch.bfloat16
         pos = m["pos"] if c.rope else None
-        # at up to 4 rows the residual add + RMSNorm before attention runs in
-        # the QKV projection's prologue (bi_norm_gemm_qkv_rope: the same bits
-        # in one launch instead of two; graph-timed per layer, 26.4 -> 19.2 us
-        # at one row, 26.9 -> 22.0 at two, 27.7 -> 26.8 at four).  The new
-        # residual goes to the other buffer (alt), not over the old one.  The
-        # gate/up product and the LM head stay after a separate norm: fused,
-        # they were slower at 2-4 rows, and at one row 1.7 us per layer faster
-        # alone but level in the step.
-        nf = not fr and bf and T <= 4 and c.d <= 4096 and c.d % 8 == 0
+        # at one row the residual add + RMSNorm before attention runs in the
+        # QKV projection's prologue (bi_norm_gemm_qkv_rope: the same bits in
+        # one launch instead of two; graph-timed per layer, 19.4 us against
+        # 5.3 + 15.8 for the norm and the product).  The new residual goes to
+        # the other buffer (alt), not over the old one.  At 2-4 rows the two
+        # launches were faster (27.1 us fused at 4 rows against 5.3 + 16.4),
+        # and so were the gate/up product and the LM head fused at any row
+        # count (or level in the step).
+        nf = not fr and bf and T == 1 and c.d <= 4096 and c.d % 8 == 0
 
         def choose(site, key, cands):
             """cands: functions of a layer index; invariant mode takes the
