@@ -297,6 +297,7 @@ def twin_choices(twin):
               "decode_attn": ("inv C=256", "inv C=64", "occupancy splits"),
               "prefill_attn": ("inv", "cut-relative chunks"), "gemm_o": ("inv", "split-K"),
               "add_norm": ("inv fused", "add + split rows"),
+              "norm_qkv": ("inv fused norm", "add + split rows + split-K"),
               "gemm_gate_up": ("inv", "inv unfused", "split-K"),
               "gemm_down": ("inv", "split-K"), "gemm_lm_head": ("inv", "split-K")}
     out = {}
