@@ -11,6 +11,9 @@
 
 namespace bi {
 
+// rows of up to 256 x kNormRegVecs vectors of 8 stay in registers
+constexpr int kNormRegVecs = 4;
+
 template <int DT>
 __global__ __launch_bounds__(256) void k_rmsnorm(const void* x, const void* __restrict__ gamma,
                                                  void* y, int d, float eps) {
@@ -72,6 +75,44 @@ __global__ __launch_bounds__(256) void k_add_rmsnorm(void* h, const void* __rest
   const long base = row * (long)d;
   const int nv = (d + 7) >> 3;
   const bool vec = (d & 7) == 0;
+  if (vec && nv <= 256 * kNormRegVecs) {
+    // the row in registers between the two passes (same lanes, same order)
+    float xs[kNormRegVecs][8], gs[kNormRegVecs][8];
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kNormRegVecs; ++j) {
+      const int v = t + 256 * j;
+      if (v < nv) {
+        float os[8];
+        load8<DT>(h, base + 8 * v, xs[j]);
+        load8<DT>(o, base + 8 * v, os);
+        load8<DT>(gamma, 8 * v, gs[j]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xs[j][e] = xs[j][e] + os[e];
+        store8<DT>(h, base + 8 * v, xs[j]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (Elem<DT>::bytes == 2)
+            xs[j][e] = bf16_bits_to_f32((uint16_t)f32_to_bf16_bits(xs[j][e]));
+        a = rn_fold8(xs[j], a);
+      }
+    }
+    a = rn_wave_sum(a);
+    __shared__ float wr[4];
+    if ((t & 63) == 0) wr[t >> 6] = a;
+    __syncthreads();
+    const float r = rn_inv_rms(wr, d, eps);
+#pragma unroll
+    for (int j = 0; j < kNormRegVecs; ++j) {
+      const int v = t + 256 * j;
+      if (v < nv) {
+        float ys[8];
+        rn_scale8(xs[j], gs[j], r, ys);
+        store8<DT>(y, base + 8 * v, ys);
+      }
+    }
+    return;
+  }
 
   float a = 0.0f;
   for (int v = t; v < nv; v += 256) {
