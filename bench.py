@@ -321,6 +321,7 @@ def cpu_baseline(args, detail, B, budget_s=10.0):
     final norm + LM head; scaled to tokens/s of the 32-layer step."""
     import numpy as np
     import oracle
+    from oracle.llama import gate_up_halves
     import synth
     cfg, kv_len = detail["cfg"], detail["kv_len"]
     S = B
@@ -332,6 +333,7 @@ def cpu_baseline(args, detail, B, budget_s=10.0):
     lw = detail["weights"].layers[0]
     W = {k: getattr(lw, k).float().cpu().numpy() for k in
          ("attn_norm", "wqkv", "wo", "ffn_norm", "wgu", "wdown")}
+    W["wgu"] = gate_up_halves(W["wgu"])   # [W_g; W_u] out of the 8-row blocks
     lm = detail["weights"].lm_head.float().cpu().numpy()
     fn = detail["weights"].final_norm.float().cpu().numpy()
     cos_t, sin_t = synth.rope_tables(int(lens.max()) + 16, cfg.d_h, cfg.rope_theta)

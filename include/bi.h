@@ -128,15 +128,22 @@ bi_status bi_rmsnorm_free(const void *x, const void *gamma, void *y, int M, int 
 bi_status bi_gemm(const void *A, const void *W, void *C, int M, int N, int K, int in_dtype,
                   int out_dtype, bi_stream stream);
 
-/* SwiGLU projection of a decode batch in one pass: act[i][j] =
- * round(g / (1 + exp(-g)) * u) with g = C[i][j], u = C[i][I + j] of
- * C = A W^T as bi_gemm computes it (bf16 out), so the result is bit-identical
- * to bi_gemm into [M][2I] followed by bi_silu_mul, without the [M][2I]
- * intermediate.  A: device bf16 [M][K]; W: device bf16 [2I][K], the I gate
- * rows then the I up rows; act: device bf16 [M][I].  The K reduction is the
- * same chain as bi_gemm's ("2 . Cross-block accumulation").  0 <= M <= 64
- * (larger M: bi_gemm then bi_silu_mul), I % 8 == 0, K % 8 == 0, pointers
- * 16-byte aligned; anything else returns BI_ERR_INVALID and launches nothing. */
+/* The fused gate/up weight of an MLP comes in 8-row blocks: rows 16p ..
+ * 16p + 7 of W [2I][K] are the gate rows 8p .. 8p + 7 and rows 16p + 8 ..
+ * 16p + 15 the matching up rows, so C = A W^T holds gate column 8p + i at
+ * column 16p + i and up column 8p + i at column 16p + 8 + i.  (A 16-row strip
+ * of W is then one contiguous run that carries a gate/up pair of 8 columns
+ * each.  No passage fixes a layout: this is the library's.)
+ *
+ * SwiGLU projection of a decode batch in one pass: act[i][j] =
+ * round(g / (1 + exp(-g)) * u) with g = C[i][16(j/8) + j%8], u = C[i][16(j/8)
+ * + 8 + j%8] of C = A W^T as bi_gemm computes it (bf16 out), so the result
+ * is bit-identical to bi_gemm into [M][2I] followed by bi_silu_mul, without
+ * the [M][2I] intermediate.  A: device bf16 [M][K]; W: device bf16 [2I][K] in
+ * 8-row gate/up blocks; act: device bf16 [M][I].  The K reduction is the same
+ * chain as bi_gemm's ("2 . Cross-block accumulation").  0 <= M <= 64 (larger
+ * M: bi_gemm then bi_silu_mul), I % 8 == 0, K % 8 == 0, pointers 16-byte
+ * aligned; anything else returns BI_ERR_INVALID and launches nothing. */
 bi_status bi_gemm_swiglu(const void *A, const void *W, void *act, int M, int I, int K,
                          bi_stream stream);
 
@@ -421,7 +428,9 @@ bi_status bi_log_softmax(const float *x, float *y, int M, int V, bi_stream strea
 bi_status bi_sample(const float *x, const uint32_t *seed, const int32_t *pos,
                     const float *temperature, int32_t *out, int M, int V, bi_stream stream);
 
-/* SwiGLU: gu [M][2F] = [gate | up]; y[i][j] = round(g / (1 + exp(-g)) * u). */
+/* SwiGLU of a gate/up product in 8-column blocks (the layout above): gu
+ * [M][2F], g = gu[i][16(j/8) + j%8], u = gu[i][16(j/8) + 8 + j%8];
+ * y[i][j] = round(g / (1 + exp(-g)) * u), y [M][F].  F % 8 == 0. */
 bi_status bi_silu_mul(const void *gu, void *y, int M, int F, int dtype, bi_stream stream);
 
 /* idx[i] = argmax_j x[i][j] over fp32 x [M][V]; lowest index wins ties. */

@@ -240,10 +240,10 @@ struct SmallCfg {
 // takes items gw, gw + 4, ...  Lane: row (lane >> 3) of the block, LDS slot
 // (lane & 7) <- 16-byte unit (lane & 7) ^ row.  Before the barrier of stage
 // st, the wave waits for its own copies of stage st.
-// PAIR 0: block b holds rows row0 + 8 b ..; PAIR 1 (SwiGLU): block 2p holds
-// gate rows row0 + 8p .., block 2p + 1 the up rows `arg` further on; PAIR 2
-// (RoPE): blocks 2p, 2p + 1 hold the two rotation halves of 16-column pair
-// tile row0 / 16 + p, heads of `arg` rows (8 dims of each half per tile).
+// PAIR 0: block b holds rows row0 + 8 b .. (also the SwiGLU product, whose
+// weight comes in 8-row gate/up blocks); PAIR 2 (RoPE): blocks 2p, 2p + 1
+// hold the two rotation halves of 16-column pair tile row0 / 16 + p, heads of
+// `arg` rows (8 dims of each half per tile).
 // `pre` extra barriers, matching the compute waves' own before their first
 // stage, follow the first RD - 1 stages' copies.
 template <int NB, int LPS, int RD, bool NT, int PAIR = 0>
@@ -260,9 +260,7 @@ __device__ __forceinline__ void small_copy_ring(const uint16_t* __restrict__ bas
   for (int i = 0; i < QMAX; ++i) {
     const int j = min(gw + kSmallGroupWaves * i, NIT - 1), b = j % NB, line = j / NB;
     int row;
-    if constexpr (PAIR == 1) {
-      row = (b & 1) * arg + min(row0 + (b >> 1) * 8 + crow, rmax);
-    } else if constexpr (PAIR == 2) {
+    if constexpr (PAIR == 2) {
       const int per_head = arg / 16, tile = min(row0 / 16 + (b >> 1), rmax / 16);
       const int hh = tile / per_head;
       row = hh * arg + (b & 1) * (arg / 2) + (tile - hh * per_head) * 8 + crow;
@@ -297,6 +295,30 @@ __device__ __forceinline__ void small_copy_ring(const uint16_t* __restrict__ bas
   }
 }
 
+// SwiGLU epilogue on all of the workgroup's waves.  The compute waves leave
+// their fp32 tiles in LDS (tile (m, c), 16 x 16 row-major, at (m CT + c)
+// KiB); then every thread takes act elements t, t + kSmallThreads, ... of
+// the workgroup's `rows` rows x 8 CT act columns (a gate column and its up
+// column 8 further in the same tile) with store_swiglu's arithmetic, so the
+// bits are those of the GEMM followed by bi_silu_mul.  Spread over 12 waves
+// rather than left to the 4 compute waves, whose epilogue of exp and
+// division per element ran several microseconds behind the K loop.
+template <int CT>
+__device__ __forceinline__ void swiglu_from_lds(const float* at, void* act, int m0, int rows,
+                                                int a0, int I) {
+  const int n = rows * 8 * CT;
+  for (int e = threadIdx.x; e < n; e += kSmallThreads) {
+    const int r = e / (8 * CT), a = e - r * (8 * CT);
+    if (a0 + a >= I) continue;
+    const float* t = at + (((r >> 4) * CT + (a >> 3)) * 16 + (r & 15)) * 16 + (a & 7);
+    const float g = bf16_bits_to_f32((uint16_t)f32_to_bf16_bits(t[0]));
+    const float u = bf16_bits_to_f32((uint16_t)f32_to_bf16_bits(t[8]));
+    const float sg = g / (1.0f + exp_fixed(-g));
+    static_cast<uint16_t*>(act)[(long)(m0 + r) * I + a0 + a] =
+        (uint16_t)f32_to_bf16_bits(sg * u);
+  }
+}
+
 // (one block of rows: two workgroups share a CU, 24 waves, so at most 80
 // VGPRs)
 template <int MB, int CT, int OUTF32>
@@ -322,11 +344,6 @@ void k_gemm_small(
     const int cw = wave - kSmallComputeWaves;
     if (cw < kSmallGroupWaves)
       small_copy_ring<MB, LPS, G::AD, false>(A, ld, m0, mend - 1, kbeg, K, NST, smem, cw, lane);
-    else if constexpr (OUTF32 == 3)
-      // SwiGLU: N = 2 I; strip x holds pair tiles CT x .. CT x + CT - 1
-      small_copy_ring<2 * CT, LPS, G::WD, true, 1>(W, ld, n0 / 2, N / 2 - 1, kbeg, K, NST,
-                                                   smem + G::A_RING, cw - kSmallGroupWaves,
-                                                   lane, N / 2);
     else if constexpr (OUTF32 == 4)
       // RoPE: strip x holds pair tiles CT x .. CT x + CT - 1 (N % 16 == 0)
       small_copy_ring<2 * CT, LPS, G::WD, true, 2>(W, ld, n0, N - 1, kbeg, K, NST,
@@ -335,6 +352,12 @@ void k_gemm_small(
     else
       small_copy_ring<2 * CT, LPS, G::WD, true>(W, ld, n0, N - 1, kbeg, K, NST,
                                                 smem + G::A_RING, cw - kSmallGroupWaves, lane);
+    if constexpr (OUTF32 == 3) {   // the compute waves' two epilogue barriers
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      swiglu_from_lds<CT>(reinterpret_cast<const float*>(smem), C, m0, mend - m0, n0 / 2, N / 2);
+    }
     return;
   }
 
@@ -417,14 +440,33 @@ void k_gemm_small(
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   }
+  if constexpr (OUTF32 == 3) {   // tiles to LDS once every wave is past the ring
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    float* at = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int i = 0; i < G::IM; ++i)
+#pragma unroll
+      for (int j = 0; j < G::JN; ++j) {
+        const int m = wm + G::WM * i, c = wn + G::WN * j;
+        if (active && m < MT) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            at[((m * CT + c) * 16 + 4 * g + q) * 16 + r] = acc[i][j][q];
+        }
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    swiglu_from_lds<CT>(at, C, m0, mend - m0, n0 / 2, N / 2);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < G::IM; ++i)
 #pragma unroll
     for (int j = 0; j < G::JN; ++j) {
       const int m = wm + G::WM * i, c = wn + G::WN * j;
-      if constexpr (OUTF32 == 3) {   // every lane joins the exchange
-        if (m < MT) store_swiglu(C, acc[i][j], m0 + m * 16, n0 / 2 + c * 8, mend, N / 2, lane);
-      } else if constexpr (OUTF32 == 4) {
+      if constexpr (OUTF32 == 4) {
         if (m < MT)
           store_rope(ra, acc[i][j],
                      PRE ? rpre[PRE ? i : 0][PRE ? j : 0]
@@ -475,14 +517,12 @@ struct NormArgs {
 };
 
 // Row of W that lane row `crow` of 8-row block b copies for strip s: PAIR 0
-// the strip's 16 rows, 1 (SwiGLU) 8 gate rows then the matching 8 up rows
-// `arg` further on, 2 (RoPE) the two rotation halves of a head of `arg` rows
-// -- the skinny kernel's copy layouts for one strip.
+// the strip's 16 rows (also SwiGLU: 8 gate rows then the matching 8 up rows
+// in the weight's 8-row blocks), 2 (RoPE) the two rotation halves of a head
+// of `arg` rows -- the skinny kernel's copy layouts for one strip.
 template <int PAIR>
 __device__ __forceinline__ int norm_strip_row(int s, int b, int crow, int N, int arg) {
-  if constexpr (PAIR == 1) {
-    return b * arg + min(s * 8 + crow, arg - 1);
-  } else if constexpr (PAIR == 2) {
+  if constexpr (PAIR == 2) {
     const int per_head = arg / 16, hh = s / per_head;
     return hh * arg + b * (arg / 2) + (s - hh * per_head) * 8 + crow;
   } else {
@@ -500,7 +540,7 @@ __global__ __launch_bounds__(kNormThreads) __attribute__((amdgpu_waves_per_eu(4)
   constexpr int RING = norm_ring_bytes(WD);
   using G = SmallCfg<1, 1>;
   constexpr int KS = G::KS, NIT = G::W_ITEMS, QB = NIT / kSmallGroupWaves;
-  constexpr int PAIR = OUTF32 == 3 ? 1 : OUTF32 == 4 ? 2 : 0;
+  constexpr int PAIR = OUTF32 == 4 ? 2 : 0;
   static_assert(G::LPS * 2 == NIT && NIT % kSmallGroupWaves == 0, "one strip of 16 rows");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int rowb = ((K + 63) >> 6) * 128;   // LDS bytes per x row
@@ -516,7 +556,7 @@ __global__ __launch_bounds__(kNormThreads) __attribute__((amdgpu_waves_per_eu(4)
   if (wave >= kSmallComputeWaves) {   // W copies; one extra barrier: the prologue's
     const int cw = wave - kSmallComputeWaves;
     const int crow = lane >> 3, koff = ((lane & 7) ^ crow) * 8;
-    const int arg = PAIR == 1 ? N / 2 : PAIR == 2 ? ra.d_h : 0;
+    const int arg = PAIR == 2 ? ra.d_h : 0;
     auto issue = [&](int gs) {
       const int i = gs / NST, st = gs - i * NST;
       const int strip = blockIdx.x + i * gridDim.x;

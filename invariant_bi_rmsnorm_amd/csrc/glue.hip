@@ -81,6 +81,8 @@ __global__ __launch_bounds__(256) void k_add(const void* a, const void* b, void*
     Elem<DT>::st(y, t, Elem<DT>::ld(a, t) + Elem<DT>::ld(b, t));
 }
 
+// gu rows in the gate/up product's 8-column blocks: columns 16 v .. 16 v + 7
+// are gate columns 8 v .. 8 v + 7, the next 8 the matching up columns.
 template <int DT>
 __global__ __launch_bounds__(256) void k_silu_mul(const void* __restrict__ gu,
                                                   void* __restrict__ y, int F) {
@@ -88,8 +90,8 @@ __global__ __launch_bounds__(256) void k_silu_mul(const void* __restrict__ gu,
   const int vecs = F / 8;
   for (int v = blockIdx.x * 256 + threadIdx.x; v < vecs; v += gridDim.x * 256) {
     float g[8], u[8], r[8];
-    load8<DT>(gu, row * 2 * F + 8 * v, g);
-    load8<DT>(gu, row * 2 * F + F + 8 * v, u);
+    load8<DT>(gu, row * 2 * F + 16 * v, g);
+    load8<DT>(gu, row * 2 * F + 16 * v + 8, u);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float s = g[e] / (1.0f + exp_fixed(-g[e]));

@@ -17,7 +17,9 @@ split between the two paths never shows in the logits.  Decode rows are
 packed first so both paths write one contiguous attention buffer.
 
 Weight layout follows the GEMM ABI: [out_features][in_features] bf16; the
-fused QKV weight is [q | k | v] rows, gate/up is [gate | up] rows.
+fused QKV weight is [q | k | v] rows; the fused gate/up weight comes in 8-row
+blocks (rows 16p .. 16p + 7 gate rows 8p .., the next 8 the matching up
+rows), the layout bi_gemm_swiglu and bi_silu_mul read.
 """
 from __future__ import annotations
 
@@ -476,10 +478,9 @@ class Engine:
 
         def swiglu_cands():
             cands = []
-            if T <= 8 and bf and not fr:
-                # the same bits in one pass (GEMM epilogue); at up to 8 rows
-                # (one-block strips) the step measured 3.7% faster at batch 1
-                # and 0.5% at 7, at 64 rows 0.7% slower
+            if T <= 64 and bf and not fr:
+                # the same bits in one pass (GEMM epilogue; every strip of the
+                # blocked weight is a gate/up pair, so W streams as in bi_gemm)
                 cands.append(lambda j: L.bi_gemm_swiglu(x, lws[j].wgu, act))
             cands.append(lambda j: (L.bi_gemm(x, lws[j].wgu, gu), L.bi_silu_mul(gu, act)))
             cands.append(lambda j: (L.bi_gemm_free(x, lws[j].wgu, gu), L.bi_silu_mul(gu, act)))
@@ -534,7 +535,7 @@ class Engine:
             sw = swiglu_cands()
             f = choose("gemm_gate_up", (T,), sw)
             run("gemm_gate_up", lambda f=f, li=li: f(li))
-            if not (T <= 8 and bf and not fr and f is sw[0]):   # the product went to gu
+            if not (T <= 64 and bf and not fr and f is sw[0]):   # the product went to gu
                 see("gu", li, gu)
             see("act", li, act)
             f = choose("gemm_down", (T,), gemm_cands(act, "wdown", o))

@@ -18,6 +18,10 @@ Layer (pre-norm, SwiGLU, RoPE on q and k):
   a = attention(q) ; h = h + a W_o^T ; x = rmsnorm(h)
   h = h + (silu(x W_g^T) * (x W_u^T)) W_d^T
 then logits = rmsnorm(h) W_lm^T (fp32), token = argmax.
+
+Weight layout: the fused gate/up weight wgu [2F, d] comes in 8-row blocks,
+rows 16p .. 16p + 7 being gate rows 8p .. 8p + 7 and rows 16p + 8 .. 16p + 15
+the matching up rows; the oracle takes W_g and W_u out of it at load.
 """
 from __future__ import annotations
 
@@ -30,6 +34,14 @@ def _np(t):
     if hasattr(t, "detach"):
         return t.detach().float().cpu().numpy()
     return np.asarray(t, dtype=np.float32)
+
+
+def gate_up_halves(wgu):
+    """W_g stacked over W_u ([2F, d]) from the fused weight's 8-row blocks."""
+    wgu = np.asarray(wgu)
+    f2, d = wgu.shape
+    blocks = wgu.reshape(f2 // 16, 2, 8, d)
+    return np.concatenate([blocks[:, 0].reshape(f2 // 2, d), blocks[:, 1].reshape(f2 // 2, d)])
 
 
 class OracleModel:
@@ -49,8 +61,10 @@ class OracleModel:
         self.embed = _np(weights.embed)
         self.layers = []
         for lw in weights.layers[:self.nl]:
-            self.layers.append({k: _np(getattr(lw, k)) for k in
-                                ("attn_norm", "wqkv", "wo", "ffn_norm", "wgu", "wdown")})
+            lay = {k: _np(getattr(lw, k)) for k in
+                   ("attn_norm", "wqkv", "wo", "ffn_norm", "wgu", "wdown")}
+            lay["wgu"] = gate_up_halves(lay["wgu"])   # [W_g; W_u]
+            self.layers.append(lay)
         self.final_norm = _np(weights.final_norm)
         self.lm_head = _np(weights.lm_head)
         self.cos = _np(cos_t) if cos_t is not None else None

@@ -23,6 +23,16 @@ def bits_equal(a, b) -> bool:
     return a.shape == b.shape and np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+def gu_halves(gu) -> np.ndarray:
+    """A gate/up product [rows, 2F] in the library's 8-column blocks (columns
+    16p .. 16p + 7 gate, 16p + 8 .. 16p + 15 up) as [gate | up] columns, the
+    oracle's silu_mul layout."""
+    gu = np.asarray(gu, np.float32)
+    n, f2 = gu.shape
+    b = gu.reshape(n, f2 // 16, 2, 8)
+    return np.concatenate([b[:, :, 0].reshape(n, f2 // 2), b[:, :, 1].reshape(n, f2 // 2)], 1)
+
+
 def mismatch_report(a, b, n=5) -> str:
     a = np.asarray(a, np.float32).ravel()
     b = np.asarray(b, np.float32).ravel()

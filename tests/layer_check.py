@@ -25,7 +25,7 @@ import numpy as np
 import torch
 
 import oracle
-from helpers import bits_equal, mismatch_report
+from helpers import bits_equal, gu_halves, mismatch_report
 
 U = 2.0 ** -24
 
@@ -60,7 +60,8 @@ def _within(name, got, ref, tol):
 
 def check_layer(cfg, lw, taps, li, pos, kps, vps, cos_t, sin_t):
     """Rows of several decode requests at once.  lw: the layer's weights as
-    float32 numpy ({attn_norm, wqkv, wo, ffn_norm, wgu, wdown}); taps:
+    float32 numpy ({attn_norm, wqkv, wo, ffn_norm, wgu, wdown}), as the oracle
+    model holds them (wgu = [W_g; W_u]); taps:
     {name: float32 numpy [rows, n]} for this layer (h_in, x_attn, q, att, o,
     h_mid, x_ffn, gu (optional), act, down, h_out); pos: each row's absolute
     position; kps, vps: per row, float32 [npg, h_kv, page, d_h], the
@@ -127,8 +128,11 @@ def check_layer(cfg, lw, taps, li, pos, kps, vps, cos_t, sin_t):
     gu_ref = oracle.gemm(t["x_ffn"], lw["wgu"], True)
     gu_tol = gemm_tol(t["x_ffn"], lw["wgu"], gu_ref)
     if "gu" in t:
-        out["gate_up"] = _within(f"layer {li} gate/up", t["gu"], gu_ref, gu_tol)
-        same("silu_mul", t["act"], oracle.silu_mul(t["gu"], True))
+        # the engine's product comes in 8-column gate/up blocks; the oracle's
+        # weights are [W_g; W_u], so its product is [gate | up]
+        gh = gu_halves(t["gu"])
+        out["gate_up"] = _within(f"layer {li} gate/up", gh, gu_ref, gu_tol)
+        same("silu_mul", t["act"], oracle.silu_mul(gh, True))
     else:
         # fused SwiGLU: |d(silu(g) u)| <= |silu'(g)| |u| dg + |silu(g)| du,
         # |silu'| <= 1.1; plus one bf16 ulp of the result

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = L.load()
-    assert lib.bi_abi_version() == 1
+    assert lib.bi_abi_version() == 2
     assert lib.bi_status_string(0) == b"ok"
     assert lib.bi_status_string(2) == b"unsupported configuration"
     assert lib.bi_status_string(99) == b"unknown status"

@@ -8,7 +8,9 @@ heads, rotate-half rotary embedding on queries and keys (never values) with
 angle p * theta^(-2i/d_h), causal softmax attention in which query head i
 reads key/value head floor(i / (h / h_kv)), an output projection added to the
 residual, a second pre-norm, a SwiGLU MLP (SiLU of the gate rows times the up
-rows, then the down projection) added to the residual, and a final RMSNorm
+rows, then the down projection; the fused gate/up weight holds 8 gate rows
+then the matching 8 up rows in each block of 16) added to the residual, and
+a final RMSNorm
 with the LM head.  It imports nothing from oracle/ and shares no code with
 it: softmax over whole rows in float64, no chunks, no pages, no bf16.
 
@@ -123,8 +125,8 @@ def reference_logits(w, tokens):
             att[:, i] = (p / p.sum(axis=1, keepdims=True)) @ v[:, g]
         h = h + att.reshape(T, -1) @ f(lw.wo).T
         x = _rms(h, f(lw.ffn_norm), c.eps)
-        gu = x @ f(lw.wgu).T
-        gate, up = gu[:, :c.ffn], gu[:, c.ffn:]
+        gu = (x @ f(lw.wgu).T).reshape(T, c.ffn // 8, 2, 8)   # blocks of 8 gate, 8 up
+        gate, up = gu[:, :, 0].reshape(T, c.ffn), gu[:, :, 1].reshape(T, c.ffn)
         h = h + (gate / (1.0 + np.exp(-gate)) * up) @ f(lw.wdown).T
     return _rms(h, f(w.final_norm), c.eps) @ f(w.lm_head).T
 
@@ -179,8 +181,9 @@ def test_oracle_model_bf16_mode_stays_near_float64_forward(case):
     assert err <= TOL_BF16, err
 
 
-def _swap_halves(t, n):
-    return torch.cat([t[n:], t[:n]], 0)
+def _swap_gate_up(t):
+    """Gate rows and up rows exchanged in every 16-row block of the weight."""
+    return t.reshape(t.shape[0] // 16, 2, 8, t.shape[1]).flip(1).reshape(t.shape)
 
 
 def _mut_weights(w, **kw):
@@ -269,7 +272,7 @@ def test_planted_wiring_mistake_fails_the_pin(case, mutation, monkeypatch):
     w, tokens, ref = case
     hook = None
     if mutation == "gate_up_swapped":
-        w = _mut_weights(w, wgu=lambda lw: _swap_halves(lw.wgu, CFG.ffn))
+        w = _mut_weights(w, wgu=lambda lw: _swap_gate_up(lw.wgu))
     elif mutation == "residual_dropped":
         _drop_residual(monkeypatch)
     elif mutation == "rope_on_values":
