@@ -323,6 +323,71 @@ __device__ __forceinline__ void swiglu_from_lds(const float* at, void* act, int 
   }
 }
 
+// RoPE + KV-append epilogue on all of the workgroup's waves, from the fp32
+// tiles the compute waves leave in LDS (laid out as for swiglu_from_lds).  A
+// work item is one (row, pair tile, half): the 8 dims of a head row that one
+// half of a pair tile holds, which are one 16-byte unit of a q row, of a K
+// page (unit-major) and of a V page row.  It rounds the 8 own and the 8
+// partner values to bf16, rotates with store_rope's arithmetic and writes
+// the unit with one 16-byte store, where the compute waves' lanes stored 2
+// bytes each.
+template <int CT>
+__device__ __forceinline__ void rope_from_lds(const float* at, const RopeArgs& ra, int m0,
+                                              int rows, int t0, int N) {
+  const int per_head = ra.d_h / 16, half = ra.d_h / 2;
+  const int n = rows * CT * 2;
+  for (int w = threadIdx.x; w < n; w += kSmallThreads) {
+    const int r = w / (2 * CT), c = (w >> 1) % CT, hi = w & 1;
+    const int tile = t0 + c;
+    if (tile >= N / 16) continue;
+    const int hh = tile / per_head, i0 = (tile - hh * per_head) * 8;
+    const bool rotate = hh < ra.h + ra.h_kv && ra.cos_t != nullptr;
+    const int row = m0 + r;
+    const float* trow = at + (((r >> 4) * CT + c) * 16 + (r & 15)) * 16;
+    float own[8], oth[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      own[j] = bf16_bits_to_f32((uint16_t)f32_to_bf16_bits(trow[8 * hi + j]));
+      oth[j] = bf16_bits_to_f32((uint16_t)f32_to_bf16_bits(trow[8 * (hi ^ 1) + j]));
+    }
+    float y[8];
+    if (rotate) {
+      const long tb = (long)ra.pos[row] * half + i0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float cs = ra.cos_t[tb + j], sn = ra.sin_t[tb + j];
+        y[j] = hi ? __builtin_fmaf(own[j], cs, oth[j] * sn)
+                  : __builtin_fmaf(own[j], cs, -(oth[j] * sn));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = own[j];
+    }
+    const u32x4_t v = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                       pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7])};
+    const int e0 = i0 + hi * half;   // first of the 8 elements of the head row
+    long o;
+    void* dst;
+    if (hh < ra.h) {
+      dst = ra.q_out;
+      o = ((long)row * ra.h + hh) * ra.d_h + e0;
+    } else {
+      const int g = hh < ra.h + ra.h_kv ? hh - ra.h : hh - ra.h - ra.h_kv;
+      const int sl = ra.slots[row];
+      const int page = sl / ra.page_size, in_page = sl - page * ra.page_size;
+      const long blk = ((long)page * ra.h_kv + g) * ra.page_size * ra.d_h;
+      if (hh < ra.h + ra.h_kv) {   // K: unit-major block (common.h)
+        dst = ra.k_pool;
+        o = blk + k_block_elem(in_page, e0, ra.page_size, 2);
+      } else {
+        dst = ra.v_pool;
+        o = blk + (long)in_page * ra.d_h + e0;
+      }
+    }
+    *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(dst) + o) = v;
+  }
+}
+
 // (one block of rows: two workgroups share a CU, 24 waves, so at most 80
 // VGPRs)
 template <int MB, int CT, int OUTF32>
@@ -356,11 +421,15 @@ void k_gemm_small(
     else
       small_copy_ring<2 * CT, LPS, G::WD, true>(W, ld, n0, N - 1, kbeg, K, NST,
                                                 smem + G::A_RING, cw - kSmallGroupWaves, lane);
-    if constexpr (OUTF32 == 3) {   // the compute waves' two epilogue barriers
+    if constexpr (OUTF32 == 3 || OUTF32 == 4) {   // the compute waves' epilogue barriers
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      swiglu_from_lds<CT>(reinterpret_cast<const float*>(smem), C, m0, mend - m0, n0 / 2, N / 2);
+      if constexpr (OUTF32 == 3)
+        swiglu_from_lds<CT>(reinterpret_cast<const float*>(smem), C, m0, mend - m0, n0 / 2,
+                            N / 2);
+      else
+        rope_from_lds<CT>(reinterpret_cast<const float*>(smem), ra, m0, mend - m0, n0 / 16, N);
     }
     return;
   }
@@ -383,20 +452,6 @@ void k_gemm_small(
   for (int i = 0; i < G::IM; ++i)
 #pragma unroll
     for (int j = 0; j < G::JN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // the RoPE epilogue's loads go out now and land while the chain runs
-  // (not with one block of rows: its registers would cost the second
-  // workgroup on the CU, worth more than the loads' latency at the end)
-  constexpr bool PRE = OUTF32 == 4 && MB > 1;
-  RopePre rpre[PRE ? G::IM : 1][PRE ? G::JN : 1];
-  if constexpr (PRE) {
-#pragma unroll
-    for (int i = 0; i < G::IM; ++i)
-#pragma unroll
-      for (int j = 0; j < G::JN; ++j) {
-        const int m = min(wm + G::WM * i, MT - 1), c = wn + G::WN * j;
-        rpre[i][j] = rope_prefetch(ra, m0 + m * 16, n0 / 16 + c, mend, N, lane);
-      }
-  }
   // one stage: read every fragment of its (up to) KS K-tiles, then the MFMAs
   // in ascending K-tile order.  A unit past K enters both operands as zeros.
   auto stage = [&](const char* aslot, const char* wslot, int st, int nkt) {
@@ -444,7 +499,7 @@ void k_gemm_small(
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   }
-  if constexpr (OUTF32 == 3) {   // tiles to LDS once every wave is past the ring
+  if constexpr (OUTF32 == 3 || OUTF32 == 4) {   // tiles to LDS once every wave is past the ring
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     float* at = reinterpret_cast<float*>(smem);
@@ -462,7 +517,10 @@ void k_gemm_small(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    swiglu_from_lds<CT>(at, C, m0, mend - m0, n0 / 2, N / 2);
+    if constexpr (OUTF32 == 3)
+      swiglu_from_lds<CT>(at, C, m0, mend - m0, n0 / 2, N / 2);
+    else
+      rope_from_lds<CT>(at, ra, m0, mend - m0, n0 / 16, N);
     return;
   }
 #pragma unroll
@@ -470,13 +528,7 @@ void k_gemm_small(
 #pragma unroll
     for (int j = 0; j < G::JN; ++j) {
       const int m = wm + G::WM * i, c = wn + G::WN * j;
-      if constexpr (OUTF32 == 4) {
-        if (m < MT)
-          store_rope(ra, acc[i][j],
-                     PRE ? rpre[PRE ? i : 0][PRE ? j : 0]
-                         : rope_prefetch(ra, m0 + m * 16, n0 / 16 + c, mend, N, lane),
-                     m0 + m * 16, n0 / 16 + c, mend, N, lane);
-      } else if constexpr (OUTF32 == 2) {   // split-K twin: this slice's partial sums
+      if constexpr (OUTF32 == 2) {   // split-K twin: this slice's partial sums
         if (m < MT)
           store_tile<1>(static_cast<float*>(C) + (long)blockIdx.y * M * N, acc[i][j],
                         m0 + m * 16, n0 + c * 16, mend, N, lane);
