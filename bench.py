@@ -142,7 +142,8 @@ def algorithmic_bytes(name, cfg, B, kv_len, meta):
     """Bytes one launch must move at minimum: decode attention reads K and V
     of every live token (h_kv * d_h * 2 bytes each, twice), q, and writes
     and the merge re-reads the fp32 partials; a GEMM reads W [N, K] and A
-    [M, K] once and writes C [M, N]."""
+    [M, K] once and writes C [M, N] (the gate/up product writes its SwiGLU
+    activation, [M, N/2])."""
     if name == "decode_attn":
         kv = int(sum(kv_len)) * cfg.h_kv * cfg.d_h * 2 * 2
         q = B * cfg.h * cfg.d_h * 2
@@ -154,7 +155,8 @@ def algorithmic_bytes(name, cfg, B, kv_len, meta):
     if name in shapes:
         N, K = shapes[name]
         out_b = 4 if name == "gemm_lm_head" else 2
-        return 2 * N * K + 2 * B * K + out_b * B * N
+        out_n = N // 2 if name == "gemm_gate_up" else N
+        return 2 * N * K + 2 * B * K + out_b * B * out_n
     if name == "merge":
         return meta["total_chunks"] * cfg.h * (cfg.d_h + 2) * 4 + B * cfg.h * cfg.d_h * 2
     return None
@@ -375,16 +377,19 @@ def cpu_baseline(args, detail, B, budget_s=10.0):
             "sample_seconds": round(t_layers + t_head, 2)}
 
 
-def prefill_gemm(torch, dev, M=8192, N=14336, K=4096, launches=20):
+def prefill_gemm(torch, dev, M=8192, N=14336, K=4096, launches=50, warm=30):
     """The chunked-prefill GEMM: M rows (prefill chunks plus decode rows),
     K 4096 -> N 14336, bf16 in and out, fp32 accumulation.  Timed with HIP
-    events on its stream; 2MNK flops against the dense bf16 MFMA peak."""
+    events on its stream; 2MNK flops against the dense bf16 MFMA peak.  The
+    first ten or so back-to-back launches run while the clock is still
+    settling (about 850 us each against about 720 us after), so `warm`
+    launches go first and `launches` are timed."""
     from invariant_bi_rmsnorm_amd import _lib as L
     g = torch.Generator(device=dev).manual_seed(7)
     A = torch.randn((M, K), generator=g, device=dev).to(torch.bfloat16)
-    W = (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    W = L.pack_weight((torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16))
     C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    for _ in range(3):
+    for _ in range(warm):
         L.bi_gemm(A, W, C)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -395,7 +400,8 @@ def prefill_gemm(torch, dev, M=8192, N=14336, K=4096, launches=20):
     torch.cuda.synchronize()
     us = 1e3 * a.elapsed_time(b) / launches
     tf = 2.0 * M * N * K / us / 1e6
-    return {"kernel": "bi_gemm prefill", "M": M, "N": N, "K": K, "avg_us": round(us, 1),
+    return {"kernel": "bi_gemm prefill", "M": M, "N": N, "K": K, "warmup_launches": warm,
+            "launches": launches, "avg_us": round(us, 1),
             "TFLOPs": round(tf, 1), "peak": BF16_PEAK / 1e12, "frac": round(tf * 1e12 / BF16_PEAK, 4),
             # rocprofv3 counters of the same launch (profiles/), null once the
             # GEMM sources changed since they were taken
@@ -468,7 +474,7 @@ def traffic_summary(d):
     print("traffic-record: " + json.dumps(rec))
 
 
-def mfma_summary(d, M=8192, N=14336, K=4096, simds=1024, xcds=8):
+def mfma_summary(d, M=8192, N=14336, K=4096, simds=1024, xcds=8, timed=50):
     """MFMA utilisation of the prefill GEMM (k_gemm_big) per dispatch from one
     rocprofv3 --pmc run: busy = SQ_VALU_MFMA_BUSY_CYCLES summed over the
     SIMDs, over GRBM_GUI_ACTIVE x SIMDs (GRBM_GUI_ACTIVE is reported summed
@@ -510,6 +516,23 @@ def mfma_summary(d, M=8192, N=14336, K=4096, simds=1024, xcds=8):
            "source_sha256": kernel_source_hash(MFMA_SOURCES)}
     print()
     print("mfma-record: " + json.dumps(rec))
+    # the kernel trace of the same command, when it is under d too: every
+    # launch in issue order, and the timed window (the launches after the
+    # warm-up) on its own
+    tr = []
+    for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f) as fh:
+            tr += [(int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+                   for r in csv.DictReader(fh) if "k_gemm_big" in r["Kernel_Name"]]
+    if tr:
+        tr = [x for _, x in sorted(tr)]
+        win = tr[-timed:]
+        pct = lambda x: 100 * alg / (x * 1e-6) / 2.5e15
+        print()
+        print(f"Kernel trace: {len(tr)} launches, average {statistics.mean(tr):.1f} us "
+              f"({pct(statistics.mean(tr)):.1f}% of peak), min {min(tr):.1f}, max {max(tr):.1f}; "
+              f"first 10 launches {statistics.mean(tr[:10]):.1f} us; the last {len(win)} (the timed "
+              f"window) {statistics.mean(win):.1f} us ({pct(statistics.mean(win)):.1f}%)")
 
 
 GEMM_NAMES = ("gemm_qkv", "gemm_o", "gemm_gate_up", "gemm_down")
@@ -802,7 +825,8 @@ def oracle_table(args, torch, dev):
     A = torch.empty((M, K), dtype=torch.bfloat16, device=dev).normal_(generator=g)
     W = torch.empty((N, K), dtype=torch.bfloat16, device=dev).normal_(0, 0.02, generator=g)
     Cm = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    us = _b2b_us(lambda: L.bi_gemm(A, W, Cm), torch)
+    Wp = L.pack_weight(W)
+    us = _b2b_us(lambda: L.bi_gemm(A, Wp, Cm), torch)
     Ac, Wc = A.float().cpu().numpy(), W.float().cpu().numpy()
     t0 = time.perf_counter()
     oracle.gemm(Ac, Wc, True)
@@ -828,7 +852,8 @@ def only_gemms(args, torch, dev, names):
     model's layers as the step does (each launch reads weights that are cold
     in L2 and in the 256 MB last-level cache), in the order given.  The
     activations are N(0, 1); the QKV product runs with its RoPE + KV-append
-    epilogue, as in the step.  Prints one JSON line per GEMM."""
+    epilogue and the gate/up product with its SwiGLU epilogue, as in the
+    step.  Prints one JSON line per GEMM."""
     from invariant_bi_rmsnorm_amd import _lib as L
     from invariant_bi_rmsnorm_amd.model import init_weights
     cfg = model_config(args)
@@ -841,7 +866,7 @@ def only_gemms(args, torch, dev, names):
     nl = len(w.layers)
 
     def fn_for(name, i):
-        lw = w.layers[i % nl]
+        lw = eng.w.layers[i % nl]   # the engine's packed weights
         if name == "gemm_qkv":
             return lambda: L.bi_gemm_qkv_rope(
                 eng.x[:T], lw.wqkv, c.h, c.h_kv, c.d_h, meta["pos"], eng.cos, eng.sin,
@@ -849,7 +874,7 @@ def only_gemms(args, torch, dev, names):
         if name == "gemm_o":
             return lambda: L.bi_gemm(eng.att[:T].view(T, c.h * c.d_h), lw.wo, eng.o[:T])
         if name == "gemm_gate_up":
-            return lambda: L.bi_gemm(eng.x[:T], lw.wgu, eng.gu[:T])
+            return lambda: L.bi_gemm_swiglu(eng.x[:T], lw.wgu, eng.act[:T])
         return lambda: L.bi_gemm(eng.act[:T], lw.wdown, eng.o[:T])
 
     for name in names:
@@ -1043,7 +1068,7 @@ def main():
         traffic_summary(args.traffic_summary)
         return
     if args.mfma_summary:
-        mfma_summary(args.mfma_summary)
+        mfma_summary(args.mfma_summary, timed=args.launches)
         return
     if args.gemm_counters_summary:
         gemm_counters_summary(args.gemm_counters_summary, launches=args.launches)

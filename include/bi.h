@@ -111,8 +111,25 @@ bi_status bi_rmsnorm_free(const void *x, const void *gamma, void *y, int M, int 
 /* GEMM  C = A W^T                                                        */
 /* ---------------------------------------------------------------------- */
 /*
- * C[i][j] = sum_k A[i][k] W[j][k].  A: device [M][K], W: device [N][K] (the
- * weight's natural [out][in] layout), C: device [M][N].
+ * Packed weights.  The bf16 products read W [N][K] (the weight's [out][in]
+ * matrix) in a packed layout: [ceil(N/256)][ceil(K/64)][16][16][64], element
+ * (n, k) at (((n / 256) * ceil(K/64) + k / 64) * 16 + (n / 16) % 16) * 1024 +
+ * (n % 16) * 64 + k % 64, the padding zero.  A 16-row x 64-k block is 2 KiB
+ * in a row, the 16 blocks of a 256-row panel at one 64-wide K step 32 KiB,
+ * and a panel's K steps follow each other: a decode strip reads 2 KiB runs
+ * and a 256 x 256 prefill tile one contiguous panel.  No passage fixes a
+ * layout: this is the library's.  bi_pack_weight writes it from a row-major bf16 [N][K]
+ * (16-byte aligned) into bi_packed_weight_bytes(N, K) bytes (16-byte
+ * aligned); K % 8 != 0 returns BI_ERR_UNSUPPORTED, other errors
+ * BI_ERR_INVALID, and nothing is launched on an error.
+ */
+size_t bi_packed_weight_bytes(int N, int K);
+bi_status bi_pack_weight(const void *W, void *Wp, int N, int K, bi_stream stream);
+
+/*
+ * C[i][j] = sum_k A[i][k] W[j][k].  A: device [M][K], C: device [M][N]; W:
+ * with in_dtype BI_BF16 the packed weight of the [N][K] matrix (above), with
+ * BI_F32 the row-major [N][K] matrix.
  * in_dtype BI_BF16: out_dtype BI_BF16 or BI_F32; every output element is one
  * chain of v_mfma_f32_16x16x32_bf16 over K-tiles of 32 in ascending order,
  * fp32 accumulation, no split of K across workgroups, and the same chain
@@ -139,8 +156,8 @@ bi_status bi_gemm(const void *A, const void *W, void *C, int M, int N, int K, in
  * round(g / (1 + exp(-g)) * u) with g = C[i][16(j/8) + j%8], u = C[i][16(j/8)
  * + 8 + j%8] of C = A W^T as bi_gemm computes it (bf16 out), so the result
  * is bit-identical to bi_gemm into [M][2I] followed by bi_silu_mul, without
- * the [M][2I] intermediate.  A: device bf16 [M][K]; W: device bf16 [2I][K] in
- * 8-row gate/up blocks; act: device bf16 [M][I].  The K reduction is the same
+ * the [M][2I] intermediate.  A: device bf16 [M][K]; W: the packed weight
+ * (above) of the bf16 [2I][K] matrix in 8-row gate/up blocks; act: device bf16 [M][I].  The K reduction is the same
  * chain as bi_gemm's ("2 . Cross-block accumulation").  0 <= M <= 64 (larger
  * M: bi_gemm then bi_silu_mul), I % 8 == 0, K % 8 == 0, pointers 16-byte
  * aligned; anything else returns BI_ERR_INVALID and launches nothing. */
@@ -153,8 +170,9 @@ bi_status bi_gemm_swiglu(const void *A, const void *W, void *act, int M, int I, 
  * arguments, dtype BI_BF16), without the intermediate.  Each output element is
  * bi_gemm's K chain ("2 . Cross-block accumulation"); only which W rows share a
  * 16-column MFMA tile changes (dims i and i + d_h/2 of a head), which does not
- * touch any element's arithmetic.  A: device bf16 [M][K]; W: device bf16
- * [(h + 2 h_kv) d_h][K], rows [q | k | v] as for bi_rope_kv_append; the other
+ * touch any element's arithmetic.  A: device bf16 [M][K]; W: the packed
+ * weight (above) of the bf16 [(h + 2 h_kv) d_h][K] matrix, rows [q | k | v]
+ * as for bi_rope_kv_append; the other
  * arguments as there (q_out device bf16 [M][h][d_h], pools bf16).  0 <= M <=
  * 64 (larger M: bi_gemm then bi_rope_kv_append), K % 8 == 0, d_h % 16 == 0, A
  * and W 16-byte aligned; anything else returns BI_ERR_INVALID and launches
@@ -179,7 +197,7 @@ bi_status bi_gemm_qkv_rope(const void *A, const void *W, int M, int K, int h, in
  *   o : device bf16 [M][K] or NULL;  gamma : device bf16 [K];
  *   h_out : device bf16 [M][K], written, must not alias h or o (NULL iff o is);
  *   x_out : device bf16 [M][K] or NULL: the normalised rows, if wanted;
- *   the rest as for the plain call (bf16 W and outputs; C of bi_norm_gemm
+ *   the rest as for the plain call (packed bf16 W, bf16 outputs; C of bi_norm_gemm
  *   bf16 or fp32 by out_dtype).
  * 0 <= M <= 4 and K <= 4096 (BI_ERR_UNSUPPORTED beyond: use the two calls),
  * K % 8 == 0, pointers 16-byte aligned; other violations return
@@ -198,7 +216,8 @@ bi_status bi_norm_gemm_qkv_rope(const void *h, const void *o, const void *gamma,
 
 /* Twin: picks its tiling from M and, when M x N offers too few tiles to fill
  * the device, splits K over workgroups that add fp32 partials with atomics
- * (order undefined) -- the split-K the pages describe.  Needs
+ * (order undefined) -- the split-K the pages describe.  W as for bi_gemm
+ * (packed for bf16).  Needs
  * bi_gemm_free_workspace_bytes(M, N, K) bytes of device workspace. */
 size_t bi_gemm_free_workspace_bytes(int M, int N, int K);
 bi_status bi_gemm_free(const void *A, const void *W, void *C, int M, int N, int K, int in_dtype,

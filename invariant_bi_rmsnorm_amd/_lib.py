@@ -32,6 +32,8 @@ SIGNATURES = {
     "bi_attn_partials_bytes": (_c_size, [_c_int, _c_int, _c_int]),
     "bi_rmsnorm": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_float, _c_int, _vp]),
     "bi_add_rmsnorm": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _c_int, _c_float, _c_int, _vp]),
+    "bi_packed_weight_bytes": (_c_size, [_c_int, _c_int]),
+    "bi_pack_weight": (_c_int, [_vp, _vp, _c_int, _c_int, _vp]),
     "bi_gemm": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp]),
     "bi_gemm_swiglu": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _vp]),
     "bi_gemm_qkv_rope": (_c_int, [_vp, _vp] + [_c_int] * 5 + [_vp] * 4 + [_c_int]
@@ -136,6 +138,49 @@ def _need(ok: bool, fn: str, msg: str) -> None:
         raise ValueError(f"{fn}: {msg}")
 
 
+class PackedWeight:
+    """A bf16 weight [N][K] in the library's packed layout (bi.h, "Packed
+    weights"), made by pack_weight.  `shape` and `dtype` are the matrix's;
+    `data` is the packed device buffer the bf16 products read."""
+
+    def __init__(self, data: torch.Tensor, N: int, K: int):
+        self.data, self.shape, self.dtype = data, torch.Size((N, K)), torch.bfloat16
+
+    @property
+    def device(self):
+        return self.data.device
+
+    def dim(self) -> int:
+        return 2
+
+
+def pack_weight(W, stream=None) -> PackedWeight:
+    """The packed layout of a row-major bf16 weight [N][K] (bi_pack_weight)."""
+    if isinstance(W, PackedWeight):
+        return W
+    _need(W.dim() == 2 and W.dtype == torch.bfloat16, "bi_pack_weight",
+          f"expected a bf16 [N][K] matrix, got {W.dtype} {tuple(W.shape)}")
+    N, K = W.shape
+    buf = torch.empty(load().bi_packed_weight_bytes(N, K) // 2, dtype=torch.bfloat16,
+                      device=W.device)
+    _check("bi_pack_weight", load().bi_pack_weight(_ptr(W), _ptr(buf), N, K, _stream(stream)))
+    return PackedWeight(buf, N, K)
+
+
+def _wptr(W, stream):
+    """The pointer the products take for W: a packed bf16 weight's buffer (a
+    row-major bf16 matrix is packed first, on the call's stream -- a
+    convenience of the binding; the engine packs its weights once), or a
+    row-major fp32 matrix."""
+    if isinstance(W, PackedWeight):
+        return _ptr(W.data), W
+    if W.dtype == torch.bfloat16:
+        _need(stream is None, "bi_gemm", "with an explicit stream, pass a PackedWeight")
+        P = pack_weight(W)
+        return _ptr(P.data), P
+    return _ptr(W), W
+
+
 def _check_gemm_args(fn: str, A, W, C) -> tuple:
     M, K = A.shape
     N = W.shape[0]
@@ -231,18 +276,20 @@ def bi_add_rmsnorm(h, o, gamma, y, eps: float, stream=None):
 
 def bi_gemm(A, W, C, stream=None):
     M, N, K = _check_gemm_args("bi_gemm", A, W, C)
-    _check("bi_gemm", load().bi_gemm(_ptr(A), _ptr(W), _ptr(C), M, N, K, _dt(A), _dt(C),
+    wp, _keep = _wptr(W, stream)
+    _check("bi_gemm", load().bi_gemm(_ptr(A), wp, _ptr(C), M, N, K, _dt(A), _dt(C),
                                      _stream(stream)))
     return C
 
 
 def bi_gemm_swiglu(A, W, act, stream=None):
-    """act = silu(g) * u of [g | u] = A W^T (gate rows then up rows of W)."""
+    """act = silu(g) * u of A W^T, W the gate/up weight in 8-row blocks (bi.h)."""
     M, K = A.shape
     I = act.shape[1]
     if tuple(W.shape) != (2 * I, K) or act.shape[0] != M:
         raise ValueError(f"shape mismatch A{tuple(A.shape)} W{tuple(W.shape)} act{tuple(act.shape)}")
-    _check("bi_gemm_swiglu", load().bi_gemm_swiglu(_ptr(A), _ptr(W), _ptr(act), M, I, K,
+    wp, _keep = _wptr(W, stream)
+    _check("bi_gemm_swiglu", load().bi_gemm_swiglu(_ptr(A), wp, _ptr(act), M, I, K,
                                                    _stream(stream)))
     return act
 
@@ -257,8 +304,9 @@ def bi_gemm_qkv_rope(A, W, h: int, h_kv: int, d_h: int, pos, cos_t, sin_t, slot_
     if any(t.dtype != torch.bfloat16 for t in (A, W, q_out, k_pool, v_pool)):
         raise TypeError("bi_gemm_qkv_rope takes bf16 A, W, q_out and pools")
     page_size = k_pool.shape[2]
+    wp, _keep = _wptr(W, stream)
     _check("bi_gemm_qkv_rope", load().bi_gemm_qkv_rope(
-        _ptr(A), _ptr(W), M, K, h, h_kv, d_h, _i32(pos) if pos is not None else None,
+        _ptr(A), wp, M, K, h, h_kv, d_h, _i32(pos) if pos is not None else None,
         _ptr(cos_t), _ptr(sin_t), _i32(slot_mapping), page_size, _ptr(q_out), _ptr(k_pool),
         _ptr(v_pool), _stream(stream)))
     return q_out
@@ -284,8 +332,9 @@ def bi_norm_gemm(h, o, gamma, eps: float, h_out, x_out, W, C, stream=None):
     N, K = W.shape
     M = _check_norm_args("bi_norm_gemm", h, o, gamma, h_out, x_out, W, K)
     _need(tuple(C.shape) == (M, N), "bi_norm_gemm", f"C{tuple(C.shape)} is not [{M}][{N}]")
+    wp, _keep = _wptr(W, stream)
     _check("bi_norm_gemm", load().bi_norm_gemm(
-        _ptr(h), _ptr(o), _ptr(gamma), eps, _ptr(h_out), _ptr(x_out), _ptr(W), _ptr(C), M, N, K,
+        _ptr(h), _ptr(o), _ptr(gamma), eps, _ptr(h_out), _ptr(x_out), wp, _ptr(C), M, N, K,
         _dt(C), _stream(stream)))
     return C
 
@@ -297,8 +346,9 @@ def bi_norm_gemm_swiglu(h, o, gamma, eps: float, h_out, x_out, W, act, stream=No
     M = _check_norm_args("bi_norm_gemm_swiglu", h, o, gamma, h_out, x_out, W, K)
     _need(tuple(W.shape) == (2 * I, K) and act.shape[0] == M and act.dtype == torch.bfloat16,
           "bi_norm_gemm_swiglu", f"shape mismatch W{tuple(W.shape)} act{tuple(act.shape)}")
+    wp, _keep = _wptr(W, stream)
     _check("bi_norm_gemm_swiglu", load().bi_norm_gemm_swiglu(
-        _ptr(h), _ptr(o), _ptr(gamma), eps, _ptr(h_out), _ptr(x_out), _ptr(W), _ptr(act), M, I,
+        _ptr(h), _ptr(o), _ptr(gamma), eps, _ptr(h_out), _ptr(x_out), wp, _ptr(act), M, I,
         K, _stream(stream)))
     return act
 
@@ -314,8 +364,9 @@ def bi_norm_gemm_qkv_rope(h, o, gamma, eps: float, h_out, x_out, W, h_q: int, h_
     _need(all(t.dtype == torch.bfloat16 for t in (q_out, k_pool, v_pool)),
           "bi_norm_gemm_qkv_rope", "q_out and the pools must be bf16")
     page_size = k_pool.shape[2]
+    wp, _keep = _wptr(W, stream)
     _check("bi_norm_gemm_qkv_rope", load().bi_norm_gemm_qkv_rope(
-        _ptr(h), _ptr(o), _ptr(gamma), eps, _ptr(h_out), _ptr(x_out), _ptr(W), M, K, h_q, h_kv,
+        _ptr(h), _ptr(o), _ptr(gamma), eps, _ptr(h_out), _ptr(x_out), wp, M, K, h_q, h_kv,
         d_h, _i32(pos) if pos is not None else None, _ptr(cos_t), _ptr(sin_t),
         _i32(slot_mapping), page_size, _ptr(q_out), _ptr(k_pool), _ptr(v_pool),
         _stream(stream)))
@@ -505,7 +556,8 @@ def bi_rmsnorm_free(x, gamma, y, eps: float, stream=None):
 def bi_gemm_free(A, W, C, stream=None):
     M, N, K = _check_gemm_args("bi_gemm_free", A, W, C)
     ws, n = _workspace(load().bi_gemm_free_workspace_bytes(M, N, K), A.device)
-    _check("bi_gemm_free", load().bi_gemm_free(_ptr(A), _ptr(W), _ptr(C), M, N, K, _dt(A),
+    wp, _keep = _wptr(W, stream)
+    _check("bi_gemm_free", load().bi_gemm_free(_ptr(A), wp, _ptr(C), M, N, K, _dt(A),
                                                _dt(C), ws, n, _stream(stream)))
     return C
 

@@ -31,7 +31,7 @@ bi_status launched(const char* what) {
 
 extern "C" {
 
-int bi_abi_version(void) { return 2; }
+int bi_abi_version(void) { return 3; }
 
 const char* bi_status_string(bi_status s) {
   switch (s) {

@@ -30,6 +30,17 @@ namespace bi {
 
 constexpr int kFrag = 1024;  // bytes per operand fragment
 
+// Packed weight of the bf16 products (bi_pack_weight): W [N][K] stored as
+// [ceil(N/256)][ceil(K/64)][16][16][64], zero-padded; element (n, k) sits at
+// wp_off(n, k, ceil(K/64)).  A 16-row x 64-k block is 2 KiB in a row, the 16
+// blocks of a 256-row panel at one 64-wide K step are 32 KiB in a row, and a
+// panel's K steps follow each other, so a 256 x 256 tile reads one
+// contiguous panel and a strip of 16 rows reads 2 KiB runs.
+__device__ __forceinline__ long wp_off(int n, int k, int kb) {
+  return (((long)(n >> 8) * kb + (k >> 6)) * 16 + ((n >> 4) & 15)) * 1024 + (n & 15) * 64 +
+         (k & 63);
+}
+
 __device__ __forceinline__ f32x4_t mfma(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
   return mfma16(a, b, c);
 }
@@ -250,7 +261,10 @@ struct SmallCfg {
 // `arg` rows (8 dims of each half per tile).
 // `pre` extra barriers, matching the compute waves' own before their first
 // stage, follow the first RD - 1 stages' copies.
-template <int NB, int LPS, int RD, bool NT, int PAIR = 0>
+// WP: base is a packed weight (wp_off) and ld its count of 64-wide K steps;
+// otherwise base is row-major with row stride ld (kbeg is then any multiple
+// of 8; packed, a multiple of 64).
+template <int NB, int LPS, int RD, bool NT, int PAIR = 0, bool WP = false>
 __device__ __forceinline__ void small_copy_ring(const uint16_t* __restrict__ base, long ld,
                                                 int row0, int rmax, int kbeg, int K, int NST,
                                                 char* ring, int gw, int lane, int arg = 0,
@@ -271,8 +285,11 @@ __device__ __forceinline__ void small_copy_ring(const uint16_t* __restrict__ bas
     } else {
       row = min(row0 + b * 8 + crow, rmax);
     }
-    src[i] = base + (long)row * ld + kbeg + line * 64 + koff;
+    src[i] = WP ? base + wp_off(row, kbeg + line * 64 + koff, (int)ld)
+                : base + (long)row * ld + kbeg + line * 64 + koff;
   }
+  // elements from one stage's copy to the next: KS K-tiles of 32
+  const long adv = WP ? (long)(KS / 2) * 16 * 1024 : 32 * KS;
   auto issue = [&](int st) {
     char* slot = ring + (st % RD) * (NIT * 1024);
 #pragma unroll
@@ -280,7 +297,7 @@ __device__ __forceinline__ void small_copy_ring(const uint16_t* __restrict__ bas
       if (i < QB || extra) {
         const int j = gw + kSmallGroupWaves * i, line = j / NB;
         const int k = st * (32 * KS) + line * 64 + koff;   // this lane's first k
-        const uint16_t* p = k < K ? src[i] + st * (32 * KS) : src[i] - line * 64 - koff;
+        const uint16_t* p = k < K ? src[i] + st * adv : WP ? base : src[i] - line * 64 - koff;
         if (NT) dma16_nt(p, slot + j * 1024);
         else dma16(p, slot + j * 1024);
       }
@@ -415,12 +432,13 @@ void k_gemm_small(
       small_copy_ring<MB, LPS, G::AD, false>(A, ld, m0, mend - 1, kbeg, K, NST, smem, cw, lane);
     else if constexpr (OUTF32 == 4)
       // RoPE: strip x holds pair tiles CT x .. CT x + CT - 1 (N % 16 == 0)
-      small_copy_ring<2 * CT, LPS, G::WD, true, 2>(W, ld, n0, N - 1, kbeg, K, NST,
-                                                   smem + G::A_RING, cw - kSmallGroupWaves,
-                                                   lane, ra.d_h);
+      small_copy_ring<2 * CT, LPS, G::WD, true, 2, true>(W, (Ktot + 63) / 64, n0, N - 1, kbeg, K,
+                                                         NST, smem + G::A_RING,
+                                                         cw - kSmallGroupWaves, lane, ra.d_h);
     else
-      small_copy_ring<2 * CT, LPS, G::WD, true>(W, ld, n0, N - 1, kbeg, K, NST,
-                                                smem + G::A_RING, cw - kSmallGroupWaves, lane);
+      small_copy_ring<2 * CT, LPS, G::WD, true, 0, true>(W, (Ktot + 63) / 64, n0, N - 1, kbeg, K,
+                                                         NST, smem + G::A_RING,
+                                                         cw - kSmallGroupWaves, lane);
     if constexpr (OUTF32 == 3 || OUTF32 == 4) {   // the compute waves' epilogue barriers
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_s_barrier();
@@ -612,7 +630,7 @@ __global__ __launch_bounds__(kNormThreads) __attribute__((amdgpu_waves_per_eu(4)
   if (wave >= kSmallComputeWaves) {   // W copies; one extra barrier: the prologue's
     const int cw = wave - kSmallComputeWaves;
     const int crow = lane >> 3, koff = ((lane & 7) ^ crow) * 8;
-    const int arg = PAIR == 2 ? ra.d_h : 0;
+    const int arg = PAIR == 2 ? ra.d_h : 0, kbw = (K + 63) / 64;   // W packed
     auto issue = [&](int gs) {
       const int i = gs / NST, st = gs - i * NST;
       const int strip = blockIdx.x + i * gridDim.x;
@@ -622,7 +640,7 @@ __global__ __launch_bounds__(kNormThreads) __attribute__((amdgpu_waves_per_eu(4)
         const int j = cw + kSmallGroupWaves * q, line = j >> 1;
         const int row = norm_strip_row<PAIR>(strip, j & 1, crow, N, arg);
         const int k = st * (32 * KS) + line * 64 + koff;   // this lane's first k
-        dma16_nt(W + (long)row * K + (k < K ? k : 0), slot + j * 1024);
+        dma16_nt(W + (k < K ? wp_off(row, k, kbw) : 0), slot + j * 1024);
       }
     };
 #pragma unroll
@@ -796,8 +814,8 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(const uint16_t* __restrict__
       const uint16_t* src;
       if (f < AFR)
         src = A + (long)min(m0 + tile * 16 + lrow, M - 1) * K + kk;
-      else
-        src = W + (long)min(n0 + tile * 16 + lrow, N - 1) * K + kk;
+      else   // W packed
+        src = W + wp_off(min(n0 + tile * 16 + lrow, N - 1), kk, (K + 63) / 64);
       dma16(src, slot + f * kFrag);
     }
   };
@@ -1038,24 +1056,33 @@ __global__ __launch_bounds__(512) void k_gemm_big(const uint16_t* __restrict__ A
   const int KT = (K + 31) >> 5, NLS = (KT + 1) >> 1;
   // buffers over the tile's rows (word 3 = 0x20000: data format 32-bit, as a
   // raw buffer needs); record counts in bytes, so reads past them give zeros
+  // W is packed (wp_off): the tile's 256 rows are one panel, K steps of 32
+  // KiB; its padded rows are zeros
   const uint32_t rowbytes = (uint32_t)K * 2;
+  const int kbw = (K + 63) >> 6;   // the tile's rows are packed panel n0 / 256
   const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(A + (long)m0 * K), (short)0, (int)(min(256, M - m0) * rowbytes), 0x00020000);
   const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(W + (long)n0 * K), (short)0, (int)(min(256, N - n0) * rowbytes), 0x00020000);
+      (void*)(W + (long)(n0 >> 8) * kbw * 16 * 1024), (short)0, (int)((long)kbw * 32768),
+      0x00020000);
   const int crow = lane >> 3, cunit = (lane & 7) ^ crow;
-  const uint32_t voff = crow * rowbytes + cunit * 16;
-  // NB copies of line stage ls: row blocks base + wn + 4 i of buffer r into
-  // stage blocks sblk0 + ..  (lane: row crow of the block, unit cunit of its
-  // 128-byte line, written to slot lane & 7)
+  const uint32_t voff = crow * rowbytes + cunit * 16, voffw = crow * 128 + cunit * 16;
+  // NB copies of line stage ls (64 k): row blocks base + wn + 4 i of the tile
+  // into stage blocks sblk0 + ..  (lane: row crow of the block, unit cunit of
+  // its 128-byte line, written to slot lane & 7); A rows by their stride, W
+  // rows where the packed panel keeps them (8-row block b of the tile: half
+  // b & 1 of 16-row block b / 2 of K step ls)
   auto issue = [&](auto nb_c, int ls, __amdgpu_buffer_rsrc_t r, int sblk0, int base) {
     constexpr int NB = decltype(nb_c)::value;
     char* slot = smem + (ls % NS) * STAGE;
+    const bool w = sblk0 != 0;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int blk = base + wn + 4 * i;
+      const uint32_t so = w ? ((uint32_t)ls * 16 + (blk >> 1)) * 2048 + (blk & 1) * 1024
+                            : blk * 8 * rowbytes + ls * 128;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(slot + (sblk0 + blk) * 1024), 16,
-                                               voff, blk * 8 * rowbytes + ls * 128, 0, 0);
+                                               w ? voffw : voff, so, 0, 0);
     }
   };
   using I4 = std::integral_constant<int, 4>;
@@ -1196,7 +1223,45 @@ void gemm_dispatch(const void* A, const void* W, void* C, int M, int N, int K, i
   }
 }
 
+// Packs a row-major bf16 [N][K] into the layout of wp_off: one thread per
+// 16-byte unit of the packed weight (unit u: block u / 128 = (panel, K step,
+// 16-row block of the panel), row (u % 128) / 8 of the block, 8 k at (u % 8)
+// * 8); units past N or K are zeros.
+__global__ __launch_bounds__(256) void k_pack_weight(const uint16_t* __restrict__ W,
+                                                     uint16_t* __restrict__ P, int N, int K,
+                                                     int kb, long units) {
+  const long u = (long)blockIdx.x * 256 + threadIdx.x;
+  if (u >= units) return;
+  const long blk = u >> 7;
+  const long pk = blk >> 4;   // panel * kb + K step
+  const int panel = (int)(pk / kb), ks = (int)(pk - (long)panel * kb);
+  const int n = panel * 256 + (int)(blk & 15) * 16 + (int)((u & 127) >> 3);
+  const int k = ks * 64 + (int)(u & 7) * 8;
+  u32x4_t v = {0u, 0u, 0u, 0u};
+  if (n < N && k < K) v = *reinterpret_cast<const u32x4_t*>(W + (long)n * K + k);
+  reinterpret_cast<u32x4_t*>(P)[u] = v;
+}
+
 }  // namespace bi
+
+extern "C" size_t bi_packed_weight_bytes(int N, int K) {
+  if (N < 1 || K < 1) return 0;
+  return (size_t)((K + 63) / 64) * (size_t)((N + 255) / 256) * 32768;
+}
+
+extern "C" bi_status bi_pack_weight(const void* W, void* Wp, int N, int K, bi_stream stream) {
+  using namespace bi;
+  BI_REQUIRE(N >= 1 && K >= 1, BI_ERR_INVALID, "bi_pack_weight: bad shape N=%d K=%d", N, K);
+  BI_REQUIRE(K % 8 == 0, BI_ERR_UNSUPPORTED, "bi_pack_weight: bf16 needs K %% 8 == 0 (K=%d)", K);
+  BI_REQUIRE(W && Wp && aligned16(W) && aligned16(Wp), BI_ERR_INVALID,
+             "bi_pack_weight: null or misaligned pointer");
+  const long units = (long)bi_packed_weight_bytes(N, K) / 16;
+  BI_REQUIRE(units / 256 < 0x7fffffffL, BI_ERR_INVALID, "bi_pack_weight: too large");
+  hipLaunchKernelGGL(k_pack_weight, dim3((unsigned)((units + 255) / 256)), dim3(256), 0,
+                     as_stream(stream), (const uint16_t*)W, (uint16_t*)Wp, N, K, (K + 63) / 64,
+                     units);
+  return launched("bi_pack_weight");
+}
 
 extern "C" bi_status bi_gemm(const void* A, const void* W, void* C, int M, int N, int K,
                              int in_dtype, int out_dtype, bi_stream stream) {

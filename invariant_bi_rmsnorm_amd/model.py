@@ -127,6 +127,19 @@ def init_weights(cfg: ModelConfig, seed: int, device, source: str = "device",
                    lm_head=rnd((cfg.vocab, cfg.d)))
 
 
+def packed_weights(w: Weights) -> Weights:
+    """The same weights with the matrix of every bf16 product (QKV, O,
+    gate/up, down, LM head) in the library's packed layout (bi.h, "Packed
+    weights"): what the engine's GEMMs read.  Norm gains and the embedding
+    table stay as they are; so does the caller's `w`."""
+    layers = [LayerWeights(attn_norm=lw.attn_norm, wqkv=L.pack_weight(lw.wqkv),
+                           wo=L.pack_weight(lw.wo), ffn_norm=lw.ffn_norm,
+                           wgu=L.pack_weight(lw.wgu), wdown=L.pack_weight(lw.wdown))
+              for lw in w.layers]
+    return Weights(embed=w.embed, layers=layers, final_norm=w.final_norm,
+                   lm_head=L.pack_weight(w.lm_head))
+
+
 class KVPool:
     """Paged KV storage for all layers: k, v [layers][pages][h_kv][page][d_h]."""
 
@@ -240,7 +253,9 @@ class Engine:
     def __init__(self, cfg: ModelConfig, weights: Weights, pool: KVPool, device,
                  max_rows: int = 64, max_pages_per_req: int = 512, free: bool = False,
                  mode: str | None = None):
-        self.cfg, self.w, self.pool, self.dev = cfg, weights, pool, device
+        self.cfg, self.pool, self.dev = cfg, pool, device
+        # the GEMMs read bf16 weights packed (fp32 ones row-major)
+        self.w = packed_weights(weights) if cfg.dtype == torch.bfloat16 else weights
         self.mode = mode if mode is not None else ("free" if free else "invariant")
         if self.mode not in self.MODES:
             raise ValueError(f"mode {self.mode!r} not in {self.MODES}")

@@ -347,6 +347,53 @@ def test_gemm_f32_bitwise(M, N, K):
     assert bits_equal(to_np(C), ref), mismatch_report(to_np(C), ref)
 
 
+@pytest.mark.parametrize("N,K", [(300, 72), (256, 64), (17, 8), (513, 136), (6144, 4096)])
+def test_pack_weight_places_every_element(N, K):
+    """bi_pack_weight against the layout the header states, written out on
+    the host: element (n, k) of W at (((n/256) kb + k/64) 16 + (n/16) % 16)
+    1024 + (n % 16) 64 + k % 64 with kb = ceil(K/64), and every other
+    element zero.  Bit patterns differ from element to element, so a swapped
+    pair or a shifted block fails."""
+    g = torch.Generator().manual_seed(N * 7 + K)
+    bits = torch.randint(1, 1 << 14, (N, K), generator=g, dtype=torch.int16)
+    W = bits.view(torch.bfloat16)
+    P = L.pack_weight(W.to(dev()))
+    got = P.data.cpu().view(torch.int16)
+    kb = (K + 63) // 64
+    assert got.numel() * 2 == L.load().bi_packed_weight_bytes(N, K)
+    n = torch.arange(N).view(N, 1)
+    k = torch.arange(K).view(1, K)
+    off = (((n // 256) * kb + k // 64) * 16 + (n // 16) % 16) * 1024 + (n % 16) * 64 + k % 64
+    want = torch.zeros_like(got)
+    want[off.reshape(-1)] = bits.reshape(-1)
+    assert torch.equal(got, want)
+    assert tuple(P.shape) == (N, K) and P.dtype == torch.bfloat16
+
+
+def test_packed_weight_and_row_major_calls_agree():
+    """A PackedWeight made once, the binding's own packing of a row-major
+    weight, and packing plus product on an explicit stream give the same
+    bits."""
+    M, N, K = 9, 700, 264
+    A = synth.normal((M, K), seed=3).to(torch.bfloat16).to(dev())
+    W = (synth.normal((N, K), seed=4) * 0.05).to(torch.bfloat16).to(dev())
+    C1 = torch.empty((M, N), dtype=torch.bfloat16, device=dev())
+    C2, C3 = torch.empty_like(C1), torch.empty_like(C1)
+    L.bi_gemm(A, W, C1)
+    L.bi_gemm(A, L.pack_weight(W), C2)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        P2 = L.pack_weight(W, stream=s)
+        L.bi_gemm(A, P2, C3, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+    assert torch.equal(C1.view(torch.int16), C3.view(torch.int16))
+    with pytest.raises(ValueError, match="PackedWeight"):
+        L.bi_gemm(A, W, C1, stream=s)
+
+
 # ---------------------------------------------------------------------------
 # decode attention + merge
 # ---------------------------------------------------------------------------

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     lib = L.load()
-    assert lib.bi_abi_version() == 2
+    assert lib.bi_abi_version() == 3
     assert lib.bi_status_string(0) == b"ok"
     assert lib.bi_status_string(2) == b"unsupported configuration"
     assert lib.bi_status_string(99) == b"unknown status"
@@ -160,3 +160,23 @@ def test_k_page_layout_helpers():
                         off = (p * H + g) * S * D + ((e // per) * S + t) * per + e % per
                         assert flat[off] == kb[p, g, t, e]
         assert torch.equal(L.k_pool_to_rows(dev).view(it), kb)
+
+
+def test_packed_weight_sizes_and_checks():
+    """bi_packed_weight_bytes counts whole 256-row x 64-k panels steps of
+    32 KiB; bi_pack_weight refuses bad shapes before any launch."""
+    lib = L.load()
+    assert lib.bi_packed_weight_bytes(256, 64) == 32768
+    assert lib.bi_packed_weight_bytes(300, 72) == 2 * 2 * 32768
+    assert lib.bi_packed_weight_bytes(1, 8) == 32768
+    assert lib.bi_packed_weight_bytes(128256, 4096) == 501 * 64 * 32768
+    assert lib.bi_packed_weight_bytes(0, 64) == 0 and lib.bi_packed_weight_bytes(64, 0) == 0
+    fake = ctypes.c_void_p(256)
+    assert lib.bi_pack_weight(fake, fake, 0, 64, None) == L.BI_ERR_INVALID
+    assert lib.bi_pack_weight(fake, fake, 16, 12, None) == L.BI_ERR_UNSUPPORTED
+    assert lib.bi_pack_weight(None, fake, 16, 64, None) == L.BI_ERR_INVALID
+    assert lib.bi_pack_weight(ctypes.c_void_p(258), fake, 16, 64, None) == L.BI_ERR_INVALID
+    assert b"misaligned" in lib.bi_last_error()
+    import torch
+    with pytest.raises(ValueError, match="bf16"):
+        L.pack_weight(torch.zeros((4, 8), dtype=torch.float32))
