@@ -471,8 +471,10 @@ void k_gemm_small(
 #pragma unroll
     for (int j = 0; j < G::JN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // one stage: read every fragment of its (up to) KS K-tiles, then the MFMAs
-  // in ascending K-tile order.  A unit past K enters both operands as zeros.
-  auto stage = [&](const char* aslot, const char* wslot, int st, int nkt) {
+  // in ascending K-tile order.  A unit past K enters both operands as zeros;
+  // a stage that lies wholly below K (`inside`) has no such unit, so it skips
+  // the selects (a compare and 8 v_cndmask per MFMA between dependent MFMAs).
+  auto stage = [&](auto inside, const char* aslot, const char* wslot, int st, int nkt) {
     u32x4_t a[KS][G::IM], b[KS][G::JN];
 #pragma unroll
     for (int kt = 0; kt < KS; ++kt) {
@@ -489,7 +491,7 @@ void k_gemm_small(
 #pragma unroll
     for (int kt = 0; kt < KS; ++kt) {
       if (kt < nkt) {
-        const bool tail = (st * KS + kt) * 32 + 8 * g >= K;
+        const bool tail = !decltype(inside)::value && (st * KS + kt) * 32 + 8 * g >= K;
 #pragma unroll
         for (int i = 0; i < G::IM; ++i) {
           const u32x4_t av = tail ? u32x4_t{0, 0, 0, 0} : a[kt][i];
@@ -508,11 +510,12 @@ void k_gemm_small(
     const int nkt = KT - st * KS;
     if (active) {
       if (nkt >= KS) {
-        stage(aslot, wslot, st, KS);
+        if ((st + 1) * KS * 32 <= K) stage(std::true_type{}, aslot, wslot, st, KS);
+        else stage(std::false_type{}, aslot, wslot, st, KS);
       } else {
 #pragma unroll
         for (int n = 1; n < KS; ++n)
-          if (nkt == n) stage(aslot, wslot, st, n);
+          if (nkt == n) stage(std::false_type{}, aslot, wslot, st, n);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -742,6 +745,8 @@ __global__ __launch_bounds__(kNormThreads) __attribute__((amdgpu_waves_per_eu(4)
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       const char* wslot = smem + ((i * NST + st) % WD) * (NIT * 1024);
       const int nkt = min(KS, KT - st * KS);
+      // a stage wholly below K has no unit past K: no selects
+      const bool inside = (st + 1) * KS * 32 <= K;
       if (wave == 0) {   // half a stage's fragments at a time (registers)
 #pragma unroll
         for (int hf = 0; hf < KS; hf += KS / 2) {
@@ -760,9 +765,13 @@ __global__ __launch_bounds__(kNormThreads) __attribute__((amdgpu_waves_per_eu(4)
           for (int u = 0; u < KS / 2; ++u) {
             const int kt = hf + u;
             if (kt < nkt) {
-              const bool tail = (st * KS + kt) * 32 + 8 * g >= K;
-              acc = mfma(tail ? u32x4_t{0, 0, 0, 0} : av[u],
-                         tail ? u32x4_t{0, 0, 0, 0} : bv[u], acc);
+              if (inside) {
+                acc = mfma(av[u], bv[u], acc);
+              } else {
+                const bool tail = (st * KS + kt) * 32 + 8 * g >= K;
+                acc = mfma(tail ? u32x4_t{0, 0, 0, 0} : av[u],
+                           tail ? u32x4_t{0, 0, 0, 0} : bv[u], acc);
+              }
             }
           }
         }
