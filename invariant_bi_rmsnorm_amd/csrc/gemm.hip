@@ -221,7 +221,11 @@ template <int MB, int CT>
 struct SmallCfg {
   static constexpr int MT = (MB + 1) / 2;                // 16-row tiles
   static constexpr int BLK = MB + 2 * CT;                // 8-row blocks per line
-  static constexpr int LPS0 = 24 / BLK;                  // lines of each row per stage
+  // lines of each row per stage: about 24 KiB a stage, but longer stages
+  // (fewer barriers and fragment waits per K) for the batch-64 tiles
+  static constexpr int LPS0 = MB == 4 && CT == 2   ? 6
+                              : MB == 4 && CT == 3 ? 4
+                                                   : 24 / BLK;
   static constexpr int LPS_MAX = MB == 1 ? 4 : 8;         // MB = 1: registers for two per CU
   static constexpr int LPS = LPS0 < 1 ? 1 : LPS0 > LPS_MAX ? LPS_MAX : LPS0;
   static constexpr int KS = 2 * LPS;                     // K-tiles per stage
@@ -232,7 +236,11 @@ struct SmallCfg {
   // ring) for tiles of 32 rows and 2 strips, the batch-64 O and down
   // projections: measured O 16.8 -> 15.1 us, down 43.4 -> 41.2 us, while
   // tiles of 1, 3 (with the RoPE epilogue) or 8 strips were slower with it
-  static constexpr int AD0 = (MB == 1 ? 24 : MB == 4 && CT == 2 ? 36 : 96) / A_ITEMS;
+  static constexpr int AD0 = (MB == 1                              ? 24
+                              : MB == 4 && CT == 2                 ? 36
+                              : MB == 4 && CT == 3                 ? 48
+                                                                   : 96) /
+                             A_ITEMS;
   static constexpr int AD1 = AD0 < 3 ? 3 : AD0 > 6 ? 6 : AD0;
   static constexpr int AD = AD1 < 1 + 63 / QA ? AD1 : 1 + 63 / QA;   // A ring slots
   static constexpr int A_RING = AD * A_ITEMS * 1024;
