@@ -753,8 +753,6 @@ __global__ __launch_bounds__(kNormThreads) __attribute__((amdgpu_waves_per_eu(4)
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       const char* wslot = smem + ((i * NST + st) % WD) * (NIT * 1024);
       const int nkt = min(KS, KT - st * KS);
-      // a stage wholly below K has no unit past K: no selects
-      const bool inside = (st + 1) * KS * 32 <= K;
       if (wave == 0) {   // half a stage's fragments at a time (registers)
 #pragma unroll
         for (int hf = 0; hf < KS; hf += KS / 2) {
@@ -773,13 +771,9 @@ __global__ __launch_bounds__(kNormThreads) __attribute__((amdgpu_waves_per_eu(4)
           for (int u = 0; u < KS / 2; ++u) {
             const int kt = hf + u;
             if (kt < nkt) {
-              if (inside) {
-                acc = mfma(av[u], bv[u], acc);
-              } else {
-                const bool tail = (st * KS + kt) * 32 + 8 * g >= K;
-                acc = mfma(tail ? u32x4_t{0, 0, 0, 0} : av[u],
-                           tail ? u32x4_t{0, 0, 0, 0} : bv[u], acc);
-              }
+              const bool tail = (st * KS + kt) * 32 + 8 * g >= K;
+              acc = mfma(tail ? u32x4_t{0, 0, 0, 0} : av[u],
+                         tail ? u32x4_t{0, 0, 0, 0} : bv[u], acc);
             }
           }
         }
