@@ -217,7 +217,9 @@ __device__ __forceinline__ void store_rope(const RopeArgs& ra, const f32x4_t& ac
 constexpr int kSmallCopyWaves = 8, kSmallComputeWaves = 4, kSmallGroupWaves = 4;
 constexpr int kSmallThreads = (kSmallCopyWaves + kSmallComputeWaves) * 64;
 
-template <int MB, int CT>
+// L1 (one block of rows in the skinny kernel): stages of up to 16 K-tiles,
+// whose fragments the compute wave reads one K-tile at a time
+template <int MB, int CT, bool L1 = false>
 struct SmallCfg {
   static constexpr int MT = (MB + 1) / 2;                // 16-row tiles
   static constexpr int BLK = MB + 2 * CT;                // 8-row blocks per line
@@ -226,7 +228,7 @@ struct SmallCfg {
   static constexpr int LPS0 = MB == 4 && CT == 2   ? 6
                               : MB == 4 && CT == 3 ? 4
                                                    : 24 / BLK;
-  static constexpr int LPS_MAX = MB == 1 ? 4 : 8;         // MB = 1: registers for two per CU
+  static constexpr int LPS_MAX = MB == 1 && !L1 ? 4 : 8;   // MB = 1: registers for two per CU
   static constexpr int LPS = LPS0 < 1 ? 1 : LPS0 > LPS_MAX ? LPS_MAX : LPS0;
   static constexpr int KS = 2 * LPS;                     // K-tiles per stage
   static constexpr int A_ITEMS = MB * LPS, W_ITEMS = 2 * CT * LPS;   // KiB per stage
@@ -420,7 +422,7 @@ __global__ __launch_bounds__(kSmallThreads) __attribute__((amdgpu_waves_per_eu(M
 void k_gemm_small(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W, void* C, int M, int N,
     int Ktot, int kslice, RopeArgs ra) {
-  using G = SmallCfg<MB, CT>;
+  using G = SmallCfg<MB, CT, MB == 1>;
   constexpr int KS = G::KS, LPS = G::LPS, MT = G::MT;
   // K slice of this workgroup (all of K on the invariant path; the split-K
   // twin launches several along y).  Rows keep stride Ktot.
@@ -483,6 +485,31 @@ void k_gemm_small(
   // a stage that lies wholly below K (`inside`) has no such unit, so it skips
   // the selects (a compare and 8 v_cndmask per MFMA between dependent MFMAs).
   auto stage = [&](auto inside, const char* aslot, const char* wslot, int st, int nkt) {
+    if constexpr (MB == 1) {
+      // one chain per wave and long stages: one K-tile's fragments at a time
+#pragma unroll
+      for (int kt = 0; kt < KS; ++kt) {
+        if (kt < nkt) {
+          const uint32_t off = (kt & 1) ? off1 : off0;
+          const char* abase = aslot + (kt >> 1) * (MB * 1024) + off;
+          const char* wbase = wslot + (kt >> 1) * (2 * CT * 1024) + off;
+          u32x4_t a1[G::IM], b1[G::JN];
+#pragma unroll
+          for (int i = 0; i < G::IM; ++i) a1[i] = *reinterpret_cast<const u32x4_t*>(abase + aoff[i]);
+#pragma unroll
+          for (int j = 0; j < G::JN; ++j) b1[j] = *reinterpret_cast<const u32x4_t*>(wbase + boff[j]);
+          const bool tail = !decltype(inside)::value && (st * KS + kt) * 32 + 8 * g >= K;
+#pragma unroll
+          for (int i = 0; i < G::IM; ++i) {
+            const u32x4_t av = tail ? u32x4_t{0, 0, 0, 0} : a1[i];
+#pragma unroll
+            for (int j = 0; j < G::JN; ++j)
+              acc[i][j] = mfma(av, tail ? u32x4_t{0, 0, 0, 0} : b1[j], acc[i][j]);
+          }
+        }
+      }
+      return;
+    }
     u32x4_t a[KS][G::IM], b[KS][G::JN];
 #pragma unroll
     for (int kt = 0; kt < KS; ++kt) {
@@ -898,7 +925,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(const float* __restrict__ A,
 template <int MB, int CT, int OUTF32>
 static void launch_small_k(const void* A, const void* W, void* C, int M, int N, int K,
                            hipStream_t s, int splits, int kslice, const RopeArgs& ra) {
-  constexpr int lds = SmallCfg<MB, CT>::LDS;
+  constexpr int lds = SmallCfg<MB, CT, MB == 1>::LDS;
   static bool attr = false;
   if (!attr) {
     (void)hipFuncSetAttribute((const void*)k_gemm_small<MB, CT, OUTF32>,
