@@ -62,7 +62,8 @@ typedef int bi_status;
 
 typedef void *bi_stream; /* hipStream_t */
 
-/* Version of this ABI (changes when a signature changes). */
+/* Version of this ABI: changes when a signature or the layout an argument
+ * must have changes (3: bf16 product weights in the packed layout below). */
 int bi_abi_version(void);
 /* Static text for a status code. */
 const char *bi_status_string(bi_status s);
